@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for the AlexNet path.
+
+This module only draws numbers: images, weights, labels and source images for
+the ten-view batch.  It performs none of the network's arithmetic, so both the
+HIP library's callers and the CPU oracle can take their inputs from here.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
+  1. images  x ~ N(0, 1), float32, shape [N, 3, S, S]  (S = 227, or 256 for
+     ten-view sources);
+  2. for each learned layer in order conv1..conv5, fc6..fc8: weights
+     ~ N(0, 1) * sqrt(2 / fan_in), float32 (He), fan_in = (Cin/G)*k*k or
+     in_features.  Biases are constants: 1 for conv2, conv4, conv5 and the
+     three FC layers, 0 for conv1 and conv3 (the paper's rule for which layers
+     start at 1; the fermi.ai wiki lists "the FC layers" among them);
+  3. labels uniform in [0, 1000), int32, shape [N].
+
+bf16 values are produced from float32 by round-to-nearest-even on the bit
+pattern; the float32 copy of a bf16 tensor holds exactly the bf16 value.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+# Parameter shapes only (name, Cin, Cout, kernel, grouped-in-two-tower-net);
+# strides and paddings belong to the network code, not to the input draw.
+CONV_SHAPES = (
+    ("conv1", 3, 96, 11, False),
+    ("conv2", 96, 256, 5, True),
+    ("conv3", 256, 384, 3, False),
+    ("conv4", 384, 384, 3, True),
+    ("conv5", 384, 256, 3, True),
+)
+FC_SHAPES = (("fc6", 9216, 4096), ("fc7", 4096, 4096), ("fc8", 4096, 1000))
+BIAS_ONE = {"conv2", "conv4", "conv5", "fc6", "fc7", "fc8"}
+
+IMAGE = 227
+SOURCE = 256
+CLASSES = 1000
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 array holding exactly the bf16-rounded values of ``a``."""
+    return bf16_to_f32(bf16_bits(a))
+
+
+def weight_shapes(groups: int = 1):
+    """Shapes of the 16 parameter tensors, conv weights OIHW, FC [out][in]."""
+    shapes = []
+    for name, cin, cout, k, grouped in CONV_SHAPES:
+        g = groups if grouped else 1
+        shapes.append((name, (cout, cin // g, k, k), (cout,)))
+    for name, fin, fout in FC_SHAPES:
+        shapes.append((name, (fout, fin), (fout,)))
+    return shapes
+
+
+@dataclass
+class Synthetic:
+    seed: int
+    groups: int
+    bf16: bool
+    x: np.ndarray                      # float32 (bf16-exact when bf16)
+    weights: List[np.ndarray]          # 8 float32 weight tensors (bf16-exact when bf16)
+    biases: List[np.ndarray]           # 8 float32 bias vectors
+    master_w: List[np.ndarray]         # unrounded float32 weights (fp32 master copy)
+    labels: np.ndarray                 # int32 [N]
+    names: List[str] = field(default_factory=list)
+
+    def x_bits(self) -> np.ndarray:
+        return bf16_bits(self.x)
+
+
+def synthetic(seed: int, batch: int, groups: int = 1, bf16: bool = True,
+              image: int = IMAGE, with_labels: bool = True) -> Synthetic:
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, 3, image, image), dtype=np.float32)
+    ws, bs, masters, names = [], [], [], []
+    for name, wshape, bshape in weight_shapes(groups):
+        fan_in = int(np.prod(wshape[1:]))
+        w = rng.standard_normal(wshape, dtype=np.float32) * np.float32(np.sqrt(2.0 / fan_in))
+        w = w.astype(np.float32)
+        b = np.full(bshape, 1.0 if name in BIAS_ONE else 0.0, dtype=np.float32)
+        masters.append(w)
+        ws.append(round_bf16(w) if bf16 else w)
+        bs.append(b)
+        names.append(name)
+    labels = (rng.integers(0, CLASSES, size=batch, dtype=np.int32)
+              if with_labels else np.zeros(batch, np.int32))
+    if bf16:
+        x = round_bf16(x)
+    return Synthetic(seed, groups, bf16, x, ws, bs, masters, labels, names)
+
+
+# The five workloads: (seed, batch, groups, bf16, mode)
+CONFIGS = {
+    1: dict(seed=0, batch=1, groups=1, bf16=False, mode="forward"),
+    2: dict(seed=1, batch=128, groups=1, bf16=True, mode="forward"),
+    3: dict(seed=2, batch=128, groups=2, bf16=True, mode="forward"),
+    4: dict(seed=3, batch=128, groups=1, bf16=True, mode="train"),
+    5: dict(seed=4, batch=256, groups=1, bf16=True, mode="tenview"),
+}
+
+TRAIN_HYPER = dict(lr=0.01, momentum=0.9, weight_decay=5e-4, dropout_seed=3, step=0)
+
+
+def config_inputs(cfg: int, batch: Optional[int] = None) -> Synthetic:
+    c = CONFIGS[cfg]
+    n = c["batch"] if batch is None else batch
+    image = SOURCE if c["mode"] == "tenview" else IMAGE
+    return synthetic(c["seed"], n, c["groups"], c["bf16"], image=image)
