@@ -1,0 +1,169 @@
+"""ctypes binding of libalexnet.so: one Python function per C entry point, same
+names, argument marshalling only.  Device buffers are passed as integer
+addresses (``tensor.data_ptr()``) and streams as ``hipStream_t`` handles
+(``torch.cuda.current_stream().cuda_stream``).
+
+Importing this module does not need a GPU; loading fails loudly if the
+library has not been built (``python -m deep_cnn_image_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libalexnet.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WORKSPACE, E_ALIGN, E_DEVICE, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, BF16, U8 = 0, 1, 2
+MODE_FORWARD, MODE_TRAIN, MODE_TENVIEW = 0, 1, 2
+
+EXPORTED = (
+    "alexnet_default_cfg", "alexnet_workspace_bytes", "alexnet_forward", "alexnet_forward_tenview",
+    "alexnet_train_step", "alexnet_cast_weights", "alexnet_dropout_mask", "alexnet_tap",
+    "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string",
+)
+
+
+class Cfg(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("groups", C.c_int32), ("dtype", C.c_int32),
+                ("lrn_n", C.c_int32), ("lrn_k", C.c_float), ("lrn_alpha", C.c_float),
+                ("lrn_beta", C.c_float), ("dropout_p", C.c_float)]
+
+
+class AlexNetError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+_PTR16 = C.c_void_p * 16
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m deep_cnn_image_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    vp, cfgp = C.c_void_p, C.POINTER(Cfg)
+    L.alexnet_default_cfg.argtypes = [cfgp, C.c_int32, C.c_int32, C.c_int32]
+    L.alexnet_default_cfg.restype = None
+    L.alexnet_workspace_bytes.argtypes = [cfgp, C.c_int]
+    L.alexnet_workspace_bytes.restype = C.c_size_t
+    L.alexnet_forward.argtypes = [cfgp, _PTR16, vp, vp, vp, C.c_size_t, vp]
+    L.alexnet_forward.restype = C.c_int
+    L.alexnet_forward_tenview.argtypes = [cfgp, _PTR16, vp, vp, vp, C.c_size_t, vp]
+    L.alexnet_forward_tenview.restype = C.c_int
+    L.alexnet_train_step.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, vp, C.c_float, C.c_float,
+                                     C.c_float, C.c_uint64, C.c_uint64, vp, vp, vp, C.c_size_t, vp]
+    L.alexnet_train_step.restype = C.c_int
+    L.alexnet_cast_weights.argtypes = [cfgp, _PTR16, _PTR16, vp]
+    L.alexnet_cast_weights.restype = C.c_int
+    L.alexnet_dropout_mask.argtypes = [C.c_uint64, C.c_uint64, C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_float, vp, vp]
+    L.alexnet_dropout_mask.restype = C.c_int
+    L.alexnet_tap.argtypes = [cfgp, C.c_int, C.c_int, C.POINTER(C.c_size_t), C.POINTER(C.c_int64),
+                              C.POINTER(C.c_int), C.POINTER(C.c_int)]
+    L.alexnet_tap.restype = C.c_int
+    L.alexnet_tap_count.argtypes = []
+    L.alexnet_tap_count.restype = C.c_int
+    L.alexnet_tap_name.argtypes = [C.c_int]
+    L.alexnet_tap_name.restype = C.c_char_p
+    L.alexnet_status_string.argtypes = [C.c_int]
+    L.alexnet_status_string.restype = C.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _ptr16(xs: Sequence) -> "C.Array":
+    if len(xs) != 16:
+        raise ValueError("expected 16 tensors (w1, b1, ..., w8, b8)")
+    return _PTR16(*[_ptr(t) or None for t in xs])
+
+
+def _check(status: int, where: str) -> int:
+    if status != OK:
+        raise AlexNetError(status, where)
+    return status
+
+
+def status_string(status: int) -> str:
+    return lib().alexnet_status_string(status).decode()
+
+
+def alexnet_default_cfg(batch: int, groups: int = 1, dtype: int = BF16) -> Cfg:
+    cfg = Cfg()
+    lib().alexnet_default_cfg(C.byref(cfg), batch, groups, dtype)
+    return cfg
+
+
+def alexnet_workspace_bytes(cfg: Cfg, mode: int) -> int:
+    return int(lib().alexnet_workspace_bytes(C.byref(cfg), mode))
+
+
+def alexnet_forward(cfg, params, x, probs, ws, ws_bytes, stream=0, check=True) -> int:
+    s = lib().alexnet_forward(C.byref(cfg), _ptr16(params), _ptr(x) or None, _ptr(probs) or None,
+                              _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
+    return _check(s, "alexnet_forward") if check else s
+
+
+def alexnet_forward_tenview(cfg, params, src, probs, ws, ws_bytes, stream=0, check=True) -> int:
+    s = lib().alexnet_forward_tenview(C.byref(cfg), _ptr16(params), _ptr(src) or None,
+                                      _ptr(probs) or None, _ptr(ws) or None, ws_bytes,
+                                      _ptr(stream) or None)
+    return _check(s, "alexnet_forward_tenview") if check else s
+
+
+def alexnet_train_step(cfg, master, momentum, work, x, labels, lr, momentum_coef, weight_decay,
+                       seed, step, loss, probs, ws, ws_bytes, stream=0, check=True) -> int:
+    s = lib().alexnet_train_step(C.byref(cfg), _ptr16(master), _ptr16(momentum), _ptr16(work),
+                                 _ptr(x) or None, _ptr(labels) or None, lr, momentum_coef,
+                                 weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None,
+                                 _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
+    return _check(s, "alexnet_train_step") if check else s
+
+
+def alexnet_cast_weights(cfg, master, work, stream=0, check=True) -> int:
+    s = lib().alexnet_cast_weights(C.byref(cfg), _ptr16(master), _ptr16(work), _ptr(stream) or None)
+    return _check(s, "alexnet_cast_weights") if check else s
+
+
+def alexnet_dropout_mask(seed, step, layer, rows, cols, p, mask, stream=0, check=True) -> int:
+    s = lib().alexnet_dropout_mask(seed, step, layer, rows, cols, p, _ptr(mask) or None,
+                                   _ptr(stream) or None)
+    return _check(s, "alexnet_dropout_mask") if check else s
+
+
+def alexnet_tap(cfg, mode: int, tap_id: int):
+    """(byte offset, shape tuple, dtype, layout) of a workspace tap."""
+    off = C.c_size_t()
+    shape = (C.c_int64 * 4)()
+    dt, lay = C.c_int(), C.c_int()
+    _check(lib().alexnet_tap(C.byref(cfg), mode, tap_id, C.byref(off), shape, C.byref(dt),
+                             C.byref(lay)), "alexnet_tap")
+    return off.value, tuple(shape), dt.value, lay.value
+
+
+def alexnet_tap_count() -> int:
+    return int(lib().alexnet_tap_count())
+
+
+def alexnet_tap_name(tap_id: int):
+    r = lib().alexnet_tap_name(tap_id)
+    return None if r is None else r.decode()
+
+
+def tap_ids() -> dict:
+    return {alexnet_tap_name(i): i for i in range(alexnet_tap_count())}

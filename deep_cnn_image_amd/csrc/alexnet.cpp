@@ -1,0 +1,349 @@
+// C ABI of the AlexNet library: argument validation (host only), the
+// workspace plan, and the launch sequences of the forward pass, the ten-view
+// forward pass and the training step.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/alexnet.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace ax;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ALEXNET_E_HIP;
+  if (dev < 0 || dev >= 64) return ALEXNET_E_DEVICE;
+  int s = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ALEXNET_E_HIP;
+    s = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? ALEXNET_OK : ALEXNET_E_DEVICE;
+}
+
+int check_params(const void* const* params, int n) {
+  if (!params) return ALEXNET_E_NULL;
+  for (int i = 0; i < n; ++i) {
+    if (!params[i]) return ALEXNET_E_NULL;
+    if (!aligned(params[i], 16)) return ALEXNET_E_ALIGN;
+  }
+  return ALEXNET_OK;
+}
+
+inline char* at(void* ws, const Buf& b) { return (char*)ws + b.off; }
+inline char* tp(void* ws, const Plan& p, int id) { return (char*)ws + p.tap[id].buf.off; }
+
+#define HIPCHK(x)                                  \
+  do {                                             \
+    if ((x) != hipSuccess) return ALEXNET_E_HIP;   \
+  } while (0)
+
+// Forward pass.  train: dropout masks of (seed, step); else the 1 - p scale.
+// src_hw: 227 (images) or 256 (ten-view sources).
+int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* ws, bool train,
+                    uint64_t seed, uint64_t step, hipStream_t st) {
+  const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
+  const Net& net = p.net;
+  const int N = p.N;
+  const alexnet_cfg& c = p.cfg;
+
+  // weights into the layouts the GEMM loaders read
+  HIPCHK(w_pad_rows(dt, prm[0], at(ws, p.w1p), 96, 363, 384, st));
+  for (int i = 1; i < 5; ++i) {
+    const ConvShape& s = net.conv[i];
+    HIPCHK(w_khwc(dt, prm[2 * i], at(ws, p.wr[i]), s.Cout, s.Cin / s.groups, s.K, st));
+  }
+
+  const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
+  const int hs = tenview ? 256 : 227;
+  HIPCHK(conv1_fwd(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.w1p), prm[1], tp(ws, p, T_CONV1), st));
+  HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_LRN1), (int64_t)N * 55 * 55, 96, c.lrn_k, c.lrn_alpha,
+                 c.lrn_beta, c.lrn_n, st));
+  HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1), N, 55, 55, 96, 0,
+                  st));
+  HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), st));
+  HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_LRN2), (int64_t)N * 27 * 27, 256, c.lrn_k,
+                 c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
+  HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN2), tp(ws, p, T_POOL2), (uint8_t*)tp(ws, p, T_ARG2), N, 27, 27, 256, 0,
+                  st));
+  HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), st));
+  HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), st));
+  HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), st));
+  HIPCHK(pool_fwd(dt, tp(ws, p, T_CONV5), tp(ws, p, T_POOL5), (uint8_t*)tp(ws, p, T_ARG5), N, 13, 13, 256, 1,
+                  st));
+
+  FcEpi ep{};
+  ep.relu = 1;
+  if (train) {
+    ep.drop = 1;
+    ep.thresh = (uint32_t)floor((double)c.dropout_p * 4294967296.0);
+    ep.seed = seed;
+    ep.step = step;
+  } else {
+    ep.drop = 2;
+    ep.scale = 1.f - c.dropout_p;
+  }
+  float* part = (float*)at(ws, p.part);
+  ep.layer = 0;
+  HIPCHK(fc_fwd(dt, N, 9216, 4096, tp(ws, p, T_POOL5), prm[10], prm[11], ep, tp(ws, p, T_DROP6), nullptr,
+                part, p.part_bytes, st));
+  ep.layer = 1;
+  HIPCHK(fc_fwd(dt, N, 4096, 4096, tp(ws, p, T_DROP6), prm[12], prm[13], ep, tp(ws, p, T_DROP7), nullptr,
+                part, p.part_bytes, st));
+  FcEpi lin{};
+  HIPCHK(fc_fwd(dt, N, 4096, 1000, tp(ws, p, T_DROP7), prm[14], prm[15], lin, nullptr,
+                (float*)tp(ws, p, T_LOGITS), part, p.part_bytes, st));
+  return ALEXNET_OK;
+}
+
+int enqueue_backward(const Plan& p, void* const* work, const void* x, void* ws, hipStream_t st) {
+  const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
+  const Net& net = p.net;
+  const int N = p.N;
+  const alexnet_cfg& c = p.cfg;
+  float* part = (float*)at(ws, p.part);
+  float* cs = (float*)at(ws, p.colsum);
+  auto gw = [&](int i) { return (float*)tp(ws, p, T_GW1 + i); };
+  auto gb = [&](int i) { return (float*)tp(ws, p, T_GB1 + i); };
+
+  for (int i = 1; i < 5; ++i) {
+    const ConvShape& s = net.conv[i];
+    HIPCHK(w_dgrad(dt, work[2 * i], at(ws, p.wt[i]), s.groups, s.Cout / s.groups, s.Cin / s.groups, s.K, st));
+  }
+  // FC8: dh7 = dz W8 * [drop7 > 0]   (drop7 > 0 <=> kept and ReLU active)
+  HIPCHK(fc_dgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), work[14], tp(ws, p, T_DROP7), tp(ws, p, T_DFC7),
+                  part, p.part_bytes, st));
+  HIPCHK(fc_wgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), gw(7), st));
+  HIPCHK(colsum(dt, tp(ws, p, T_DLOGITS), N, 1000, gb(7), cs, st));
+  // FC7
+  HIPCHK(fc_dgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), work[12], tp(ws, p, T_DROP6), tp(ws, p, T_DFC6),
+                  part, p.part_bytes, st));
+  HIPCHK(fc_wgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), gw(6), st));
+  HIPCHK(colsum(dt, tp(ws, p, T_DFC7), N, 4096, gb(6), cs, st));
+  // FC6 -> gradient w.r.t. the flattened pool5 output
+  HIPCHK(fc_dgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), work[10], nullptr, tp(ws, p, T_DFLAT), part,
+                  p.part_bytes, st));
+  HIPCHK(fc_wgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), gw(5), st));
+  HIPCHK(colsum(dt, tp(ws, p, T_DFC6), N, 4096, gb(5), cs, st));
+  // pool5 backward * ReLU5'
+  HIPCHK(pool_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
+                  tp(ws, p, T_DCONV5), N, 13, 13, 256, 1, st));
+  // conv5, conv4, conv3
+  const int din[5] = {-1, T_DIN2, T_DIN3, T_DCONV3, T_DCONV4};
+  const int dz[5] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5};
+  const int xin[5] = {-1, T_POOL1, T_POOL2, T_CONV3, T_CONV4};
+  const int mask[5] = {-1, -1, -1, T_CONV3, T_CONV4};
+  for (int i = 4; i >= 2; --i) {
+    const ConvShape& s = net.conv[i];
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), st));
+    HIPCHK(colsum(dt, tp(ws, p, dz[i]), (int64_t)N * s.Ho * s.Wo, s.Cout, gb(i), cs, st));
+    HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
+                      tp(ws, p, din[i]), st));
+  }
+  // pool2 -> LRN2 -> ReLU2
+  HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), nullptr, tp(ws, p, T_DLRN2), N,
+                  27, 27, 256, 0, st));
+  HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_DLRN2), tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256,
+                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
+  {
+    const ConvShape& s = net.conv[1];
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st));
+    HIPCHK(colsum(dt, tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256, gb(1), cs, st));
+    HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st));
+  }
+  // pool1 -> LRN1 -> ReLU1, then layer-1 weight gradient (no input gradient)
+  HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), nullptr, tp(ws, p, T_DLRN1), N,
+                  55, 55, 96, 0, st));
+  HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_DLRN1), tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96,
+                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
+  HIPCHK(conv1_wgrad(dt, N, 227, 227, tp(ws, p, T_DCONV1), x, part, p.part_bytes, gw(0), st));
+  HIPCHK(colsum(dt, tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96, gb(0), cs, st));
+  return ALEXNET_OK;
+}
+
+int prepare(const alexnet_cfg* cfg, int mode, void* ws, size_t ws_bytes, Plan* p) {
+  int r = make_plan(cfg, mode, p);
+  if (r != ALEXNET_OK) return r;
+  if (!ws) return ALEXNET_E_NULL;
+  if (!aligned(ws, 256)) return ALEXNET_E_ALIGN;
+  if (ws_bytes < p->total) return ALEXNET_E_WORKSPACE;
+  return ALEXNET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void alexnet_default_cfg(alexnet_cfg* cfg, int32_t batch, int32_t groups, int32_t dtype) {
+  if (!cfg) return;
+  cfg->batch = batch;
+  cfg->groups = groups;
+  cfg->dtype = dtype;
+  cfg->lrn_n = 5;
+  cfg->lrn_k = 2.f;
+  cfg->lrn_alpha = 1e-4f;
+  cfg->lrn_beta = 0.75f;
+  cfg->dropout_p = 0.5f;
+}
+
+size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode) {
+  Plan p;
+  return make_plan(cfg, mode, &p) == ALEXNET_OK ? p.total : 0;
+}
+
+int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x, float* probs,
+                    void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int r = prepare(cfg, ALEXNET_MODE_FORWARD, ws, ws_bytes, &p);
+  if (r != ALEXNET_OK) return r;
+  if ((r = check_params(params, 16)) != ALEXNET_OK) return r;
+  if (!x || !probs) return ALEXNET_E_NULL;
+  if (!aligned(x, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  if ((r = enqueue_forward(p, params, x, ws, false, 0, 0, st)) != ALEXNET_OK) return r;
+  if (softmax((const float*)tp(ws, p, T_LOGITS), probs, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
+  return ALEXNET_OK;
+}
+
+int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16], const void* src,
+                            float* probs, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int r = prepare(cfg, ALEXNET_MODE_TENVIEW, ws, ws_bytes, &p);
+  if (r != ALEXNET_OK) return r;
+  if ((r = check_params(params, 16)) != ALEXNET_OK) return r;
+  if (!src || !probs) return ALEXNET_E_NULL;
+  if (!aligned(src, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  if ((r = enqueue_forward(p, params, src, ws, false, 0, 0, st)) != ALEXNET_OK) return r;
+  float* vp = (float*)tp(ws, p, T_VIEWPROBS);
+  if (softmax((const float*)tp(ws, p, T_LOGITS), vp, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
+  if (view_mean(vp, probs, cfg->batch, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
+  return ALEXNET_OK;
+}
+
+int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                       void* const work[16], const void* x, const int32_t* labels, float lr,
+                       float momentum_coef, float weight_decay, uint64_t seed, uint64_t step, float* loss,
+                       float* probs, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int r = prepare(cfg, ALEXNET_MODE_TRAIN, ws, ws_bytes, &p);
+  if (r != ALEXNET_OK) return r;
+  if ((r = check_params((const void* const*)master, 16)) != ALEXNET_OK) return r;
+  if ((r = check_params((const void* const*)momentum, 16)) != ALEXNET_OK) return r;
+  if ((r = check_params((const void* const*)work, 16)) != ALEXNET_OK) return r;
+  if (!x || !labels || !loss) return ALEXNET_E_NULL;
+  if (!aligned(x, 16) || !aligned(labels, 4) || !aligned(loss, 4)) return ALEXNET_E_ALIGN;
+  if (probs && !aligned(probs, 16)) return ALEXNET_E_ALIGN;
+  if (!isfinite(lr) || !isfinite(momentum_coef) || !isfinite(weight_decay)) return ALEXNET_E_ARG;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  hipStream_t st = (hipStream_t)stream;
+  const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
+  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st)) != ALEXNET_OK) return r;
+  if (softmax_ce(dt, (const float*)tp(ws, p, T_LOGITS), labels, probs, tp(ws, p, T_DLOGITS),
+                 (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
+    return ALEXNET_E_HIP;
+  if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
+  if ((r = enqueue_backward(p, work, x, ws, st)) != ALEXNET_OK) return r;
+  TensorSet ts;
+  for (int i = 0; i < 8; ++i) {
+    ts.master[2 * i] = master[2 * i];
+    ts.master[2 * i + 1] = master[2 * i + 1];
+    ts.mom[2 * i] = momentum[2 * i];
+    ts.mom[2 * i + 1] = momentum[2 * i + 1];
+    ts.grad[2 * i] = (const float*)tp(ws, p, T_GW1 + i);
+    ts.grad[2 * i + 1] = (const float*)tp(ws, p, T_GB1 + i);
+    ts.work[2 * i] = work[2 * i];
+    ts.work[2 * i + 1] = work[2 * i + 1];
+    ts.n[2 * i] = p.net.wcount[i];
+    ts.n[2 * i + 1] = p.net.bcount[i];
+  }
+  if (sgd(dt, ts, lr, momentum_coef, weight_decay, st) != hipSuccess) return ALEXNET_E_HIP;
+  return ALEXNET_OK;
+}
+
+int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* const work[16], void* stream) {
+  Plan p;
+  int r = make_plan(cfg, ALEXNET_MODE_FORWARD, &p);
+  if (r != ALEXNET_OK) return r;
+  if ((r = check_params((const void* const*)master, 16)) != ALEXNET_OK) return r;
+  if ((r = check_params((const void* const*)work, 16)) != ALEXNET_OK) return r;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  TensorSet ts;
+  for (int i = 0; i < 8; ++i) {
+    ts.master[2 * i] = master[2 * i];
+    ts.master[2 * i + 1] = master[2 * i + 1];
+    ts.mom[2 * i] = ts.mom[2 * i + 1] = nullptr;
+    ts.grad[2 * i] = ts.grad[2 * i + 1] = nullptr;
+    ts.work[2 * i] = work[2 * i];
+    ts.work[2 * i + 1] = work[2 * i + 1];
+    ts.n[2 * i] = p.net.wcount[i];
+    ts.n[2 * i + 1] = p.net.bcount[i];
+  }
+  const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
+  return cast_weights(dt, ts, (hipStream_t)stream) == hipSuccess ? ALEXNET_OK : ALEXNET_E_HIP;
+}
+
+int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t rows, int32_t cols, float p,
+                         uint8_t* mask, void* stream) {
+  if (!mask) return ALEXNET_E_NULL;
+  if (rows < 0 || cols < 0 || cols % 4 != 0 || layer < 0) return ALEXNET_E_SHAPE;
+  if (!aligned(mask, 4)) return ALEXNET_E_ALIGN;
+  if (!(p >= 0.f && p < 1.f)) return ALEXNET_E_ARG;
+  if ((int64_t)rows * cols == 0) return ALEXNET_OK;
+  int r = check_device();
+  if (r != ALEXNET_OK) return r;
+  const uint32_t thresh = (uint32_t)floor((double)p * 4294967296.0);
+  return ax::dropout_mask(seed, step, layer, rows, cols, thresh, mask, (hipStream_t)stream) == hipSuccess
+             ? ALEXNET_OK
+             : ALEXNET_E_HIP;
+}
+
+int alexnet_tap(const alexnet_cfg* cfg, int mode, int tap_id, size_t* offset, int64_t shape[4], int* dtype,
+                int* layout) {
+  if (!offset || !shape || !dtype || !layout) return ALEXNET_E_NULL;
+  Plan p;
+  int r = make_plan(cfg, mode, &p);
+  if (r != ALEXNET_OK) return r;
+  if (tap_id < 0 || tap_id >= T_COUNT || !p.tap[tap_id].present) return ALEXNET_E_ARG;
+  const TapDesc& t = p.tap[tap_id];
+  *offset = t.buf.off;
+  for (int i = 0; i < 4; ++i) shape[i] = t.shape[i];
+  *dtype = t.dtype;
+  *layout = t.layout;
+  return ALEXNET_OK;
+}
+
+int alexnet_tap_count(void) { return T_COUNT; }
+const char* alexnet_tap_name(int tap_id) { return tap_name(tap_id); }
+
+const char* alexnet_status_string(int s) {
+  switch (s) {
+    case ALEXNET_OK: return "ok";
+    case ALEXNET_E_NULL: return "null pointer";
+    case ALEXNET_E_SHAPE: return "batch or groups out of range";
+    case ALEXNET_E_DTYPE: return "unsupported dtype";
+    case ALEXNET_E_WORKSPACE: return "workspace too small";
+    case ALEXNET_E_ALIGN: return "misaligned pointer";
+    case ALEXNET_E_DEVICE: return "device is not gfx950";
+    case ALEXNET_E_HIP: return "HIP error while enqueueing";
+    case ALEXNET_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,836 @@
+// AlexNet kernels for gfx950 and their launchers.
+//
+// Dense contractions go through the MFMA GEMM core in gemm.hpp.  The rest are
+// bandwidth-bound kernels over NHWC activations: each thread owns one pixel
+// and a run of 8 consecutive channels, so every global access is a 16-byte
+// (bf16) or 2x16-byte (fp32) vector access and a wavefront covers contiguous
+// memory.
+#include "common.hpp"
+#include "gemm.hpp"
+#include "launch.hpp"
+
+namespace ax {
+
+static constexpr int TPB = 256;
+
+static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
+
+// =========================================================================
+// GEMM launches
+// =========================================================================
+template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP>
+static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
+                           int splits, hipStream_t st) {
+  GemmGrid gg;
+  gg.M = M; gg.N = N; gg.K = K;
+  gg.tiles_m = cdiv(M, BM);
+  gg.tiles_n = cdiv(N, BN);
+  const int kt = cdiv(K, BK);
+  gg.splits = eff_splits(K, splits);
+  gg.kt_per_split = cdiv(kt, gg.splits);
+  dim3 grid(gg.tiles_m * gg.tiles_n, 1, groups * gg.splits);
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP>), grid, dim3(NTHREADS), 0, st, al, bl,
+                     ep, gg);
+  return hipGetLastError();
+}
+
+// ---- layer 1 forward: NCHW images -> NHWC [N][55][55][96]
+template <typename T>
+static hipError_t conv1_fwd_t(const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
+                              const void* b1, void* y, hipStream_t st) {
+  constexpr int BM = 128, BN = 96;
+  LdConv1<T, BM> a;
+  a.p = (const T*)x; a.src = Conv1Src{Hs, Ws, tenview, 227}; a.M = Nimg * 3025;
+  LdKC<T, BN> b;
+  b.p = (const T*)w1p; b.ld = 384; b.rows = 96; b.K = 384; b.gstride = 0;
+  EpBiasRelu<T> e;
+  e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
+  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, 384, 1, 1, st);
+}
+
+hipError_t conv1_fwd(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
+                     const void* b1, void* y, hipStream_t st) {
+  return dt == BF16 ? conv1_fwd_t<bf16>(x, Hs, Ws, tenview, Nimg, w1p, b1, y, st)
+                    : conv1_fwd_t<float>(x, Hs, Ws, tenview, Nimg, w1p, b1, y, st);
+}
+
+// Picks the n-tile for an output width N: 128 when it divides, else 96, else
+// 48 (four waves stacked along m), else 128 with a ragged last tile.
+template <typename T, class Fn>
+static hipError_t by_bn(int N, Fn&& fn) {
+  if (N % 128 == 0) return fn.template operator()<128, 2, 2>();
+  if (N % 96 == 0) return fn.template operator()<96, 2, 2>();
+  if (N % 48 == 0 && N <= 96) return fn.template operator()<48, 4, 1>();
+  return fn.template operator()<128, 2, 2>();
+}
+
+template <typename T>
+struct ConvFwdFn {
+  ConvShape s; const void* x; const void* wr; const void* b; void* y; hipStream_t st;
+  template <int BN, int WGM, int WGN>
+  hipError_t operator()() const {
+    constexpr int BM = 128;
+    const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
+    LdIm2col<T, BM> a;
+    a.p = (const T*)x;
+    a.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
+    a.M = s.Nimg * s.Ho * s.Wo;
+    a.K = s.K * s.K * Cig;
+    LdKC<T, BN> bl;
+    bl.p = (const T*)wr; bl.ld = a.K; bl.rows = Cog; bl.K = a.K; bl.gstride = (int64_t)Cog * a.K;
+    EpBiasRelu<T> e;
+    e.out = (T*)y; e.bias = (const T*)b; e.ldo = s.Cout; e.M = a.M; e.N = Cog;
+    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cog, a.K, s.groups, 1, st);
+  }
+};
+
+hipError_t conv_fwd(DType dt, const ConvShape& s, const void* x, const void* wr, const void* b, void* y,
+                    hipStream_t st) {
+  const int Cog = s.Cout / s.groups;
+  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st}; return by_bn<bf16>(Cog, f); }
+  ConvFwdFn<float> f{s, x, wr, b, y, st};
+  return by_bn<float>(Cog, f);
+}
+
+template <typename T>
+struct ConvDgradFn {
+  ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; hipStream_t st;
+  template <int BN, int WGM, int WGN>
+  hipError_t operator()() const {
+    constexpr int BM = 128;
+    const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
+    // dX = stride-1 convolution of dY with flipped, transposed weights, pad K-1-p
+    LdIm2col<T, BM> a;
+    a.p = (const T*)dy;
+    a.cg = ConvGeom{s.Ho, s.Wo, s.Cout, Cog, s.K, s.K, 1, s.K - 1 - s.pad, s.H, s.W};
+    a.M = s.Nimg * s.H * s.W;
+    a.K = s.K * s.K * Cog;
+    LdKC<T, BN> bl;
+    bl.p = (const T*)wt; bl.ld = a.K; bl.rows = Cig; bl.K = a.K; bl.gstride = (int64_t)Cig * a.K;
+    EpMask<T> e;
+    e.out = (T*)dx; e.mask = (const T*)mask; e.ldo = s.Cin; e.M = a.M; e.N = Cig;
+    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cig, a.K, s.groups, 1, st);
+  }
+};
+
+hipError_t conv_dgrad(DType dt, const ConvShape& s, const void* dy, const void* wt, const void* mask,
+                      void* dx, hipStream_t st) {
+  if (s.stride != 1) return hipErrorInvalidValue;
+  const int Cig = s.Cin / s.groups;
+  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st}; return by_bn<bf16>(Cig, f); }
+  ConvDgradFn<float> f{s, dy, wt, mask, dx, st};
+  return by_bn<float>(Cig, f);
+}
+
+// ---- weight gradients: split-K partials, then an ordered reduction
+static int wgrad_splits(int tiles, int K) {
+  int want = cdiv(2 * 256, tiles);
+  if (want > 256) want = 256;
+  return eff_splits(K, want);
+}
+
+size_t conv_wgrad_part_bytes(const ConvShape& s) {
+  const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
+  const int N = s.K * s.K * Cig, P = s.Nimg * s.Ho * s.Wo;
+  const int tiles = cdiv(Cog, 128) * cdiv(N, 128) * s.groups;
+  return (size_t)s.groups * wgrad_splits(tiles, P) * Cog * N * sizeof(float);
+}
+size_t conv1_wgrad_part_bytes(int Nimg) {
+  const int tiles = cdiv(96, 128) * cdiv(368, 128);
+  return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * 368 * sizeof(float);
+}
+
+// gw[co][ci][kh][kw] = sum_s part[g][s][co_l][(kh*KW + kw)*Cg + ci]   (rkhwc = 1)
+//                   or sum_s part[g][s][co_l][ci*KH*KW + kh*KW + kw]  (rkhwc = 0)
+__global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg, int Np, int Cg,
+                               int KH, int KW, int rkhwc, float* __restrict__ gw) {
+  const int64_t o = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  const int KK = KH * KW;
+  const int64_t total = (int64_t)G * Mg * Cg * KK;
+  if (o >= total) return;
+  const int co = (int)(o / (Cg * KK));
+  const int rem = (int)(o - (int64_t)co * Cg * KK);
+  const int ci = rem / KK, t = rem - ci * KK;
+  const int g = co / Mg, col = co - g * Mg;
+  const int r = rkhwc ? t * Cg + ci : rem;
+  const float* p = part + ((int64_t)g * S * Mg + col) * Np + r;
+  float acc = 0.f;
+  for (int s = 0; s < S; ++s) acc += p[(int64_t)s * Mg * Np];
+  gw[o] = acc;
+}
+
+template <typename T>
+static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x, float* part,
+                               size_t part_bytes, float* gw, hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
+  const int N = s.K * s.K * Cig, P = s.Nimg * s.Ho * s.Wo;
+  const int tiles = cdiv(Cog, BM) * cdiv(N, BN) * s.groups;
+  const int S = wgrad_splits(tiles, P);
+  if ((size_t)s.groups * S * Cog * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  LdKO<T, BM> a;
+  a.p = (const T*)dy; a.ld = s.Cout; a.rows = Cog; a.K = P; a.gstride = Cog;
+  LdWgradB<T, BN> b;
+  b.p = (const T*)x;
+  b.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
+  b.rows = N; b.P = P;
+  EpF32 e;
+  e.out = part; e.ldo = N; e.M = Cog; e.N = N; e.splits = S;
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_wgrad_reduce, grid1d((int64_t)s.Cout * Cig * s.K * s.K), dim3(TPB), 0, st, part,
+                     s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
+  return hipGetLastError();
+}
+
+hipError_t conv_wgrad(DType dt, const ConvShape& s, const void* dy, const void* x, float* part,
+                      size_t part_bytes, float* gw, hipStream_t st) {
+  return dt == BF16 ? conv_wgrad_t<bf16>(s, dy, x, part, part_bytes, gw, st)
+                    : conv_wgrad_t<float>(s, dy, x, part, part_bytes, gw, st);
+}
+
+template <typename T>
+static hipError_t conv1_wgrad_t(int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
+                                size_t part_bytes, float* gw, hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  const int N = 368, P = Nimg * 3025;
+  const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
+  if ((size_t)S * 96 * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  LdKO<T, BM> a;
+  a.p = (const T*)dy; a.ld = 96; a.rows = 96; a.K = P; a.gstride = 0;
+  LdConv1WgradB<T, BN> b;
+  b.p = (const T*)x; b.Hs = Hs; b.Ws = Ws; b.P = P;
+  EpF32 e;
+  e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * 363), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 0,
+                     gw);
+  return hipGetLastError();
+}
+
+hipError_t conv1_wgrad(DType dt, int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
+                       size_t part_bytes, float* gw, hipStream_t st) {
+  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, Hs, Ws, dy, x, part, part_bytes, gw, st)
+                    : conv1_wgrad_t<float>(Nimg, Hs, Ws, dy, x, part, part_bytes, gw, st);
+}
+
+// ---- fully-connected layers
+static int fc_splits(int M, int N, int K) {
+  const int tiles = cdiv(M, 128) * cdiv(N, 128);
+  int want = cdiv(256, tiles);
+  if (want > 8) want = 8;
+  return eff_splits(K, want);
+}
+size_t fc_fwd_part_bytes(int M, int K, int O) {
+  return (size_t)fc_splits(M, O, K) * M * O * sizeof(float);
+}
+size_t fc_dgrad_part_bytes(int M, int K, int O) {
+  return (size_t)fc_splits(M, K, O) * M * K * sizeof(float);
+}
+
+// out = epi(sum_s part[s][m][n] + b[n]) for 4 consecutive n per thread.
+template <typename T>
+__global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N, const T* __restrict__ bias,
+                            FcEpi ep, const T* __restrict__ mask, T* __restrict__ out,
+                            float* __restrict__ out_f32) {
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  const int64_t total = (int64_t)M * N / 4;
+  if (t >= total) return;
+  const int64_t e0 = t * 4;
+  const int m = (int)(e0 / N), n = (int)(e0 - (int64_t)m * N);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * N + n);
+    v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+  }
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += Num<T>::load(bias[n + i]);
+  }
+  if (ep.relu) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] > 0.f ? v[i] : 0.f;
+  }
+  if (ep.drop == 1) {
+    // element e = m*N + n (N % 4 == 0, so the four share one Philox block)
+    const uint4 r = philox4x32_10(make_uint4((uint32_t)(e0 >> 2), (uint32_t)ep.layer, (uint32_t)ep.step,
+                                             (uint32_t)(ep.step >> 32)),
+                                  (uint32_t)ep.seed, (uint32_t)(ep.seed >> 32));
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = w[i] < ep.thresh ? 0.f : v[i];
+  } else if (ep.drop == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= ep.scale;
+  }
+  if (mask) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = Num<T>::load(mask[e0 + i]) > 0.f ? v[i] : 0.f;
+  }
+  if (out_f32) {
+    *reinterpret_cast<float4*>(out_f32 + e0) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[e0 + i] = Num<T>::store(v[i]);
+  }
+}
+
+template <typename T>
+static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, const void* b,
+                           const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes,
+                           hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  const int S = fc_splits(M, O, K);
+  if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  LdKC<T, BM> a;
+  a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
+  LdKC<T, BN> bl;
+  bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
+  EpF32 e;
+  e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, O, K, 1, S, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O,
+                     (const T*)b, ep, (const T*)nullptr, (T*)y, y_f32);
+  return hipGetLastError();
+}
+
+hipError_t fc_fwd(DType dt, int M, int K, int O, const void* x, const void* w, const void* b,
+                  const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t st) {
+  return dt == BF16 ? fc_fwd_t<bf16>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st)
+                    : fc_fwd_t<float>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st);
+}
+
+template <typename T>
+static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w, const void* mask,
+                             void* dx, float* part, size_t part_bytes, hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  const int S = fc_splits(M, K, O);
+  if ((size_t)S * M * K * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  LdKC<T, BM> a;
+  a.p = (const T*)dy; a.ld = O; a.rows = M; a.K = O; a.gstride = 0;
+  LdKO<T, BN> bl;
+  bl.p = (const T*)w; bl.ld = K; bl.rows = K; bl.K = O; bl.gstride = 0;
+  EpF32 e;
+  e.out = part; e.ldo = K; e.M = M; e.N = K; e.splits = S;
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, K, O, 1, S, st);
+  if (err != hipSuccess) return err;
+  FcEpi none{};
+  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K,
+                     (const T*)nullptr, none, (const T*)mask, (T*)dx, (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t fc_dgrad(DType dt, int M, int K, int O, const void* dy, const void* w, const void* mask,
+                    void* dx, float* part, size_t part_bytes, hipStream_t st) {
+  return dt == BF16 ? fc_dgrad_t<bf16>(M, K, O, dy, w, mask, dx, part, part_bytes, st)
+                    : fc_dgrad_t<float>(M, K, O, dy, w, mask, dx, part, part_bytes, st);
+}
+
+template <typename T>
+static hipError_t fc_wgrad_t(int M, int K, int O, const void* dy, const void* x, float* gw,
+                             hipStream_t st) {
+  constexpr int BM = 128, BN = 128;
+  LdKO<T, BM> a;
+  a.p = (const T*)dy; a.ld = O; a.rows = O; a.K = M; a.gstride = 0;
+  LdKO<T, BN> bl;
+  bl.p = (const T*)x; bl.ld = K; bl.rows = K; bl.K = M; bl.gstride = 0;
+  EpF32 e;
+  e.out = gw; e.ldo = K; e.M = O; e.N = K; e.splits = 1;
+  return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st);
+}
+
+hipError_t fc_wgrad(DType dt, int M, int K, int O, const void* dy, const void* x, float* gw,
+                    hipStream_t st) {
+  return dt == BF16 ? fc_wgrad_t<bf16>(M, K, O, dy, x, gw, st) : fc_wgrad_t<float>(M, K, O, dy, x, gw, st);
+}
+
+// =========================================================================
+// Weight re-layouts
+// =========================================================================
+template <typename T>
+__global__ void k_w_khwc(const T* __restrict__ w, T* __restrict__ o, int Cout, int Cg, int K) {
+  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (i >= (int64_t)Cout * Cg * K * K) return;
+  int t = (int)i;
+  const int ci = t % Cg; t /= Cg;
+  const int kw = t % K; t /= K;
+  const int kh = t % K;
+  const int co = t / K;
+  o[i] = w[(((int64_t)co * Cg + ci) * K + kh) * K + kw];
+}
+
+template <typename T>
+__global__ void k_w_pad(const T* __restrict__ w, T* __restrict__ o, int rows, int k, int kpad) {
+  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (i >= (int64_t)rows * kpad) return;
+  const int r = (int)(i / kpad), c = (int)(i - (int64_t)r * kpad);
+  o[i] = c < k ? w[(int64_t)r * k + c] : T(0);
+}
+
+template <typename T>
+__global__ void k_w_dgrad(const T* __restrict__ w, T* __restrict__ o, int G, int Cog, int Cig, int K) {
+  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (i >= (int64_t)G * Cig * K * K * Cog) return;
+  int t = (int)i;
+  const int col = t % Cog; t /= Cog;
+  const int kw = t % K; t /= K;
+  const int kh = t % K; t /= K;
+  const int ci = t % Cig;
+  const int g = t / Cig;
+  o[i] = w[((((int64_t)g * Cog + col) * Cig + ci) * K + (K - 1 - kh)) * K + (K - 1 - kw)];
+}
+
+hipError_t w_khwc(DType dt, const void* w, void* out, int Cout, int Cg, int K, hipStream_t st) {
+  const dim3 g = grid1d((int64_t)Cout * Cg * K * K);
+  if (dt == BF16) hipLaunchKernelGGL((k_w_khwc<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, Cout, Cg, K);
+  else hipLaunchKernelGGL((k_w_khwc<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, Cout, Cg, K);
+  return hipGetLastError();
+}
+hipError_t w_pad_rows(DType dt, const void* w, void* out, int rows, int k, int kpad, hipStream_t st) {
+  const dim3 g = grid1d((int64_t)rows * kpad);
+  if (dt == BF16) hipLaunchKernelGGL((k_w_pad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, rows, k, kpad);
+  else hipLaunchKernelGGL((k_w_pad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, rows, k, kpad);
+  return hipGetLastError();
+}
+hipError_t w_dgrad(DType dt, const void* w, void* out, int G, int Cog, int Cig, int K, hipStream_t st) {
+  const dim3 g = grid1d((int64_t)G * Cig * K * K * Cog);
+  if (dt == BF16) hipLaunchKernelGGL((k_w_dgrad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, G, Cog, Cig, K);
+  else hipLaunchKernelGGL((k_w_dgrad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, G, Cog, Cig, K);
+  return hipGetLastError();
+}
+
+// =========================================================================
+// Local response normalisation across channels, NHWC
+//   b_i = a_i * S_i^-beta,  S_i = k + alpha * sum_{|j-i| <= half, 0 <= j < C} a_j^2
+// =========================================================================
+__device__ __forceinline__ float pow_neg_beta(float S, float beta, bool b075) {
+  if (b075) { const float r = rsqrtf(S); return r * sqrtf(r); }   // S^-1/2 * S^-1/4
+  return exp2f(-beta * log2f(S));
+}
+
+// Loads channels c0-8 .. c0+15 of one pixel (zero outside [0, C)).
+template <typename T>
+__device__ __forceinline__ void load24(const T* px, int c0, int C, float* v) {
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int cc = c0 + (q - 1) * 8;
+    if (cc >= 0 && cc < C) Pack8<T>::load(px + cc, v + q * 8);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[q * 8 + i] = 0.f;
+    }
+  }
+}
+
+template <typename T>
+__global__ void k_lrn_fwd(const T* __restrict__ a, T* __restrict__ b, int64_t npix, int C, float k,
+                          float alpha, float beta, int half) {
+  const int cpp = C >> 3;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (t >= npix * cpp) return;
+  const int64_t pix = t / cpp;
+  const int c0 = (int)(t - pix * cpp) * 8;
+  const T* px = a + pix * C;
+  float v[24];
+  load24(px, c0, C, v);
+  const bool b075 = beta == 0.75f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float s = 0.f;
+    for (int j = -half; j <= half; ++j) { const float x = v[8 + i + j]; s += x * x; }
+    o[i] = v[8 + i] * pow_neg_beta(k + alpha * s, beta, b075);
+  }
+  Pack8<T>::store(b + pix * C + c0, o);
+}
+
+// Backward of LRN fused with the preceding ReLU's mask [a > 0]:
+//   da_j = g_j S_j^-beta - 2 alpha beta a_j sum_{|i-j| <= half} g_i a_i S_i^(-beta-1)
+// half <= 4 (window <= 9): needs a over c0-8 .. c0+15 and g over c0-4 .. c0+11.
+template <typename T>
+__global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* __restrict__ da,
+                          int64_t npix, int C, float k, float alpha, float beta, int half) {
+  const int cpp = C >> 3;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (t >= npix * cpp) return;
+  const int64_t pix = t / cpp;
+  const int c0 = (int)(t - pix * cpp) * 8;
+  float av[24], gv[24];
+  load24(a + pix * C, c0, C, av);
+  load24(g + pix * C, c0, C, gv);
+  const bool b075 = beta == 0.75f;
+  // S, S^-beta and g a S^(-beta-1) at relative channels 4 .. 19 (= c0-4 .. c0+11)
+  float pb[16], tt[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rel = r + 4;
+    float s = 0.f;
+    for (int j = -half; j <= half; ++j) { const float x = av[rel + j]; s += x * x; }
+    const float S = k + alpha * s;
+    const float p = pow_neg_beta(S, beta, b075);
+    pb[r] = p;
+    tt[r] = gv[rel] * av[rel] * (p / S);
+  }
+  float o[8];
+  const float c2 = 2.f * alpha * beta;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = i + 4;   // index into pb/tt for channel c0+i
+    float cross = 0.f;
+    for (int j = -half; j <= half; ++j) cross += tt[r + j];
+    const float aj = av[8 + i];
+    const float d = gv[8 + i] * pb[r] - c2 * aj * cross;
+    o[i] = aj > 0.f ? d : 0.f;
+  }
+  Pack8<T>::store(da + pix * C + c0, o);
+}
+
+hipError_t lrn_fwd(DType dt, const void* a, void* b, int64_t npix, int C, float k, float alpha, float beta,
+                   int n, hipStream_t st) {
+  const dim3 g = grid1d(npix * (C / 8));
+  if (dt == BF16) hipLaunchKernelGGL((k_lrn_fwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (bf16*)b, npix, C, k, alpha, beta, n / 2);
+  else hipLaunchKernelGGL((k_lrn_fwd<float>), g, dim3(TPB), 0, st, (const float*)a, (float*)b, npix, C, k, alpha, beta, n / 2);
+  return hipGetLastError();
+}
+hipError_t lrn_bwd(DType dt, const void* a, const void* gr, void* da, int64_t npix, int C, float k,
+                   float alpha, float beta, int n, hipStream_t st) {
+  if (n / 2 > 4) return hipErrorInvalidValue;
+  const dim3 g = grid1d(npix * (C / 8));
+  if (dt == BF16) hipLaunchKernelGGL((k_lrn_bwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (const bf16*)gr, (bf16*)da, npix, C, k, alpha, beta, n / 2);
+  else hipLaunchKernelGGL((k_lrn_bwd<float>), g, dim3(TPB), 0, st, (const float*)a, (const float*)gr, (float*)da, npix, C, k, alpha, beta, n / 2);
+  return hipGetLastError();
+}
+
+// =========================================================================
+// Overlapping max-pool 3x3 / stride 2, NHWC, with argmax (dy*3 + dx of the
+// first maximum in a row-major scan of the window)
+// =========================================================================
+template <typename T, bool FLAT>
+__global__ void k_pool_fwd(const T* __restrict__ x, T* __restrict__ y, uint8_t* __restrict__ arg, int N,
+                           int H, int W, int C, int Ho, int Wo) {
+  const int cpp = C >> 3;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (t >= (int64_t)N * Ho * Wo * cpp) return;
+  const int64_t pix = t / cpp;
+  const int c0 = (int)(t - pix * cpp) * 8;
+  const int wo = (int)(pix % Wo);
+  const int ho = (int)((pix / Wo) % Ho);
+  const int n = (int)(pix / ((int64_t)Wo * Ho));
+  float best[8], v[8];
+  uint32_t bi[8];
+  const T* base = x + (((int64_t)n * H + 2 * ho) * W + 2 * wo) * C + c0;
+  Pack8<T>::load(base, best);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bi[i] = 0;
+#pragma unroll
+  for (int d = 1; d < 9; ++d) {
+    const int dy = d / 3, dx = d % 3;
+    Pack8<T>::load(base + ((int64_t)dy * W + dx) * C, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (v[i] > best[i]) { best[i] = v[i]; bi[i] = d; }
+  }
+  const uint32_t lo = bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24);
+  const uint32_t hi = bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24);
+  *reinterpret_cast<uint2*>(arg + pix * C + c0) = make_uint2(lo, hi);
+  if (FLAT) {
+    T* yo = y + (int64_t)n * C * Ho * Wo + ho * Wo + wo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) yo[(int64_t)(c0 + i) * Ho * Wo] = Num<T>::store(best[i]);
+  } else {
+    Pack8<T>::store(y + pix * C + c0, best);
+  }
+}
+
+template <typename T, bool FLAT>
+__global__ void k_pool_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
+                           const T* __restrict__ mask, T* __restrict__ dx, int N, int H, int W, int C,
+                           int Ho, int Wo) {
+  const int cpp = C >> 3;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (t >= (int64_t)N * H * W * cpp) return;
+  const int64_t pix = t / cpp;
+  const int c0 = (int)(t - pix * cpp) * 8;
+  const int w = (int)(pix % W);
+  const int h = (int)((pix / W) % H);
+  const int n = (int)(pix / ((int64_t)W * H));
+  // windows (i, j) with 2i <= h <= 2i + 2 and 2j <= w <= 2j + 2
+  const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
+  const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int i = i0; i <= i1; ++i)
+    for (int j = j0; j <= j1; ++j) {
+      const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
+      const int64_t op = ((int64_t)n * Ho + i) * Wo + j;
+      const uint2 am = *reinterpret_cast<const uint2*>(arg + op * C + c0);
+      float g[8];
+      if (FLAT) {
+        const T* gp = dy + (int64_t)n * C * Ho * Wo + i * Wo + j;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g[q] = Num<T>::load(gp[(int64_t)(c0 + q) * Ho * Wo]);
+      } else {
+        Pack8<T>::load(dy + op * C + c0, g);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+        if (b == code) acc[q] += g[q];
+      }
+    }
+  if (mask) {
+    float mk[8];
+    Pack8<T>::load(mask + pix * C + c0, mk);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
+  }
+  Pack8<T>::store(dx + pix * C + c0, acc);
+}
+
+hipError_t pool_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C, int flat,
+                    hipStream_t st) {
+  const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
+  const dim3 g = grid1d((int64_t)N * Ho * Wo * (C / 8));
+  if (dt == BF16) {
+    if (flat) hipLaunchKernelGGL((k_pool_fwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
+    else hipLaunchKernelGGL((k_pool_fwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
+  } else {
+    if (flat) hipLaunchKernelGGL((k_pool_fwd<float, true>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
+    else hipLaunchKernelGGL((k_pool_fwd<float, false>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
+  }
+  return hipGetLastError();
+}
+
+hipError_t pool_bwd(DType dt, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N, int H,
+                    int W, int C, int flat, hipStream_t st) {
+  const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
+  const dim3 g = grid1d((int64_t)N * H * W * (C / 8));
+  if (dt == BF16) {
+    if (flat) hipLaunchKernelGGL((k_pool_bwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
+    else hipLaunchKernelGGL((k_pool_bwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
+  } else {
+    if (flat) hipLaunchKernelGGL((k_pool_bwd<float, true>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
+    else hipLaunchKernelGGL((k_pool_bwd<float, false>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
+  }
+  return hipGetLastError();
+}
+
+// =========================================================================
+// Softmax, cross-entropy, ten-view mean: one wavefront per row
+// =========================================================================
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T, bool CE>
+__global__ void k_softmax(const float* __restrict__ z, const int32_t* __restrict__ labels,
+                          float* __restrict__ p, T* __restrict__ dz, float* __restrict__ rowloss, int M,
+                          int O) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* zr = z + (int64_t)row * O;
+  float mx = -INFINITY;
+  for (int i = lane; i < O; i += 64) mx = fmaxf(mx, zr[i]);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int i = lane; i < O; i += 64) s += expf(zr[i] - mx);
+  s = wave_sum(s);
+  const float inv = 1.f / s;
+  int y = 0;
+  if (CE) { y = labels[row]; y = y < 0 ? 0 : (y >= O ? O - 1 : y); }
+  for (int i = lane; i < O; i += 64) {
+    const float pi = expf(zr[i] - mx) * inv;
+    if (p) p[(int64_t)row * O + i] = pi;
+    if (CE) dz[(int64_t)row * O + i] = Num<T>::store((pi - (i == y ? 1.f : 0.f)) / (float)M);
+  }
+  if (CE && lane == 0) rowloss[row] = -(zr[y] - mx - logf(s));
+}
+
+hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t st) {
+  hipLaunchKernelGGL((k_softmax<float, false>), dim3(cdiv(M, TPB / 64)), dim3(TPB), 0, st, z,
+                     (const int32_t*)nullptr, p, (float*)nullptr, (float*)nullptr, M, O);
+  return hipGetLastError();
+}
+hipError_t softmax_ce(DType dt, const float* z, const int32_t* labels, float* p, void* dz, float* rowloss,
+                      int M, int O, hipStream_t st) {
+  const dim3 g(cdiv(M, TPB / 64));
+  if (dt == BF16) hipLaunchKernelGGL((k_softmax<bf16, true>), g, dim3(TPB), 0, st, z, labels, p, (bf16*)dz, rowloss, M, O);
+  else hipLaunchKernelGGL((k_softmax<float, true>), g, dim3(TPB), 0, st, z, labels, p, (float*)dz, rowloss, M, O);
+  return hipGetLastError();
+}
+
+// out = (sum of v[0..n)) / n, one workgroup, fixed reduction order.
+__global__ void k_mean_reduce(const float* __restrict__ v, int n, float* __restrict__ out) {
+  __shared__ float sh[TPB];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += TPB) s += v[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = TPB / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = sh[0] / (float)n;
+}
+hipError_t mean_reduce(const float* v, int n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_mean_reduce, dim3(1), dim3(TPB), 0, st, v, n, out);
+  return hipGetLastError();
+}
+
+__global__ void k_view_mean(const float* __restrict__ p, float* __restrict__ out, int N, int O) {
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (t >= (int64_t)N * O) return;
+  const int n = (int)(t / O), i = (int)(t - (int64_t)n * O);
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < 10; ++v) s += p[((int64_t)n * 10 + v) * O + i];
+  out[t] = s / 10.f;
+}
+hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t st) {
+  hipLaunchKernelGGL(k_view_mean, grid1d((int64_t)N * O), dim3(TPB), 0, st, p, out, N, O);
+  return hipGetLastError();
+}
+
+// =========================================================================
+// Column sums (bias gradients): two ordered passes
+// =========================================================================
+static constexpr int COLSUM_ROWS = 512;
+
+template <typename T>
+__global__ void k_colsum1(const T* __restrict__ x, int64_t rows, int C, float* __restrict__ part) {
+  const int c = blockIdx.y * TPB + threadIdx.x;
+  if (c >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.x * COLSUM_ROWS;
+  const int64_t r1 = min(r0 + COLSUM_ROWS, rows);
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += Num<T>::load(x[r * C + c]);
+  part[(int64_t)blockIdx.x * C + c] = s;
+}
+__global__ void k_colsum2(const float* __restrict__ part, int nb, int C, float* __restrict__ out) {
+  const int c = blockIdx.x * TPB + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * C + c];
+  out[c] = s;
+}
+size_t colsum_scratch_bytes(int64_t rows, int C) {
+  return (size_t)cdiv(rows, COLSUM_ROWS) * C * sizeof(float);
+}
+hipError_t colsum(DType dt, const void* x, int64_t rows, int C, float* out, float* scratch, hipStream_t st) {
+  const int nb = cdiv(rows, COLSUM_ROWS);
+  const dim3 g1(nb, cdiv(C, TPB));
+  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, scratch);
+  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, scratch);
+  hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB)), dim3(TPB), 0, st, scratch, nb, C, out);
+  return hipGetLastError();
+}
+
+// =========================================================================
+// SGD with momentum and weight decay over all 16 parameter tensors, and the
+// refresh of the working copies.  Four elements per thread.
+// =========================================================================
+struct MultiArgs {
+  float* w[16];
+  float* v[16];
+  const float* g[16];
+  void* wb[16];
+  int64_t start[17];   // first 4-element chunk of each tensor
+  float lr, mom, wdlr;
+};
+
+__device__ __forceinline__ int find_tensor(const int64_t* start, int64_t c) {
+  int ti = 0;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) ti += c >= start[i] ? 1 : 0;
+  return ti;
+}
+
+template <typename T, bool SGD>
+__global__ void k_multi(MultiArgs a) {
+  const int64_t c = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (c >= a.start[16]) return;
+  const int ti = find_tensor(a.start, c);
+  const int64_t e = (c - a.start[ti]) * 4;
+  float4 w = *reinterpret_cast<const float4*>(a.w[ti] + e);
+  if (SGD) {
+    float4 v = *reinterpret_cast<const float4*>(a.v[ti] + e);
+    const float4 g = *reinterpret_cast<const float4*>(a.g[ti] + e);
+    v.x = a.mom * v.x - a.wdlr * w.x - a.lr * g.x;
+    v.y = a.mom * v.y - a.wdlr * w.y - a.lr * g.y;
+    v.z = a.mom * v.z - a.wdlr * w.z - a.lr * g.z;
+    v.w = a.mom * v.w - a.wdlr * w.w - a.lr * g.w;
+    w.x += v.x; w.y += v.y; w.z += v.z; w.w += v.w;
+    *reinterpret_cast<float4*>(a.v[ti] + e) = v;
+    *reinterpret_cast<float4*>(a.w[ti] + e) = w;
+  }
+  T* o = reinterpret_cast<T*>(a.wb[ti]) + e;
+  if (sizeof(T) == 2) {
+    const uint32_t lo = (uint32_t)f2bf(w.x) | ((uint32_t)f2bf(w.y) << 16);
+    const uint32_t hi = (uint32_t)f2bf(w.z) | ((uint32_t)f2bf(w.w) << 16);
+    *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(o) = w;
+  }
+}
+
+static hipError_t run_multi(DType dt, const TensorSet& ts, bool sgd, float lr, float mom, float wd,
+                            hipStream_t st) {
+  MultiArgs a;
+  a.start[0] = 0;
+  for (int i = 0; i < 16; ++i) {
+    if (ts.n[i] % 4) return hipErrorInvalidValue;
+    a.w[i] = ts.master[i]; a.v[i] = ts.mom[i]; a.g[i] = ts.grad[i]; a.wb[i] = ts.work[i];
+    a.start[i + 1] = a.start[i] + ts.n[i] / 4;
+  }
+  a.lr = lr; a.mom = mom; a.wdlr = wd * lr;
+  const dim3 g = grid1d(a.start[16]);
+  if (dt == BF16) {
+    if (sgd) hipLaunchKernelGGL((k_multi<bf16, true>), g, dim3(TPB), 0, st, a);
+    else hipLaunchKernelGGL((k_multi<bf16, false>), g, dim3(TPB), 0, st, a);
+  } else {
+    if (sgd) hipLaunchKernelGGL((k_multi<float, true>), g, dim3(TPB), 0, st, a);
+    else hipLaunchKernelGGL((k_multi<float, false>), g, dim3(TPB), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t sgd(DType dt, const TensorSet& ts, float lr, float mom, float wd, hipStream_t st) {
+  return run_multi(dt, ts, true, lr, mom, wd, st);
+}
+hipError_t cast_weights(DType dt, const TensorSet& ts, hipStream_t st) {
+  return run_multi(dt, ts, false, 0.f, 0.f, 0.f, st);
+}
+
+// =========================================================================
+// Dropout keep-mask (the same draw the FC6/FC7 epilogues make)
+// =========================================================================
+__global__ void k_dropout_mask(uint64_t seed, uint64_t step, int layer, int64_t total, uint32_t thresh,
+                               uint8_t* __restrict__ mask) {
+  const int64_t q = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (q * 4 >= total) return;
+  const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)layer, (uint32_t)step, (uint32_t)(step >> 32)),
+                                (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t w = (r.x < thresh ? 0u : 1u) | ((r.y < thresh ? 0u : 1u) << 8) |
+                     ((r.z < thresh ? 0u : 1u) << 16) | ((r.w < thresh ? 0u : 1u) << 24);
+  *reinterpret_cast<uint32_t*>(mask + q * 4) = w;
+}
+hipError_t dropout_mask(uint64_t seed, uint64_t step, int layer, int rows, int cols, uint32_t thresh,
+                        uint8_t* mask, hipStream_t st) {
+  const int64_t total = (int64_t)rows * cols;
+  hipLaunchKernelGGL(k_dropout_mask, grid1d(total / 4), dim3(TPB), 0, st, seed, step, layer, total, thresh,
+                     mask);
+  return hipGetLastError();
+}
+
+}  // namespace ax

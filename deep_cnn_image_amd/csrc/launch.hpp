@@ -1,0 +1,110 @@
+// Host-side launchers for the AlexNet HIP kernels.  Every launcher enqueues on
+// `st` and returns the launch status; shapes are checked by the caller.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ax {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Split-K factor actually used for K (in elements) when `want` splits are
+// requested: every split gets at least one 32-wide k-tile and none is empty.
+inline int eff_splits(int K, int want) {
+  const int kt = cdiv(K, 32);
+  if (want < 1) want = 1;
+  if (want > kt) want = kt;
+  const int per = cdiv(kt, want);
+  return cdiv(kt, per);
+}
+
+struct ConvShape {
+  int Nimg, H, W, Cin, Cout, K, stride, pad, groups, Ho, Wo;
+};
+
+// ---- weight re-layouts (per call; weights change every training step)
+hipError_t w_khwc(DType, const void* w_oihw, void* out, int Cout, int Cg, int K, hipStream_t);
+hipError_t w_pad_rows(DType, const void* w, void* out, int rows, int k, int kpad, hipStream_t);
+hipError_t w_dgrad(DType, const void* w_oihw, void* out, int G, int Coutg, int Cing, int K,
+                   hipStream_t);
+
+// ---- convolutions (bf16 MFMA or fp32 MFMA, fp32 accumulate)
+// layer 1 from NCHW images (or ten-view sources), y NHWC = relu(conv + b)
+hipError_t conv1_fwd(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
+                     const void* b1, void* y, hipStream_t);
+// NHWC conv + bias + ReLU (layers 2-5)
+hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, const void* b, void* y,
+                    hipStream_t);
+// dX (NHWC) = conv^T(dY) * [mask > 0] (mask optional) for stride-1 layers
+hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, const void* mask,
+                      void* dx, hipStream_t);
+// fp32 weight gradient (OIHW) of layers 2-5; `part` is split-K scratch
+hipError_t conv_wgrad(DType, const ConvShape&, const void* dy, const void* x, float* part,
+                      size_t part_bytes, float* gw, hipStream_t);
+// fp32 weight gradient of layer 1 from NCHW images
+hipError_t conv1_wgrad(DType, int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
+                       size_t part_bytes, float* gw, hipStream_t);
+size_t conv_wgrad_part_bytes(const ConvShape&);
+size_t conv1_wgrad_part_bytes(int Nimg);
+
+// ---- fully-connected layers
+struct FcEpi {
+  int relu;             // 1: ReLU
+  int drop;             // 0: none, 1: Philox keep-mask (training), 2: multiply by `scale`
+  float scale;
+  uint32_t thresh;      // drop iff Philox word < thresh
+  uint64_t seed, step;
+  int layer;
+};
+// y[M][O] = epi(x[M][K] W[O][K]^T + b); y is cfg dtype, or fp32 if y_f32
+hipError_t fc_fwd(DType, int M, int K, int O, const void* x, const void* w, const void* b,
+                  const FcEpi&, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t);
+// dx[M][K] = (dy[M][O] W[O][K]) * [mask > 0] (mask optional)
+hipError_t fc_dgrad(DType, int M, int K, int O, const void* dy, const void* w, const void* mask,
+                    void* dx, float* part, size_t part_bytes, hipStream_t);
+// dW[O][K] fp32 = dy^T x
+hipError_t fc_wgrad(DType, int M, int K, int O, const void* dy, const void* x, float* gw,
+                    hipStream_t);
+size_t fc_fwd_part_bytes(int M, int K, int O);
+size_t fc_dgrad_part_bytes(int M, int K, int O);
+
+// ---- bandwidth-bound layers (NHWC, C % 8 == 0)
+hipError_t lrn_fwd(DType, const void* a, void* b, int64_t npix, int C, float k, float alpha,
+                   float beta, int n, hipStream_t);
+hipError_t lrn_bwd(DType, const void* a, const void* g, void* da, int64_t npix, int C, float k,
+                   float alpha, float beta, int n, hipStream_t);
+// 3x3/s2 max-pool; flat_out: y written [N][C*Ho*Wo] in (c,h,w) order
+hipError_t pool_fwd(DType, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C,
+                    int flat_out, hipStream_t);
+// gather-form backward; flat_dy: dy is [N][C*Ho*Wo] in (c,h,w) order; mask optional
+hipError_t pool_bwd(DType, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N,
+                    int H, int W, int C, int flat_dy, hipStream_t);
+
+// ---- softmax, loss, ten-view mean, column sums
+hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t);
+hipError_t softmax_ce(DType, const float* z, const int32_t* labels, float* p, void* dz,
+                      float* rowloss, int M, int O, hipStream_t);
+hipError_t mean_reduce(const float* v, int n, float* out, hipStream_t);
+hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t);
+// out[c] = sum over rows of x[rows][C] (fp32), via `scratch` (colsum_scratch_bytes)
+hipError_t colsum(DType, const void* x, int64_t rows, int C, float* out, float* scratch,
+                  hipStream_t);
+size_t colsum_scratch_bytes(int64_t rows, int C);
+
+// ---- optimizer, casts, dropout mask
+struct TensorSet {
+  float* master[16];
+  float* mom[16];
+  const float* grad[16];
+  void* work[16];
+  int64_t n[16];
+};
+hipError_t sgd(DType work_dtype, const TensorSet&, float lr, float momentum, float wd, hipStream_t);
+hipError_t cast_weights(DType work_dtype, const TensorSet&, hipStream_t);
+hipError_t dropout_mask(uint64_t seed, uint64_t step, int layer, int rows, int cols,
+                        uint32_t thresh, uint8_t* mask, hipStream_t);
+
+}  // namespace ax

@@ -1,0 +1,75 @@
+"""torch-side plumbing around the C ABI: device buffers for parameters,
+workspace and outputs, and typed views of workspace taps.  torch only
+allocates memory and supplies the stream; every step of the network runs in
+libalexnet.so."""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .inputs import bf16_bits
+
+TORCH_DT = {B.F32: torch.float32, B.BF16: torch.bfloat16, B.U8: torch.uint8}
+
+
+def to_device(a: np.ndarray, dtype: int, device) -> torch.Tensor:
+    """Upload a float32 array as fp32, or as bf16 (round to nearest even)."""
+    if dtype == B.BF16:
+        bits = bf16_bits(np.ascontiguousarray(a, np.float32))
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+
+
+def stream_handle() -> int:
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+class Session:
+    """One configuration (batch, groups, dtype, mode) with its workspace."""
+
+    def __init__(self, batch: int, groups: int = 1, dtype: int = B.BF16, mode: int = B.MODE_FORWARD,
+                 device: str = "cuda:0"):
+        self.cfg = B.alexnet_default_cfg(batch, groups, dtype)
+        self.mode = mode
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.ws_bytes = B.alexnet_workspace_bytes(self.cfg, mode)
+        if self.ws_bytes == 0:
+            raise B.AlexNetError(B.E_ARG, "alexnet_workspace_bytes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self._taps = B.tap_ids()
+
+    # ------------------------------------------------------------- taps
+    def tap(self, name: str) -> torch.Tensor:
+        off, shape, dt, _layout = B.alexnet_tap(self.cfg, self.mode, self._taps[name])
+        tdt = TORCH_DT[dt]
+        n = int(np.prod(shape))
+        nbytes = n * torch.empty((), dtype=tdt).element_size()
+        return self.ws[off:off + nbytes].view(tdt).view(*[int(s) for s in shape])
+
+    # ------------------------------------------------------------- params
+    def upload_params(self, weights: Sequence[np.ndarray], biases: Sequence[np.ndarray],
+                      dtype: Optional[int] = None) -> List[torch.Tensor]:
+        dt = self.dtype if dtype is None else dtype
+        out = []
+        for w, b in zip(weights, biases):
+            out.append(to_device(w, dt, self.device))
+            out.append(to_device(b, dt, self.device))
+        return out
+
+    # ------------------------------------------------------------- calls
+    def forward(self, params, x: torch.Tensor, probs: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if probs is None:
+            probs = torch.empty((self.cfg.batch, 1000), dtype=torch.float32, device=self.device)
+        fn = B.alexnet_forward_tenview if self.mode == B.MODE_TENVIEW else B.alexnet_forward
+        fn(self.cfg, params, x, probs, self.ws, self.ws_bytes, stream_handle())
+        return probs
+
+    def train_step(self, master, momentum, work, x, labels, loss, probs=None, lr=0.01,
+                   momentum_coef=0.9, weight_decay=5e-4, seed=3, step=0):
+        B.alexnet_train_step(self.cfg, master, momentum, work, x, labels, lr, momentum_coef,
+                             weight_decay, seed, step, loss, probs, self.ws, self.ws_bytes,
+                             stream_handle())

@@ -1,0 +1,160 @@
+/*
+ * alexnet.h -- C ABI of the MI355X (gfx950) AlexNet forward / training-step
+ * library (libalexnet.so).
+ *
+ * The network is the eight-learned-layer net of Krizhevsky, Sutskever and
+ * Hinton (NeurIPS 2012) as described on the paper-graph-ui summary ("Overall
+ * Architecture (Layer-by-Layer Specification)", "ReLU Nonlinearity", "Local
+ * Response Normalization", "Overlapping Pooling", "Dropout", "Training
+ * Procedure Details") and the fermi.ai wiki (layer list with paddings,
+ * ALEXNET_FORWARD / TRAIN_STEP):
+ *
+ *   conv1 96@11x11/s4/p0 -> ReLU -> LRN -> maxpool 3/s2
+ *   conv2 256@5x5/p2     -> ReLU -> LRN -> maxpool 3/s2     (groups 1 or 2)
+ *   conv3 384@3x3/p1 -> ReLU;  conv4 384@3x3/p1 -> ReLU      (conv4 groups 1 or 2)
+ *   conv5 256@3x3/p1 -> ReLU -> maxpool 3/s2 -> flatten (c,h,w) = 9216 (groups 1 or 2)
+ *   fc6 9216->4096 -> ReLU -> dropout;  fc7 4096->4096 -> ReLU -> dropout
+ *   fc8 4096->1000 -> softmax
+ *
+ * The paper's two-GPU split with same-GPU connectivity in layers 2, 4 and 5
+ * is expressed on one GPU as groups = 2 on conv2, conv4 and conv5.
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major.  Images are NCHW [N][3][227][227] (ten-view
+ *    sources [N][3][256][256]); conv weights OIHW [Cout][Cin/G][k][k]; FC
+ *    weights [out][in]; biases [out].
+ *  - "params" is an array of 16 device pointers in the order
+ *    w1, b1, w2, b2, ..., w8, b8.
+ *  - Element type of images, params and work weights is cfg->dtype (fp32 or
+ *    bf16 bit patterns); master weights, momentum, probabilities and the loss
+ *    are fp32; labels are int32 in [0, 1000).
+ *  - All pointers are device pointers unless stated otherwise and must be
+ *    16-byte aligned; the workspace must be 256-byte aligned.  The caller owns
+ *    every buffer, including the workspace.  The library allocates nothing
+ *    and keeps no mutable global state; calls are reentrant given distinct
+ *    workspaces.
+ *  - Calls validate their arguments on the host before any launch and return
+ *    an alexnet_status; on error nothing is enqueued.  Work is enqueued on
+ *    `stream` (a hipStream_t, 0 = the default stream) and runs
+ *    asynchronously; device faults surface at the caller's synchronisation.
+ *  - Activations, gradients and working weights are stored in cfg->dtype;
+ *    every sum accumulates in fp32.
+ */
+#ifndef ALEXNET_H
+#define ALEXNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ALEXNET_OK = 0,
+  ALEXNET_E_NULL = -1,      /* a required pointer is null                      */
+  ALEXNET_E_SHAPE = -2,     /* batch or groups out of range                    */
+  ALEXNET_E_DTYPE = -3,     /* dtype not F32/BF16                              */
+  ALEXNET_E_WORKSPACE = -4, /* workspace smaller than alexnet_workspace_bytes  */
+  ALEXNET_E_ALIGN = -5,     /* pointer misaligned                              */
+  ALEXNET_E_DEVICE = -6,    /* current device is not gfx950                    */
+  ALEXNET_E_HIP = -7,       /* a HIP call failed while enqueueing              */
+  ALEXNET_E_ARG = -8        /* other invalid argument (mode, tap id, LRN size) */
+} alexnet_status;
+
+typedef enum { ALEXNET_F32 = 0, ALEXNET_BF16 = 1, ALEXNET_U8 = 2 } alexnet_dtype;
+
+typedef enum {
+  ALEXNET_MODE_FORWARD = 0, /* inference forward pass (dropout off, x0.5 scale) */
+  ALEXNET_MODE_TRAIN = 1,   /* training step                                   */
+  ALEXNET_MODE_TENVIEW = 2  /* ten-view inference over 256x256 sources          */
+} alexnet_mode;
+
+typedef struct {
+  int32_t batch;     /* images per call; ten-view: source images (10 views each). 1..4096 */
+  int32_t groups;    /* 1 = single tower; 2 = conv2/conv4/conv5 split in two groups    */
+  int32_t dtype;     /* ALEXNET_F32 or ALEXNET_BF16                                    */
+  int32_t lrn_n;     /* LRN window (odd, 1..15), 5 on the pages                        */
+  float lrn_k;       /* 2                                                              */
+  float lrn_alpha;   /* 1e-4, multiplies the window sum of squares directly            */
+  float lrn_beta;    /* 0.75                                                           */
+  float dropout_p;   /* 0.5: training drop probability; inference scales by 1 - p      */
+} alexnet_cfg;
+
+/* Fills *cfg with the pages' constants: k = 2, n = 5, alpha = 1e-4,
+ * beta = 0.75, dropout p = 0.5. */
+void alexnet_default_cfg(alexnet_cfg* cfg, int32_t batch, int32_t groups, int32_t dtype);
+
+/* Workspace bytes for one call in `mode`; 0 if cfg is invalid.  Host only. */
+size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode);
+
+/* Inference forward pass (fermi.ai ALEXNET_FORWARD; paper-graph-ui layer list,
+ * test-time dropout rule "use all neurons, multiply outputs by 0.5").
+ *   x     [batch][3][227][227] cfg->dtype
+ *   probs [batch][1000] fp32 softmax output (written) */
+int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x,
+                    float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* Ten-patch test-time averaging (paper-graph-ui "Data Augmentation": the four
+ * corner 227x227 patches and the centre patch, each also mirrored, softmax
+ * outputs averaged).  View v of source n is batch row n*10 + v; views 0..4 are
+ * offsets (0,0), (0,29), (29,0), (29,29), (14,14) as (y,x), views 5..9 the
+ * same patches mirrored left-right.  The crops are read directly by layer 1.
+ *   src   [batch][3][256][256] cfg->dtype
+ *   probs [batch][1000] fp32, mean of the ten views' softmax outputs */
+int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16], const void* src,
+                            float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* One training step (fermi.ai TRAIN_STEP; paper-graph-ui "Dropout" and
+ * "Training Procedure Details"): forward with dropout masks drawn from
+ * Philox4x32-10 keyed by (seed, step) (see alexnet_dropout_mask), the mean
+ * cross-entropy of the softmax w.r.t. `labels`, backpropagation through all
+ * eight layers, then for each of the 16 parameter tensors
+ *     v <- momentum*v - weight_decay*lr*w - lr*g ;  w <- w + v
+ * on the fp32 master weights, and the working copies refreshed from the new
+ * master (round to nearest even for bf16).
+ *   master[16]   fp32, in/out          momentum[16] fp32, in/out
+ *   work[16]     cfg->dtype, in (used by forward/backward), out (refreshed)
+ *   x            [batch][3][227][227] cfg->dtype
+ *   labels       [batch] int32 in [0, 1000); out-of-range labels give an
+ *                undefined loss and gradient but never an out-of-bounds access
+ *   loss         one fp32 (device), the batch-mean cross-entropy
+ *   probs        optional [batch][1000] fp32 softmax output (may be null)
+ * The gradients stay in the workspace (taps) until the next call. */
+int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                       void* const work[16], const void* x, const int32_t* labels, float lr,
+                       float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
+                       float* loss, float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* work[i] <- cfg->dtype copy of master[i] (round to nearest even), all 16
+ * tensors.  For fp32 work tensors this is a copy. */
+int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* const work[16],
+                         void* stream);
+
+/* The dropout keep-mask used by alexnet_train_step for layer `layer`
+ * (0 = fc6, 1 = fc7) at `step`: mask[r][c] = 1 keeps unit c of row r, 0 drops
+ * it.  Element e = r*cols + c takes word (e mod 4) of
+ * Philox4x32-10(counter = (e/4, layer, step mod 2^32, step / 2^32),
+ *              key = (seed mod 2^32, seed / 2^32))
+ * and is dropped iff that word < floor(p * 2^32).  cols must be a multiple
+ * of 4.  mask: device [rows][cols] uint8 (written). */
+int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t rows, int32_t cols,
+                         float p, uint8_t* mask, void* stream);
+
+/* Test and diagnostic access to the tensors a call leaves in its workspace.
+ * Host only.  For tap `tap_id` of a call in `mode` with `cfg`, returns its
+ * byte offset into the workspace, its shape (unused trailing dims = 1), its
+ * element type (alexnet_dtype) and its layout: 0 = NHWC activation
+ * [N][H][W][C], 1 = row-major matrix / vector, 2 = OIHW or [out][in] weight
+ * gradient (fp32).  Returns ALEXNET_E_ARG for a tap the mode does not have. */
+int alexnet_tap(const alexnet_cfg* cfg, int mode, int tap_id, size_t* offset, int64_t shape[4],
+                int* dtype, int* layout);
+int alexnet_tap_count(void);
+const char* alexnet_tap_name(int tap_id); /* NULL if out of range */
+
+const char* alexnet_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ALEXNET_H */

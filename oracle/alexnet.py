@@ -35,11 +35,12 @@ def _g(groups, grouped):
     return groups if grouped else 1
 
 
-def forward(weights, biases, x, groups=1, train=False, seed=0, step=0):
+def forward(weights, biases, x, groups=1, train=False, seed=0, step=0, masks=None):
     """Forward pass.  Returns a dict holding every intermediate (NCHW / [N, F]).
 
     weights/biases: 8 arrays each (conv OIHW, FC [out][in]).  In train mode the
-    FC6/FC7 outputs are multiplied by the Philox keep-masks of (seed, step).
+    FC6/FC7 outputs are multiplied by the Philox keep-masks of (seed, step), or
+    by ``masks`` = (mask6, mask7) when given (rows of a larger batch's masks).
     """
     t = {}
     n = x.shape[0]
@@ -64,7 +65,8 @@ def forward(weights, biases, x, groups=1, train=False, seed=0, step=0):
         hz = L.relu(L.fc(h, weights[li], biases[li]))
         t[f"fc{li + 1}"] = hz                       # ReLU output before dropout
         if train:
-            m = L.dropout_mask(seed, step, fi, n, hz.shape[1], DROPOUT_P)
+            m = (L.dropout_mask(seed, step, fi, n, hz.shape[1], DROPOUT_P) if masks is None
+                 else np.asarray(masks[fi], np.uint8))
             t[f"mask{li + 1}"] = m
             h = hz * m
         else:

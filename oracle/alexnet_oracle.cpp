@@ -312,21 +312,28 @@ void orc_fc_fwd(const double* x, int M, int K, const double* w, const double* b,
 
 void orc_fc_bwd(const double* dy, const double* x, const double* w, int M, int K, int O,
                 double* dx, double* dw, double* db) {
+  // Each output element is a sum over o (for dx) or m (for dW) taken in
+  // ascending order; the loops run along rows so W and x are read contiguously.
   if (dx) {
-#pragma omp parallel for collapse(2)
-    for (int m = 0; m < M; ++m)
-      for (int k = 0; k < K; ++k) {
-        double acc = 0.0;
-        for (int o = 0; o < O; ++o) acc += dy[(size_t)m * O + o] * w[(size_t)o * K + k];
-        dx[(size_t)m * K + k] = acc;
+#pragma omp parallel for
+    for (int m = 0; m < M; ++m) {
+      double* out = dx + (size_t)m * K;
+      for (int k = 0; k < K; ++k) out[k] = 0.0;
+      for (int o = 0; o < O; ++o) {
+        const double d = dy[(size_t)m * O + o];
+        const double* wr = w + (size_t)o * K;
+        for (int k = 0; k < K; ++k) out[k] += d * wr[k];
       }
+    }
   }
 #pragma omp parallel for
   for (int o = 0; o < O; ++o) {
-    for (int k = 0; k < K; ++k) {
-      double acc = 0.0;
-      for (int m = 0; m < M; ++m) acc += dy[(size_t)m * O + o] * x[(size_t)m * K + k];
-      dw[(size_t)o * K + k] = acc;
+    double* out = dw + (size_t)o * K;
+    for (int k = 0; k < K; ++k) out[k] = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double d = dy[(size_t)m * O + o];
+      const double* xr = x + (size_t)m * K;
+      for (int k = 0; k < K; ++k) out[k] += d * xr[k];
     }
     if (db) {
       double acc = 0.0;

@@ -1,0 +1,145 @@
+"""Host-only tests of the C ABI: the library loads without a GPU, exports every
+symbol the header declares, validates arguments before any launch, and plans
+a consistent workspace.  No compute call reaches the device here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from deep_cnn_image_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "alexnet.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(alexnet_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_default_cfg_holds_page_constants():
+    c = B.alexnet_default_cfg(128, 2, B.BF16)
+    assert (c.batch, c.groups, c.dtype, c.lrn_n) == (128, 2, B.BF16, 5)
+    assert c.lrn_k == 2.0 and c.lrn_alpha == float(np.float32(1e-4)) and c.lrn_beta == 0.75
+    assert c.dropout_p == 0.5
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("batch", -1), ("batch", 5000), ("groups", 3),
+                                         ("groups", 0), ("dtype", 7), ("lrn_n", 4), ("lrn_n", 11),
+                                         ("lrn_k", 0.0), ("dropout_p", 1.0)])
+def test_invalid_cfg_gives_zero_workspace(field, value):
+    c = B.alexnet_default_cfg(4, 1, B.BF16)
+    setattr(c, field, value)
+    assert B.alexnet_workspace_bytes(c, B.MODE_FORWARD) == 0
+
+
+def test_tenview_batch_limit():
+    c = B.alexnet_default_cfg(512, 1, B.BF16)
+    assert B.alexnet_workspace_bytes(c, B.MODE_TENVIEW) > 0
+    c.batch = 513
+    assert B.alexnet_workspace_bytes(c, B.MODE_TENVIEW) == 0
+    assert B.alexnet_workspace_bytes(c, 3) == 0
+
+
+FAKE = 1 << 40          # a 256-aligned non-null address; never dereferenced on error paths
+
+
+def fake_params(align=256):
+    return [FAKE + i * 4096 for i in range(16)]
+
+
+def test_forward_validation_errors_before_launch():
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    ws = B.alexnet_workspace_bytes(c, B.MODE_FORWARD)
+    p = fake_params()
+    f = lambda **kw: B.alexnet_forward(kw.get("cfg", c), kw.get("params", p), kw.get("x", FAKE),
+                                       kw.get("probs", FAKE), kw.get("ws", FAKE),
+                                       kw.get("wsb", ws), 0, check=False)
+    assert f(ws=0) == B.E_NULL
+    assert f(ws=FAKE + 16) == B.E_ALIGN
+    assert f(wsb=ws - 1) == B.E_WORKSPACE
+    assert f(x=0) == B.E_NULL
+    assert f(x=FAKE + 2) == B.E_ALIGN
+    assert f(params=p[:15] + [0]) == B.E_NULL
+    assert f(params=p[:15] + [FAKE + 8]) == B.E_ALIGN
+    bad = B.alexnet_default_cfg(2, 3, B.BF16)
+    assert f(cfg=bad) == B.E_SHAPE
+    bad = B.alexnet_default_cfg(2, 1, 9)
+    assert f(cfg=bad) == B.E_DTYPE
+    null_cfg = B.lib().alexnet_forward(None, B._ptr16(p), FAKE, FAKE, FAKE, ws, None)
+    assert null_cfg == B.E_NULL
+
+
+def test_train_validation_errors_before_launch():
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    ws = B.alexnet_workspace_bytes(c, B.MODE_TRAIN)
+    p = fake_params()
+    f = lambda **kw: B.alexnet_train_step(c, kw.get("m", p), kw.get("v", p), kw.get("w", p),
+                                          kw.get("x", FAKE), kw.get("y", FAKE), 0.01, 0.9, 5e-4, 3, 0,
+                                          kw.get("loss", FAKE), None, FAKE, kw.get("wsb", ws), 0,
+                                          check=False)
+    assert f(wsb=ws - 256) == B.E_WORKSPACE
+    assert f(y=0) == B.E_NULL
+    assert f(loss=0) == B.E_NULL
+    assert f(m=p[:3] + [0] + p[4:]) == B.E_NULL
+    assert f(w=p[:3] + [FAKE + 4] + p[4:]) == B.E_ALIGN
+    assert B.alexnet_train_step(c, p, p, p, FAKE, FAKE, float("nan"), 0.9, 5e-4, 3, 0, FAKE, None,
+                                FAKE, ws, 0, check=False) == B.E_ARG
+
+
+def test_dropout_mask_validation():
+    assert B.alexnet_dropout_mask(3, 0, 0, 4, 4096, 0.5, 0, check=False) == B.E_NULL
+    assert B.alexnet_dropout_mask(3, 0, 0, 4, 4095, 0.5, FAKE, check=False) == B.E_SHAPE
+    assert B.alexnet_dropout_mask(3, 0, 0, 4, 4096, 1.5, FAKE, check=False) == B.E_ARG
+    assert B.alexnet_dropout_mask(3, 0, 0, 0, 4096, 0.5, FAKE, check=False) == B.OK   # empty: no launch
+
+
+@pytest.mark.parametrize("mode", [B.MODE_FORWARD, B.MODE_TRAIN, B.MODE_TENVIEW])
+@pytest.mark.parametrize("groups", [1, 2])
+def test_taps_are_disjoint_and_inside_workspace(mode, groups):
+    c = B.alexnet_default_cfg(3, groups, B.BF16)
+    total = B.alexnet_workspace_bytes(c, mode)
+    n_img = 30 if mode == B.MODE_TENVIEW else 3
+    spans = []
+    esz = {B.F32: 4, B.BF16: 2, B.U8: 1}
+    for name, i in B.tap_ids().items():
+        try:
+            off, shape, dt, layout = B.alexnet_tap(c, mode, i)
+        except B.AlexNetError as e:
+            assert e.status == B.E_ARG
+            continue
+        assert off % 256 == 0
+        nbytes = int(np.prod(shape)) * esz[dt]
+        spans.append((off, off + nbytes, name))
+        if layout == 0:
+            assert shape[0] == n_img
+    spans.sort()
+    for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (na, nb)
+    assert spans[-1][1] <= total
+
+
+def test_tap_shapes_follow_the_layer_list():
+    c = B.alexnet_default_cfg(2, 2, B.BF16)
+    ids = B.tap_ids()
+    get = lambda n: B.alexnet_tap(c, B.MODE_TRAIN, ids[n])[1]
+    assert get("conv1") == (2, 55, 55, 96) and get("pool1") == (2, 27, 27, 96)
+    assert get("conv2") == (2, 27, 27, 256) and get("pool2") == (2, 13, 13, 256)
+    assert get("conv3") == (2, 13, 13, 384) and get("conv5") == (2, 13, 13, 256)
+    assert get("pool5") == (2, 9216, 1, 1) and get("logits") == (2, 1000, 1, 1)
+    assert get("gw2") == (256, 48, 5, 5) and get("gw4") == (384, 192, 3, 3)
+    assert get("gw3") == (384, 256, 3, 3) and get("gw6") == (4096, 9216, 1, 1)
+    with pytest.raises(B.AlexNetError):
+        B.alexnet_tap(c, B.MODE_FORWARD, ids["gw1"])

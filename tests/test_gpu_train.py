@@ -1,0 +1,295 @@
+"""GPU parity of the training step (through the C ABI) against the CPU oracle.
+
+Batch 3 is compared end to end element by element (loss, probabilities, all
+16 gradients, the updated momentum and weights) and layer by layer in the
+backward pass (each oracle layer fed the HIP path's stored tensors).  The
+full batch of 128 is compared on the properties the oracle can afford at
+that size: per-image losses of sampled images, the dropout masks, the FC
+backward and channel subsets of the conv weight gradients on the HIP path's
+own tensors, and the SGD update of every parameter."""
+import numpy as np
+import pytest
+import torch
+
+from deep_cnn_image_amd import binding as B
+from deep_cnn_image_amd import inputs as I
+from deep_cnn_image_amd.session import Session, stream_handle, to_device
+
+from gpu_helpers import (DEV, TOL_BF16, TOL_F32_OUT, TOL_LAYER_BF16, flat, host, nchw, params_f32,
+                         rel_l2, say)
+
+pytestmark = pytest.mark.gpu
+
+NHWC = {"conv1", "lrn1", "pool1", "arg1", "conv2", "lrn2", "pool2", "arg2", "conv3", "conv4", "conv5",
+        "arg5", "dconv5", "dconv4", "dconv3", "din3", "dlrn2", "dconv2", "din2", "dlrn1", "dconv1"}
+TAPS = ("conv1", "lrn1", "pool1", "arg1", "conv2", "lrn2", "pool2", "arg2", "conv3", "conv4", "conv5",
+        "pool5", "arg5", "drop6", "drop7", "logits", "dlogits", "dfc7", "dfc6", "dflat", "dconv5",
+        "dconv4", "dconv3", "din3", "dlrn2", "dconv2", "din2", "dlrn1", "dconv1", "rowloss")
+HYPER = dict(lr=0.01, momentum_coef=0.9, weight_decay=5e-4)
+
+
+def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None):
+    n = syn.x.shape[0]
+    say(f"[gpu] train batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed} step={step}")
+    sess = Session(n, syn.groups, dtype, B.MODE_TRAIN, DEV)
+    master = params_f32(syn.master_w, syn.biases)
+    if v0 is None:
+        mom = [torch.zeros_like(m) for m in master]
+    else:
+        mom = [torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(DEV) for v in v0]
+    tdt = torch.bfloat16 if dtype == B.BF16 else torch.float32
+    work = [torch.empty(m.shape, dtype=tdt, device=DEV) for m in master]
+    B.alexnet_cast_weights(sess.cfg, master, work, stream_handle())
+    x = to_device(syn.x, dtype, DEV)
+    labels = torch.from_numpy(syn.labels.astype(np.int32)).to(DEV)
+    loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+    probs = torch.empty((n, 1000), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    r = dict(master0=[host(m) for m in master], mom0=[host(v) for v in mom],
+             work0=[w.clone() for w in work])
+    sess.train_step(master, mom, work, x, labels, loss, probs, seed=seed, step=step, **{
+        "lr": HYPER["lr"], "momentum_coef": HYPER["momentum_coef"], "weight_decay": HYPER["weight_decay"]})
+    torch.cuda.synchronize()
+    r.update(sess=sess, loss=float(loss.item()), probs=host(probs), master=[host(m) for m in master],
+             mom=[host(v) for v in mom], work=[w.clone() for w in work],
+             gw=[host(sess.tap(f"gw{i + 1}")) for i in range(8)],
+             gb=[host(sess.tap(f"gb{i + 1}")).ravel() for i in range(8)],
+             taps={k: sess.tap(k).clone() for k in TAPS})
+    return r
+
+
+def hostify(taps, rows=None):
+    out = {}
+    for k, v in taps.items():
+        t = v if rows is None else v[torch.as_tensor(rows, device=v.device)]
+        out[k] = nchw(t) if k in NHWC else flat(t)
+    return out
+
+
+def gpu_masks(n, seed=3, step=0):
+    out = []
+    for layer in (0, 1):
+        m = torch.empty((n, 4096), dtype=torch.uint8, device=DEV)
+        B.alexnet_dropout_mask(seed, step, layer, n, 4096, 0.5, m, stream_handle())
+        torch.cuda.synchronize()
+        out.append(m.cpu().numpy())
+    return out
+
+
+def check_sgd(r, syn):
+    """Every element of every tensor: v = mu v0 - wd lr w0 - lr g to within fp32
+    rounding of the three terms; w = fl(w0 + v) exactly; work = bf16(w)."""
+    lr, mu, wd = HYPER["lr"], HYPER["momentum_coef"], HYPER["weight_decay"]
+    eps = np.finfo(np.float32).eps
+    grads = []
+    for i in range(8):
+        grads += [r["gw"][i], r["gb"][i]]
+    for j in range(16):
+        w0 = r["master0"][j].ravel()
+        v0 = r["mom0"][j].ravel()
+        g = grads[j].ravel()
+        terms = (np.abs(mu * v0) + np.abs(np.float32(wd * lr) * w0) + np.abs(lr * g))
+        vref = mu * v0 - np.float64(np.float32(wd * lr)) * w0 - lr * g
+        v = r["mom"][j].ravel()
+        assert np.all(np.abs(v - vref) <= 3 * eps * terms + 1e-30), j
+        w = r["master"][j].ravel()
+        assert np.array_equal(w.astype(np.float32), (w0.astype(np.float32) + v.astype(np.float32))), j
+        wb = r["work"][j].float().cpu().numpy().ravel()
+        if r["work"][j].dtype == torch.bfloat16:
+            assert np.array_equal(wb, I.round_bf16(w.astype(np.float32))), j
+        else:
+            assert np.array_equal(wb, w.astype(np.float32)), j
+
+
+# ----------------------------------------------------------------------- batch 3
+@pytest.fixture(scope="module")
+def small(orc):
+    syn = I.config_inputs(4, batch=3)
+    r = run_train(syn)
+    z = [np.zeros_like(w, dtype=np.float64) for w in syn.master_w]
+    zb = [np.zeros_like(b, dtype=np.float64) for b in syn.biases]
+    o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
+                               syn.labels, 1, lr=0.01, momentum=0.9, weight_decay=5e-4, seed=3, step=0)
+    return syn, r, o
+
+
+def test_cast_weights_round_to_nearest_even(small):
+    syn, r, _ = small
+    for j, w in enumerate(r["work0"]):
+        ref = (syn.master_w[j // 2] if j % 2 == 0 else syn.biases[j // 2])
+        assert np.array_equal(w.float().cpu().numpy(), I.round_bf16(ref)), j
+
+
+def test_dropout_masks_bit_exact(orc, small):
+    syn, r, o = small
+    gm = gpu_masks(3)
+    for i, name in enumerate(("mask6", "mask7")):
+        assert np.array_equal(gm[i], o["taps"][name]), name
+    h = hostify(r["taps"])
+    assert np.all(h["drop6"][gm[0] == 0] == 0) and np.all(h["drop7"][gm[1] == 0] == 0)
+
+
+def test_loss_probs_and_gradients_end_to_end(small):
+    syn, r, o = small
+    e_loss = abs(r["loss"] - o["loss"]) / abs(o["loss"])
+    e_probs = rel_l2(r["probs"], o["taps"]["probs"])
+    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
+    eb = [rel_l2(r["gb"][i], o["grad_b"][i]) for i in range(8)]
+    say(f"[gpu] loss {r['loss']:.6f} vs {o['loss']:.6f} ({e_loss:.2e}); probs {e_probs:.2e}")
+    say("[gpu] grad_w rel-L2:", [f"{e:.2e}" for e in ew])
+    say("[gpu] grad_b rel-L2:", [f"{e:.2e}" for e in eb])
+    assert e_loss <= TOL_BF16 and e_probs <= TOL_BF16
+    assert max(ew) <= TOL_BF16 and max(eb) <= TOL_BF16
+    h = hostify(r["taps"])
+    eg = {k: rel_l2(h[k], o["gtaps"][k]) for k in ("dlogits", "dfc7", "dfc6", "dflat", "dconv5", "dconv4",
+                                                    "dconv3", "din3", "dconv2", "din2", "dconv1")}
+    say("[gpu] activation-gradient rel-L2:", {k: f"{v:.2e}" for k, v in eg.items()})
+    assert max(eg.values()) <= TOL_BF16
+
+
+def test_sgd_update_end_to_end(small):
+    syn, r, o = small
+    # the momentum after one step from v0 = 0 is the step itself: dw = v
+    for i in range(8):
+        assert rel_l2(r["mom"][2 * i], o["vw"][i]) <= TOL_BF16, i
+        assert rel_l2(r["mom"][2 * i + 1], o["vb"][i]) <= TOL_BF16, i
+        assert rel_l2(r["master"][2 * i] - r["master0"][2 * i], o["w"][i] - syn.master_w[i]) <= TOL_BF16, i
+    check_sgd(r, syn)
+
+
+def test_backward_layerwise(orc, small):
+    """Each backward layer of the oracle fed the HIP path's stored tensors."""
+    syn, r, o = small
+    h = hostify(r["taps"])
+    W = syn.weights
+    e = {}
+    loss, dz = orc.ce_loss_grad(orc.softmax(h["logits"]), syn.labels)
+    e["dlogits"] = rel_l2(h["dlogits"], dz)
+    e["rowloss"] = rel_l2(h["rowloss"].ravel(), -np.log(orc.softmax(h["logits"])[np.arange(3), syn.labels]))
+    dx, dw, db = orc.fc_bwd(h["dlogits"], h["drop7"], W[7])
+    e["dfc7"] = rel_l2(h["dfc7"], dx * (h["drop7"] > 0))
+    e["gw8"], e["gb8"] = rel_l2(r["gw"][7], dw), rel_l2(r["gb"][7], db)
+    dx, dw, db = orc.fc_bwd(h["dfc7"], h["drop6"], W[6])
+    e["dfc6"] = rel_l2(h["dfc6"], dx * (h["drop6"] > 0))
+    e["gw7"], e["gb7"] = rel_l2(r["gw"][6], dw), rel_l2(r["gb"][6], db)
+    dx, dw, db = orc.fc_bwd(h["dfc6"], h["pool5"], W[5])
+    e["dflat"] = rel_l2(h["dflat"], dx)
+    e["gw6"], e["gb6"] = rel_l2(r["gw"][5], dw), rel_l2(r["gb"][5], db)
+    d5 = orc.maxpool_bwd(h["dflat"].reshape(3, 256, 6, 6), h["arg5"], h["conv5"].shape)
+    e["dconv5"] = rel_l2(h["dconv5"], d5 * (h["conv5"] > 0))
+    dw, db = orc.conv2d_bwd_weight(h["dconv5"], h["conv4"], W[4].shape, 1, 1)
+    e["gw5"], e["gb5"] = rel_l2(r["gw"][4], dw), rel_l2(r["gb"][4], db)
+    dx = orc.conv2d_bwd_data(h["dconv5"], W[4], h["conv4"].shape, 1, 1)
+    e["dconv4"] = rel_l2(h["dconv4"], dx * (h["conv4"] > 0))
+    dw, db = orc.conv2d_bwd_weight(h["dconv4"], h["conv3"], W[3].shape, 1, 1)
+    e["gw4"], e["gb4"] = rel_l2(r["gw"][3], dw), rel_l2(r["gb"][3], db)
+    dx = orc.conv2d_bwd_data(h["dconv4"], W[3], h["conv3"].shape, 1, 1)
+    e["dconv3"] = rel_l2(h["dconv3"], dx * (h["conv3"] > 0))
+    dw, db = orc.conv2d_bwd_weight(h["dconv3"], h["pool2"], W[2].shape, 1, 1)
+    e["gw3"], e["gb3"] = rel_l2(r["gw"][2], dw), rel_l2(r["gb"][2], db)
+    e["din3"] = rel_l2(h["din3"], orc.conv2d_bwd_data(h["dconv3"], W[2], h["pool2"].shape, 1, 1))
+    e["dlrn2"] = rel_l2(h["dlrn2"], orc.maxpool_bwd(h["din3"], h["arg2"], h["conv2"].shape))
+    e["dconv2"] = rel_l2(h["dconv2"], orc.lrn_bwd(h["conv2"], h["dlrn2"]) * (h["conv2"] > 0))
+    dw, db = orc.conv2d_bwd_weight(h["dconv2"], h["pool1"], W[1].shape, 1, 2)
+    e["gw2"], e["gb2"] = rel_l2(r["gw"][1], dw), rel_l2(r["gb"][1], db)
+    e["din2"] = rel_l2(h["din2"], orc.conv2d_bwd_data(h["dconv2"], W[1], h["pool1"].shape, 1, 2))
+    e["dlrn1"] = rel_l2(h["dlrn1"], orc.maxpool_bwd(h["din2"], h["arg1"], h["conv1"].shape))
+    e["dconv1"] = rel_l2(h["dconv1"], orc.lrn_bwd(h["conv1"], h["dlrn1"]) * (h["conv1"] > 0))
+    dw, db = orc.conv2d_bwd_weight(h["dconv1"], syn.x, W[0].shape, 4, 0)
+    e["gw1"], e["gb1"] = rel_l2(r["gw"][0], dw), rel_l2(r["gb"][0], db)
+    say("[gpu] backward layer-isolated rel-L2:", {k: f"{v:.2e}" for k, v in e.items()})
+    for k, v in e.items():
+        limit = TOL_F32_OUT if k[:2] in ("gw", "gb") or k == "rowloss" else TOL_LAYER_BF16
+        assert v <= limit, (k, v)
+
+
+def test_grouped_train_step_small(orc):
+    syn = I.synthetic(5, 2, groups=2, bf16=True)
+    r = run_train(syn)
+    z = [np.zeros_like(w, dtype=np.float64) for w in syn.master_w]
+    zb = [np.zeros_like(b, dtype=np.float64) for b in syn.biases]
+    o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
+                               syn.labels, 2, seed=3, step=0)
+    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
+    say("[gpu] grouped grad_w rel-L2:", [f"{x:.2e}" for x in ew])
+    assert max(ew) <= TOL_BF16
+    assert abs(r["loss"] - o["loss"]) / abs(o["loss"]) <= TOL_BF16
+
+
+def test_fp32_train_step_small(orc):
+    syn = I.synthetic(6, 2, groups=1, bf16=False)
+    v0 = [np.random.default_rng(7).standard_normal(a.shape).astype(np.float32) * 1e-3
+          for a in sum(([w, b] for w, b in zip(syn.master_w, syn.biases)), [])]
+    r = run_train(syn, dtype=B.F32, seed=11, step=2**32 + 5, v0=v0)
+    vw = [v0[2 * i].astype(np.float64) for i in range(8)]
+    vb = [v0[2 * i + 1].astype(np.float64) for i in range(8)]
+    o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, vw, vb, syn.x,
+                               syn.labels, 1, seed=11, step=2**32 + 5)
+    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
+    say("[gpu] fp32 grad_w rel-L2:", [f"{x:.2e}" for x in ew])
+    assert max(ew) <= 1e-4
+    assert abs(r["loss"] - o["loss"]) / abs(o["loss"]) <= 1e-5
+    check_sgd(r, syn)
+
+
+def test_train_step_is_deterministic():
+    syn = I.config_inputs(4, batch=2)
+    a = run_train(syn)
+    b = run_train(syn)
+    for i in range(8):
+        assert np.array_equal(a["gw"][i], b["gw"][i]) and np.array_equal(a["gb"][i], b["gb"][i]), i
+    assert a["loss"] == b["loss"]
+
+
+# ----------------------------------------------------------------------- full batch 128
+def test_full_batch128_train_step(orc):
+    syn = I.config_inputs(4)
+    r = run_train(syn)
+    n = 128
+    gm = gpu_masks(n)
+    om = [orc.dropout_mask(3, 0, layer, n, 4096) for layer in (0, 1)]
+    assert np.array_equal(gm[0], om[0]) and np.array_equal(gm[1], om[1])
+    rows = np.array([0, 64, 127])
+    hs = hostify(r["taps"], rows)
+    t = orc.alexnet.forward(syn.weights, syn.biases, syn.x[rows], 1, train=True,
+                            masks=(om[0][rows], om[1][rows]))
+    rl = -np.log(t["probs"][np.arange(3), syn.labels[rows]])
+    e_rl = rel_l2(hs["rowloss"].ravel(), rl)
+    e_p = rel_l2(r["probs"][rows], t["probs"])
+    say(f"[gpu] bs128 sampled row losses rel-L2 {e_rl:.2e}, probs {e_p:.2e}, loss {r['loss']:.5f}")
+    assert e_rl <= TOL_BF16 and e_p <= TOL_BF16
+    allrow = host(r["taps"]["rowloss"]).ravel()
+    assert abs(r["loss"] - allrow.mean()) <= 1e-5 * abs(allrow.mean())
+    # FC backward at full size on the HIP path's own tensors
+    h = hostify({k: r["taps"][k] for k in ("dlogits", "drop7", "dfc7", "drop6", "dfc6", "pool5", "dflat")})
+    W = syn.weights
+    dx, dw, db = orc.fc_bwd(h["dlogits"], h["drop7"], W[7])
+    e = {"dfc7": rel_l2(h["dfc7"], dx * (h["drop7"] > 0)), "gw8": rel_l2(r["gw"][7], dw),
+         "gb8": rel_l2(r["gb"][7], db)}
+    dx, dw, db = orc.fc_bwd(h["dfc7"], h["drop6"], W[6])
+    e.update(dfc6=rel_l2(h["dfc6"], dx * (h["drop6"] > 0)), gw7=rel_l2(r["gw"][6], dw), gb7=rel_l2(r["gb"][6], db))
+    # FC6 on sampled images (data gradient is per image) and sampled output units
+    dx, _, _ = orc.fc_bwd(h["dfc6"][rows], h["pool5"][rows], W[5])
+    e["dflat[rows]"] = rel_l2(h["dflat"][rows], dx)
+    units = np.array([0, 1000, 4095])
+    _, dw, db = orc.fc_bwd(h["dfc6"][:, units], h["pool5"], W[5][units], want_dx=False)
+    e.update({"gw6[units]": rel_l2(r["gw"][5][units], dw), "gb6[units]": rel_l2(r["gb"][5][units], db)})
+    # conv weight gradients on channel subsets (all 128 images), per-image data gradients on samples
+    ch = np.array([0, 37, 95])
+    d1 = nchw(r["taps"]["dconv1"])
+    dw, db = orc.conv2d_bwd_weight(d1[:, ch], syn.x, (3, 3, 11, 11), 4, 0)
+    e["gw1[ch]"], e["gb1[ch]"] = rel_l2(r["gw"][0][ch], dw), rel_l2(r["gb"][0][ch], db)
+    del d1
+    ch5 = np.array([1, 128, 255])
+    d5 = nchw(r["taps"]["dconv5"])
+    c4 = nchw(r["taps"]["conv4"])
+    dw, db = orc.conv2d_bwd_weight(d5[:, ch5], c4, (3, 384, 3, 3), 1, 1)
+    e["gw5[ch]"], e["gb5[ch]"] = rel_l2(r["gw"][4][ch5], dw), rel_l2(r["gb"][4][ch5], db)
+    hs2 = hostify({k: r["taps"][k] for k in ("dconv2", "pool1", "din2", "conv2", "dlrn2")}, rows)
+    e["din2[rows]"] = rel_l2(hs2["din2"], orc.conv2d_bwd_data(hs2["dconv2"], W[1], hs2["pool1"].shape, 1, 2))
+    e["dconv2[rows]"] = rel_l2(hs2["dconv2"], orc.lrn_bwd(hs2["conv2"], hs2["dlrn2"]) * (hs2["conv2"] > 0))
+    say("[gpu] bs128 isolated backward rel-L2:", {k: f"{v:.2e}" for k, v in e.items()})
+    for k, v in e.items():
+        limit = TOL_F32_OUT if k[:2] in ("gw", "gb") else TOL_LAYER_BF16
+        assert v <= limit, (k, v)
+    check_sgd(r, syn)
