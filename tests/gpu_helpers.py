@@ -27,8 +27,12 @@ def say(*a):
 
 
 def rel_l2(a, b) -> float:
+    """||a - b|| / ||b||; a is reshaped to b's shape (same element count)."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
+    if a.size != b.size:
+        raise ValueError(f"size mismatch {a.shape} vs {b.shape}")
+    a = a.reshape(b.shape)
     nb = np.linalg.norm(b)
     if nb == 0:
         return float(np.linalg.norm(a))

@@ -66,6 +66,25 @@ def hostify(taps, rows=None):
     return out
 
 
+def oracle_backward_on_state(orc, syn, r, groups, masks):
+    """The oracle's whole backward pass (every layer, bf16 storage between
+    layers) run over the HIP path's saved forward state, so that both sides
+    take every ReLU-mask and pool-argmax decision on the same stored values.
+    The head (logits, softmax) is recomputed by the oracle from the stored
+    FC7 output.  Returns (loss, grad_w, grad_b, activation gradients)."""
+    h = hostify(r["taps"])
+    t = {"x": syn.x.astype(np.float64)}
+    for k in ("conv1", "conv2", "conv3", "conv4", "conv5", "pool1", "pool2", "arg1", "arg2", "arg5",
+              "drop6", "drop7"):
+        t[k] = h[k]
+    t["pool5"] = h["pool5"].reshape(-1, 256, 6, 6)
+    t["flat"] = h["pool5"]
+    t["fc6"], t["fc7"] = h["drop6"], h["drop7"]       # mask * [h > 0] == [drop > 0]
+    t["mask6"], t["mask7"] = masks
+    t["probs"] = orc.softmax(orc.fc(h["drop7"], syn.weights[7], syn.biases[7]))
+    return orc.alexnet.backward(syn.weights, t, syn.labels, groups, store="bf16")
+
+
 def gpu_masks(n, seed=3, step=0):
     out = []
     for layer in (0, 1):
@@ -109,19 +128,29 @@ def small(orc):
     z = [np.zeros_like(w, dtype=np.float64) for w in syn.master_w]
     zb = [np.zeros_like(b, dtype=np.float64) for b in syn.biases]
     o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
-                               syn.labels, 1, lr=0.01, momentum=0.9, weight_decay=5e-4, seed=3, step=0)
-    return syn, r, o
+                               syn.labels, 1, lr=0.01, momentum=0.9, weight_decay=5e-4, seed=3, step=0,
+                               store="bf16")
+    o64 = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
+                                 syn.labels, 1, lr=0.01, momentum=0.9, weight_decay=5e-4, seed=3, step=0)
+    sh = oracle_backward_on_state(orc, syn, r, 1, (o["taps"]["mask6"], o["taps"]["mask7"]))
+    # Diagnostic only: fully independent runs diverge by ~1e-3 in the forward pass,
+    # so pre-activations within that distance of zero flip their ReLU masks and
+    # route whole gradient elements differently.
+    for name, ref in (("bf16-storage", o), ("float64", o64)):
+        say(f"[gpu] independent-run grad_w rel-L2 vs {name} oracle:",
+            [f"{rel_l2(r['gw'][i], ref['grad_w'][i]):.2e}" for i in range(8)])
+    return syn, r, o, sh
 
 
 def test_cast_weights_round_to_nearest_even(small):
-    syn, r, _ = small
+    syn, r, _, _ = small
     for j, w in enumerate(r["work0"]):
         ref = (syn.master_w[j // 2] if j % 2 == 0 else syn.biases[j // 2])
         assert np.array_equal(w.float().cpu().numpy(), I.round_bf16(ref)), j
 
 
 def test_dropout_masks_bit_exact(orc, small):
-    syn, r, o = small
+    syn, r, o, _ = small
     gm = gpu_masks(3)
     for i, name in enumerate(("mask6", "mask7")):
         assert np.array_equal(gm[i], o["taps"][name]), name
@@ -130,36 +159,40 @@ def test_dropout_masks_bit_exact(orc, small):
 
 
 def test_loss_probs_and_gradients_end_to_end(small):
-    syn, r, o = small
+    syn, r, o, sh = small
     e_loss = abs(r["loss"] - o["loss"]) / abs(o["loss"])
     e_probs = rel_l2(r["probs"], o["taps"]["probs"])
-    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
-    eb = [rel_l2(r["gb"][i], o["grad_b"][i]) for i in range(8)]
     say(f"[gpu] loss {r['loss']:.6f} vs {o['loss']:.6f} ({e_loss:.2e}); probs {e_probs:.2e}")
-    say("[gpu] grad_w rel-L2:", [f"{e:.2e}" for e in ew])
-    say("[gpu] grad_b rel-L2:", [f"{e:.2e}" for e in eb])
     assert e_loss <= TOL_BF16 and e_probs <= TOL_BF16
+    loss_sh, gw, gb, gt = sh
+    ew = [rel_l2(r["gw"][i], gw[i]) for i in range(8)]
+    eb = [rel_l2(r["gb"][i], gb[i]) for i in range(8)]
+    say("[gpu] grad_w rel-L2 (oracle backward on the same forward state):", [f"{e:.2e}" for e in ew])
+    say("[gpu] grad_b rel-L2 (oracle backward on the same forward state):", [f"{e:.2e}" for e in eb])
     assert max(ew) <= TOL_BF16 and max(eb) <= TOL_BF16
+    assert abs(r["loss"] - loss_sh) / abs(loss_sh) <= 1e-4
     h = hostify(r["taps"])
-    eg = {k: rel_l2(h[k], o["gtaps"][k]) for k in ("dlogits", "dfc7", "dfc6", "dflat", "dconv5", "dconv4",
-                                                    "dconv3", "din3", "dconv2", "din2", "dconv1")}
+    eg = {k: rel_l2(h[k], gt[k]) for k in ("dlogits", "dfc7", "dfc6", "dflat", "dconv5", "dconv4",
+                                            "dconv3", "din3", "dlrn2", "dconv2", "din2", "dlrn1", "dconv1")}
     say("[gpu] activation-gradient rel-L2:", {k: f"{v:.2e}" for k, v in eg.items()})
     assert max(eg.values()) <= TOL_BF16
 
 
-def test_sgd_update_end_to_end(small):
-    syn, r, o = small
-    # the momentum after one step from v0 = 0 is the step itself: dw = v
+def test_sgd_update_end_to_end(orc, small):
+    syn, r, o, sh = small
+    _, gw, gb, _ = sh
     for i in range(8):
-        assert rel_l2(r["mom"][2 * i], o["vw"][i]) <= TOL_BF16, i
-        assert rel_l2(r["mom"][2 * i + 1], o["vb"][i]) <= TOL_BF16, i
-        assert rel_l2(r["master"][2 * i] - r["master0"][2 * i], o["w"][i] - syn.master_w[i]) <= TOL_BF16, i
+        w1, v1 = orc.sgd(syn.master_w[i], np.zeros(syn.master_w[i].shape), gw[i], 0.01, 0.9, 5e-4)
+        assert rel_l2(r["mom"][2 * i], v1) <= TOL_BF16, i
+        assert rel_l2(r["master"][2 * i] - r["master0"][2 * i], w1 - syn.master_w[i]) <= TOL_BF16, i
+        b1, u1 = orc.sgd(syn.biases[i], np.zeros(syn.biases[i].shape), gb[i], 0.01, 0.9, 5e-4)
+        assert rel_l2(r["mom"][2 * i + 1], u1) <= TOL_BF16, i
     check_sgd(r, syn)
 
 
 def test_backward_layerwise(orc, small):
     """Each backward layer of the oracle fed the HIP path's stored tensors."""
-    syn, r, o = small
+    syn, r, o, _ = small
     h = hostify(r["taps"])
     W = syn.weights
     e = {}
@@ -209,11 +242,15 @@ def test_grouped_train_step_small(orc):
     z = [np.zeros_like(w, dtype=np.float64) for w in syn.master_w]
     zb = [np.zeros_like(b, dtype=np.float64) for b in syn.biases]
     o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
-                               syn.labels, 2, seed=3, step=0)
-    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
-    say("[gpu] grouped grad_w rel-L2:", [f"{x:.2e}" for x in ew])
-    assert max(ew) <= TOL_BF16
+                               syn.labels, 2, seed=3, step=0, store="bf16")
     assert abs(r["loss"] - o["loss"]) / abs(o["loss"]) <= TOL_BF16
+    _, gw, gb, _ = oracle_backward_on_state(orc, syn, r, 2, (o["taps"]["mask6"], o["taps"]["mask7"]))
+    ew = [rel_l2(r["gw"][i], gw[i]) for i in range(8)]
+    eb = [rel_l2(r["gb"][i], gb[i]) for i in range(8)]
+    say("[gpu] grouped grad_w rel-L2:", [f"{x:.2e}" for x in ew])
+    say("[gpu] grouped independent-run grad_w rel-L2:",
+        [f"{rel_l2(r['gw'][i], o['grad_w'][i]):.2e}" for i in range(8)])
+    assert max(ew) <= TOL_BF16 and max(eb) <= TOL_BF16
 
 
 def test_fp32_train_step_small(orc):
@@ -252,7 +289,7 @@ def test_full_batch128_train_step(orc):
     rows = np.array([0, 64, 127])
     hs = hostify(r["taps"], rows)
     t = orc.alexnet.forward(syn.weights, syn.biases, syn.x[rows], 1, train=True,
-                            masks=(om[0][rows], om[1][rows]))
+                            masks=(om[0][rows], om[1][rows]), store="bf16")
     rl = -np.log(t["probs"][np.arange(3), syn.labels[rows]])
     e_rl = rel_l2(hs["rowloss"].ravel(), rl)
     e_p = rel_l2(r["probs"][rows], t["probs"])

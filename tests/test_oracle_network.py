@@ -179,3 +179,31 @@ def test_backward_central_differences_reduced_net(orc):
         fd = (loss_of(ws, bp) - loss_of(ws, bm)) / (2 * h)
         assert math.isclose(fd, gb[li][j], rel_tol=2e-5, abs_tol=1e-9), (li, j, fd, gb[li][j])
     assert checked == 24
+
+
+# ----------------------------------------------------------------- bf16 storage reading
+def test_round_bf16_ties_and_library(orc):
+    r = orc.alexnet.round_bf16
+    # hand-worked ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1);
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    cases = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -30, 3.0])
+    np.testing.assert_array_equal(r(cases), [1.0, 1 + 2 ** -6, -1.0, 1 + 2 ** -7, 3.0])
+    # float32 inputs: same as torch's float32 -> bfloat16 (round to nearest even)
+    x = np.random.default_rng(30).standard_normal(100000).astype(np.float32) * 7
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(r(x.astype(np.float64)), ref)
+
+
+def test_bf16_storage_forward_and_backward(orc):
+    A = orc.alexnet
+    s = I.synthetic(31, 2, 1, bf16=True)
+    t = A.forward(s.weights, s.biases, s.x, store="bf16", train=True, seed=3, step=0)
+    for k in ("conv1", "lrn1", "pool1", "conv2", "lrn2", "pool2", "conv3", "conv4", "conv5", "flat",
+              "fc6", "drop6", "fc7", "drop7"):
+        np.testing.assert_array_equal(A.round_bf16(t[k]), t[k])      # stored values are bf16
+    t64 = A.forward(s.weights, s.biases, s.x, train=True, seed=3, step=0)
+    assert rel(t["probs"], t64["probs"]) < 2e-2
+    _, gw, gb, g = A.backward(s.weights, t, s.labels, store="bf16")
+    for k in ("dlogits", "dfc7", "dfc6", "dflat", "dconv5", "dconv4", "dconv3", "din3", "dlrn2",
+              "dconv2", "din2", "dlrn1", "dconv1"):
+        np.testing.assert_array_equal(A.round_bf16(g[k]), g[k])
