@@ -15,14 +15,26 @@
 // use v_mfma_f32_16x16x4_f32.  Four waves per workgroup, 64-wide.
 #pragma once
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace ax {
 
-constexpr int BK = 32;
+constexpr int BK = GEMM_BK;
 constexpr int NTHREADS = 256;
 
 template <typename T> struct VecOf { static constexpr int V = 16 / sizeof(T); };
 template <typename T> struct Lds { static constexpr int LS = BK + VecOf<T>::V; };  // padded row
+
+// LDS element offset of (row, col) in a [rows][LS] tile.  The 16-byte granule
+// index along k is XOR-ed with bits 4..6 of the row: the transposed pair
+// writes of k-outer loaders (16 lanes on rows 8 apart) then spread over all
+// banks, while the MFMA fragment reads (16 consecutive rows, same granule)
+// see one constant permutation and stay conflict-free thanks to the pad.
+template <typename T>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  constexpr int G = VecOf<T>::V;
+  return row * Lds<T>::LS + (((col / G) ^ ((row >> 4) & 7)) * G) + (col % G);
+}
 
 struct GemmGrid {
   int M, N, K;          // per group
@@ -32,7 +44,37 @@ struct GemmGrid {
 };
 
 // ------------------------------------------------------------------ loaders
-// Common shape: chunk c of the tile covers V consecutive elements.
+// Interface: setup(r0, g, k_begin) once per tile, then load() fetches the
+// current BK-wide k-slice into registers and steps to the next one, and
+// store(lds) writes the registers into the LDS tile [rows][BK + pad].  All
+// index decomposition happens in setup(); load() only adds and compares.
+//
+// K-contiguous sources write 16-byte chunks straight into LDS.  K-outer
+// sources (rows contiguous, k outer) are transposed on the way: each thread
+// holds two consecutive k-rows of one 16-byte row chunk and writes them as
+// 32-bit (bf16) or 64-bit (fp32) pairs.
+
+template <typename T> struct PairStore;
+template <> struct PairStore<bf16> {
+  // rows e of chunk lo/hi (k, k+1) -> d[e*LS] = (lo_e, hi_e)
+  template <int LS>
+  static __device__ __forceinline__ void run(bf16* d, uint4 lo, uint4 hi) {
+    const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, b[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint32_t*>(d + (2 * i) * LS) = (a[i] & 0xFFFFu) | (b[i] << 16);
+      *reinterpret_cast<uint32_t*>(d + (2 * i + 1) * LS) = (a[i] >> 16) | (b[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct PairStore<float> {
+  template <int LS>
+  static __device__ __forceinline__ void run(float* d, uint4 lo, uint4 hi) {
+    const uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w}, b[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint2*>(d + i * LS) = make_uint2(a[i], b[i]);
+  }
+};
 
 // Rows contiguous along k: element (r, k) at base[r * ld + k].  Needs K % V == 0
 // and 16-byte aligned rows.
@@ -42,64 +84,64 @@ struct LdKC {
   static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
   static constexpr int LS = Lds<T>::LS;
   const T* p; int64_t ld; int rows; int K; int64_t gstride;
-  const T* base; int r0;
+  const T* base; int r0, k;
   uint4 reg[NCH];
-  __device__ void setup(int r0_, int g) { r0 = r0_; base = p + (int64_t)g * gstride; }
-  __device__ void load(int k0) {
+  __device__ void setup(int r0_, int g, int kb) { r0 = r0_; k = kb; base = p + (int64_t)g * gstride; }
+  __device__ void load() {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (c < NCHUNK) {
-        const int r = r0 + c / CPR, k = k0 + (c % CPR) * V;
-        if (r < rows && k < K) v = *reinterpret_cast<const uint4*>(base + r * ld + k);
+        const int r = r0 + c / CPR, kk = k + (c % CPR) * V;
+        if (r < rows && kk < K) v = *reinterpret_cast<const uint4*>(base + r * ld + kk);
       }
       reg[i] = v;
     }
+    k += BK;
   }
   __device__ void store(T* s) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + (c / CPR) * LS + (c % CPR) * V) = reg[i];
+      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
     }
   }
 };
 
 // Rows contiguous, k outer: element (r, k) at base[k * ld + r].  Needs
-// rows % V == 0.  The slice is transposed on its way into LDS.
+// rows % V == 0.
 template <typename T, int R>
 struct LdKO {
-  static constexpr int V = VecOf<T>::V, CPK = R / V, NCHUNK = BK * CPK;
-  static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
+  static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
+  static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
   static constexpr int LS = Lds<T>::LS;
   const T* p; int64_t ld; int rows; int K; int64_t gstride;
-  const T* base; int r0;
-  uint4 reg[NCH];
-  __device__ void setup(int r0_, int g) { r0 = r0_; base = p + (int64_t)g * gstride; }
-  __device__ void load(int k0) {
+  const T* base; int r0, k;
+  uint4 lo[NT], hi[NT];
+  __device__ void setup(int r0_, int g, int kb) { r0 = r0_; k = kb; base = p + (int64_t)g * gstride; }
+  __device__ void load() {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < NCHUNK) {
-        const int k = k0 + c / CPK, r = r0 + (c % CPK) * V;
-        if (r < rows && k < K) v = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + r);
+      uint4 a = make_uint4(0, 0, 0, 0), b = a;
+      if (c < NTASK) {
+        const int kk = k + 2 * (c / CPK), r = r0 + (c % CPK) * V;
+        if (r < rows) {
+          const T* q = base + (int64_t)kk * ld + r;
+          if (kk < K) a = *reinterpret_cast<const uint4*>(q);
+          if (kk + 1 < K) b = *reinterpret_cast<const uint4*>(q + ld);
+        }
       }
-      reg[i] = v;
+      lo[i] = a; hi[i] = b;
     }
+    k += BK;
   }
   __device__ void store(T* s) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) {
-        T e[V];
-        unpack_u4(reg[i], e);
-        T* d = s + (c % CPK) * V * LS + c / CPK;
-#pragma unroll
-        for (int j = 0; j < V; ++j) d[j * LS] = e[j];
-      }
+      if (c < NTASK) PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
     }
   }
 };
@@ -120,8 +162,9 @@ struct LdIm2col {
   const T* p; ConvGeom cg; int M; int K;
   int hb[NCH], wb[NCH];
   const T* rowp[NCH];
+  int kc[NCH], kh[NCH], kw[NCH], ci[NCH];
   uint4 reg[NCH];
-  __device__ void setup(int r0, int g) {
+  __device__ void setup(int r0, int g, int kb) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
@@ -135,29 +178,33 @@ struct LdIm2col {
         wb[i] = wo * cg.stride - cg.pad;
         rowp[i] = p + (int64_t)n * cg.H * cg.W * cg.Ctot + g * cg.Cg;
       }
+      const int k = kb + (c % CPR) * V;
+      const int tap = k / cg.Cg;
+      kc[i] = k; ci[i] = k - tap * cg.Cg; kh[i] = tap / cg.KW; kw[i] = tap - kh[i] * cg.KW;
     }
   }
-  __device__ void load(int k0) {
+  __device__ void load() {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      const int k = k0 + (c % CPR) * V;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < NCHUNK && k < K) {
-        const int tap = k / cg.Cg, ci = k - tap * cg.Cg;
-        const int kh = tap / cg.KW, kw = tap - kh * cg.KW;
-        const int hi = hb[i] + kh, wi = wb[i] + kw;
-        if ((unsigned)hi < (unsigned)cg.H && (unsigned)wi < (unsigned)cg.W)
-          v = *reinterpret_cast<const uint4*>(rowp[i] + ((int64_t)hi * cg.W + wi) * cg.Ctot + ci);
-      }
+      const int hi = hb[i] + kh[i], wi = wb[i] + kw[i];
+      if (c < NCHUNK && kc[i] < K && (unsigned)hi < (unsigned)cg.H && (unsigned)wi < (unsigned)cg.W)
+        v = *reinterpret_cast<const uint4*>(rowp[i] + ((int64_t)hi * cg.W + wi) * cg.Ctot + ci[i]);
       reg[i] = v;
+      kc[i] += BK;
+      ci[i] += BK;
+      while (ci[i] >= cg.Cg) {
+        ci[i] -= cg.Cg;
+        if (++kw[i] == cg.KW) { kw[i] = 0; ++kh[i]; }
+      }
     }
   }
   __device__ void store(T* s) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + (c / CPR) * LS + (c % CPR) * V) = reg[i];
+      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
     }
   }
 };
@@ -179,6 +226,25 @@ __device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, i
   flip = v >= 5;
 }
 
+// (c, kh, kw) of a layer-1 reduction index, stepped one position at a time.
+struct Conv1K {
+  int k, ch, kh, kw;
+  __device__ __forceinline__ void set(int kk) {
+    k = kk; ch = kk / 121; const int r = kk - ch * 121; kh = r / 11; kw = r - kh * 11;
+  }
+  __device__ __forceinline__ void step() {
+    ++k;
+    if (++kw == 11) { kw = 0; if (++kh == 11) { kh = 0; ++ch; } }
+  }
+  // advance by n < 121 positions
+  template <int n>
+  __device__ __forceinline__ void skip() {
+    k += n; kw += n % 11; kh += n / 11;
+    if (kw >= 11) { kw -= 11; ++kh; }
+    if (kh >= 11) { kh -= 11; ++ch; }
+  }
+};
+
 template <typename T, int R>
 struct LdConv1 {
   static constexpr int V = VecOf<T>::V, CPR = BK / V, NCHUNK = R * CPR;
@@ -186,147 +252,169 @@ struct LdConv1 {
   static constexpr int LS = Lds<T>::LS;
   static constexpr int KREAL = 3 * 11 * 11;
   const T* p; Conv1Src src; int M;
-  const T* img[NCH]; int y[NCH], x[NCH], dir[NCH];
+  const T* img[NCH]; int dir[NCH];
+  Conv1K kk[NCH];
   uint4 reg[NCH];
-  __device__ void setup(int r0, int) {
+  __device__ void setup(int r0, int, int kb) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       const int m = r0 + c / CPR;
-      img[i] = nullptr; y[i] = 0; x[i] = 0; dir[i] = 1;
+      img[i] = nullptr; dir[i] = 1;
       if (c < NCHUNK && m < M) {
         const int n = m / 3025, rem = m - n * 3025;
         const int ho = rem / 55, wo = rem - ho * 55;
         if (src.tenview) {
           int y0, x0, flip;
           tenview_offset(n % 10, src.Hs - src.crop, y0, x0, flip);
-          img[i] = p + (int64_t)(n / 10) * 3 * src.Hs * src.Ws;
-          y[i] = y0 + ho * 4;
-          x[i] = flip ? x0 + src.crop - 1 - wo * 4 : x0 + wo * 4;
+          const int x = flip ? x0 + src.crop - 1 - wo * 4 : x0 + wo * 4;
+          img[i] = p + (int64_t)(n / 10) * 3 * src.Hs * src.Ws + (int64_t)(y0 + ho * 4) * src.Ws + x;
           dir[i] = flip ? -1 : 1;
         } else {
-          img[i] = p + (int64_t)n * 3 * src.Hs * src.Ws;
-          y[i] = ho * 4; x[i] = wo * 4;
+          img[i] = p + (int64_t)n * 3 * src.Hs * src.Ws + (int64_t)(ho * 4) * src.Ws + wo * 4;
         }
       }
+      kk[i].set(kb + (c % CPR) * V);
     }
   }
-  __device__ void load(int k0) {
+  __device__ void load() {
+    const int plane = src.Hs * src.Ws;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + i * NTHREADS;
       T e[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const int k = k0 + (c % CPR) * V + j;
         T val = T(0);
-        if (c < NCHUNK && img[i] && k < KREAL) {
-          const int ch = k / 121, r = k - ch * 121;
-          const int kh = r / 11, kw = r - kh * 11;
-          val = img[i][((int64_t)ch * src.Hs + y[i] + kh) * src.Ws + x[i] + dir[i] * kw];
-        }
+        if (img[i] && kk[i].k < KREAL)
+          val = img[i][kk[i].ch * plane + kk[i].kh * src.Ws + dir[i] * kk[i].kw];
         e[j] = val;
+        kk[i].step();
       }
       reg[i] = pack_u4(e);
+      kk[i].template skip<BK - V>();
     }
   }
   __device__ void store(T* s) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + (c / CPR) * LS + (c % CPR) * V) = reg[i];
+      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
     }
+  }
+};
+
+// Output pixel p = (n, ho, wo) over [Nimg][Ho][Wo], stepped by BK at a time.
+struct PixelIter {
+  int p, n, ho, wo;
+  __device__ __forceinline__ void set(int pp, int Ho, int Wo) {
+    p = pp; const int hw = Ho * Wo; n = pp / hw; const int rem = pp - n * hw; ho = rem / Wo; wo = rem - ho * Wo;
+  }
+  __device__ __forceinline__ void advance(int Ho, int Wo) {
+    p += BK; wo += BK;
+    while (wo >= Wo) { wo -= Wo; if (++ho == Ho) { ho = 0; ++n; } }
   }
 };
 
 // Weight-gradient B operand: element (r = (kh, kw, ci), k = output pixel p) =
 // X[n(p)][ho*s - pad + kh][wo*s - pad + kw][g*Cg + ci] of an NHWC tensor.
-// k is outer, so the slice is transposed into LDS.  Needs Cg % V == 0.
+// Needs Cg % V == 0 (a row chunk never straddles two taps).
 template <typename T, int R>
 struct LdWgradB {
-  static constexpr int V = VecOf<T>::V, CPK = R / V, NCHUNK = BK * CPK;
-  static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
+  static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
+  static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
   static constexpr int LS = Lds<T>::LS;
   const T* p; ConvGeom cg; int rows; int P;   // rows = KH*KW*Cg, P = Nimg*Ho*Wo
-  int r0; const T* gbase;
-  uint4 reg[NCH];
-  __device__ void setup(int r0_, int g) { r0 = r0_; gbase = p + g * cg.Cg; }
-  __device__ void load(int k0) {
+  const T* colp[NT]; int hoff[NT], woff[NT]; bool rok[NT];
+  PixelIter it[NT];
+  uint4 lo[NT], hi[NT];
+  __device__ void setup(int r0, int g, int kb) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int pk = k0 + c / CPK, r = r0 + (c % CPK) * V;
-      if (c < NCHUNK && pk < P && r < rows) {
-        const int tap = r / cg.Cg, ci = r - tap * cg.Cg;
-        const int kh = tap / cg.KW, kw = tap - kh * cg.KW;
-        const int hw = cg.Ho * cg.Wo;
-        const int n = pk / hw, rem = pk - n * hw;
-        const int ho = rem / cg.Wo, wo = rem - ho * cg.Wo;
-        const int hi = ho * cg.stride - cg.pad + kh, wi = wo * cg.stride - cg.pad + kw;
-        if ((unsigned)hi < (unsigned)cg.H && (unsigned)wi < (unsigned)cg.W)
-          v = *reinterpret_cast<const uint4*>(gbase + (((int64_t)n * cg.H + hi) * cg.W + wi) * cg.Ctot + ci);
-      }
-      reg[i] = v;
+      const int r = r0 + (c % CPK) * V;
+      rok[i] = c < NTASK && r < rows;
+      const int rr = rok[i] ? r : 0;
+      const int tap = rr / cg.Cg, ci = rr - tap * cg.Cg;
+      const int kh = tap / cg.KW, kw = tap - kh * cg.KW;
+      hoff[i] = kh - cg.pad; woff[i] = kw - cg.pad;
+      colp[i] = p + g * cg.Cg + ci;
+      it[i].set(kb + 2 * (c / CPK), cg.Ho, cg.Wo);
+    }
+  }
+  __device__ __forceinline__ uint4 fetch(int i, const PixelIter& q) const {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    const int h = q.ho * cg.stride + hoff[i], w = q.wo * cg.stride + woff[i];
+    if (rok[i] && q.p < P && (unsigned)h < (unsigned)cg.H && (unsigned)w < (unsigned)cg.W)
+      v = *reinterpret_cast<const uint4*>(colp[i] + (((int64_t)q.n * cg.H + h) * cg.W + w) * cg.Ctot);
+    return v;
+  }
+  __device__ void load() {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      PixelIter q = it[i];
+      lo[i] = fetch(i, q);
+      ++q.p; if (++q.wo == cg.Wo) { q.wo = 0; if (++q.ho == cg.Ho) { q.ho = 0; ++q.n; } }
+      hi[i] = fetch(i, q);
+      it[i].advance(cg.Ho, cg.Wo);
     }
   }
   __device__ void store(T* s) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) {
-        T e[V];
-        unpack_u4(reg[i], e);
-        T* d = s + (c % CPK) * V * LS + c / CPK;
-#pragma unroll
-        for (int j = 0; j < V; ++j) d[j * LS] = e[j];
-      }
+      if (c < NTASK) PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
     }
   }
 };
 
 // Layer-1 weight-gradient B operand: element (r = (c, kh, kw), k = output pixel)
-// of the NCHW input images (scalar gathers; r beyond 363 reads as zero).
+// of the NCHW input images; r beyond 363 reads as zero.
 template <typename T, int R>
 struct LdConv1WgradB {
-  static constexpr int V = VecOf<T>::V, CPK = R / V, NCHUNK = BK * CPK;
-  static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
+  static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
+  static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
   static constexpr int LS = Lds<T>::LS;
   const T* p; int Hs, Ws; int P;
-  int r0;
-  T reg[NCH][V];
-  __device__ void setup(int r0_, int) { r0 = r0_; }
-  __device__ void load(int k0) {
+  int off[NT][V];
+  PixelIter it[NT];
+  T lo[NT][V], hi[NT][V];
+  __device__ void setup(int r0, int, int kb) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      const int pk = k0 + c / CPK, rb = r0 + (c % CPK) * V;
-      const bool ok = c < NCHUNK && pk < P;
-      int n = 0, ho = 0, wo = 0;
-      if (ok) { n = pk / 3025; const int rem = pk - n * 3025; ho = rem / 55; wo = rem - ho * 55; }
-      const T* img = p + (int64_t)n * 3 * Hs * Ws;
+      Conv1K q;
+      q.set(r0 + (c % CPK) * V);
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const int r = rb + j;
-        T val = T(0);
-        if (ok && r < 363) {
-          const int ch = r / 121, q = r - ch * 121;
-          const int kh = q / 11, kw = q - kh * 11;
-          val = img[((int64_t)ch * Hs + ho * 4 + kh) * Ws + wo * 4 + kw];
-        }
-        reg[i][j] = val;
+        off[i][j] = (c < NTASK && q.k < 363) ? (q.ch * Hs + q.kh) * Ws + q.kw : -1;
+        q.step();
       }
+      it[i].set(kb + 2 * (c / CPK), 55, 55);
+    }
+  }
+  __device__ __forceinline__ void fetch(int i, const PixelIter& q, T (&e)[V]) const {
+    const T* img = p + (int64_t)q.n * 3 * Hs * Ws + (q.ho * 4) * Ws + q.wo * 4;
+    const bool ok = q.p < P;
+#pragma unroll
+    for (int j = 0; j < V; ++j) e[j] = (ok && off[i][j] >= 0) ? img[off[i][j]] : T(0);
+  }
+  __device__ void load() {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      PixelIter q = it[i];
+      fetch(i, q, lo[i]);
+      ++q.p; if (++q.wo == 55) { q.wo = 0; if (++q.ho == 55) { q.ho = 0; ++q.n; } }
+      fetch(i, q, hi[i]);
+      it[i].advance(55, 55);
     }
   }
   __device__ void store(T* s) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) {
-        T* d = s + (c % CPK) * V * LS + c / CPK;
-#pragma unroll
-        for (int j = 0; j < V; ++j) d[j * LS] = reg[i][j];
-      }
+      if (c < NTASK)
+        PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), pack_u4(lo[i]),
+                                       pack_u4(hi[i]));
     }
   }
 };
@@ -381,36 +469,40 @@ template <typename T, int FM, int FN> struct Mma;
 
 template <int FM, int FN>
 struct Mma<bf16, FM, FN> {
-  static constexpr int LS = Lds<bf16>::LS;
-  static __device__ __forceinline__ void run(const bf16* As, const bf16* Bs, f32x4_t (&acc)[FM][FN],
-                                             int lane) {
+  // As/Bs: LDS tiles; ra/rb: first row of this wave's slice in each tile
+  static __device__ __forceinline__ void run(const bf16* As, int ra, const bf16* Bs, int rb,
+                                             f32x4_t (&acc)[FM][FN], int lane) {
     const int r = lane & 15, kq = (lane >> 4) * 8;
-    bf16x8_t a[FM], b[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(As + (i * 16 + r) * LS + kq);
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[FM], b[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (j * 16 + r) * LS + kq);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off<bf16>(ra + i * 16 + r, kk + kq));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off<bf16>(rb + j * 16 + r, kk + kq));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
   }
 };
 
 template <int FM, int FN>
 struct Mma<float, FM, FN> {
-  static constexpr int LS = Lds<float>::LS;
-  static __device__ __forceinline__ void run(const float* As, const float* Bs, f32x4_t (&acc)[FM][FN],
-                                             int lane) {
+  static __device__ __forceinline__ void run(const float* As, int ra, const float* Bs, int rb,
+                                             f32x4_t (&acc)[FM][FN], int lane) {
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 4) {
       float a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = As[(i * 16 + r) * LS + kk + kq];
+      for (int i = 0; i < FM; ++i) a[i] = As[lds_off<float>(ra + i * 16 + r, kk + kq)];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = Bs[(j * 16 + r) * LS + kk + kq];
+      for (int j = 0; j < FN; ++j) b[j] = Bs[lds_off<float>(rb + j * 16 + r, kk + kq)];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -453,8 +545,8 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
   const int kt0 = s * gg.kt_per_split;
   const int kt1 = min(kt0 + gg.kt_per_split, total_kt);
 
-  al.setup(m0, g);
-  bl.setup(n0, g);
+  al.setup(m0, g, kt0 * BK);
+  bl.setup(n0, g, kt0 * BK);
   f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -462,16 +554,16 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (kt0 < kt1) {
-    al.load(kt0 * BK);
-    bl.load(kt0 * BK);
+    al.load();
+    bl.load();
     al.store(As);
     bl.store(Bs);
     __syncthreads();
     for (int kt = kt0; kt < kt1; ++kt) {
       const int cur = (kt - kt0) & 1;
       const bool more = kt + 1 < kt1;
-      if (more) { al.load((kt + 1) * BK); bl.load((kt + 1) * BK); }
-      Mma<T, FM, FN>::run(As + cur * A_EL + wm * WTM * LS, Bs + cur * B_EL + wn * WTN * LS, acc, lane);
+      if (more) { al.load(); bl.load(); }
+      Mma<T, FM, FN>::run(As + cur * A_EL, wm * WTM, Bs + cur * B_EL, wn * WTN, acc, lane);
       if (more) { al.store(As + (cur ^ 1) * A_EL); bl.store(Bs + (cur ^ 1) * B_EL); }
       __syncthreads();
     }

@@ -703,36 +703,73 @@ hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t st) {
 }
 
 // =========================================================================
-// Column sums (bias gradients): two ordered passes
+// Column sums (bias gradients) of a [rows][C] matrix, C % 8 == 0.  Pass 1:
+// block b sums its contiguous row range; each thread owns one 8-column chunk
+// and a fixed subset of the rows, and the block combines those in a fixed
+// order.  Pass 2: one wavefront per column adds the per-block partials with a
+// fixed butterfly.  No atomics: the result does not depend on timing.
 // =========================================================================
-static constexpr int COLSUM_ROWS = 512;
+static constexpr int COLSUM_CW = 2048;   // columns per block (256 chunks of 8)
+
+static int colsum_blocks(int64_t rows) {
+  int64_t rb = (rows + 511) / 512;
+  if (rb < 32) rb = 32;
+  return (int)((rows + rb - 1) / rb);
+}
 
 template <typename T>
-__global__ void k_colsum1(const T* __restrict__ x, int64_t rows, int C, float* __restrict__ part) {
-  const int c = blockIdx.y * TPB + threadIdx.x;
-  if (c >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.x * COLSUM_ROWS;
-  const int64_t r1 = min(r0 + COLSUM_ROWS, rows);
-  float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += Num<T>::load(x[r * C + c]);
-  part[(int64_t)blockIdx.x * C + c] = s;
+__global__ void k_colsum1(const T* __restrict__ x, int64_t rows, int C, int64_t rb, float* __restrict__ part) {
+  __shared__ float sh[TPB][9];
+  const int c0 = blockIdx.y * COLSUM_CW;
+  const int w = min(COLSUM_CW, C - c0);
+  const int cpr = w >> 3, nrl = TPB / cpr;
+  const int t = threadIdx.x, cc = t % cpr, rl = t / cpr;
+  const int64_t r0 = (int64_t)blockIdx.x * rb, r1 = min(r0 + rb, rows);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  if (rl < nrl) {
+    for (int64_t r = r0 + rl; r < r1; r += nrl) {
+      float v[8];
+      Pack8<T>::load(x + r * C + c0 + cc * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sh[t][e] = acc[e];
+  __syncthreads();
+  for (int col = t; col < w; col += TPB) {
+    const int q = col >> 3, e = col & 7;
+    float s = 0.f;
+    for (int j = 0; j < nrl; ++j) s += sh[j * cpr + q][e];
+    part[(int64_t)blockIdx.x * C + c0 + col] = s;
+  }
 }
+
 __global__ void k_colsum2(const float* __restrict__ part, int nb, int C, float* __restrict__ out) {
-  const int c = blockIdx.x * TPB + threadIdx.x;
-  if (c >= C) return;
+  const int lane = threadIdx.x & 63;
+  const int col = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
+  if (col >= C) return;
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * C + c];
-  out[c] = s;
+  for (int b = lane; b < nb; b += 64) s += part[(int64_t)b * C + col];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) out[col] = s;
 }
+
 size_t colsum_scratch_bytes(int64_t rows, int C) {
-  return (size_t)cdiv(rows, COLSUM_ROWS) * C * sizeof(float);
+  return (size_t)colsum_blocks(rows) * C * sizeof(float);
 }
+
 hipError_t colsum(DType dt, const void* x, int64_t rows, int C, float* out, float* scratch, hipStream_t st) {
-  const int nb = cdiv(rows, COLSUM_ROWS);
-  const dim3 g1(nb, cdiv(C, TPB));
-  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, scratch);
-  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, scratch);
-  hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB)), dim3(TPB), 0, st, scratch, nb, C, out);
+  if (C % 8) return hipErrorInvalidValue;
+  const int nb = colsum_blocks(rows);
+  const int64_t rb = (rows + nb - 1) / nb;
+  const dim3 g1(nb, cdiv(C, COLSUM_CW));
+  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, rb, scratch);
+  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, rb, scratch);
+  hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB / 64)), dim3(TPB), 0, st, scratch, nb, C, out);
   return hipGetLastError();
 }
 

@@ -11,10 +11,13 @@ enum DType { F32 = 0, BF16 = 1 };
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// Reduction depth of one GEMM k-tile (elements).
+constexpr int GEMM_BK = 64;
+
 // Split-K factor actually used for K (in elements) when `want` splits are
-// requested: every split gets at least one 32-wide k-tile and none is empty.
+// requested: every split gets at least one k-tile and none is empty.
 inline int eff_splits(int K, int want) {
-  const int kt = cdiv(K, 32);
+  const int kt = cdiv(K, GEMM_BK);
   if (want < 1) want = 1;
   if (want > kt) want = kt;
   const int per = cdiv(kt, want);
