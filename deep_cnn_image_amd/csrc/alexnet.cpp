@@ -61,7 +61,7 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   const alexnet_cfg& c = p.cfg;
 
   // weights into the layouts the GEMM loaders read
-  HIPCHK(w_pad_rows(dt, prm[0], at(ws, p.w1p), 96, 363, 384, st));
+  HIPCHK(conv1_w_s2d(dt, prm[0], at(ws, p.w1s), st));
   for (int i = 1; i < 5; ++i) {
     const ConvShape& s = net.conv[i];
     HIPCHK(w_khwc(dt, prm[2 * i], at(ws, p.wr[i]), s.Cout, s.Cin / s.groups, s.K, st));
@@ -69,7 +69,8 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
 
   const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
   const int hs = tenview ? 256 : 227;
-  HIPCHK(conv1_fwd(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.w1p), prm[1], tp(ws, p, T_CONV1), st));
+  HIPCHK(conv1_s2d(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st));
+  HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st));
   HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_LRN1), (int64_t)N * 55 * 55, 96, c.lrn_k, c.lrn_alpha,
                  c.lrn_beta, c.lrn_n, st));
   HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1), N, 55, 55, 96, 0,
@@ -109,7 +110,7 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   return ALEXNET_OK;
 }
 
-int enqueue_backward(const Plan& p, void* const* work, const void* x, void* ws, hipStream_t st) {
+int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -169,7 +170,7 @@ int enqueue_backward(const Plan& p, void* const* work, const void* x, void* ws, 
                   55, 55, 96, 0, st));
   HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_DLRN1), tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96,
                  c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
-  HIPCHK(conv1_wgrad(dt, N, 227, 227, tp(ws, p, T_DCONV1), x, part, p.part_bytes, gw(0), st));
+  HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st));
   HIPCHK(colsum(dt, tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96, gb(0), cs, st));
   return ALEXNET_OK;
 }
@@ -258,7 +259,7 @@ int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* c
                  (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
     return ALEXNET_E_HIP;
   if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
-  if ((r = enqueue_backward(p, work, x, ws, st)) != ALEXNET_OK) return r;
+  if ((r = enqueue_backward(p, work, ws, st)) != ALEXNET_OK) return r;
   TensorSet ts;
   for (int i = 0; i < 8; ++i) {
     ts.master[2 * i] = master[2 * i];

@@ -209,100 +209,6 @@ struct LdIm2col {
   }
 };
 
-// Layer-1 input: NCHW images with three channels, stride 4, 11x11, no padding;
-// k = (c, kh, kw) = the OIHW order of the layer-1 weights (363 values, zero
-// beyond).  In ten-view mode image n is view n % 10 of source n / 10: the
-// crop offset and mirroring are applied on the fly.
-struct Conv1Src {
-  int Hs, Ws;        // source plane size (227, or 256 for ten-view sources)
-  int tenview;       // 0 or 1
-  int crop;          // 227
-};
-
-__device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, int& flip) {
-  const int b = v % 5;
-  y0 = (b == 2 || b == 3) ? d : (b == 4 ? d / 2 : 0);
-  x0 = (b == 1 || b == 3) ? d : (b == 4 ? d / 2 : 0);
-  flip = v >= 5;
-}
-
-// (c, kh, kw) of a layer-1 reduction index, stepped one position at a time.
-struct Conv1K {
-  int k, ch, kh, kw;
-  __device__ __forceinline__ void set(int kk) {
-    k = kk; ch = kk / 121; const int r = kk - ch * 121; kh = r / 11; kw = r - kh * 11;
-  }
-  __device__ __forceinline__ void step() {
-    ++k;
-    if (++kw == 11) { kw = 0; if (++kh == 11) { kh = 0; ++ch; } }
-  }
-  // advance by n < 121 positions
-  template <int n>
-  __device__ __forceinline__ void skip() {
-    k += n; kw += n % 11; kh += n / 11;
-    if (kw >= 11) { kw -= 11; ++kh; }
-    if (kh >= 11) { kh -= 11; ++ch; }
-  }
-};
-
-template <typename T, int R>
-struct LdConv1 {
-  static constexpr int V = VecOf<T>::V, CPR = BK / V, NCHUNK = R * CPR;
-  static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
-  static constexpr int KREAL = 3 * 11 * 11;
-  const T* p; Conv1Src src; int M;
-  const T* img[NCH]; int dir[NCH];
-  Conv1K kk[NCH];
-  uint4 reg[NCH];
-  __device__ void setup(int r0, int, int kb) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + i * NTHREADS;
-      const int m = r0 + c / CPR;
-      img[i] = nullptr; dir[i] = 1;
-      if (c < NCHUNK && m < M) {
-        const int n = m / 3025, rem = m - n * 3025;
-        const int ho = rem / 55, wo = rem - ho * 55;
-        if (src.tenview) {
-          int y0, x0, flip;
-          tenview_offset(n % 10, src.Hs - src.crop, y0, x0, flip);
-          const int x = flip ? x0 + src.crop - 1 - wo * 4 : x0 + wo * 4;
-          img[i] = p + (int64_t)(n / 10) * 3 * src.Hs * src.Ws + (int64_t)(y0 + ho * 4) * src.Ws + x;
-          dir[i] = flip ? -1 : 1;
-        } else {
-          img[i] = p + (int64_t)n * 3 * src.Hs * src.Ws + (int64_t)(ho * 4) * src.Ws + wo * 4;
-        }
-      }
-      kk[i].set(kb + (c % CPR) * V);
-    }
-  }
-  __device__ void load() {
-    const int plane = src.Hs * src.Ws;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      T e[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        T val = T(0);
-        if (img[i] && kk[i].k < KREAL)
-          val = img[i][kk[i].ch * plane + kk[i].kh * src.Ws + dir[i] * kk[i].kw];
-        e[j] = val;
-        kk[i].step();
-      }
-      reg[i] = pack_u4(e);
-      kk[i].template skip<BK - V>();
-    }
-  }
-  __device__ void store(T* s) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
-    }
-  }
-};
-
 // Output pixel p = (n, ho, wo) over [Nimg][Ho][Wo], stepped by BK at a time.
 struct PixelIter {
   int p, n, ho, wo;
@@ -363,58 +269,6 @@ struct LdWgradB {
     for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
       if (c < NTASK) PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
-    }
-  }
-};
-
-// Layer-1 weight-gradient B operand: element (r = (c, kh, kw), k = output pixel)
-// of the NCHW input images; r beyond 363 reads as zero.
-template <typename T, int R>
-struct LdConv1WgradB {
-  static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
-  static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
-  const T* p; int Hs, Ws; int P;
-  int off[NT][V];
-  PixelIter it[NT];
-  T lo[NT][V], hi[NT][V];
-  __device__ void setup(int r0, int, int kb) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int c = threadIdx.x + i * NTHREADS;
-      Conv1K q;
-      q.set(r0 + (c % CPK) * V);
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        off[i][j] = (c < NTASK && q.k < 363) ? (q.ch * Hs + q.kh) * Ws + q.kw : -1;
-        q.step();
-      }
-      it[i].set(kb + 2 * (c / CPK), 55, 55);
-    }
-  }
-  __device__ __forceinline__ void fetch(int i, const PixelIter& q, T (&e)[V]) const {
-    const T* img = p + (int64_t)q.n * 3 * Hs * Ws + (q.ho * 4) * Ws + q.wo * 4;
-    const bool ok = q.p < P;
-#pragma unroll
-    for (int j = 0; j < V; ++j) e[j] = (ok && off[i][j] >= 0) ? img[off[i][j]] : T(0);
-  }
-  __device__ void load() {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      PixelIter q = it[i];
-      fetch(i, q, lo[i]);
-      ++q.p; if (++q.wo == 55) { q.wo = 0; if (++q.ho == 55) { q.ho = 0; ++q.n; } }
-      fetch(i, q, hi[i]);
-      it[i].advance(55, 55);
-    }
-  }
-  __device__ void store(T* s) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int c = threadIdx.x + i * NTHREADS;
-      if (c < NTASK)
-        PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), pack_u4(lo[i]),
-                                       pack_u4(hi[i]));
     }
   }
 };

@@ -34,24 +34,101 @@ static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int 
   return hipGetLastError();
 }
 
-// ---- layer 1 forward: NCHW images -> NHWC [N][55][55][96]
-template <typename T>
-static hipError_t conv1_fwd_t(const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
-                              const void* b1, void* y, hipStream_t st) {
-  constexpr int BM = 128, BN = 96;
-  LdConv1<T, BM> a;
-  a.p = (const T*)x; a.src = Conv1Src{Hs, Ws, tenview, 227}; a.M = Nimg * 3025;
-  LdKC<T, BN> b;
-  b.p = (const T*)w1p; b.ld = 384; b.rows = 96; b.K = 384; b.gstride = 0;
-  EpBiasRelu<T> e;
-  e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
-  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, 384, 1, 1, st);
+// ---- layer 1: space-to-depth
+// The stride-4 11x11 convolution over 3 channels is evaluated as a stride-1
+// 3x3 convolution over 4x4 pixel blocks: X'[n][bh][bw][c*16 + dh*4 + dw] =
+// x[n][c][4bh+dh][4bw+dw] (zero beyond the 227x227 image), 57x57 blocks of 48
+// values, and W'[co][kh'][kw'][c*16 + dh*4 + dw] = W[co][c][4kh'+dh][4kw'+dw]
+// (zero where 4kh'+dh or 4kw'+dw >= 11).  Output (ho, wo) reads blocks
+// (ho + kh', wo + kw'), i.e. pixels 4ho + kh, 4wo + kw: the same sum.
+static constexpr int S2D_B = 57, S2D_C = 48, S2D_K = 3 * 3 * S2D_C;
+
+__device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, int& flip) {
+  const int b = v % 5;
+  y0 = (b == 2 || b == 3) ? d : (b == 4 ? d / 2 : 0);
+  x0 = (b == 1 || b == 3) ? d : (b == 4 ? d / 2 : 0);
+  flip = v >= 5;
 }
 
-hipError_t conv1_fwd(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
-                     const void* b1, void* y, hipStream_t st) {
-  return dt == BF16 ? conv1_fwd_t<bf16>(x, Hs, Ws, tenview, Nimg, w1p, b1, y, st)
-                    : conv1_fwd_t<float>(x, Hs, Ws, tenview, Nimg, w1p, b1, y, st);
+// One workgroup per (image, block row): stage the 12 input rows (3 channels x
+// 4 rows, 228 columns with the last one zero) in LDS, then write the 57 x 48
+// values of the block row contiguously.  Ten-view mode: image n is view n % 10
+// of source n / 10 (227x227 crop at the view's offset, mirrored for views 5..9).
+template <typename T>
+__global__ void k_s2d(const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws, int tenview) {
+  __shared__ T rows[12][228];
+  const int n = blockIdx.x / S2D_B, bh = blockIdx.x - n * S2D_B;
+  int y0 = 0, x0 = 0, flip = 0;
+  const T* img;
+  if (tenview) {
+    tenview_offset(n % 10, Hs - 227, y0, x0, flip);
+    img = x + (int64_t)(n / 10) * 3 * Hs * Ws;
+  } else {
+    img = x + (int64_t)n * 3 * Hs * Ws;
+  }
+  for (int i = threadIdx.x; i < 12 * 228; i += TPB) {
+    const int r = i / 228, xc = i - r * 228;
+    const int c = r >> 2, yc = 4 * bh + (r & 3);
+    T v = T(0);
+    if (yc < 227 && xc < 227) {
+      const int sx = flip ? x0 + 226 - xc : x0 + xc;
+      v = img[((int64_t)c * Hs + y0 + yc) * Ws + sx];
+    }
+    rows[r][xc] = v;
+  }
+  __syncthreads();
+  T* out = xs + (int64_t)blockIdx.x * S2D_B * S2D_C;
+  for (int i = threadIdx.x; i < S2D_B * S2D_C; i += TPB) {
+    const int bw = i / S2D_C, q = i - bw * S2D_C;
+    const int c = q >> 4, dh = (q >> 2) & 3, dw = q & 3;
+    out[i] = rows[c * 4 + dh][4 * bw + dw];
+  }
+}
+
+template <typename T>
+__global__ void k_w1_s2d(const T* __restrict__ w, T* __restrict__ o) {
+  const int i = blockIdx.x * TPB + threadIdx.x;
+  if (i >= 96 * S2D_K) return;
+  const int co = i / S2D_K, r = i - co * S2D_K;
+  const int tap = r / S2D_C, q = r - tap * S2D_C;
+  const int kh = (tap / 3) * 4 + ((q >> 2) & 3), kw = (tap % 3) * 4 + (q & 3), c = q >> 4;
+  o[i] = (kh < 11 && kw < 11) ? w[((co * 3 + c) * 11 + kh) * 11 + kw] : T(0);
+}
+
+hipError_t conv1_s2d(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs,
+                     hipStream_t st) {
+  const dim3 g(Nimg * S2D_B);
+  if (dt == BF16) hipLaunchKernelGGL((k_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview);
+  else hipLaunchKernelGGL((k_s2d<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)xs, Hs, Ws, tenview);
+  return hipGetLastError();
+}
+
+hipError_t conv1_w_s2d(DType dt, const void* w, void* out, hipStream_t st) {
+  const dim3 g = grid1d(96 * S2D_K);
+  if (dt == BF16) hipLaunchKernelGGL((k_w1_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out);
+  else hipLaunchKernelGGL((k_w1_s2d<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out);
+  return hipGetLastError();
+}
+
+static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
+
+template <typename T>
+static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
+                              hipStream_t st) {
+  constexpr int BM = 128, BN = 96;
+  LdIm2col<T, BM> a;
+  a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
+  LdKC<T, BN> b;
+  b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
+  EpBiasRelu<T> e;
+  e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
+  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, S2D_K, 1, 1, st);
+}
+
+hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
+                     hipStream_t st) {
+  return dt == BF16 ? conv1_fwd_t<bf16>(xs, Nimg, ws2d, b1, y, st)
+                    : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, st);
 }
 
 // Picks the n-tile for an output width N: 128 when it divides, else 96, else
@@ -136,12 +213,14 @@ size_t conv_wgrad_part_bytes(const ConvShape& s) {
   return (size_t)s.groups * wgrad_splits(tiles, P) * Cog * N * sizeof(float);
 }
 size_t conv1_wgrad_part_bytes(int Nimg) {
-  const int tiles = cdiv(96, 128) * cdiv(368, 128);
-  return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * 368 * sizeof(float);
+  const int tiles = cdiv(96, 128) * cdiv(S2D_K, 128);
+  return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * S2D_K * sizeof(float);
 }
 
-// gw[co][ci][kh][kw] = sum_s part[g][s][co_l][(kh*KW + kw)*Cg + ci]   (rkhwc = 1)
-//                   or sum_s part[g][s][co_l][ci*KH*KW + kh*KW + kw]  (rkhwc = 0)
+// gw[co][ci][kh][kw] = sum_s part[g][s][co_l][r] with
+//   r = (kh*KW + kw)*Cg + ci                                  (mode 1)
+//   r = ci*KH*KW + kh*KW + kw                                 (mode 0)
+//   r = ((kh/4)*3 + kw/4)*48 + ci*16 + (kh%4)*4 + kw%4        (mode 2: layer 1, space-to-depth)
 __global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg, int Np, int Cg,
                                int KH, int KW, int rkhwc, float* __restrict__ gw) {
   const int64_t o = (int64_t)blockIdx.x * TPB + threadIdx.x;
@@ -152,7 +231,12 @@ __global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int
   const int rem = (int)(o - (int64_t)co * Cg * KK);
   const int ci = rem / KK, t = rem - ci * KK;
   const int g = co / Mg, col = co - g * Mg;
-  const int r = rkhwc ? t * Cg + ci : rem;
+  int r;
+  if (rkhwc == 1) r = t * Cg + ci;
+  else if (rkhwc == 2) {
+    const int kh = t / KW, kw = t - kh * KW;
+    r = ((kh >> 2) * 3 + (kw >> 2)) * 48 + ci * 16 + (kh & 3) * 4 + (kw & 3);
+  } else r = rem;
   const float* p = part + ((int64_t)g * S * Mg + col) * Np + r;
   float acc = 0.f;
   for (int s = 0; s < S; ++s) acc += p[(int64_t)s * Mg * Np];
@@ -190,29 +274,29 @@ hipError_t conv_wgrad(DType dt, const ConvShape& s, const void* dy, const void* 
 }
 
 template <typename T>
-static hipError_t conv1_wgrad_t(int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
-                                size_t part_bytes, float* gw, hipStream_t st) {
+static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
+                                float* gw, hipStream_t st) {
   constexpr int BM = 128, BN = 128;
-  const int N = 368, P = Nimg * 3025;
+  const int N = S2D_K, P = Nimg * 3025;
   const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
   if ((size_t)S * 96 * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
   LdKO<T, BM> a;
   a.p = (const T*)dy; a.ld = 96; a.rows = 96; a.K = P; a.gstride = 0;
-  LdConv1WgradB<T, BN> b;
-  b.p = (const T*)x; b.Hs = Hs; b.Ws = Ws; b.P = P;
+  LdWgradB<T, BN> b;
+  b.p = (const T*)xs; b.cg = conv1_geom(); b.rows = N; b.P = P;
   EpF32 e;
   e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
   hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * 363), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 0,
+  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * 363), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
                      gw);
   return hipGetLastError();
 }
 
-hipError_t conv1_wgrad(DType dt, int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
-                       size_t part_bytes, float* gw, hipStream_t st) {
-  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, Hs, Ws, dy, x, part, part_bytes, gw, st)
-                    : conv1_wgrad_t<float>(Nimg, Hs, Ws, dy, x, part, part_bytes, gw, st);
+hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
+                       float* gw, hipStream_t st) {
+  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, st)
+                    : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, st);
 }
 
 // ---- fully-connected layers
@@ -362,14 +446,6 @@ __global__ void k_w_khwc(const T* __restrict__ w, T* __restrict__ o, int Cout, i
 }
 
 template <typename T>
-__global__ void k_w_pad(const T* __restrict__ w, T* __restrict__ o, int rows, int k, int kpad) {
-  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (i >= (int64_t)rows * kpad) return;
-  const int r = (int)(i / kpad), c = (int)(i - (int64_t)r * kpad);
-  o[i] = c < k ? w[(int64_t)r * k + c] : T(0);
-}
-
-template <typename T>
 __global__ void k_w_dgrad(const T* __restrict__ w, T* __restrict__ o, int G, int Cog, int Cig, int K) {
   const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
   if (i >= (int64_t)G * Cig * K * K * Cog) return;
@@ -386,12 +462,6 @@ hipError_t w_khwc(DType dt, const void* w, void* out, int Cout, int Cg, int K, h
   const dim3 g = grid1d((int64_t)Cout * Cg * K * K);
   if (dt == BF16) hipLaunchKernelGGL((k_w_khwc<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, Cout, Cg, K);
   else hipLaunchKernelGGL((k_w_khwc<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, Cout, Cg, K);
-  return hipGetLastError();
-}
-hipError_t w_pad_rows(DType dt, const void* w, void* out, int rows, int k, int kpad, hipStream_t st) {
-  const dim3 g = grid1d((int64_t)rows * kpad);
-  if (dt == BF16) hipLaunchKernelGGL((k_w_pad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, rows, k, kpad);
-  else hipLaunchKernelGGL((k_w_pad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, rows, k, kpad);
   return hipGetLastError();
 }
 hipError_t w_dgrad(DType dt, const void* w, void* out, int G, int Cog, int Cig, int K, hipStream_t st) {

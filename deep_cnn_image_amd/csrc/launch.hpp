@@ -30,14 +30,19 @@ struct ConvShape {
 
 // ---- weight re-layouts (per call; weights change every training step)
 hipError_t w_khwc(DType, const void* w_oihw, void* out, int Cout, int Cg, int K, hipStream_t);
-hipError_t w_pad_rows(DType, const void* w, void* out, int rows, int k, int kpad, hipStream_t);
 hipError_t w_dgrad(DType, const void* w_oihw, void* out, int G, int Coutg, int Cing, int K,
                    hipStream_t);
 
 // ---- convolutions (bf16 MFMA or fp32 MFMA, fp32 accumulate)
-// layer 1 from NCHW images (or ten-view sources), y NHWC = relu(conv + b)
-hipError_t conv1_fwd(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, const void* w1p,
-                     const void* b1, void* y, hipStream_t);
+// Layer 1 runs as a 3x3 stride-1 convolution over 4x4 pixel blocks:
+// xs [N][57][57][48] from NCHW images (or ten-view sources, cropped and
+// mirrored), ws [96][432] from the OIHW weights.
+constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
+constexpr size_t S2D_W_ELEMS = 96 * 432;
+hipError_t conv1_s2d(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs, hipStream_t);
+hipError_t conv1_w_s2d(DType, const void* w_oihw, void* ws, hipStream_t);
+// y NHWC [N][55][55][96] = relu(conv1 + b)
+hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t);
 // NHWC conv + bias + ReLU (layers 2-5)
 hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, const void* b, void* y,
                     hipStream_t);
@@ -47,9 +52,9 @@ hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, c
 // fp32 weight gradient (OIHW) of layers 2-5; `part` is split-K scratch
 hipError_t conv_wgrad(DType, const ConvShape&, const void* dy, const void* x, float* part,
                       size_t part_bytes, float* gw, hipStream_t);
-// fp32 weight gradient of layer 1 from NCHW images
-hipError_t conv1_wgrad(DType, int Nimg, int Hs, int Ws, const void* dy, const void* x, float* part,
-                       size_t part_bytes, float* gw, hipStream_t);
+// fp32 weight gradient (OIHW) of layer 1 from the space-to-depth input xs
+hipError_t conv1_wgrad(DType, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
+                       float* gw, hipStream_t);
 size_t conv_wgrad_part_bytes(const ConvShape&);
 size_t conv1_wgrad_part_bytes(int Nimg);
 

@@ -82,8 +82,9 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
   const bool train = mode == ALEXNET_MODE_TRAIN;
 
   Alloc a;
-  // re-laid-out working weights
-  p->w1p = a.take(96 * 384 * e);
+  // layer-1 input as 4x4 pixel blocks, and re-laid-out working weights
+  p->xs2d = a.take((size_t)N * S2D_ELEMS * e);
+  p->w1s = a.take(S2D_W_ELEMS * e);
   for (int i = 1; i < 5; ++i) {
     p->wr[i] = a.take((size_t)net.wcount[i] * e);
     if (train) p->wt[i] = a.take((size_t)net.wcount[i] * e);

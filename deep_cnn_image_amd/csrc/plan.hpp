@@ -46,7 +46,7 @@ struct Plan {
   int N;          // images through the network (ten-view: 10 * batch)
   int esz;        // bytes per activation element
   Net net;
-  Buf w1p, wr[5], wt[5];
+  Buf xs2d, w1s, wr[5], wt[5];   // layer-1 blocks, re-laid-out weights
   TapDesc tap[T_COUNT];
   Buf part, colsum;
   size_t part_bytes = 0, colsum_bytes = 0;
