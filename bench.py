@@ -1,17 +1,19 @@
 """Benchmark: AlexNet training step (forward, loss, backward, SGD) at batch 128
-on one MI355X, bf16 with fp32 accumulation, synthetic inputs.
+on one MI355X, bf16 with fp32 accumulation and fp32 master weights, synthetic
+inputs resident in HBM.
 
-Prints one JSON line.  `value` is training images/s over the timed steps;
-the forward pass alone (batch 128, single tower and two-tower) is reported
-beside it, as are the roofline figure of the dominant kernel and the CPU
-oracle timed on a bounded sample.
+Prints one JSON line.  `value` is training images/s over the timed steps.
+Beside it: the forward pass alone at batch 128 (single tower and two-tower),
+per-kernel MFMA / HBM fractions from HIP events recorded around each kernel
+(one untimed diagnostic pass), the roofline figure of the dominant kernel
+measured with HIP events inside the timed region, and the CPU oracle timed on
+a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
 
 import argparse
-import ctypes as C
 import json
 import os
 import sys
@@ -20,6 +22,54 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+CONV = {  # name: (Cin, Cout, k, Ho, grouped)
+    "CONV1": (3, 96, 11, 55, False), "CONV2": (96, 256, 5, 27, True), "CONV3": (256, 384, 3, 13, False),
+    "CONV4": (384, 384, 3, 13, True), "CONV5": (384, 256, 3, 13, True),
+}
+N_PARAMS_SINGLE = 62_378_344
+
+
+def conv_flops(name, n, groups):
+    cin, cout, k, ho, grouped = CONV[name]
+    g = groups if grouped else 1
+    return 2.0 * cout * (cin // g) * k * k * n * ho * ho
+
+
+def kernel_work(kt, n, groups):
+    """Algorithmic work of one launch: ("mfma", FLOP) or ("hbm", bytes).
+    Bytes count each input read once and each output written once (bf16
+    activations, uint8 argmax, fp32 optimizer state)."""
+    e = 2
+    layer, _, op = kt.partition("_")
+    if layer.startswith("CONV") and op in ("FWD", "WGRAD", "DGRAD"):
+        return "mfma", conv_flops(layer, n, groups)
+    if kt.startswith("FC"):
+        fin, fout = {"FC6": (9216, 4096), "FC7": (4096, 4096), "FC8": (4096, 1000)}[layer]
+        # weight streaming bound at this batch: weights + activations once
+        if op == "FWD":
+            return "hbm", e * (fin * fout + n * fin + n * fout)
+        if op == "DGRAD":
+            return "hbm", e * (fin * fout + n * fout + n * fin)
+        return "hbm", e * (n * fout + n * fin) + 4 * fin * fout          # WGRAD: fp32 dW
+    act = {"55x96": n * 55 * 55 * 96, "27x96": n * 27 * 27 * 96, "27x256": n * 27 * 27 * 256,
+           "13x256": n * 13 * 13 * 256, "6x256": n * 6 * 6 * 256}
+    table = {
+        "S2D": e * (n * 3 * 227 * 227 + n * 57 * 57 * 48),
+        "LRN1_FWD": 2 * e * act["55x96"], "LRN2_FWD": 2 * e * act["27x256"],
+        "LRN1_BWD": 3 * e * act["55x96"], "LRN2_BWD": 3 * e * act["27x256"],
+        "POOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
+        "POOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
+        "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
+        "POOL1_BWD": (e + 1) * act["27x96"] + e * act["55x96"],
+        "POOL2_BWD": (e + 1) * act["13x256"] + e * act["27x256"],
+        "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
+        "SGD": 22 * N_PARAMS_SINGLE,
+    }
+    return "hbm", float(table[kt])
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -27,7 +77,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["train", "forward", "all"], default="all")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="images in the CPU-oracle sample")
     return ap.parse_args()
 
 
@@ -48,79 +98,166 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     B.lib()
-    out = {}
+    h = I.TRAIN_HYPER
 
-    def timed(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
+    def new_events(k):
+        evs = []
+        for _ in range(k):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(); b.record()
+            evs.append((a, b))
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(warmup + i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        return evs
 
     # ---------------------------------------------------------------- training step
-    if args.only in ("train", "all"):
-        syn = I.config_inputs(4)
-        n = syn.x.shape[0]
-        sess = Session(n, 1, B.BF16, B.MODE_TRAIN, dev)
-        master = []
-        for w, b in zip(syn.master_w, syn.biases):
-            master += [torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)]
-        mom = [torch.zeros_like(m) for m in master]
-        work = [torch.empty(m.shape, dtype=torch.bfloat16, device=dev) for m in master]
-        B.alexnet_cast_weights(sess.cfg, master, work, stream_handle())
-        x = to_device(syn.x, B.BF16, dev)
-        labels = torch.from_numpy(syn.labels).to(dev)
-        loss = torch.zeros(1, dtype=torch.float32, device=dev)
-        h = I.TRAIN_HYPER
+    syn = I.config_inputs(4)
+    n = syn.x.shape[0]
+    sess = Session(n, 1, B.BF16, B.MODE_TRAIN, dev)
+    master = []
+    for w, b in zip(syn.master_w, syn.biases):
+        master += [torch.from_numpy(w).to(dev), torch.from_numpy(b).to(dev)]
+    mom = [torch.zeros_like(m) for m in master]
+    work = [torch.empty(m.shape, dtype=torch.bfloat16, device=dev) for m in master]
+    B.alexnet_cast_weights(sess.cfg, master, work, stream_handle())
+    x = to_device(syn.x, B.BF16, dev)
+    labels = torch.from_numpy(syn.labels).to(dev)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = stream_handle()
 
-        def step(i):
-            sess.train_step(master, mom, work, x, labels, loss, None, lr=h["lr"],
-                            momentum_coef=h["momentum"], weight_decay=h["weight_decay"],
-                            seed=h["dropout_seed"], step=i)
+    def train(i, timers=()):
+        B.alexnet_train_step_timed(sess.cfg, master, mom, work, x, labels, h["lr"], h["momentum"],
+                                   h["weight_decay"], h["dropout_seed"], i, loss, None, sess.ws,
+                                   sess.ws_bytes, stream, list(timers))
 
-        out["train_s"] = timed(step, args.steps, args.warmup)
-        out["train_n"] = n
-        out["loss"] = float(loss.item())
-        del sess
+    step = 0
+    for _ in range(args.warmup):
+        train(step); step += 1
+    torch.cuda.synchronize()
+
+    # diagnostic pass (untimed): every kernel bracketed by its own events
+    diag_steps = 3
+    names = list(B.KERNELS)
+    evs = [new_events(len(names)) for _ in range(diag_steps)]
+    for d in range(diag_steps):
+        train(step, [(B.KT[nm], evs[d][j][0].cuda_event, evs[d][j][1].cuda_event)
+                     for j, nm in enumerate(names)])
+        step += 1
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for j, nm in enumerate(names):
+        ms = [evs[d][j][0].elapsed_time(evs[d][j][1]) for d in range(diag_steps)]
+        if min(ms) > 0:
+            per_kernel[nm] = sum(ms) / len(ms)
+    dominant = max(per_kernel, key=per_kernel.get)
+
+    # timed region: events only around the dominant kernel
+    tev = new_events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        train(step, [(B.KT[dominant], tev[i][0].cuda_event, tev[i][1].cuda_event)])
+        step += 1
+    torch.cuda.synchronize()
+    train_s = (time.perf_counter() - t0) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in tev) / args.steps
+    final_loss = float(loss.item())
+    del sess
 
     # ---------------------------------------------------------------- forward passes
-    if args.only in ("forward", "all"):
-        for cfg, key in ((2, "fwd"), (3, "fwd_grouped")):
-            syn = I.config_inputs(cfg)
-            n = syn.x.shape[0]
-            sess = Session(n, syn.groups, B.BF16, B.MODE_FORWARD, dev)
-            params = sess.upload_params(syn.weights, syn.biases)
-            x = to_device(syn.x, B.BF16, dev)
-            probs = torch.empty((n, 1000), dtype=torch.float32, device=dev)
-            out[key + "_s"] = timed(lambda i: sess.forward(params, x, probs), args.steps, args.warmup)
-            out[key + "_n"] = n
-            del sess
+    fwd = {}
+    fwd_kernels = {}
+    for cfg, key in ((2, "single"), (3, "two_tower")):
+        s2 = I.config_inputs(cfg)
+        n2 = s2.x.shape[0]
+        fs = Session(n2, s2.groups, B.BF16, B.MODE_FORWARD, dev)
+        params = fs.upload_params(s2.weights, s2.biases)
+        x2 = to_device(s2.x, B.BF16, dev)
+        probs = torch.empty((n2, 1000), dtype=torch.float32, device=dev)
+
+        def fwd_call(timers=()):
+            B.alexnet_forward_timed(fs.cfg, params, x2, probs, fs.ws, fs.ws_bytes, stream, list(timers))
+
+        for _ in range(args.warmup):
+            fwd_call()
+        fnames = [nm for nm in names if nm.endswith("_FWD") or nm == "S2D"]
+        fev = new_events(len(fnames))
+        fwd_call([(B.KT[nm], fev[j][0].cuda_event, fev[j][1].cuda_event) for j, nm in enumerate(fnames)])
+        torch.cuda.synchronize()
+        fwd_kernels[key] = {nm: fev[j][0].elapsed_time(fev[j][1]) for j, nm in enumerate(fnames)}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fwd_call()
+        torch.cuda.synchronize()
+        fwd[key] = (time.perf_counter() - t0) / args.steps
+        del fs
+
+    # ---------------------------------------------------------------- fractions of roofline
+    def frac(nm, ms, groups=1):
+        kind, work = kernel_work(nm, n, groups)
+        if kind == "mfma":
+            return {"bound": "mfma", "TFLOP/s": round(work / (ms * 1e-3) / 1e12, 1),
+                    "frac": round(work / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "us": round(ms * 1e3, 2)}
+        return {"bound": "hbm", "GB/s": round(work / (ms * 1e-3) / 1e9, 1),
+                "frac": round(work / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2)}
+
+    kernels_train = {nm: frac(nm, ms) for nm, ms in per_kernel.items()}
+    conv_fwd_flops = sum(conv_flops(c, n, 1) for c in CONV)
+    conv_fwd_ms = sum(fwd_kernels["single"][c + "_FWD"] for c in CONV)
+    conv_train_flops = conv_fwd_flops * 3 - conv_flops("CONV1", n, 1)   # fwd + wgrad + dgrad (no conv1 dgrad)
+    conv_train_ms = sum(ms for nm, ms in per_kernel.items() if nm.startswith("CONV"))
+
+    kind, work = kernel_work(dominant, n, 1)
+    achieved = work / (dom_ms * 1e-3) / (1e12 if kind == "mfma" else 1e9)
+    peak = PEAK_BF16_TFLOPS if kind == "mfma" else PEAK_HBM_GBS
+    roofline = {"kernel": dominant, "bound": kind, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s" if kind == "mfma" else "GB/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "avg_launch_us": round(dom_ms * 1e3, 2),
+                "work_per_launch": work}
 
     rec = {
         "metric": "images/s AlexNet bs128 fwd and train step; conv MFMA % of bf16 peak",
-        "value": round(out["train_n"] / out["train_s"], 1) if "train_s" in out else None,
+        "value": round(n / train_s, 1),
         "unit": "images/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(out.get("train_s", 0.0) * 1e3, 4),
+        "ms_per_step": round(train_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "AlexNet training step, batch 128, single tower, bf16 with fp32 "
-                               "accumulate and fp32 master weights", "global_batch": 128},
+        "config": {"workload": "AlexNet training step (forward, cross-entropy, backward, SGD momentum "
+                               "0.9 wd 5e-4), batch 128, single tower, 3x227x227 N(0,1) images, "
+                               "bf16 activations/weights with fp32 accumulate and fp32 master weights",
+                   "global_batch": n},
+        "loss": round(final_loss, 5),
+        "forward": {"images_per_s": round(n / fwd["single"], 1), "ms": round(fwd["single"] * 1e3, 4),
+                    "conv_mfma_frac": round(conv_fwd_flops / (conv_fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "forward_two_tower": {"images_per_s": round(n / fwd["two_tower"], 1),
+                              "ms": round(fwd["two_tower"] * 1e3, 4)},
+        "train_conv_mfma_frac": round(conv_train_flops / (conv_train_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels_train": kernels_train,
+        "kernels_forward": {nm: frac(nm, ms) for nm, ms in fwd_kernels["single"].items()},
+        "roofline": roofline,
     }
-    if "fwd_s" in out:
-        rec["forward"] = {"images_per_s": round(out["fwd_n"] / out["fwd_s"], 1),
-                          "ms": round(out["fwd_s"] * 1e3, 4)}
-    if "fwd_grouped_s" in out:
-        rec["forward_two_tower"] = {"images_per_s": round(out["fwd_grouped_n"] / out["fwd_grouped_s"], 1),
-                                    "ms": round(out["fwd_grouped_s"] * 1e3, 4)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        k = args.cpu_sample
+        s3 = I.config_inputs(4, batch=k)
+        zw = [np.zeros(w.shape) for w in s3.master_w]
+        zb = [np.zeros(b.shape) for b in s3.biases]
+        t0 = time.perf_counter()
+        oracle.alexnet.train_step(s3.weights, s3.biases, s3.master_w, s3.biases, zw, zb, s3.x, s3.labels, 1,
+                                  seed=3, step=0, store="bf16")
+        cpu_s = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(k / cpu_s, 3), "unit": "images/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"one training step (forward, loss, backward, SGD) on {k} images of the "
+                                         f"batch-128 workload, float64 direct loops, {cpu_s:.1f} s"}
     print(json.dumps(rec), flush=True)
 
 

@@ -22,14 +22,29 @@ MODE_FORWARD, MODE_TRAIN, MODE_TENVIEW = 0, 1, 2
 EXPORTED = (
     "alexnet_default_cfg", "alexnet_workspace_bytes", "alexnet_forward", "alexnet_forward_tenview",
     "alexnet_train_step", "alexnet_cast_weights", "alexnet_dropout_mask", "alexnet_tap",
-    "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string",
+    "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string", "alexnet_forward_timed",
+    "alexnet_train_step_timed",
 )
+
+# alexnet_kernel ids (kernel-timing hooks)
+KERNELS = (
+    "S2D", "CONV1_FWD", "CONV2_FWD", "CONV3_FWD", "CONV4_FWD", "CONV5_FWD", "LRN1_FWD", "LRN2_FWD",
+    "POOL1_FWD", "POOL2_FWD", "POOL5_FWD", "FC6_FWD", "FC7_FWD", "FC8_FWD", "FC8_DGRAD", "FC7_DGRAD",
+    "FC6_DGRAD", "FC8_WGRAD", "FC7_WGRAD", "FC6_WGRAD", "POOL5_BWD", "CONV5_WGRAD", "CONV4_WGRAD",
+    "CONV3_WGRAD", "CONV2_WGRAD", "CONV1_WGRAD", "CONV5_DGRAD", "CONV4_DGRAD", "CONV3_DGRAD",
+    "CONV2_DGRAD", "POOL2_BWD", "LRN2_BWD", "POOL1_BWD", "LRN1_BWD", "SGD",
+)
+KT = {name: i + 1 for i, name in enumerate(KERNELS)}
 
 
 class Cfg(C.Structure):
     _fields_ = [("batch", C.c_int32), ("groups", C.c_int32), ("dtype", C.c_int32),
                 ("lrn_n", C.c_int32), ("lrn_k", C.c_float), ("lrn_alpha", C.c_float),
                 ("lrn_beta", C.c_float), ("dropout_p", C.c_float)]
+
+
+class Timer(C.Structure):
+    _fields_ = [("kernel", C.c_int32), ("start", C.c_void_p), ("stop", C.c_void_p)]
 
 
 class AlexNetError(RuntimeError):
@@ -61,6 +76,13 @@ def lib():
     L.alexnet_train_step.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, vp, C.c_float, C.c_float,
                                      C.c_float, C.c_uint64, C.c_uint64, vp, vp, vp, C.c_size_t, vp]
     L.alexnet_train_step.restype = C.c_int
+    tp = C.POINTER(Timer)
+    L.alexnet_forward_timed.argtypes = [cfgp, _PTR16, vp, vp, vp, C.c_size_t, vp, tp, C.c_int32]
+    L.alexnet_forward_timed.restype = C.c_int
+    L.alexnet_train_step_timed.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, vp, C.c_float, C.c_float,
+                                           C.c_float, C.c_uint64, C.c_uint64, vp, vp, vp, C.c_size_t,
+                                           vp, tp, C.c_int32]
+    L.alexnet_train_step_timed.restype = C.c_int
     L.alexnet_cast_weights.argtypes = [cfgp, _PTR16, _PTR16, vp]
     L.alexnet_cast_weights.restype = C.c_int
     L.alexnet_dropout_mask.argtypes = [C.c_uint64, C.c_uint64, C.c_int32, C.c_int32, C.c_int32,
@@ -133,6 +155,31 @@ def alexnet_train_step(cfg, master, momentum, work, x, labels, lr, momentum_coef
                                  weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None,
                                  _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
     return _check(s, "alexnet_train_step") if check else s
+
+
+def _timers(timers):
+    """[(kernel id, start event handle, stop event handle), ...] -> (array, n)."""
+    if not timers:
+        return None, 0
+    arr = (Timer * len(timers))(*[Timer(k, s, e) for k, s, e in timers])
+    return arr, len(timers)
+
+
+def alexnet_forward_timed(cfg, params, x, probs, ws, ws_bytes, stream, timers, check=True) -> int:
+    arr, n = _timers(timers)
+    s = lib().alexnet_forward_timed(C.byref(cfg), _ptr16(params), _ptr(x) or None, _ptr(probs) or None,
+                                    _ptr(ws) or None, ws_bytes, _ptr(stream) or None, arr, n)
+    return _check(s, "alexnet_forward_timed") if check else s
+
+
+def alexnet_train_step_timed(cfg, master, momentum, work, x, labels, lr, momentum_coef, weight_decay,
+                             seed, step, loss, probs, ws, ws_bytes, stream, timers, check=True) -> int:
+    arr, n = _timers(timers)
+    s = lib().alexnet_train_step_timed(C.byref(cfg), _ptr16(master), _ptr16(momentum), _ptr16(work),
+                                       _ptr(x) or None, _ptr(labels) or None, lr, momentum_coef,
+                                       weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None,
+                                       _ptr(ws) or None, ws_bytes, _ptr(stream) or None, arr, n)
+    return _check(s, "alexnet_train_step_timed") if check else s
 
 
 def alexnet_cast_weights(cfg, master, work, stream=0, check=True) -> int:

@@ -43,6 +43,27 @@ int check_params(const void* const* params, int n) {
   return ALEXNET_OK;
 }
 
+// Kernel timers of one call, indexed by alexnet_kernel.
+struct Timers {
+  KTimer t[ALEXNET_KT_COUNT];
+  bool on[ALEXNET_KT_COUNT] = {};
+  const KTimer* operator()(int id) const { return on[id] ? &t[id] : nullptr; }
+};
+
+int load_timers(const alexnet_timer* timers, int32_t n, Timers* out) {
+  if (n < 0) return ALEXNET_E_ARG;
+  if (n > 0 && !timers) return ALEXNET_E_NULL;
+  for (int i = 0; i < n; ++i) {
+    const int k = timers[i].kernel;
+    if (k < 1 || k >= ALEXNET_KT_COUNT) return ALEXNET_E_ARG;
+    if (!timers[i].start || !timers[i].stop) return ALEXNET_E_NULL;
+    out->t[k].start = (hipEvent_t)timers[i].start;
+    out->t[k].stop = (hipEvent_t)timers[i].stop;
+    out->on[k] = true;
+  }
+  return ALEXNET_OK;
+}
+
 inline char* at(void* ws, const Buf& b) { return (char*)ws + b.off; }
 inline char* tp(void* ws, const Plan& p, int id) { return (char*)ws + p.tap[id].buf.off; }
 
@@ -54,7 +75,7 @@ inline char* tp(void* ws, const Plan& p, int id) { return (char*)ws + p.tap[id].
 // Forward pass.  train: dropout masks of (seed, step); else the 1 - p scale.
 // src_hw: 227 (images) or 256 (ten-view sources).
 int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* ws, bool train,
-                    uint64_t seed, uint64_t step, hipStream_t st) {
+                    uint64_t seed, uint64_t step, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -69,22 +90,27 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
 
   const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
   const int hs = tenview ? 256 : 227;
-  HIPCHK(conv1_s2d(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st));
-  HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st));
+  HIPCHK(conv1_s2d(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
+  HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st,
+                   T(ALEXNET_KT_CONV1_FWD)));
   HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_LRN1), (int64_t)N * 55 * 55, 96, c.lrn_k, c.lrn_alpha,
-                 c.lrn_beta, c.lrn_n, st));
+                 c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN1_FWD)));
   HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1), N, 55, 55, 96, 0,
-                  st));
-  HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), st));
+                  st, T(ALEXNET_KT_POOL1_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), st,
+                  T(ALEXNET_KT_CONV2_FWD)));
   HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_LRN2), (int64_t)N * 27 * 27, 256, c.lrn_k,
-                 c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
+                 c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN2_FWD)));
   HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN2), tp(ws, p, T_POOL2), (uint8_t*)tp(ws, p, T_ARG2), N, 27, 27, 256, 0,
-                  st));
-  HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), st));
-  HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), st));
-  HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), st));
+                  st, T(ALEXNET_KT_POOL2_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), st,
+                  T(ALEXNET_KT_CONV3_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), st,
+                  T(ALEXNET_KT_CONV4_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), st,
+                  T(ALEXNET_KT_CONV5_FWD)));
   HIPCHK(pool_fwd(dt, tp(ws, p, T_CONV5), tp(ws, p, T_POOL5), (uint8_t*)tp(ws, p, T_ARG5), N, 13, 13, 256, 1,
-                  st));
+                  st, T(ALEXNET_KT_POOL5_FWD)));
 
   FcEpi ep{};
   ep.relu = 1;
@@ -100,17 +126,17 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   float* part = (float*)at(ws, p.part);
   ep.layer = 0;
   HIPCHK(fc_fwd(dt, N, 9216, 4096, tp(ws, p, T_POOL5), prm[10], prm[11], ep, tp(ws, p, T_DROP6), nullptr,
-                part, p.part_bytes, st));
+                part, p.part_bytes, st, T(ALEXNET_KT_FC6_FWD)));
   ep.layer = 1;
   HIPCHK(fc_fwd(dt, N, 4096, 4096, tp(ws, p, T_DROP6), prm[12], prm[13], ep, tp(ws, p, T_DROP7), nullptr,
-                part, p.part_bytes, st));
+                part, p.part_bytes, st, T(ALEXNET_KT_FC7_FWD)));
   FcEpi lin{};
   HIPCHK(fc_fwd(dt, N, 4096, 1000, tp(ws, p, T_DROP7), prm[14], prm[15], lin, nullptr,
-                (float*)tp(ws, p, T_LOGITS), part, p.part_bytes, st));
+                (float*)tp(ws, p, T_LOGITS), part, p.part_bytes, st, T(ALEXNET_KT_FC8_FWD)));
   return ALEXNET_OK;
 }
 
-int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st) {
+int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -126,51 +152,61 @@ int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st)
   }
   // FC8: dh7 = dz W8 * [drop7 > 0]   (drop7 > 0 <=> kept and ReLU active)
   HIPCHK(fc_dgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), work[14], tp(ws, p, T_DROP7), tp(ws, p, T_DFC7),
-                  part, p.part_bytes, st));
-  HIPCHK(fc_wgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), gw(7), st));
+                  part, p.part_bytes, st, T(ALEXNET_KT_FC8_DGRAD)));
+  HIPCHK(fc_wgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), gw(7), st,
+                  T(ALEXNET_KT_FC8_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DLOGITS), N, 1000, gb(7), cs, st));
   // FC7
   HIPCHK(fc_dgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), work[12], tp(ws, p, T_DROP6), tp(ws, p, T_DFC6),
-                  part, p.part_bytes, st));
-  HIPCHK(fc_wgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), gw(6), st));
+                  part, p.part_bytes, st, T(ALEXNET_KT_FC7_DGRAD)));
+  HIPCHK(fc_wgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), gw(6), st,
+                  T(ALEXNET_KT_FC7_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DFC7), N, 4096, gb(6), cs, st));
   // FC6 -> gradient w.r.t. the flattened pool5 output
   HIPCHK(fc_dgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), work[10], nullptr, tp(ws, p, T_DFLAT), part,
-                  p.part_bytes, st));
-  HIPCHK(fc_wgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), gw(5), st));
+                  p.part_bytes, st, T(ALEXNET_KT_FC6_DGRAD)));
+  HIPCHK(fc_wgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), gw(5), st,
+                  T(ALEXNET_KT_FC6_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DFC6), N, 4096, gb(5), cs, st));
   // pool5 backward * ReLU5'
   HIPCHK(pool_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
-                  tp(ws, p, T_DCONV5), N, 13, 13, 256, 1, st));
+                  tp(ws, p, T_DCONV5), N, 13, 13, 256, 1, st, T(ALEXNET_KT_POOL5_BWD)));
   // conv5, conv4, conv3
   const int din[5] = {-1, T_DIN2, T_DIN3, T_DCONV3, T_DCONV4};
   const int dz[5] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5};
   const int xin[5] = {-1, T_POOL1, T_POOL2, T_CONV3, T_CONV4};
   const int mask[5] = {-1, -1, -1, T_CONV3, T_CONV4};
+  const int ktw[5] = {ALEXNET_KT_CONV1_WGRAD, ALEXNET_KT_CONV2_WGRAD, ALEXNET_KT_CONV3_WGRAD,
+                      ALEXNET_KT_CONV4_WGRAD, ALEXNET_KT_CONV5_WGRAD};
+  const int ktd[5] = {0, ALEXNET_KT_CONV2_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV4_DGRAD,
+                      ALEXNET_KT_CONV5_DGRAD};
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), st));
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), st, T(ktw[i])));
     HIPCHK(colsum(dt, tp(ws, p, dz[i]), (int64_t)N * s.Ho * s.Wo, s.Cout, gb(i), cs, st));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
-                      tp(ws, p, din[i]), st));
+                      tp(ws, p, din[i]), st, T(ktd[i])));
   }
   // pool2 -> LRN2 -> ReLU2
   HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), nullptr, tp(ws, p, T_DLRN2), N,
-                  27, 27, 256, 0, st));
+                  27, 27, 256, 0, st, T(ALEXNET_KT_POOL2_BWD)));
   HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_DLRN2), tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256,
-                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
+                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN2_BWD)));
   {
     const ConvShape& s = net.conv[1];
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st));
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st,
+                      T(ALEXNET_KT_CONV2_WGRAD)));
     HIPCHK(colsum(dt, tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256, gb(1), cs, st));
-    HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st));
+    HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st,
+                      T(ALEXNET_KT_CONV2_DGRAD)));
   }
   // pool1 -> LRN1 -> ReLU1, then layer-1 weight gradient (no input gradient)
   HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), nullptr, tp(ws, p, T_DLRN1), N,
-                  55, 55, 96, 0, st));
+                  55, 55, 96, 0, st, T(ALEXNET_KT_POOL1_BWD)));
   HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_DLRN1), tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96,
-                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st));
-  HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st));
+                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN1_BWD)));
+  HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st,
+                     T(ALEXNET_KT_CONV1_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96, gb(0), cs, st));
   return ALEXNET_OK;
 }
@@ -205,19 +241,27 @@ size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode) {
   return make_plan(cfg, mode, &p) == ALEXNET_OK ? p.total : 0;
 }
 
-int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x, float* probs,
-                    void* ws, size_t ws_bytes, void* stream) {
+int alexnet_forward_timed(const alexnet_cfg* cfg, const void* const params[16], const void* x, float* probs,
+                          void* ws, size_t ws_bytes, void* stream, const alexnet_timer* timers,
+                          int32_t n_timers) {
   Plan p;
   int r = prepare(cfg, ALEXNET_MODE_FORWARD, ws, ws_bytes, &p);
   if (r != ALEXNET_OK) return r;
   if ((r = check_params(params, 16)) != ALEXNET_OK) return r;
   if (!x || !probs) return ALEXNET_E_NULL;
   if (!aligned(x, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
+  Timers T;
+  if ((r = load_timers(timers, n_timers, &T)) != ALEXNET_OK) return r;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  if ((r = enqueue_forward(p, params, x, ws, false, 0, 0, st)) != ALEXNET_OK) return r;
+  if ((r = enqueue_forward(p, params, x, ws, false, 0, 0, st, T)) != ALEXNET_OK) return r;
   if (softmax((const float*)tp(ws, p, T_LOGITS), probs, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;
+}
+
+int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x, float* probs,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return alexnet_forward_timed(cfg, params, x, probs, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16], const void* src,
@@ -230,17 +274,18 @@ int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16]
   if (!aligned(src, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  if ((r = enqueue_forward(p, params, src, ws, false, 0, 0, st)) != ALEXNET_OK) return r;
+  if ((r = enqueue_forward(p, params, src, ws, false, 0, 0, st, Timers())) != ALEXNET_OK) return r;
   float* vp = (float*)tp(ws, p, T_VIEWPROBS);
   if (softmax((const float*)tp(ws, p, T_LOGITS), vp, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
   if (view_mean(vp, probs, cfg->batch, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;
 }
 
-int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
-                       void* const work[16], const void* x, const int32_t* labels, float lr,
-                       float momentum_coef, float weight_decay, uint64_t seed, uint64_t step, float* loss,
-                       float* probs, void* ws, size_t ws_bytes, void* stream) {
+int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                             void* const work[16], const void* x, const int32_t* labels, float lr,
+                             float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
+                             float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
+                             const alexnet_timer* timers, int32_t n_timers) {
   Plan p;
   int r = prepare(cfg, ALEXNET_MODE_TRAIN, ws, ws_bytes, &p);
   if (r != ALEXNET_OK) return r;
@@ -251,15 +296,17 @@ int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* c
   if (!aligned(x, 16) || !aligned(labels, 4) || !aligned(loss, 4)) return ALEXNET_E_ALIGN;
   if (probs && !aligned(probs, 16)) return ALEXNET_E_ALIGN;
   if (!isfinite(lr) || !isfinite(momentum_coef) || !isfinite(weight_decay)) return ALEXNET_E_ARG;
+  Timers T;
+  if ((r = load_timers(timers, n_timers, &T)) != ALEXNET_OK) return r;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
   const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
-  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st)) != ALEXNET_OK) return r;
+  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st, T)) != ALEXNET_OK) return r;
   if (softmax_ce(dt, (const float*)tp(ws, p, T_LOGITS), labels, probs, tp(ws, p, T_DLOGITS),
                  (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
     return ALEXNET_E_HIP;
   if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
-  if ((r = enqueue_backward(p, work, ws, st)) != ALEXNET_OK) return r;
+  if ((r = enqueue_backward(p, work, ws, st, T)) != ALEXNET_OK) return r;
   TensorSet ts;
   for (int i = 0; i < 8; ++i) {
     ts.master[2 * i] = master[2 * i];
@@ -273,8 +320,16 @@ int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* c
     ts.n[2 * i] = p.net.wcount[i];
     ts.n[2 * i + 1] = p.net.bcount[i];
   }
-  if (sgd(dt, ts, lr, momentum_coef, weight_decay, st) != hipSuccess) return ALEXNET_E_HIP;
+  if (sgd(dt, ts, lr, momentum_coef, weight_decay, st, T(ALEXNET_KT_SGD)) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;
+}
+
+int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                       void* const work[16], const void* x, const int32_t* labels, float lr,
+                       float momentum_coef, float weight_decay, uint64_t seed, uint64_t step, float* loss,
+                       float* probs, void* ws, size_t ws_bytes, void* stream) {
+  return alexnet_train_step_timed(cfg, master, momentum, work, x, labels, lr, momentum_coef, weight_decay,
+                                  seed, step, loss, probs, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* const work[16], void* stream) {

@@ -15,22 +15,27 @@ static constexpr int TPB = 256;
 
 static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
 
+static inline void rec_start(const KTimer* kt, hipStream_t st) { if (kt) hipEventRecord(kt->start, st); }
+static inline void rec_stop(const KTimer* kt, hipStream_t st) { if (kt) hipEventRecord(kt->stop, st); }
+
 // =========================================================================
 // GEMM launches
 // =========================================================================
 template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP>
 static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
-                           int splits, hipStream_t st) {
+                           int splits, hipStream_t st, const KTimer* kt = nullptr) {
   GemmGrid gg;
   gg.M = M; gg.N = N; gg.K = K;
   gg.tiles_m = cdiv(M, BM);
   gg.tiles_n = cdiv(N, BN);
-  const int kt = cdiv(K, BK);
+  const int ktiles = cdiv(K, BK);
   gg.splits = eff_splits(K, splits);
-  gg.kt_per_split = cdiv(kt, gg.splits);
+  gg.kt_per_split = cdiv(ktiles, gg.splits);
   dim3 grid(gg.tiles_m * gg.tiles_n, 1, groups * gg.splits);
+  rec_start(kt, st);
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP>), grid, dim3(NTHREADS), 0, st, al, bl,
                      ep, gg);
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -96,10 +101,12 @@ __global__ void k_w1_s2d(const T* __restrict__ w, T* __restrict__ o) {
 }
 
 hipError_t conv1_s2d(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs,
-                     hipStream_t st) {
+                     hipStream_t st, const KTimer* kt) {
   const dim3 g(Nimg * S2D_B);
+  rec_start(kt, st);
   if (dt == BF16) hipLaunchKernelGGL((k_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview);
   else hipLaunchKernelGGL((k_s2d<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)xs, Hs, Ws, tenview);
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -114,7 +121,7 @@ static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3,
 
 template <typename T>
 static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
-                              hipStream_t st) {
+                              hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 96;
   LdIm2col<T, BM> a;
   a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
@@ -122,13 +129,13 @@ static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const 
   b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
   EpBiasRelu<T> e;
   e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
-  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, S2D_K, 1, 1, st);
+  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
 }
 
 hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
-                     hipStream_t st) {
-  return dt == BF16 ? conv1_fwd_t<bf16>(xs, Nimg, ws2d, b1, y, st)
-                    : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, st);
+                     hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? conv1_fwd_t<bf16>(xs, Nimg, ws2d, b1, y, st, kt)
+                    : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, st, kt);
 }
 
 // Picks the n-tile for an output width N: 128 when it divides, else 96, else
@@ -143,7 +150,7 @@ static hipError_t by_bn(int N, Fn&& fn) {
 
 template <typename T>
 struct ConvFwdFn {
-  ConvShape s; const void* x; const void* wr; const void* b; void* y; hipStream_t st;
+  ConvShape s; const void* x; const void* wr; const void* b; void* y; hipStream_t st; const KTimer* kt;
   template <int BN, int WGM, int WGN>
   hipError_t operator()() const {
     constexpr int BM = 128;
@@ -157,21 +164,21 @@ struct ConvFwdFn {
     bl.p = (const T*)wr; bl.ld = a.K; bl.rows = Cog; bl.K = a.K; bl.gstride = (int64_t)Cog * a.K;
     EpBiasRelu<T> e;
     e.out = (T*)y; e.bias = (const T*)b; e.ldo = s.Cout; e.M = a.M; e.N = Cog;
-    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cog, a.K, s.groups, 1, st);
+    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cog, a.K, s.groups, 1, st, kt);
   }
 };
 
 hipError_t conv_fwd(DType dt, const ConvShape& s, const void* x, const void* wr, const void* b, void* y,
-                    hipStream_t st) {
+                    hipStream_t st, const KTimer* kt) {
   const int Cog = s.Cout / s.groups;
-  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st}; return by_bn<bf16>(Cog, f); }
-  ConvFwdFn<float> f{s, x, wr, b, y, st};
+  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st, kt}; return by_bn<bf16>(Cog, f); }
+  ConvFwdFn<float> f{s, x, wr, b, y, st, kt};
   return by_bn<float>(Cog, f);
 }
 
 template <typename T>
 struct ConvDgradFn {
-  ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; hipStream_t st;
+  ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; hipStream_t st; const KTimer* kt;
   template <int BN, int WGM, int WGN>
   hipError_t operator()() const {
     constexpr int BM = 128;
@@ -186,16 +193,16 @@ struct ConvDgradFn {
     bl.p = (const T*)wt; bl.ld = a.K; bl.rows = Cig; bl.K = a.K; bl.gstride = (int64_t)Cig * a.K;
     EpMask<T> e;
     e.out = (T*)dx; e.mask = (const T*)mask; e.ldo = s.Cin; e.M = a.M; e.N = Cig;
-    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cig, a.K, s.groups, 1, st);
+    return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cig, a.K, s.groups, 1, st, kt);
   }
 };
 
 hipError_t conv_dgrad(DType dt, const ConvShape& s, const void* dy, const void* wt, const void* mask,
-                      void* dx, hipStream_t st) {
+                      void* dx, hipStream_t st, const KTimer* kt) {
   if (s.stride != 1) return hipErrorInvalidValue;
   const int Cig = s.Cin / s.groups;
-  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st}; return by_bn<bf16>(Cig, f); }
-  ConvDgradFn<float> f{s, dy, wt, mask, dx, st};
+  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st, kt}; return by_bn<bf16>(Cig, f); }
+  ConvDgradFn<float> f{s, dy, wt, mask, dx, st, kt};
   return by_bn<float>(Cig, f);
 }
 
@@ -245,7 +252,7 @@ __global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int
 
 template <typename T>
 static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x, float* part,
-                               size_t part_bytes, float* gw, hipStream_t st) {
+                               size_t part_bytes, float* gw, hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
   const int N = s.K * s.K * Cig, P = s.Nimg * s.Ho * s.Wo;
@@ -260,7 +267,7 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
   b.rows = N; b.P = P;
   EpF32 e;
   e.out = part; e.ldo = N; e.M = Cog; e.N = N; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_wgrad_reduce, grid1d((int64_t)s.Cout * Cig * s.K * s.K), dim3(TPB), 0, st, part,
                      s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
@@ -268,14 +275,14 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
 }
 
 hipError_t conv_wgrad(DType dt, const ConvShape& s, const void* dy, const void* x, float* part,
-                      size_t part_bytes, float* gw, hipStream_t st) {
-  return dt == BF16 ? conv_wgrad_t<bf16>(s, dy, x, part, part_bytes, gw, st)
-                    : conv_wgrad_t<float>(s, dy, x, part, part_bytes, gw, st);
+                      size_t part_bytes, float* gw, hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? conv_wgrad_t<bf16>(s, dy, x, part, part_bytes, gw, st, kt)
+                    : conv_wgrad_t<float>(s, dy, x, part, part_bytes, gw, st, kt);
 }
 
 template <typename T>
 static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                                float* gw, hipStream_t st) {
+                                float* gw, hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int N = S2D_K, P = Nimg * 3025;
   const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
@@ -286,7 +293,7 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   b.p = (const T*)xs; b.cg = conv1_geom(); b.rows = N; b.P = P;
   EpF32 e;
   e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * 363), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
                      gw);
@@ -294,9 +301,9 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
 }
 
 hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                       float* gw, hipStream_t st) {
-  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, st)
-                    : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, st);
+                       float* gw, hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, st, kt)
+                    : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, st, kt);
 }
 
 // ---- fully-connected layers
@@ -363,7 +370,7 @@ __global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N,
 template <typename T>
 static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, const void* b,
                            const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes,
-                           hipStream_t st) {
+                           hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int S = fc_splits(M, O, K);
   if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
@@ -373,7 +380,7 @@ static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, co
   bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, O, K, 1, S, st);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, O, K, 1, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O,
                      (const T*)b, ep, (const T*)nullptr, (T*)y, y_f32);
@@ -381,14 +388,15 @@ static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, co
 }
 
 hipError_t fc_fwd(DType dt, int M, int K, int O, const void* x, const void* w, const void* b,
-                  const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t st) {
-  return dt == BF16 ? fc_fwd_t<bf16>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st)
-                    : fc_fwd_t<float>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st);
+                  const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t st,
+                  const KTimer* kt) {
+  return dt == BF16 ? fc_fwd_t<bf16>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st, kt)
+                    : fc_fwd_t<float>(M, K, O, x, w, b, ep, y, y_f32, part, part_bytes, st, kt);
 }
 
 template <typename T>
 static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w, const void* mask,
-                             void* dx, float* part, size_t part_bytes, hipStream_t st) {
+                             void* dx, float* part, size_t part_bytes, hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int S = fc_splits(M, K, O);
   if ((size_t)S * M * K * sizeof(float) > part_bytes) return hipErrorInvalidValue;
@@ -398,7 +406,7 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
   bl.p = (const T*)w; bl.ld = K; bl.rows = K; bl.K = O; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = K; e.M = M; e.N = K; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, K, O, 1, S, st);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, K, O, 1, S, st, kt);
   if (err != hipSuccess) return err;
   FcEpi none{};
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K,
@@ -407,14 +415,14 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
 }
 
 hipError_t fc_dgrad(DType dt, int M, int K, int O, const void* dy, const void* w, const void* mask,
-                    void* dx, float* part, size_t part_bytes, hipStream_t st) {
-  return dt == BF16 ? fc_dgrad_t<bf16>(M, K, O, dy, w, mask, dx, part, part_bytes, st)
-                    : fc_dgrad_t<float>(M, K, O, dy, w, mask, dx, part, part_bytes, st);
+                    void* dx, float* part, size_t part_bytes, hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? fc_dgrad_t<bf16>(M, K, O, dy, w, mask, dx, part, part_bytes, st, kt)
+                    : fc_dgrad_t<float>(M, K, O, dy, w, mask, dx, part, part_bytes, st, kt);
 }
 
 template <typename T>
 static hipError_t fc_wgrad_t(int M, int K, int O, const void* dy, const void* x, float* gw,
-                             hipStream_t st) {
+                             hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   LdKO<T, BM> a;
   a.p = (const T*)dy; a.ld = O; a.rows = O; a.K = M; a.gstride = 0;
@@ -422,12 +430,13 @@ static hipError_t fc_wgrad_t(int M, int K, int O, const void* dy, const void* x,
   bl.p = (const T*)x; bl.ld = K; bl.rows = K; bl.K = M; bl.gstride = 0;
   EpF32 e;
   e.out = gw; e.ldo = K; e.M = O; e.N = K; e.splits = 1;
-  return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st);
+  return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st, kt);
 }
 
 hipError_t fc_wgrad(DType dt, int M, int K, int O, const void* dy, const void* x, float* gw,
-                    hipStream_t st) {
-  return dt == BF16 ? fc_wgrad_t<bf16>(M, K, O, dy, x, gw, st) : fc_wgrad_t<float>(M, K, O, dy, x, gw, st);
+                    hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? fc_wgrad_t<bf16>(M, K, O, dy, x, gw, st, kt)
+                    : fc_wgrad_t<float>(M, K, O, dy, x, gw, st, kt);
 }
 
 // =========================================================================
@@ -558,18 +567,22 @@ __global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* _
 }
 
 hipError_t lrn_fwd(DType dt, const void* a, void* b, int64_t npix, int C, float k, float alpha, float beta,
-                   int n, hipStream_t st) {
+                   int n, hipStream_t st, const KTimer* kt) {
   const dim3 g = grid1d(npix * (C / 8));
+  rec_start(kt, st);
   if (dt == BF16) hipLaunchKernelGGL((k_lrn_fwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (bf16*)b, npix, C, k, alpha, beta, n / 2);
   else hipLaunchKernelGGL((k_lrn_fwd<float>), g, dim3(TPB), 0, st, (const float*)a, (float*)b, npix, C, k, alpha, beta, n / 2);
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 hipError_t lrn_bwd(DType dt, const void* a, const void* gr, void* da, int64_t npix, int C, float k,
-                   float alpha, float beta, int n, hipStream_t st) {
+                   float alpha, float beta, int n, hipStream_t st, const KTimer* kt) {
   if (n / 2 > 4) return hipErrorInvalidValue;
   const dim3 g = grid1d(npix * (C / 8));
+  rec_start(kt, st);
   if (dt == BF16) hipLaunchKernelGGL((k_lrn_bwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (const bf16*)gr, (bf16*)da, npix, C, k, alpha, beta, n / 2);
   else hipLaunchKernelGGL((k_lrn_bwd<float>), g, dim3(TPB), 0, st, (const float*)a, (const float*)gr, (float*)da, npix, C, k, alpha, beta, n / 2);
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -661,9 +674,10 @@ __global__ void k_pool_bwd(const T* __restrict__ dy, const uint8_t* __restrict__
 }
 
 hipError_t pool_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C, int flat,
-                    hipStream_t st) {
+                    hipStream_t st, const KTimer* kt) {
   const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
   const dim3 g = grid1d((int64_t)N * Ho * Wo * (C / 8));
+  rec_start(kt, st);
   if (dt == BF16) {
     if (flat) hipLaunchKernelGGL((k_pool_fwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
     else hipLaunchKernelGGL((k_pool_fwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
@@ -671,13 +685,15 @@ hipError_t pool_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H
     if (flat) hipLaunchKernelGGL((k_pool_fwd<float, true>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
     else hipLaunchKernelGGL((k_pool_fwd<float, false>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
   }
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
 hipError_t pool_bwd(DType dt, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N, int H,
-                    int W, int C, int flat, hipStream_t st) {
+                    int W, int C, int flat, hipStream_t st, const KTimer* kt) {
   const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
   const dim3 g = grid1d((int64_t)N * H * W * (C / 8));
+  rec_start(kt, st);
   if (dt == BF16) {
     if (flat) hipLaunchKernelGGL((k_pool_bwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
     else hipLaunchKernelGGL((k_pool_bwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
@@ -685,6 +701,7 @@ hipError_t pool_bwd(DType dt, const void* dy, const uint8_t* arg, const void* ma
     if (flat) hipLaunchKernelGGL((k_pool_bwd<float, true>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
     else hipLaunchKernelGGL((k_pool_bwd<float, false>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
   }
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -892,7 +909,7 @@ __global__ void k_multi(MultiArgs a) {
 }
 
 static hipError_t run_multi(DType dt, const TensorSet& ts, bool sgd, float lr, float mom, float wd,
-                            hipStream_t st) {
+                            hipStream_t st, const KTimer* kt = nullptr) {
   MultiArgs a;
   a.start[0] = 0;
   for (int i = 0; i < 16; ++i) {
@@ -902,6 +919,7 @@ static hipError_t run_multi(DType dt, const TensorSet& ts, bool sgd, float lr, f
   }
   a.lr = lr; a.mom = mom; a.wdlr = wd * lr;
   const dim3 g = grid1d(a.start[16]);
+  rec_start(kt, st);
   if (dt == BF16) {
     if (sgd) hipLaunchKernelGGL((k_multi<bf16, true>), g, dim3(TPB), 0, st, a);
     else hipLaunchKernelGGL((k_multi<bf16, false>), g, dim3(TPB), 0, st, a);
@@ -909,11 +927,13 @@ static hipError_t run_multi(DType dt, const TensorSet& ts, bool sgd, float lr, f
     if (sgd) hipLaunchKernelGGL((k_multi<float, true>), g, dim3(TPB), 0, st, a);
     else hipLaunchKernelGGL((k_multi<float, false>), g, dim3(TPB), 0, st, a);
   }
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
-hipError_t sgd(DType dt, const TensorSet& ts, float lr, float mom, float wd, hipStream_t st) {
-  return run_multi(dt, ts, true, lr, mom, wd, st);
+hipError_t sgd(DType dt, const TensorSet& ts, float lr, float mom, float wd, hipStream_t st,
+               const KTimer* kt) {
+  return run_multi(dt, ts, true, lr, mom, wd, st, kt);
 }
 hipError_t cast_weights(DType dt, const TensorSet& ts, hipStream_t st) {
   return run_multi(dt, ts, false, 0.f, 0.f, 0.f, st);

@@ -9,6 +9,12 @@ namespace ax {
 
 enum DType { F32 = 0, BF16 = 1 };
 
+// Optional events recorded on the launch stream right before and after one
+// kernel launch (the MFMA kernel for GEMM layers).
+struct KTimer {
+  hipEvent_t start, stop;
+};
+
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Reduction depth of one GEMM k-tile (elements).
@@ -39,22 +45,28 @@ hipError_t w_dgrad(DType, const void* w_oihw, void* out, int G, int Coutg, int C
 // mirrored), ws [96][432] from the OIHW weights.
 constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
 constexpr size_t S2D_W_ELEMS = 96 * 432;
-hipError_t conv1_s2d(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs, hipStream_t);
+hipError_t conv1_s2d(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs, hipStream_t,
+                      const KTimer* kt = nullptr);
 hipError_t conv1_w_s2d(DType, const void* w_oihw, void* ws, hipStream_t);
 // y NHWC [N][55][55][96] = relu(conv1 + b)
-hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t);
+hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t,
+                      const KTimer* kt = nullptr);
 // NHWC conv + bias + ReLU (layers 2-5)
 hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, const void* b, void* y,
-                    hipStream_t);
+                    hipStream_t,
+                      const KTimer* kt = nullptr);
 // dX (NHWC) = conv^T(dY) * [mask > 0] (mask optional) for stride-1 layers
 hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, const void* mask,
-                      void* dx, hipStream_t);
+                      void* dx, hipStream_t,
+                      const KTimer* kt = nullptr);
 // fp32 weight gradient (OIHW) of layers 2-5; `part` is split-K scratch
 hipError_t conv_wgrad(DType, const ConvShape&, const void* dy, const void* x, float* part,
-                      size_t part_bytes, float* gw, hipStream_t);
+                      size_t part_bytes, float* gw, hipStream_t,
+                      const KTimer* kt = nullptr);
 // fp32 weight gradient (OIHW) of layer 1 from the space-to-depth input xs
 hipError_t conv1_wgrad(DType, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                       float* gw, hipStream_t);
+                       float* gw, hipStream_t,
+                      const KTimer* kt = nullptr);
 size_t conv_wgrad_part_bytes(const ConvShape&);
 size_t conv1_wgrad_part_bytes(int Nimg);
 
@@ -69,27 +81,34 @@ struct FcEpi {
 };
 // y[M][O] = epi(x[M][K] W[O][K]^T + b); y is cfg dtype, or fp32 if y_f32
 hipError_t fc_fwd(DType, int M, int K, int O, const void* x, const void* w, const void* b,
-                  const FcEpi&, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t);
+                  const FcEpi&, void* y, float* y_f32, float* part, size_t part_bytes, hipStream_t,
+                      const KTimer* kt = nullptr);
 // dx[M][K] = (dy[M][O] W[O][K]) * [mask > 0] (mask optional)
 hipError_t fc_dgrad(DType, int M, int K, int O, const void* dy, const void* w, const void* mask,
-                    void* dx, float* part, size_t part_bytes, hipStream_t);
+                    void* dx, float* part, size_t part_bytes, hipStream_t,
+                      const KTimer* kt = nullptr);
 // dW[O][K] fp32 = dy^T x
 hipError_t fc_wgrad(DType, int M, int K, int O, const void* dy, const void* x, float* gw,
-                    hipStream_t);
+                    hipStream_t,
+                      const KTimer* kt = nullptr);
 size_t fc_fwd_part_bytes(int M, int K, int O);
 size_t fc_dgrad_part_bytes(int M, int K, int O);
 
 // ---- bandwidth-bound layers (NHWC, C % 8 == 0)
 hipError_t lrn_fwd(DType, const void* a, void* b, int64_t npix, int C, float k, float alpha,
-                   float beta, int n, hipStream_t);
+                   float beta, int n, hipStream_t,
+                      const KTimer* kt = nullptr);
 hipError_t lrn_bwd(DType, const void* a, const void* g, void* da, int64_t npix, int C, float k,
-                   float alpha, float beta, int n, hipStream_t);
+                   float alpha, float beta, int n, hipStream_t,
+                      const KTimer* kt = nullptr);
 // 3x3/s2 max-pool; flat_out: y written [N][C*Ho*Wo] in (c,h,w) order
 hipError_t pool_fwd(DType, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C,
-                    int flat_out, hipStream_t);
+                    int flat_out, hipStream_t,
+                      const KTimer* kt = nullptr);
 // gather-form backward; flat_dy: dy is [N][C*Ho*Wo] in (c,h,w) order; mask optional
 hipError_t pool_bwd(DType, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N,
-                    int H, int W, int C, int flat_dy, hipStream_t);
+                    int H, int W, int C, int flat_dy, hipStream_t,
+                      const KTimer* kt = nullptr);
 
 // ---- softmax, loss, ten-view mean, column sums
 hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t);
@@ -110,7 +129,8 @@ struct TensorSet {
   void* work[16];
   int64_t n[16];
 };
-hipError_t sgd(DType work_dtype, const TensorSet&, float lr, float momentum, float wd, hipStream_t);
+hipError_t sgd(DType work_dtype, const TensorSet&, float lr, float momentum, float wd, hipStream_t,
+                      const KTimer* kt = nullptr);
 hipError_t cast_weights(DType work_dtype, const TensorSet&, hipStream_t);
 hipError_t dropout_mask(uint64_t seed, uint64_t step, int layer, int rows, int cols,
                         uint32_t thresh, uint8_t* mask, hipStream_t);

@@ -141,6 +141,46 @@ int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* 
 int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t rows, int32_t cols,
                          float p, uint8_t* mask, void* stream);
 
+/* Kernel timing (diagnostics).  The *_timed variants behave exactly like
+ * the plain calls and additionally record caller-created HIP events
+ * (hipEvent_t handles passed as void*) on `stream` immediately before and
+ * after the launch of the named kernel; for GEMM layers that is the MFMA
+ * kernel alone, not its split-K reduction.  A kernel the call does not launch
+ * records nothing.  timers may be NULL when n_timers is 0. */
+typedef enum {
+  ALEXNET_KT_S2D = 1,          /* layer-1 input staging (4x4 pixel blocks)      */
+  ALEXNET_KT_CONV1_FWD, ALEXNET_KT_CONV2_FWD, ALEXNET_KT_CONV3_FWD, ALEXNET_KT_CONV4_FWD,
+  ALEXNET_KT_CONV5_FWD,
+  ALEXNET_KT_LRN1_FWD, ALEXNET_KT_LRN2_FWD,
+  ALEXNET_KT_POOL1_FWD, ALEXNET_KT_POOL2_FWD, ALEXNET_KT_POOL5_FWD,
+  ALEXNET_KT_FC6_FWD, ALEXNET_KT_FC7_FWD, ALEXNET_KT_FC8_FWD,
+  ALEXNET_KT_FC8_DGRAD, ALEXNET_KT_FC7_DGRAD, ALEXNET_KT_FC6_DGRAD,
+  ALEXNET_KT_FC8_WGRAD, ALEXNET_KT_FC7_WGRAD, ALEXNET_KT_FC6_WGRAD,
+  ALEXNET_KT_POOL5_BWD,
+  ALEXNET_KT_CONV5_WGRAD, ALEXNET_KT_CONV4_WGRAD, ALEXNET_KT_CONV3_WGRAD, ALEXNET_KT_CONV2_WGRAD,
+  ALEXNET_KT_CONV1_WGRAD,
+  ALEXNET_KT_CONV5_DGRAD, ALEXNET_KT_CONV4_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV2_DGRAD,
+  ALEXNET_KT_POOL2_BWD, ALEXNET_KT_LRN2_BWD, ALEXNET_KT_POOL1_BWD, ALEXNET_KT_LRN1_BWD,
+  ALEXNET_KT_SGD,
+  ALEXNET_KT_COUNT
+} alexnet_kernel;
+
+typedef struct {
+  int32_t kernel;  /* alexnet_kernel */
+  void* start;     /* hipEvent_t recorded before the launch */
+  void* stop;      /* hipEvent_t recorded after the launch  */
+} alexnet_timer;
+
+int alexnet_forward_timed(const alexnet_cfg* cfg, const void* const params[16], const void* x,
+                          float* probs, void* ws, size_t ws_bytes, void* stream,
+                          const alexnet_timer* timers, int32_t n_timers);
+int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16],
+                             float* const momentum[16], void* const work[16], const void* x,
+                             const int32_t* labels, float lr, float momentum_coef,
+                             float weight_decay, uint64_t seed, uint64_t step, float* loss,
+                             float* probs, void* ws, size_t ws_bytes, void* stream,
+                             const alexnet_timer* timers, int32_t n_timers);
+
 /* Test and diagnostic access to the tensors a call leaves in its workspace.
  * Host only.  For tap `tap_id` of a call in `mode` with `cfg`, returns its
  * byte offset into the workspace, its shape (unused trailing dims = 1), its

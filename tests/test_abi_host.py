@@ -143,3 +143,23 @@ def test_tap_shapes_follow_the_layer_list():
     assert get("gw3") == (384, 256, 3, 3) and get("gw6") == (4096, 9216, 1, 1)
     with pytest.raises(B.AlexNetError):
         B.alexnet_tap(c, B.MODE_FORWARD, ids["gw1"])
+
+
+def test_kernel_ids_match_header():
+    txt = open(HEADER).read()
+    body = txt[txt.index("typedef enum {\n  ALEXNET_KT_S2D"):txt.index("} alexnet_kernel;")]
+    names = re.findall(r"ALEXNET_KT_([A-Z0-9_]+)", body)
+    assert names[-1] == "COUNT"
+    assert tuple(names[:-1]) == B.KERNELS
+
+
+def test_timer_validation_before_launch():
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    ws = B.alexnet_workspace_bytes(c, B.MODE_FORWARD)
+    p = fake_params()
+    f = lambda t: B.alexnet_forward_timed(c, p, FAKE, FAKE, FAKE, ws, 0, t, check=False)
+    assert f([(0, FAKE, FAKE)]) == B.E_ARG                       # id out of range
+    assert f([(len(B.KERNELS) + 1, FAKE, FAKE)]) == B.E_ARG
+    assert f([(B.KT["CONV2_FWD"], 0, FAKE)]) == B.E_NULL
+    arr, _ = B._timers([(B.KT["CONV2_FWD"], FAKE, FAKE)])
+    assert B.lib().alexnet_forward_timed(C.byref(c), B._ptr16(p), FAKE, FAKE, FAKE, ws, None, arr, -1) == B.E_ARG
