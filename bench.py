@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="images in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -242,6 +244,15 @@ def main():
         "kernels_forward": {nm: frac(nm, ms) for nm, ms in fwd_kernels["single"].items()},
         "roofline": roofline,
     }
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
+        del src, dst
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
