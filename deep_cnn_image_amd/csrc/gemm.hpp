@@ -4,12 +4,17 @@
 //   C[m][n] = sum_k A[m][k] * B[n][k]
 //
 // A and B are never materialised: an operand loader gathers one BK-wide slice
-// of the tile straight from the source tensor into registers (16-byte vector
-// loads where the source is contiguous along k or along rows) and writes it to
-// LDS in a k-contiguous layout [rows][BK + pad].  Two LDS buffers alternate so
-// the next slice is fetched while the matrix cores work on the current one.
-// The accumulator tile goes through LDS once more so that the epilogue writes
-// 16-byte chunks along n.
+// of the tile straight from the source tensor into a k-contiguous LDS tile.
+// Two LDS buffers alternate so the next slice is fetched while the matrix
+// cores work on the current one.  The accumulator tile goes through LDS once
+// more so that the epilogue writes 16-byte chunks along n.
+//
+// bf16 sources contiguous along k (plain rows, implicit im2col) are fetched
+// with direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): the data never
+// passes through VGPRs, no ds_write is issued, and a padding element is an
+// out-of-range buffer offset, which the hardware returns as zero.  Other
+// sources (k-outer operands, fp32) go through registers: 16-byte global loads,
+// then ds_write into LDS.
 //
 // bf16 operands use v_mfma_f32_16x16x32_bf16 (fp32 accumulate); fp32 operands
 // use v_mfma_f32_16x16x4_f32.  Four waves per workgroup, 64-wide.
@@ -23,18 +28,83 @@ constexpr int BK = GEMM_BK;
 constexpr int NTHREADS = 256;
 
 template <typename T> struct VecOf { static constexpr int V = 16 / sizeof(T); };
-template <typename T> struct Lds { static constexpr int LS = BK + VecOf<T>::V; };  // padded row
+// LDS tile layouts [rows][LS] with an XOR swizzle of the 16-byte granule
+// index along k.  MFMA fragment reads touch 16 consecutive rows at one
+// granule; the layouts keep those reads and the loaders' writes free of bank
+// conflicts (64 banks of 4 bytes).
+//
+// LayoutKC, for loaders that write whole 16-byte granules of a row
+// (k-contiguous sources): unpadded rows, so 16 lanes writing two rows cover
+// all banks; the granule is XOR-ed with (row >> 1) & 7 (bf16, 8 granules per
+// row) or row & 15 (fp32, 16 granules), which spreads the 16 rows of a
+// fragment read over all banks.
+template <typename T> struct LayoutKC {
+  static constexpr int LS = BK;
+  static __device__ __forceinline__ int off(int row, int col) {
+    constexpr int G = VecOf<T>::V;
+    const int s = sizeof(T) == 2 ? ((row >> 1) & 7) : (row & 15);
+    return row * LS + (((col / G) ^ s) * G) + (col % G);
+  }
+};
+// LayoutKO, for k-outer loaders whose transposed pair writes put 16 lanes on
+// rows 8 apart: rows padded by one granule and the granule XOR-ed with bits
+// 4..6 of the row.
+template <typename T> struct LayoutKO {
+  static constexpr int LS = BK + VecOf<T>::V;
+  static __device__ __forceinline__ int off(int row, int col) {
+    constexpr int G = VecOf<T>::V;
+    return row * LS + (((col / G) ^ ((row >> 4) & 7)) * G) + (col % G);
+  }
+};
 
-// LDS element offset of (row, col) in a [rows][LS] tile.  The 16-byte granule
-// index along k is XOR-ed with bits 4..6 of the row: the transposed pair
-// writes of k-outer loaders (16 lanes on rows 8 apart) then spread over all
-// banks, while the MFMA fragment reads (16 consecutive rows, same granule)
-// see one constant permutation and stay conflict-free thanks to the pad.
-template <typename T>
-__device__ __forceinline__ int lds_off(int row, int col) {
-  constexpr int G = VecOf<T>::V;
-  return row * Lds<T>::LS + (((col / G) ^ ((row >> 4) & 7)) * G) + (col % G);
+// ------------------------------------------------------------------ direct-to-LDS
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr uint32_t BUF_OOB = 0x80000000u;   // >= every buffer size used: reads as zero
+
+// Raw buffer descriptor (stride 0, byte-granular range check) over `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
+
+// 16 bytes per lane from byte offset `off` into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t off, bf16* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, (int)off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (loads complete in order, so the older ones have landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), which would
+// also wait for every direct-to-LDS load still in flight.  Callers order the
+// loads themselves with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One wave instruction fills 8 rows (1 KB) of a LayoutKC<bf16> tile.  The R/8
+// row slots are dealt to the four waves as j = wave + 4 i; a wave short of a
+// slot repeats its own previous one (same bytes to the same place), so every
+// wave issues NI loads per k-slice and can wait on a fixed count.  Slot j
+// keeps the parity of the wave, so the swizzled k granule a lane fetches is
+// fixed for the whole k loop.
+template <int R>
+struct DmaSlots {
+  static_assert(R % 8 == 0, "tile rows");
+  static constexpr int NSLOT = R / 8, NI = (NSLOT + 3) / 4;
+  static __device__ __forceinline__ int slot(int wave, int i) {
+    const int j = wave + 4 * i;
+    return j < NSLOT ? j : j - 4;
+  }
+  // k granule (of 8) that `lane` fetches for a slot of parity `odd`
+  static __device__ __forceinline__ int granule(int lane, int odd) {
+    return (lane & 7) ^ ((odd << 2) | ((lane >> 4) & 3));
+  }
+};
 
 struct GemmGrid {
   int M, N, K;          // per group
@@ -80,9 +150,10 @@ template <> struct PairStore<float> {
 // and 16-byte aligned rows.
 template <typename T, int R>
 struct LdKC {
+  using Layout = LayoutKC<T>;
+  static constexpr bool DMA = false;
   static constexpr int V = VecOf<T>::V, CPR = BK / V, NCHUNK = R * CPR;
   static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
   const T* p; int64_t ld; int rows; int K; int64_t gstride;
   const T* base; int r0, k;
   uint4 reg[NCH];
@@ -104,7 +175,7 @@ struct LdKC {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
+      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + Layout::off(c / CPR, (c % CPR) * V)) = reg[i];
     }
   }
 };
@@ -113,9 +184,11 @@ struct LdKC {
 // rows % V == 0.
 template <typename T, int R>
 struct LdKO {
+  using Layout = LayoutKO<T>;
+  static constexpr bool DMA = false;
   static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
   static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
+  static constexpr int LS = Layout::LS;
   const T* p; int64_t ld; int rows; int K; int64_t gstride;
   const T* base; int r0, k;
   uint4 lo[NT], hi[NT];
@@ -141,7 +214,7 @@ struct LdKO {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NTASK) PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
+      if (c < NTASK) PairStore<T>::template run<LS>(s + Layout::off((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
     }
   }
 };
@@ -156,9 +229,10 @@ struct ConvGeom {
 
 template <typename T, int R>
 struct LdIm2col {
+  using Layout = LayoutKC<T>;
+  static constexpr bool DMA = false;
   static constexpr int V = VecOf<T>::V, CPR = BK / V, NCHUNK = R * CPR;
   static constexpr int NCH = (NCHUNK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
   const T* p; ConvGeom cg; int M; int K;
   int hb[NCH], wb[NCH];
   const T* rowp[NCH];
@@ -204,7 +278,96 @@ struct LdIm2col {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + lds_off<T>(c / CPR, (c % CPR) * V)) = reg[i];
+      if (c < NCHUNK) *reinterpret_cast<uint4*>(s + Layout::off(c / CPR, (c % CPR) * V)) = reg[i];
+    }
+  }
+};
+
+// Direct-to-LDS version of LdKC for bf16: rows of a k-contiguous matrix
+// (row stride ld elements, group g at g * gstride).  issue(lds) fetches the
+// current k-slice into the tile and steps to the next one.
+template <int R>
+struct DmaKC {
+  static constexpr bool DMA = true;
+  using Layout = LayoutKC<bf16>;
+  using Slots = DmaSlots<R>;
+  static constexpr int NI = Slots::NI;
+  const bf16* p; int64_t ld; int rows; int K; int64_t gstride;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[NI];
+  int kc;
+  __device__ void setup(int r0, int g, int kb) {
+    const bf16* base = p + (int64_t)g * gstride;
+    rs = buf_rsrc(base, (uint32_t)(((int64_t)(rows - 1) * ld + K) * 2));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gcol = Slots::granule(lane, wave & 1) * 8;
+    kc = kb + gcol;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = r0 + Slots::slot(wave, i) * 8 + (lane >> 3);
+      off[i] = r < rows ? (uint32_t)((r * ld + kc) * 2) : BUF_OOB;
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = threadIdx.x >> 6;
+    const bool kok = kc < K;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      dma16(rs, kok ? off[i] : BUF_OOB, s + Slots::slot(wave, i) * 8 * BK);
+      off[i] += BK * 2;
+    }
+    kc += BK;
+  }
+};
+
+// Direct-to-LDS version of LdIm2col for bf16 (same row and k decomposition).
+template <int R>
+struct DmaIm2col {
+  static constexpr bool DMA = true;
+  using Layout = LayoutKC<bf16>;
+  using Slots = DmaSlots<R>;
+  static constexpr int NI = Slots::NI;
+  const bf16* p; ConvGeom cg; int M; int K;
+  __amdgpu_buffer_rsrc_t rs;
+  int hb[NI], wb[NI], pix[NI];   // pix: element offset of input pixel (hb, wb) of the row's image
+  int kc, kh, kw, ci;
+  __device__ void setup(int r0, int g, int kb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hw = cg.Ho * cg.Wo;
+    const int nimg = (M + hw - 1) / hw;
+    rs = buf_rsrc(p, (uint32_t)((int64_t)nimg * cg.H * cg.W * cg.Ctot * 2));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int m = r0 + Slots::slot(wave, i) * 8 + (lane >> 3);
+      hb[i] = -(1 << 28); wb[i] = 0; pix[i] = 0;
+      if (m < M) {
+        const int n = m / hw, rem = m - n * hw;
+        const int ho = rem / cg.Wo, wo = rem - ho * cg.Wo;
+        hb[i] = ho * cg.stride - cg.pad;
+        wb[i] = wo * cg.stride - cg.pad;
+        pix[i] = ((n * cg.H + hb[i]) * cg.W + wb[i]) * cg.Ctot + g * cg.Cg;
+      }
+    }
+    kc = kb + Slots::granule(lane, wave & 1) * 8;
+    const int tap = kc / cg.Cg;
+    ci = kc - tap * cg.Cg; kh = tap / cg.KW; kw = tap - kh * cg.KW;
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = threadIdx.x >> 6;
+    const bool kok = kc < K;
+    const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int hi = hb[i] + kh, wi = wb[i] + kw;
+      const bool ok = kok && (unsigned)hi < (unsigned)cg.H && (unsigned)wi < (unsigned)cg.W;
+      const uint32_t o = ok ? (uint32_t)(pix[i] + tapoff) * 2u : BUF_OOB;
+      dma16(rs, o, s + Slots::slot(wave, i) * 8 * BK);
+    }
+    kc += BK;
+    ci += BK;
+    while (ci >= cg.Cg) {
+      ci -= cg.Cg;
+      if (++kw == cg.KW) { kw = 0; ++kh; }
     }
   }
 };
@@ -226,9 +389,11 @@ struct PixelIter {
 // Needs Cg % V == 0 (a row chunk never straddles two taps).
 template <typename T, int R>
 struct LdWgradB {
+  using Layout = LayoutKO<T>;
+  static constexpr bool DMA = false;
   static constexpr int V = VecOf<T>::V, CPK = R / V, NTASK = (BK / 2) * CPK;
   static constexpr int NT = (NTASK + NTHREADS - 1) / NTHREADS;
-  static constexpr int LS = Lds<T>::LS;
+  static constexpr int LS = Layout::LS;
   const T* p; ConvGeom cg; int rows; int P;   // rows = KH*KW*Cg, P = Nimg*Ho*Wo
   const T* colp[NT]; int hoff[NT], woff[NT]; bool rok[NT];
   PixelIter it[NT];
@@ -268,7 +433,7 @@ struct LdWgradB {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int c = threadIdx.x + i * NTHREADS;
-      if (c < NTASK) PairStore<T>::template run<LS>(s + lds_off<T>((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
+      if (c < NTASK) PairStore<T>::template run<LS>(s + Layout::off((c % CPK) * V, 2 * (c / CPK)), lo[i], hi[i]);
     }
   }
 };
@@ -319,10 +484,10 @@ struct EpF32 {
 };
 
 // ------------------------------------------------------------------ MFMA steps
-template <typename T, int FM, int FN> struct Mma;
+template <typename T, int FM, int FN, class LA, class LB> struct Mma;
 
-template <int FM, int FN>
-struct Mma<bf16, FM, FN> {
+template <int FM, int FN, class LA, class LB>
+struct Mma<bf16, FM, FN, LA, LB> {
   // As/Bs: LDS tiles; ra/rb: first row of this wave's slice in each tile
   static __device__ __forceinline__ void run(const bf16* As, int ra, const bf16* Bs, int rb,
                                              f32x4_t (&acc)[FM][FN], int lane) {
@@ -332,10 +497,10 @@ struct Mma<bf16, FM, FN> {
       bf16x8_t a[FM], b[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off<bf16>(ra + i * 16 + r, kk + kq));
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + LA::off(ra + i * 16 + r, kk + kq));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off<bf16>(rb + j * 16 + r, kk + kq));
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + LB::off(rb + j * 16 + r, kk + kq));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -345,8 +510,8 @@ struct Mma<bf16, FM, FN> {
   }
 };
 
-template <int FM, int FN>
-struct Mma<float, FM, FN> {
+template <int FM, int FN, class LA, class LB>
+struct Mma<float, FM, FN, LA, LB> {
   static __device__ __forceinline__ void run(const float* As, int ra, const float* Bs, int rb,
                                              f32x4_t (&acc)[FM][FN], int lane) {
     const int r = lane & 15, kq = lane >> 4;
@@ -354,9 +519,9 @@ struct Mma<float, FM, FN> {
     for (int kk = 0; kk < BK; kk += 4) {
       float a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = As[lds_off<float>(ra + i * 16 + r, kk + kq)];
+      for (int i = 0; i < FM; ++i) a[i] = As[LA::off(ra + i * 16 + r, kk + kq)];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = Bs[lds_off<float>(rb + j * 16 + r, kk + kq)];
+      for (int j = 0; j < FN; ++j) b[j] = Bs[LB::off(rb + j * 16 + r, kk + kq)];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -370,11 +535,12 @@ struct Mma<float, FM, FN> {
 template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP>
 __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   static_assert(WGM * WGN == 4, "four waves");
-  constexpr int LS = Lds<T>::LS;
+  using LA = typename AL::Layout;
+  using LB = typename BL::Layout;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_EL = BM * LS, B_EL = BN * LS;
+  constexpr int A_EL = BM * LA::LS, B_EL = BN * LB::LS;
   constexpr int MAIN_BYTES = 2 * (A_EL + B_EL) * (int)sizeof(T);
   constexpr int CST = BN + 4;
   constexpr int EPI_BYTES = BM * CST * 4;
@@ -407,7 +573,25 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (kt0 < kt1) {
+  static_assert(AL::DMA == BL::DMA, "both operands direct-to-LDS or neither");
+  if constexpr (AL::DMA) {
+    // Slice kt lands in buffer kt & 1.  The barrier at the top of an
+    // iteration publishes the slice every wave waited for and guarantees that
+    // all waves are done with the other buffer, which the next slice then
+    // overwrites while the matrix cores work.
+    if (kt0 < kt1) {
+      al.issue(As);
+      bl.issue(Bs);
+      for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (kt + 1 < kt1) { al.issue(As + (cur ^ 1) * A_EL); bl.issue(Bs + (cur ^ 1) * B_EL); }
+        Mma<T, FM, FN, LA, LB>::run(As + cur * A_EL, wm * WTM, Bs + cur * B_EL, wn * WTN, acc, lane);
+      }
+    }
+    lds_barrier();   // all fragment reads done before the epilogue reuses LDS
+  } else if (kt0 < kt1) {
     al.load();
     bl.load();
     al.store(As);
@@ -417,7 +601,7 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
       const int cur = (kt - kt0) & 1;
       const bool more = kt + 1 < kt1;
       if (more) { al.load(); bl.load(); }
-      Mma<T, FM, FN>::run(As + cur * A_EL, wm * WTM, Bs + cur * B_EL, wn * WTN, acc, lane);
+      Mma<T, FM, FN, LA, LB>::run(As + cur * A_EL, wm * WTM, Bs + cur * B_EL, wn * WTN, acc, lane);
       if (more) { al.store(As + (cur ^ 1) * A_EL); bl.store(Bs + (cur ^ 1) * B_EL); }
       __syncthreads();
     }

@@ -13,6 +13,12 @@ namespace ax {
 
 static constexpr int TPB = 256;
 
+// k-contiguous operand loaders: direct-to-LDS for bf16, through registers for fp32
+template <typename T, int R>
+using RowsLd = std::conditional_t<std::is_same<T, bf16>::value, DmaKC<R>, LdKC<T, R>>;
+template <typename T, int R>
+using Im2colLd = std::conditional_t<std::is_same<T, bf16>::value, DmaIm2col<R>, LdIm2col<T, R>>;
+
 static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
 
 static inline void rec_start(const KTimer* kt, hipStream_t st) { if (kt) hipEventRecord(kt->start, st); }
@@ -123,9 +129,9 @@ template <typename T>
 static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
                               hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 96;
-  LdIm2col<T, BM> a;
+  Im2colLd<T, BM> a;
   a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
-  LdKC<T, BN> b;
+  RowsLd<T, BN> b;
   b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
   EpBiasRelu<T> e;
   e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
@@ -155,12 +161,12 @@ struct ConvFwdFn {
   hipError_t operator()() const {
     constexpr int BM = 128;
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
-    LdIm2col<T, BM> a;
+    Im2colLd<T, BM> a;
     a.p = (const T*)x;
     a.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
     a.M = s.Nimg * s.Ho * s.Wo;
     a.K = s.K * s.K * Cig;
-    LdKC<T, BN> bl;
+    RowsLd<T, BN> bl;
     bl.p = (const T*)wr; bl.ld = a.K; bl.rows = Cog; bl.K = a.K; bl.gstride = (int64_t)Cog * a.K;
     EpBiasRelu<T> e;
     e.out = (T*)y; e.bias = (const T*)b; e.ldo = s.Cout; e.M = a.M; e.N = Cog;
@@ -184,12 +190,12 @@ struct ConvDgradFn {
     constexpr int BM = 128;
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
     // dX = stride-1 convolution of dY with flipped, transposed weights, pad K-1-p
-    LdIm2col<T, BM> a;
+    Im2colLd<T, BM> a;
     a.p = (const T*)dy;
     a.cg = ConvGeom{s.Ho, s.Wo, s.Cout, Cog, s.K, s.K, 1, s.K - 1 - s.pad, s.H, s.W};
     a.M = s.Nimg * s.H * s.W;
     a.K = s.K * s.K * Cog;
-    LdKC<T, BN> bl;
+    RowsLd<T, BN> bl;
     bl.p = (const T*)wt; bl.ld = a.K; bl.rows = Cig; bl.K = a.K; bl.gstride = (int64_t)Cig * a.K;
     EpMask<T> e;
     e.out = (T*)dx; e.mask = (const T*)mask; e.ldo = s.Cin; e.M = a.M; e.N = Cig;
@@ -374,9 +380,9 @@ static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, co
   constexpr int BM = 128, BN = 128;
   const int S = fc_splits(M, O, K);
   if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  LdKC<T, BM> a;
+  RowsLd<T, BM> a;
   a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
-  LdKC<T, BN> bl;
+  RowsLd<T, BN> bl;
   bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
