@@ -40,10 +40,15 @@ template <typename T> struct VecOf { static constexpr int V = 16 / sizeof(T); };
 // fragment read over all banks.
 template <typename T> struct LayoutKC {
   static constexpr int LS = BK;
+  template <int R> static constexpr int tile_elems() { return R * LS; }
   static __device__ __forceinline__ int off(int row, int col) {
     constexpr int G = VecOf<T>::V;
     const int s = sizeof(T) == 2 ? ((row >> 1) & 7) : (row & 15);
     return row * LS + (((col / G) ^ s) * G) + (col % G);
+  }
+  // bf16 MFMA fragment: rows c0 + (lane & 15), k = kk + 8 (lane >> 4) .. + 7
+  static __device__ __forceinline__ bf16x8_t frag(const bf16* t, int c0, int kk, int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(t + off(c0 + (lane & 15), kk + (lane >> 4) * 8));
   }
 };
 // LayoutKO, for k-outer loaders whose transposed pair writes put 16 lanes on
@@ -51,9 +56,46 @@ template <typename T> struct LayoutKC {
 // 4..6 of the row.
 template <typename T> struct LayoutKO {
   static constexpr int LS = BK + VecOf<T>::V;
+  template <int R> static constexpr int tile_elems() { return R * LS; }
   static __device__ __forceinline__ int off(int row, int col) {
     constexpr int G = VecOf<T>::V;
     return row * LS + (((col / G) ^ ((row >> 4) & 7)) * G) + (col % G);
+  }
+  static __device__ __forceinline__ bf16x8_t frag(const bf16* t, int c0, int kk, int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(t + off(c0 + (lane & 15), kk + (lane >> 4) * 8));
+  }
+};
+
+// LayoutTR, for bf16 k-outer operands fetched direct-to-LDS: the tile is kept
+// as the source stores it, [BK k-rows][128 operand rows] (256-byte k-rows),
+// with the 16-byte granule index XOR-ed with swz(k).  Fragments are read with
+// ds_read_b64_tr_b16, which transposes within each 16-lane group: lane i of
+// the group receives element i % 4 of the 8-byte chunk addressed by lane
+// 4 e + i / 4, as its element e.  Lane t addressing k-row k0 + t / 4 at
+// operand rows c0 + 4 (t % 4) .. + 3 thus receives operand row c0 + t,
+// k = k0 .. k0 + 3; two such reads (k0 and k0 + 4) make an MFMA fragment.
+// swz(k) gives the 16 k-rows one read touches (bits 0..1 and 3 of k differ)
+// eight distinct even granule offsets, so each half-wave covers all banks.
+struct LayoutTR {
+  static constexpr int LS = 128;
+  template <int R> static constexpr int tile_elems() {
+    static_assert(R <= LS, "operand rows per tile");
+    return BK * LS;
+  }
+  static __device__ __forceinline__ int swz(int k) { return ((k & 3) | ((k >> 1) & 4)) << 1; }
+  static __device__ __forceinline__ int off(int k, int col) {
+    return k * LS + (((col >> 3) ^ swz(k)) << 3) + (col & 7);
+  }
+  static __device__ __forceinline__ bf16x8_t frag(const bf16* t, int c0, int kk, int lane) {
+    const int q = lane & 15;
+    const int k = kk + (lane >> 4) * 8 + (q >> 2), col = c0 + 4 * (q & 3);
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + off(k, col)));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + off(k + 4, col)));
+    const v8s both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, both);
   }
 };
 
@@ -384,6 +426,99 @@ struct PixelIter {
   }
 };
 
+// Lanes of a direct-to-LDS k-outer tile (LayoutTR): the BK/4 slots of 4
+// k-rows (1 KB) are dealt to the waves as j = wave + 4 i.  Lane l fills k-row
+// 4 j + l / 16 at physical granule l % 16; the swizzle then maps it to the same
+// logical granule (8 operand rows) for every slot of its wave.
+struct TrSlots {
+  static constexpr int NI = BK / 16;
+  static __device__ __forceinline__ int krow(int wave, int i, int lane) { return 4 * (wave + 4 * i) + (lane >> 4); }
+  static __device__ __forceinline__ int granule(int wave, int lane) {
+    return (lane & 15) ^ LayoutTR::swz(krow(wave, 0, lane));
+  }
+};
+
+// Direct-to-LDS k-outer operand for bf16: element (r, k) at base[k * ld + r]
+// (base = p + g * gstride), r < rows, k < K.
+template <int R>
+struct DmaKO {
+  static constexpr bool DMA = true;
+  using Layout = LayoutTR;
+  static constexpr int NI = TrSlots::NI;
+  const bf16* p; int64_t ld; int rows; int K; int64_t gstride;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[NI];
+  int kr;          // k of this lane's first slot
+  bool cok;
+  __device__ void setup(int r0, int g, int kb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rs = buf_rsrc(p + (int64_t)g * gstride, (uint32_t)(((int64_t)(K - 1) * ld + rows) * 2));
+    const int col = r0 + TrSlots::granule(wave, lane) * 8;
+    cok = col < rows;
+    kr = kb + TrSlots::krow(wave, 0, lane);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) off[i] = (uint32_t)(((int64_t)(kr + 16 * i) * ld + col) * 2);
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool ok = cok && kr + 16 * i < K;
+      dma16(rs, ok ? off[i] : BUF_OOB, s + 4 * (wave + 4 * i) * LayoutTR::LS);
+      off[i] += (uint32_t)(BK * ld * 2);
+    }
+    kr += BK;
+  }
+};
+
+// Direct-to-LDS weight-gradient B operand for bf16 (same element definition
+// as LdWgradB below): each lane keeps one operand-row granule, i.e. one tap
+// and channel run, and steps its k-rows (output pixels) BK at a time.
+template <int R>
+struct DmaWgradB {
+  static constexpr bool DMA = true;
+  using Layout = LayoutTR;
+  static constexpr int NI = TrSlots::NI;
+  const bf16* p; ConvGeom cg; int rows; int P;   // rows = KH*KW*Cg, P = Nimg*Ho*Wo
+  __amdgpu_buffer_rsrc_t rs;
+  int hoff, woff, coff, dq, dr;
+  bool cok;
+  int pn[NI], pho[NI], pwo[NI], pp[NI];
+  __device__ void setup(int r0, int g, int kb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hw = cg.Ho * cg.Wo;
+    const int nimg = (P + hw - 1) / hw;
+    rs = buf_rsrc(p, (uint32_t)((int64_t)nimg * cg.H * cg.W * cg.Ctot * 2));
+    const int r = r0 + TrSlots::granule(wave, lane) * 8;
+    cok = r < rows;
+    const int rr = cok ? r : 0;
+    const int tap = rr / cg.Cg, ci = rr - tap * cg.Cg;
+    const int kh = tap / cg.KW, kw = tap - kh * cg.KW;
+    hoff = kh - cg.pad; woff = kw - cg.pad; coff = g * cg.Cg + ci;
+    dq = BK / cg.Wo; dr = BK - dq * cg.Wo;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = kb + TrSlots::krow(wave, i, lane);
+      pp[i] = q; pn[i] = q / hw;
+      const int rem = q - pn[i] * hw;
+      pho[i] = rem / cg.Wo; pwo[i] = rem - pho[i] * cg.Wo;
+    }
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int h = pho[i] * cg.stride + hoff, w = pwo[i] * cg.stride + woff;
+      const bool ok = cok && pp[i] < P && (unsigned)h < (unsigned)cg.H && (unsigned)w < (unsigned)cg.W;
+      const uint32_t o = ok ? (uint32_t)(((pn[i] * cg.H + h) * cg.W + w) * cg.Ctot + coff) * 2u : BUF_OOB;
+      dma16(rs, o, s + 4 * (wave + 4 * i) * LayoutTR::LS);
+      pp[i] += BK; pwo[i] += dr; pho[i] += dq;
+      if (pwo[i] >= cg.Wo) { pwo[i] -= cg.Wo; ++pho[i]; }
+      while (pho[i] >= cg.Ho) { pho[i] -= cg.Ho; ++pn[i]; }
+    }
+  }
+};
+
 // Weight-gradient B operand: element (r = (kh, kw, ci), k = output pixel p) =
 // X[n(p)][ho*s - pad + kh][wo*s - pad + kw][g*Cg + ci] of an NHWC tensor.
 // Needs Cg % V == 0 (a row chunk never straddles two taps).
@@ -491,16 +626,13 @@ struct Mma<bf16, FM, FN, LA, LB> {
   // As/Bs: LDS tiles; ra/rb: first row of this wave's slice in each tile
   static __device__ __forceinline__ void run(const bf16* As, int ra, const bf16* Bs, int rb,
                                              f32x4_t (&acc)[FM][FN], int lane) {
-    const int r = lane & 15, kq = (lane >> 4) * 8;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       bf16x8_t a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + LA::off(ra + i * 16 + r, kk + kq));
+      for (int i = 0; i < FM; ++i) a[i] = LA::frag(As, ra + i * 16, kk, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + LB::off(rb + j * 16 + r, kk + kq));
+      for (int j = 0; j < FN; ++j) b[j] = LB::frag(Bs, rb + j * 16, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -540,7 +672,7 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_EL = BM * LA::LS, B_EL = BN * LB::LS;
+  constexpr int A_EL = LA::template tile_elems<BM>(), B_EL = LB::template tile_elems<BN>();
   constexpr int MAIN_BYTES = 2 * (A_EL + B_EL) * (int)sizeof(T);
   constexpr int CST = BN + 4;
   constexpr int EPI_BYTES = BM * CST * 4;

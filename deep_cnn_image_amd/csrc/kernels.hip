@@ -18,6 +18,11 @@ template <typename T, int R>
 using RowsLd = std::conditional_t<std::is_same<T, bf16>::value, DmaKC<R>, LdKC<T, R>>;
 template <typename T, int R>
 using Im2colLd = std::conditional_t<std::is_same<T, bf16>::value, DmaIm2col<R>, LdIm2col<T, R>>;
+// k-outer operand loaders: direct-to-LDS with transposing fragment reads for bf16
+template <typename T, int R>
+using ColsLd = std::conditional_t<std::is_same<T, bf16>::value, DmaKO<R>, LdKO<T, R>>;
+template <typename T, int R>
+using WgradBLd = std::conditional_t<std::is_same<T, bf16>::value, DmaWgradB<R>, LdWgradB<T, R>>;
 
 static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
 
@@ -265,9 +270,9 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
   const int tiles = cdiv(Cog, BM) * cdiv(N, BN) * s.groups;
   const int S = wgrad_splits(tiles, P);
   if ((size_t)s.groups * S * Cog * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  LdKO<T, BM> a;
+  ColsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = s.Cout; a.rows = Cog; a.K = P; a.gstride = Cog;
-  LdWgradB<T, BN> b;
+  WgradBLd<T, BN> b;
   b.p = (const T*)x;
   b.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
   b.rows = N; b.P = P;
@@ -293,9 +298,9 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   const int N = S2D_K, P = Nimg * 3025;
   const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
   if ((size_t)S * 96 * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  LdKO<T, BM> a;
+  ColsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = 96; a.rows = 96; a.K = P; a.gstride = 0;
-  LdWgradB<T, BN> b;
+  WgradBLd<T, BN> b;
   b.p = (const T*)xs; b.cg = conv1_geom(); b.rows = N; b.P = P;
   EpF32 e;
   e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
@@ -406,9 +411,9 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
   constexpr int BM = 128, BN = 128;
   const int S = fc_splits(M, K, O);
   if ((size_t)S * M * K * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  LdKC<T, BM> a;
+  RowsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = O; a.rows = M; a.K = O; a.gstride = 0;
-  LdKO<T, BN> bl;
+  ColsLd<T, BN> bl;
   bl.p = (const T*)w; bl.ld = K; bl.rows = K; bl.K = O; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = K; e.M = M; e.N = K; e.splits = S;
@@ -430,9 +435,9 @@ template <typename T>
 static hipError_t fc_wgrad_t(int M, int K, int O, const void* dy, const void* x, float* gw,
                              hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
-  LdKO<T, BM> a;
+  ColsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = O; a.rows = O; a.K = M; a.gstride = 0;
-  LdKO<T, BN> bl;
+  ColsLd<T, BN> bl;
   bl.p = (const T*)x; bl.ld = K; bl.rows = K; bl.K = M; bl.gstride = 0;
   EpF32 e;
   e.out = gw; e.ldo = K; e.M = O; e.N = K; e.splits = 1;
