@@ -218,8 +218,10 @@ hipError_t conv_dgrad(DType dt, const ConvShape& s, const void* dy, const void* 
 }
 
 // ---- weight gradients: split-K partials, then an ordered reduction
+// Enough splits to fill the chip once at two resident workgroups per CU, and
+// never more than that: a few workgroups beyond it would cost a second round.
 static int wgrad_splits(int tiles, int K) {
-  int want = cdiv(2 * 256, tiles);
+  int want = (2 * 256) / tiles;
   if (want > 256) want = 256;
   return eff_splits(K, want);
 }
@@ -235,30 +237,43 @@ size_t conv1_wgrad_part_bytes(int Nimg) {
   return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * S2D_K * sizeof(float);
 }
 
-// gw[co][ci][kh][kw] = sum_s part[g][s][co_l][r] with
+// gw[co][ci][kh][kw] = sum over s = 0..S-1, in order, of part[g][s][col][r]
+// with co = g*Mg + col and
 //   r = (kh*KW + kw)*Cg + ci                                  (mode 1)
-//   r = ci*KH*KW + kh*KW + kw                                 (mode 0)
-//   r = ((kh/4)*3 + kw/4)*48 + ci*16 + (kh%4)*4 + kw%4        (mode 2: layer 1, space-to-depth)
+//   r = ((kh/4)*3 + kw/4)*48 + ci*16 + (kh%4)*4 + kw%4        (mode 2: layer 1, space-to-depth;
+//                                                               r outside the 11x11 taps is dropped)
+// One thread per four consecutive r of one output channel, so the partial
+// rows are read with 16-byte coalesced loads.  Needs Np % 4 == 0.
 __global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg, int Np, int Cg,
-                               int KH, int KW, int rkhwc, float* __restrict__ gw) {
-  const int64_t o = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  const int KK = KH * KW;
-  const int64_t total = (int64_t)G * Mg * Cg * KK;
-  if (o >= total) return;
-  const int co = (int)(o / (Cg * KK));
-  const int rem = (int)(o - (int64_t)co * Cg * KK);
-  const int ci = rem / KK, t = rem - ci * KK;
+                               int KH, int KW, int mode, float* __restrict__ gw) {
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  const int np4 = Np >> 2;
+  if (t >= (int64_t)G * Mg * np4) return;
+  const int co = (int)(t / np4);
+  const int r0 = (int)(t - (int64_t)co * np4) * 4;
   const int g = co / Mg, col = co - g * Mg;
-  int r;
-  if (rkhwc == 1) r = t * Cg + ci;
-  else if (rkhwc == 2) {
-    const int kh = t / KW, kw = t - kh * KW;
-    r = ((kh >> 2) * 3 + (kw >> 2)) * 48 + ci * 16 + (kh & 3) * 4 + (kw & 3);
-  } else r = rem;
-  const float* p = part + ((int64_t)g * S * Mg + col) * Np + r;
-  float acc = 0.f;
-  for (int s = 0; s < S; ++s) acc += p[(int64_t)s * Mg * Np];
-  gw[o] = acc;
+  const float* p = part + ((int64_t)g * S * Mg + col) * Np + r0;
+  const int64_t ss = (int64_t)Mg * Np;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(p + s * ss);
+    a[0] += q.x; a[1] += q.y; a[2] += q.z; a[3] += q.w;
+  }
+  float* out = gw + (int64_t)co * Cg * KH * KW;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + i;
+    int ci, kh, kw;
+    if (mode == 2) {
+      const int tap = r / 48, q = r - tap * 48;
+      ci = q >> 4; kh = (tap / 3) * 4 + ((q >> 2) & 3); kw = (tap % 3) * 4 + (q & 3);
+      if (kh >= KH || kw >= KW) continue;
+    } else {
+      const int tp = r / Cg;
+      ci = r - tp * Cg; kh = tp / KW; kw = tp - kh * KW;
+    }
+    out[(ci * KH + kh) * KW + kw] = a[i];
+  }
 }
 
 template <typename T>
@@ -280,7 +295,7 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
   e.out = part; e.ldo = N; e.M = Cog; e.N = N; e.splits = S;
   hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, grid1d((int64_t)s.Cout * Cig * s.K * s.K), dim3(TPB), 0, st, part,
+  hipLaunchKernelGGL(k_wgrad_reduce, grid1d((int64_t)s.Cout * N / 4), dim3(TPB), 0, st, part,
                      s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
   return hipGetLastError();
 }
@@ -306,7 +321,7 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
   hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * 363), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
+  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
                      gw);
   return hipGetLastError();
 }
