@@ -237,26 +237,42 @@ size_t conv1_wgrad_part_bytes(int Nimg) {
   return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * S2D_K * sizeof(float);
 }
 
-// gw[co][ci][kh][kw] = sum over s = 0..S-1, in order, of part[g][s][col][r]
-// with co = g*Mg + col and
+// gw[co][ci][kh][kw] = sum over the S split partials part[g][s][col][r], with
+// co = g*Mg + col and
 //   r = (kh*KW + kw)*Cg + ci                                  (mode 1)
 //   r = ((kh/4)*3 + kw/4)*48 + ci*16 + (kh%4)*4 + kw%4        (mode 2: layer 1, space-to-depth;
 //                                                               r outside the 11x11 taps is dropped)
-// One thread per four consecutive r of one output channel, so the partial
-// rows are read with 16-byte coalesced loads.  Needs Np % 4 == 0.
-__global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg, int Np, int Cg,
-                               int KH, int KW, int mode, float* __restrict__ gw) {
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+// A block covers 32 runs of four consecutive r (16-byte coalesced loads along
+// the partial rows) with 8 split groups: group j sums splits j, j+8, ... in
+// order, then the 8 group sums are added in order of j.  Needs Np % 4 == 0.
+constexpr int WR_Q = 32, WR_G = TPB / WR_Q;
+__global__ void __launch_bounds__(TPB) k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg,
+                                                      int Np, int Cg, int KH, int KW, int mode,
+                                                      float* __restrict__ gw) {
+  __shared__ float4 red[WR_G][WR_Q];
+  const int qd = threadIdx.x % WR_Q, j = threadIdx.x / WR_Q;
+  const int64_t t = (int64_t)blockIdx.x * WR_Q + qd;
   const int np4 = Np >> 2;
-  if (t >= (int64_t)G * Mg * np4) return;
-  const int co = (int)(t / np4);
-  const int r0 = (int)(t - (int64_t)co * np4) * 4;
+  const bool live = t < (int64_t)G * Mg * np4;
+  const int co = live ? (int)(t / np4) : 0;
+  const int r0 = live ? (int)(t - (int64_t)co * np4) * 4 : 0;
   const int g = co / Mg, col = co - g * Mg;
-  const float* p = part + ((int64_t)g * S * Mg + col) * Np + r0;
-  const int64_t ss = (int64_t)Mg * Np;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    const float* p = part + ((int64_t)g * S * Mg + col) * Np + r0;
+    const int64_t ss = (int64_t)Mg * Np;
+    for (int s = j; s < S; s += WR_G) {
+      const float4 q = *reinterpret_cast<const float4*>(p + s * ss);
+      acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+    }
+  }
+  red[j][qd] = acc;
+  __syncthreads();
+  if (j != 0 || !live) return;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float4 q = *reinterpret_cast<const float4*>(p + s * ss);
+#pragma unroll
+  for (int jj = 0; jj < WR_G; ++jj) {
+    const float4 q = red[jj][qd];
     a[0] += q.x; a[1] += q.y; a[2] += q.z; a[3] += q.w;
   }
   float* out = gw + (int64_t)co * Cg * KH * KW;
@@ -275,6 +291,8 @@ __global__ void k_wgrad_reduce(const float* __restrict__ part, int G, int S, int
     out[(ci * KH + kh) * KW + kw] = a[i];
   }
 }
+
+static dim3 wgrad_reduce_grid(int64_t outputs4) { return dim3((unsigned)((outputs4 + WR_Q - 1) / WR_Q)); }
 
 template <typename T>
 static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x, float* part,
@@ -295,7 +313,7 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
   e.out = part; e.ldo = N; e.M = Cog; e.N = N; e.splits = S;
   hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, grid1d((int64_t)s.Cout * N / 4), dim3(TPB), 0, st, part,
+  hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid((int64_t)s.Cout * N / 4), dim3(TPB), 0, st, part,
                      s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
   return hipGetLastError();
 }
@@ -321,7 +339,7 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
   hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, grid1d(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
+  hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
                      gw);
   return hipGetLastError();
 }
@@ -510,11 +528,6 @@ hipError_t w_dgrad(DType dt, const void* w, void* out, int G, int Cog, int Cig, 
 // Local response normalisation across channels, NHWC
 //   b_i = a_i * S_i^-beta,  S_i = k + alpha * sum_{|j-i| <= half, 0 <= j < C} a_j^2
 // =========================================================================
-__device__ __forceinline__ float pow_neg_beta(float S, float beta, bool b075) {
-  if (b075) { const float r = rsqrtf(S); return r * sqrtf(r); }   // S^-1/2 * S^-1/4
-  return exp2f(-beta * log2f(S));
-}
-
 // Loads channels c0-8 .. c0+15 of one pixel (zero outside [0, C)).
 template <typename T>
 __device__ __forceinline__ void load24(const T* px, int c0, int C, float* v) {
@@ -529,87 +542,141 @@ __device__ __forceinline__ void load24(const T* px, int c0, int C, float* v) {
   }
 }
 
-template <typename T>
-__global__ void k_lrn_fwd(const T* __restrict__ a, T* __restrict__ b, int64_t npix, int C, float k,
-                          float alpha, float beta, int half) {
-  const int cpp = C >> 3;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (t >= npix * cpp) return;
-  const int64_t pix = t / cpp;
+// One thread per pixel and run of 8 channels; window half-width H and the
+// beta == 3/4 case are compile-time, so every loop below unrolls completely.
+// With beta == 3/4: r = rsqrt(S), S^-beta = r sqrt(r), S^(-beta-1) = S^-beta r^2.
+template <bool B075>
+__device__ __forceinline__ void lrn_pows(float S, float beta, float& p, float& q) {
+  if (B075) {
+    const float r = rsqrtf(S);
+    p = r * sqrtf(r);
+    q = p * r * r;
+  } else {
+    p = exp2f(-beta * log2f(S));
+    q = p / S;
+  }
+}
+
+template <typename T, int H, bool B075>
+__global__ void k_lrn_fwd(const T* __restrict__ a, T* __restrict__ b, uint32_t total, int C, float k,
+                          float alpha, float beta) {
+  const uint32_t t = blockIdx.x * TPB + threadIdx.x;
+  if (t >= total) return;
+  const uint32_t cpp = (uint32_t)C >> 3;
+  const uint32_t pix = t / cpp;
   const int c0 = (int)(t - pix * cpp) * 8;
-  const T* px = a + pix * C;
   float v[24];
-  load24(px, c0, C, v);
-  const bool b075 = beta == 0.75f;
+  load24(a + (size_t)pix * C, c0, C, v);
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float s = 0.f;
-    for (int j = -half; j <= half; ++j) { const float x = v[8 + i + j]; s += x * x; }
-    o[i] = v[8 + i] * pow_neg_beta(k + alpha * s, beta, b075);
+#pragma unroll
+    for (int j = -H; j <= H; ++j) s += v[8 + i + j] * v[8 + i + j];
+    float p, q;
+    lrn_pows<B075>(k + alpha * s, beta, p, q);
+    o[i] = v[8 + i] * p;
   }
-  Pack8<T>::store(b + pix * C + c0, o);
+  Pack8<T>::store(b + (size_t)pix * C + c0, o);
 }
 
 // Backward of LRN fused with the preceding ReLU's mask [a > 0]:
-//   da_j = g_j S_j^-beta - 2 alpha beta a_j sum_{|i-j| <= half} g_i a_i S_i^(-beta-1)
-// half <= 4 (window <= 9): needs a over c0-8 .. c0+15 and g over c0-4 .. c0+11.
-template <typename T>
+//   da_j = g_j S_j^-beta - 2 alpha beta a_j sum_{|i-j| <= H} g_i a_i S_i^(-beta-1)
+// The 8 + 2H channels c0-H .. c0+7+H carry the per-channel terms; a is needed
+// over c0-2H .. c0+7+2H (inside c0-8 .. c0+15 for H <= 4).
+template <typename T, int H, bool B075>
 __global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* __restrict__ da,
-                          int64_t npix, int C, float k, float alpha, float beta, int half) {
-  const int cpp = C >> 3;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (t >= npix * cpp) return;
-  const int64_t pix = t / cpp;
+                          uint32_t total, int C, float k, float alpha, float beta) {
+  const uint32_t t = blockIdx.x * TPB + threadIdx.x;
+  if (t >= total) return;
+  const uint32_t cpp = (uint32_t)C >> 3;
+  const uint32_t pix = t / cpp;
   const int c0 = (int)(t - pix * cpp) * 8;
   float av[24], gv[24];
-  load24(a + pix * C, c0, C, av);
-  load24(g + pix * C, c0, C, gv);
-  const bool b075 = beta == 0.75f;
-  // S, S^-beta and g a S^(-beta-1) at relative channels 4 .. 19 (= c0-4 .. c0+11)
-  float pb[16], tt[16];
+  load24(a + (size_t)pix * C, c0, C, av);
+  load24(g + (size_t)pix * C, c0, C, gv);
+  constexpr int NR = 8 + 2 * H;
+  float pb[NR], tt[NR];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rel = r + 4;
+  for (int r = 0; r < NR; ++r) {
+    const int rel = 8 - H + r;
     float s = 0.f;
-    for (int j = -half; j <= half; ++j) { const float x = av[rel + j]; s += x * x; }
-    const float S = k + alpha * s;
-    const float p = pow_neg_beta(S, beta, b075);
+#pragma unroll
+    for (int j = -H; j <= H; ++j) s += av[rel + j] * av[rel + j];
+    float p, q;
+    lrn_pows<B075>(k + alpha * s, beta, p, q);
     pb[r] = p;
-    tt[r] = gv[rel] * av[rel] * (p / S);
+    tt[r] = gv[rel] * av[rel] * q;
   }
   float o[8];
   const float c2 = 2.f * alpha * beta;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = i + 4;   // index into pb/tt for channel c0+i
     float cross = 0.f;
-    for (int j = -half; j <= half; ++j) cross += tt[r + j];
+#pragma unroll
+    for (int j = -H; j <= H; ++j) cross += tt[i + H + j];
     const float aj = av[8 + i];
-    const float d = gv[8 + i] * pb[r] - c2 * aj * cross;
+    const float d = gv[8 + i] * pb[i + H] - c2 * aj * cross;
     o[i] = aj > 0.f ? d : 0.f;
   }
-  Pack8<T>::store(da + pix * C + c0, o);
+  Pack8<T>::store(da + (size_t)pix * C + c0, o);
 }
+
+// Calls fn.operator()<H, B075>() for the window half-width and beta.
+template <class Fn>
+static hipError_t lrn_dispatch(int half, float beta, Fn&& fn) {
+  const bool b075 = beta == 0.75f;
+#define AX_LRN_CASE(HH) \
+  case HH: return b075 ? fn.template operator()<HH, true>() : fn.template operator()<HH, false>();
+  switch (half) {
+    AX_LRN_CASE(0) AX_LRN_CASE(1) AX_LRN_CASE(2) AX_LRN_CASE(3) AX_LRN_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef AX_LRN_CASE
+}
+
+template <typename T>
+struct LrnFwdFn {
+  const void* a; void* b; uint32_t total; int C; float k, alpha, beta; hipStream_t st;
+  template <int H, bool B075>
+  hipError_t operator()() const {
+    hipLaunchKernelGGL((k_lrn_fwd<T, H, B075>), grid1d(total), dim3(TPB), 0, st, (const T*)a, (T*)b, total, C,
+                       k, alpha, beta);
+    return hipGetLastError();
+  }
+};
+template <typename T>
+struct LrnBwdFn {
+  const void* a; const void* g; void* da; uint32_t total; int C; float k, alpha, beta; hipStream_t st;
+  template <int H, bool B075>
+  hipError_t operator()() const {
+    hipLaunchKernelGGL((k_lrn_bwd<T, H, B075>), grid1d(total), dim3(TPB), 0, st, (const T*)a, (const T*)g,
+                       (T*)da, total, C, k, alpha, beta);
+    return hipGetLastError();
+  }
+};
 
 hipError_t lrn_fwd(DType dt, const void* a, void* b, int64_t npix, int C, float k, float alpha, float beta,
                    int n, hipStream_t st, const KTimer* kt) {
-  const dim3 g = grid1d(npix * (C / 8));
+  const int64_t total = npix * (C / 8);
+  if (total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   rec_start(kt, st);
-  if (dt == BF16) hipLaunchKernelGGL((k_lrn_fwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (bf16*)b, npix, C, k, alpha, beta, n / 2);
-  else hipLaunchKernelGGL((k_lrn_fwd<float>), g, dim3(TPB), 0, st, (const float*)a, (float*)b, npix, C, k, alpha, beta, n / 2);
+  const hipError_t e = dt == BF16
+      ? lrn_dispatch(n / 2, beta, LrnFwdFn<bf16>{a, b, (uint32_t)total, C, k, alpha, beta, st})
+      : lrn_dispatch(n / 2, beta, LrnFwdFn<float>{a, b, (uint32_t)total, C, k, alpha, beta, st});
   rec_stop(kt, st);
-  return hipGetLastError();
+  return e;
 }
 hipError_t lrn_bwd(DType dt, const void* a, const void* gr, void* da, int64_t npix, int C, float k,
                    float alpha, float beta, int n, hipStream_t st, const KTimer* kt) {
-  if (n / 2 > 4) return hipErrorInvalidValue;
-  const dim3 g = grid1d(npix * (C / 8));
+  const int64_t total = npix * (C / 8);
+  if (total >= (int64_t)1 << 31) return hipErrorInvalidValue;
   rec_start(kt, st);
-  if (dt == BF16) hipLaunchKernelGGL((k_lrn_bwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)a, (const bf16*)gr, (bf16*)da, npix, C, k, alpha, beta, n / 2);
-  else hipLaunchKernelGGL((k_lrn_bwd<float>), g, dim3(TPB), 0, st, (const float*)a, (const float*)gr, (float*)da, npix, C, k, alpha, beta, n / 2);
+  const hipError_t e = dt == BF16
+      ? lrn_dispatch(n / 2, beta, LrnBwdFn<bf16>{a, gr, da, (uint32_t)total, C, k, alpha, beta, st})
+      : lrn_dispatch(n / 2, beta, LrnBwdFn<float>{a, gr, da, (uint32_t)total, C, k, alpha, beta, st});
   rec_stop(kt, st);
-  return hipGetLastError();
+  return e;
 }
 
 // =========================================================================
