@@ -151,7 +151,8 @@ struct DmaSlots {
 struct GemmGrid {
   int M, N, K;          // per group
   int tiles_m, tiles_n; // tile counts
-  int splits;           // split-K factor (blockIdx.z = group * splits + split)
+  int splits;           // split-K factor
+  int groups;           // independent GEMMs (convolution groups)
   int kt_per_split;     // k-tiles per split
 };
 
@@ -341,7 +342,7 @@ struct DmaKC {
   __device__ void setup(int r0, int g, int kb) {
     const bf16* base = p + (int64_t)g * gstride;
     rs = buf_rsrc(base, (uint32_t)(((int64_t)(rows - 1) * ld + K) * 2));
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gcol = Slots::granule(lane, wave & 1) * 8;
     kc = kb + gcol;
 #pragma unroll
@@ -351,7 +352,7 @@ struct DmaKC {
     }
   }
   __device__ __forceinline__ void issue(bf16* s) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool kok = kc < K;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -374,7 +375,7 @@ struct DmaIm2col {
   int hb[NI], wb[NI], pix[NI];   // pix: element offset of input pixel (hb, wb) of the row's image
   int kc, kh, kw, ci;
   __device__ void setup(int r0, int g, int kb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = cg.Ho * cg.Wo;
     const int nimg = (M + hw - 1) / hw;
     rs = buf_rsrc(p, (uint32_t)((int64_t)nimg * cg.H * cg.W * cg.Ctot * 2));
@@ -395,13 +396,13 @@ struct DmaIm2col {
     ci = kc - tap * cg.Cg; kh = tap / cg.KW; kw = tap - kh * cg.KW;
   }
   __device__ __forceinline__ void issue(bf16* s) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool kok = kc < K;
     const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int hi = hb[i] + kh, wi = wb[i] + kw;
-      const bool ok = kok && (unsigned)hi < (unsigned)cg.H && (unsigned)wi < (unsigned)cg.W;
+      const bool ok = kok & ((unsigned)hi < (unsigned)cg.H) & ((unsigned)wi < (unsigned)cg.W);
       const uint32_t o = ok ? (uint32_t)(pix[i] + tapoff) * 2u : BUF_OOB;
       dma16(rs, o, s + Slots::slot(wave, i) * 8 * BK);
     }
@@ -451,7 +452,7 @@ struct DmaKO {
   int kr;          // k of this lane's first slot
   bool cok;
   __device__ void setup(int r0, int g, int kb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     rs = buf_rsrc(p + (int64_t)g * gstride, (uint32_t)(((int64_t)(K - 1) * ld + rows) * 2));
     const int col = r0 + TrSlots::granule(wave, lane) * 8;
     cok = col < rows;
@@ -460,10 +461,10 @@ struct DmaKO {
     for (int i = 0; i < NI; ++i) off[i] = (uint32_t)(((int64_t)(kr + 16 * i) * ld + col) * 2);
   }
   __device__ __forceinline__ void issue(bf16* s) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bool ok = cok && kr + 16 * i < K;
+      const bool ok = cok & (kr + 16 * i < K);
       dma16(rs, ok ? off[i] : BUF_OOB, s + 4 * (wave + 4 * i) * LayoutTR::LS);
       off[i] += (uint32_t)(BK * ld * 2);
     }
@@ -485,7 +486,7 @@ struct DmaWgradB {
   bool cok;
   int pn[NI], pho[NI], pwo[NI], pp[NI];
   __device__ void setup(int r0, int g, int kb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = cg.Ho * cg.Wo;
     const int nimg = (P + hw - 1) / hw;
     rs = buf_rsrc(p, (uint32_t)((int64_t)nimg * cg.H * cg.W * cg.Ctot * 2));
@@ -505,17 +506,104 @@ struct DmaWgradB {
     }
   }
   __device__ __forceinline__ void issue(bf16* s) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int h = pho[i] * cg.stride + hoff, w = pwo[i] * cg.stride + woff;
-      const bool ok = cok && pp[i] < P && (unsigned)h < (unsigned)cg.H && (unsigned)w < (unsigned)cg.W;
+      const bool ok = cok & (pp[i] < P) & ((unsigned)h < (unsigned)cg.H) & ((unsigned)w < (unsigned)cg.W);
       const uint32_t o = ok ? (uint32_t)(((pn[i] * cg.H + h) * cg.W + w) * cg.Ctot + coff) * 2u : BUF_OOB;
       dma16(rs, o, s + 4 * (wave + 4 * i) * LayoutTR::LS);
       pp[i] += BK; pwo[i] += dr; pho[i] += dq;
       if (pwo[i] >= cg.Wo) { pwo[i] -= cg.Wo; ++pho[i]; }
       while (pho[i] >= cg.Ho) { pho[i] -= cg.Ho; ++pn[i]; }
     }
+  }
+};
+
+// Weight gradients sum over all (image, output position) pairs in any order.
+// With the batch a multiple of BK, the *pixel-major* order k = pos * Nimg + n
+// (image fastest) gives every BK-wide k-slice a single output position pos:
+// everything but the image offset of a k-row is then uniform per slice or
+// fixed per lane, and the per-slice address work is a handful of scalar and
+// vector adds.  Both operands of one GEMM must use the same order.
+struct PixMajor {
+  int nimg, wo_n;          // images (a multiple of BK), output width
+  int n0, pos, ho, wo;     // image of k-row 0 and output position of the current slice
+  __device__ void set(int kb, int Nimg, int Wo) {
+    nimg = Nimg; wo_n = Wo;
+    pos = kb / Nimg; n0 = kb - pos * Nimg; ho = pos / Wo; wo = pos - ho * Wo;
+  }
+  __device__ __forceinline__ void advance() {
+    n0 += BK;
+    if (n0 == nimg) { n0 = 0; ++pos; if (++wo == wo_n) { wo = 0; ++ho; } }
+  }
+};
+
+// DmaKO in pixel-major order for dY^T: element (r, k = pos * Nimg + n) =
+// base[(n * HoWo + pos) * ld + r], base = p + g * gstride.
+template <int R>
+struct DmaKOPix {
+  static constexpr bool DMA = true;
+  using Layout = LayoutTR;
+  static constexpr int NI = TrSlots::NI;
+  const bf16* p; int64_t ld; int rows; int Nimg; int HoWo, Wo; int64_t gstride;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[NI];   // byte offset of (k-row image, column) relative to image n0, position 0
+  PixMajor pm;
+  __device__ void setup(int r0, int g, int kb) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rs = buf_rsrc(p + (int64_t)g * gstride, (uint32_t)((int64_t)Nimg * HoWo * ld * 2));
+    const int col = r0 + TrSlots::granule(wave, lane) * 8;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      off[i] = col < rows ? (uint32_t)(((int64_t)TrSlots::krow(wave, i, lane) * HoWo * ld + col) * 2) : BUF_OOB;
+    pm.set(kb, Nimg, Wo);
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t u = (uint32_t)(((int64_t)pm.n0 * HoWo + pm.pos) * ld * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      dma16(rs, off[i] == BUF_OOB ? BUF_OOB : off[i] + u, s + 4 * (wave + 4 * i) * LayoutTR::LS);
+    pm.advance();
+  }
+};
+
+// DmaWgradB in pixel-major order: element (r = (kh, kw, ci), k = pos * Nimg + n) =
+// X[n][ho*s - pad + kh][wo*s - pad + kw][g*Cg + ci] with pos = (ho, wo).
+template <int R>
+struct DmaWgradBPix {
+  static constexpr bool DMA = true;
+  using Layout = LayoutTR;
+  static constexpr int NI = TrSlots::NI;
+  const bf16* p; ConvGeom cg; int rows; int Nimg;
+  __amdgpu_buffer_rsrc_t rs;
+  int hoff, woff, coff;
+  bool cok;
+  uint32_t roff[NI];   // byte offset of the k-row's image relative to image n0
+  PixMajor pm;
+  __device__ void setup(int r0, int g, int kb) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t img = (int64_t)cg.H * cg.W * cg.Ctot;
+    rs = buf_rsrc(p, (uint32_t)(Nimg * img * 2));
+    const int r = r0 + TrSlots::granule(wave, lane) * 8;
+    cok = r < rows;
+    const int rr = cok ? r : 0;
+    const int tap = rr / cg.Cg, ci = rr - tap * cg.Cg;
+    const int kh = tap / cg.KW, kw = tap - kh * cg.KW;
+    hoff = kh - cg.pad; woff = kw - cg.pad; coff = g * cg.Cg + ci;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) roff[i] = (uint32_t)(TrSlots::krow(wave, i, lane) * img * 2);
+    pm.set(kb, Nimg, cg.Wo);
+  }
+  __device__ __forceinline__ void issue(bf16* s) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = pm.ho * cg.stride + hoff, w = pm.wo * cg.stride + woff;
+    const bool ok = cok & ((unsigned)h < (unsigned)cg.H) & ((unsigned)w < (unsigned)cg.W);
+    const uint32_t b = (uint32_t)(((pm.n0 * cg.H + h) * cg.W + w) * cg.Ctot + coff) * 2u;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16(rs, ok ? roff[i] + b : BUF_OOB, s + 4 * (wave + 4 * i) * LayoutTR::LS);
+    pm.advance();
   }
 };
 
@@ -623,6 +711,27 @@ template <typename T, int FM, int FN, class LA, class LB> struct Mma;
 
 template <int FM, int FN, class LA, class LB>
 struct Mma<bf16, FM, FN, LA, LB> {
+  // All fragments of one BK slice, read before the next slice's loads are
+  // issued and multiplied while those loads are in flight.
+  struct Frags { bf16x8_t a[BK / 32][FM], b[BK / 32][FN]; };
+  static __device__ __forceinline__ void read(const bf16* As, int ra, const bf16* Bs, int rb, Frags& f, int lane) {
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) f.a[s][i] = LA::frag(As, ra + i * 16, s * 32, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) f.b[s][j] = LB::frag(Bs, rb + j * 16, s * 32, lane);
+    }
+  }
+  static __device__ __forceinline__ void mul(const Frags& f, f32x4_t (&acc)[FM][FN]) {
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+  }
   // As/Bs: LDS tiles; ra/rb: first row of this wave's slice in each tile
   static __device__ __forceinline__ void run(const bf16* As, int ra, const bf16* Bs, int rb,
                                              f32x4_t (&acc)[FM][FN], int lane) {
@@ -681,17 +790,22 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + 2 * A_EL;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave offsets scalar
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // Tile order: consecutive logical tiles (same m-row, neighbouring n) are kept
-  // on one XCD so they share its L2; hardware deals workgroups round-robin
-  // over the eight XCDs.
+  // Work order.  The 1-D grid enumerates (group, split, tile) with tiles
+  // fastest.  Hardware deals workgroups round-robin over the eight XCDs, each
+  // with its own L2; the remap gives XCD x one contiguous run of that order
+  // (the first nb % 8 XCDs one workgroup more), so workgroups that share
+  // operand rows (neighbouring tiles, tiles of one split) share an L2.
   const int nb = gridDim.x;
-  int b = blockIdx.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  const int bm = b / gg.tiles_n, bn = b - bm * gg.tiles_n;
-  const int g = blockIdx.z / gg.splits, s = blockIdx.z - g * gg.splits;
+  const int x = blockIdx.x & 7, q = nb >> 3, r = nb & 7;
+  const int b = x * q + (x < r ? x : r) + (blockIdx.x >> 3);
+  const int tiles = gg.tiles_m * gg.tiles_n;
+  const int gs = b / tiles, t = b - gs * tiles;
+  const int g = gs / gg.splits, s = gs - g * gg.splits;
+  const int bm = t / gg.tiles_n, bn = t - bm * gg.tiles_n;
   const int m0 = bm * BM, n0 = bn * BN;
   const int total_kt = (gg.K + BK - 1) / BK;
   const int kt0 = s * gg.kt_per_split;
@@ -711,16 +825,32 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
     // iteration publishes the slice every wave waited for and guarantees that
     // all waves are done with the other buffer, which the next slice then
     // overwrites while the matrix cores work.
+    // Unrolled by two so the buffer offsets are compile-time constants.
     if (kt0 < kt1) {
       al.issue(As);
       bl.issue(Bs);
-      for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
+      // Fragments of the current slice are read into registers before the
+      // next slice's loads are issued, so no LDS read has to wait for them.
+      using MM = Mma<T, FM, FN, LA, LB>;
+      auto step = [&](auto cur_c, int kt) {
+        constexpr int CUR = decltype(cur_c)::value;
         wait_vmcnt<0>();
         lds_barrier();
-        if (kt + 1 < kt1) { al.issue(As + (cur ^ 1) * A_EL); bl.issue(Bs + (cur ^ 1) * B_EL); }
-        Mma<T, FM, FN, LA, LB>::run(As + cur * A_EL, wm * WTM, Bs + cur * B_EL, wn * WTN, acc, lane);
+        typename MM::Frags f;
+        MM::read(As + CUR * A_EL, wm * WTM, Bs + CUR * B_EL, wn * WTN, f, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < kt1) { al.issue(As + (CUR ^ 1) * A_EL); bl.issue(Bs + (CUR ^ 1) * B_EL); }
+        __builtin_amdgcn_sched_barrier(0);
+        MM::mul(f, acc);
+        // keep the next slice's wait and barrier behind these products
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      int kt = kt0;
+      for (; kt + 1 < kt1; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
       }
+      if (kt < kt1) step(std::integral_constant<int, 0>{}, kt);
     }
     lds_barrier();   // all fragment reads done before the epilogue reuses LDS
   } else if (kt0 < kt1) {

@@ -42,7 +42,8 @@ static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int 
   const int ktiles = cdiv(K, BK);
   gg.splits = eff_splits(K, splits);
   gg.kt_per_split = cdiv(ktiles, gg.splits);
-  dim3 grid(gg.tiles_m * gg.tiles_n, 1, groups * gg.splits);
+  gg.groups = groups;
+  dim3 grid(gg.tiles_m * gg.tiles_n * groups * gg.splits);
   rec_start(kt, st);
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP>), grid, dim3(NTHREADS), 0, st, al, bl,
                      ep, gg);
@@ -303,15 +304,24 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
   const int tiles = cdiv(Cog, BM) * cdiv(N, BN) * s.groups;
   const int S = wgrad_splits(tiles, P);
   if ((size_t)s.groups * S * Cog * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  ColsLd<T, BM> a;
-  a.p = (const T*)dy; a.ld = s.Cout; a.rows = Cog; a.K = P; a.gstride = Cog;
-  WgradBLd<T, BN> b;
-  b.p = (const T*)x;
-  b.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
-  b.rows = N; b.P = P;
+  const ConvGeom cg{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
   EpF32 e;
   e.out = part; e.ldo = N; e.M = Cog; e.N = N; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
+  hipError_t err;
+  if (std::is_same<T, bf16>::value && s.Nimg % BK == 0) {
+    DmaKOPix<BM> a;
+    a.p = (const bf16*)dy; a.ld = s.Cout; a.rows = Cog; a.Nimg = s.Nimg; a.HoWo = s.Ho * s.Wo; a.Wo = s.Wo;
+    a.gstride = Cog;
+    DmaWgradBPix<BN> b;
+    b.p = (const bf16*)x; b.cg = cg; b.rows = N; b.Nimg = s.Nimg;
+    err = run_gemm<bf16, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
+  } else {
+    ColsLd<T, BM> a;
+    a.p = (const T*)dy; a.ld = s.Cout; a.rows = Cog; a.K = P; a.gstride = Cog;
+    WgradBLd<T, BN> b;
+    b.p = (const T*)x; b.cg = cg; b.rows = N; b.P = P;
+    err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
+  }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid((int64_t)s.Cout * N / 4), dim3(TPB), 0, st, part,
                      s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
@@ -331,13 +341,16 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   const int N = S2D_K, P = Nimg * 3025;
   const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
   if ((size_t)S * 96 * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  EpF32 e;
+  e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
+  hipError_t err;
+  // Pixel order (image-major): layer 1's large images make the pixel-major
+  // order scatter its reads.
   ColsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = 96; a.rows = 96; a.K = P; a.gstride = 0;
   WgradBLd<T, BN> b;
   b.p = (const T*)xs; b.cg = conv1_geom(); b.rows = N; b.P = P;
-  EpF32 e;
-  e.out = part; e.ldo = N; e.M = 96; e.N = N; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
+  err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
                      gw);

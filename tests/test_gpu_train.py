@@ -322,6 +322,20 @@ def test_full_batch128_train_step(orc):
     c4 = nchw(r["taps"]["conv4"])
     dw, db = orc.conv2d_bwd_weight(d5[:, ch5], c4, (3, 384, 3, 3), 1, 1)
     e["gw5[ch]"], e["gb5[ch]"] = rel_l2(r["gw"][4][ch5], dw), rel_l2(r["gb"][4][ch5], db)
+    del d5, c4
+    # conv2 (5x5, pad 2) and conv3 weight gradients: the batch-wide reduction at bs128
+    d2 = nchw(r["taps"]["dconv2"])
+    p1 = nchw(r["taps"]["pool1"])
+    ch2 = np.array([0, 131, 255])
+    dw, db = orc.conv2d_bwd_weight(d2[:, ch2], p1, (3, 96, 5, 5), 1, 2)
+    e["gw2[ch]"], e["gb2[ch]"] = rel_l2(r["gw"][1][ch2], dw), rel_l2(r["gb"][1][ch2], db)
+    del d2, p1
+    d3 = nchw(r["taps"]["dconv3"])
+    p2 = nchw(r["taps"]["pool2"])
+    ch3 = np.array([5, 200, 383])
+    dw, db = orc.conv2d_bwd_weight(d3[:, ch3], p2, (3, 256, 3, 3), 1, 1)
+    e["gw3[ch]"], e["gb3[ch]"] = rel_l2(r["gw"][2][ch3], dw), rel_l2(r["gb"][2][ch3], db)
+    del d3, p2
     hs2 = hostify({k: r["taps"][k] for k in ("dconv2", "pool1", "din2", "conv2", "dlrn2")}, rows)
     e["din2[rows]"] = rel_l2(hs2["din2"], orc.conv2d_bwd_data(hs2["dconv2"], W[1], hs2["pool1"].shape, 1, 2))
     e["dconv2[rows]"] = rel_l2(hs2["dconv2"], orc.lrn_bwd(hs2["conv2"], hs2["dlrn2"]) * (hs2["conv2"] > 0))
