@@ -22,6 +22,9 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+#include <utility>
+
 namespace ax {
 
 constexpr int BK = GEMM_BK;
@@ -119,6 +122,23 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until at most min(ahead, MAXA) slices of OPS loads each are in flight.
+template <int OPS, int MAXA>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) wait_vmcnt<MAXA * OPS>();
+    else wait_ahead<OPS, MAXA - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Calls f(integral_constant<int, I>) for I in the sequence, in order.
+template <int... I, class F>
+__device__ __forceinline__ void unroll_steps(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(), which would
@@ -773,8 +793,11 @@ struct Mma<float, FM, FN, LA, LB> {
 };
 
 // ------------------------------------------------------------------ kernel
-template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP>
-__global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
+template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP, int ST = 2>
+// bf16 kernels are held to two waves per SIMD (two workgroups per CU), which
+// the tile sizes and the grid sizing assume.
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   static_assert(WGM * WGN == 4, "four waves");
   using LA = typename AL::Layout;
   using LB = typename BL::Layout;
@@ -782,13 +805,14 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int A_EL = LA::template tile_elems<BM>(), B_EL = LB::template tile_elems<BN>();
-  constexpr int MAIN_BYTES = 2 * (A_EL + B_EL) * (int)sizeof(T);
+  static_assert(ST >= 2 && (ST == 2 || AL::DMA), "LDS stages: 2, or more with direct-to-LDS operands");
+  constexpr int MAIN_BYTES = ST * (A_EL + B_EL) * (int)sizeof(T);
   constexpr int CST = BN + 4;
-  constexpr int EPI_BYTES = BM * CST * 4;
+  constexpr int EPI_BYTES = WTM * CST * 4;   // one wave row of the tile at a time
   constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   T* As = reinterpret_cast<T*>(smem);
-  T* Bs = As + 2 * A_EL;
+  T* Bs = As + ST * A_EL;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave offsets scalar
@@ -821,36 +845,47 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
 
   static_assert(AL::DMA == BL::DMA, "both operands direct-to-LDS or neither");
   if constexpr (AL::DMA) {
-    // Slice kt lands in buffer kt & 1.  The barrier at the top of an
-    // iteration publishes the slice every wave waited for and guarantees that
-    // all waves are done with the other buffer, which the next slice then
-    // overwrites while the matrix cores work.
-    // Unrolled by two so the buffer offsets are compile-time constants.
+    // ST LDS buffers; slice kt lands in buffer (kt - kt0) % ST and up to
+    // ST - 1 slices are in flight.  At the top of an iteration a wave waits
+    // until its own loads of slice kt have landed (loads complete in order,
+    // so it may leave the later slices outstanding); the barrier then
+    // publishes the slice from every wave and guarantees that all waves are
+    // done with the buffer read one iteration earlier, which the slice
+    // ST - 1 ahead then overwrites while the matrix cores work.  Fragments of
+    // the current slice are read into registers before those loads are
+    // issued, so no LDS read has to wait for them.  The loop is unrolled by ST
+    // so that buffer offsets are compile-time constants.
     if (kt0 < kt1) {
-      al.issue(As);
-      bl.issue(Bs);
-      // Fragments of the current slice are read into registers before the
-      // next slice's loads are issued, so no LDS read has to wait for them.
+      constexpr int OPS = AL::NI + BL::NI;   // loads per wave per slice
+      static_assert((ST - 2) * OPS < 64, "vmcnt range");
+#pragma unroll
+      for (int p = 0; p < ST - 1; ++p)
+        if (kt0 + p < kt1) { al.issue(As + p * A_EL); bl.issue(Bs + p * B_EL); }
       using MM = Mma<T, FM, FN, LA, LB>;
       auto step = [&](auto cur_c, int kt) {
         constexpr int CUR = decltype(cur_c)::value;
-        wait_vmcnt<0>();
+        const int ahead = kt1 - 1 - kt;   // slices issued after this one: min(ahead, ST - 2)
+        wait_ahead<OPS, ST - 2>(ahead);
         lds_barrier();
         typename MM::Frags f;
         MM::read(As + CUR * A_EL, wm * WTM, Bs + CUR * B_EL, wn * WTN, f, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < kt1) { al.issue(As + (CUR ^ 1) * A_EL); bl.issue(Bs + (CUR ^ 1) * B_EL); }
+        if (kt + ST - 1 < kt1) {
+          constexpr int NXT = (CUR + ST - 1) % ST;
+          al.issue(As + NXT * A_EL);
+          bl.issue(Bs + NXT * B_EL);
+        }
         __builtin_amdgcn_sched_barrier(0);
         MM::mul(f, acc);
         // keep the next slice's wait and barrier behind these products
         __builtin_amdgcn_sched_barrier(0);
       };
       int kt = kt0;
-      for (; kt + 1 < kt1; kt += 2) {
-        step(std::integral_constant<int, 0>{}, kt);
-        step(std::integral_constant<int, 1>{}, kt + 1);
-      }
-      if (kt < kt1) step(std::integral_constant<int, 0>{}, kt);
+      for (; kt + ST - 1 < kt1; kt += ST)
+        unroll_steps(std::make_integer_sequence<int, ST>{}, [&](auto i) { step(i, kt + decltype(i)::value); });
+      unroll_steps(std::make_integer_sequence<int, ST - 1>{}, [&](auto i) {
+        if (kt + decltype(i)::value < kt1) step(i, kt + decltype(i)::value);
+      });
     }
     lds_barrier();   // all fragment reads done before the epilogue reuses LDS
   } else if (kt0 < kt1) {
@@ -869,27 +904,33 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm(AL al, BL bl, EP ep, GemmGrid
     }
   }
 
-  // accumulators -> LDS tile [BM][BN] fp32
+  // Epilogue, one wave row (WTM rows of the tile) at a time: the waves of
+  // that row stage their accumulators in LDS as fp32, then all threads hand
+  // 8-column runs to the epilogue functor.
   float* Cs = reinterpret_cast<float*>(smem);
-  {
-    const int cr = (lane >> 4) * 4, cc = lane & 15;
+  constexpr int CPRO = BN / 8, NOUT = WTM * CPRO;
+#pragma unroll 1
+  for (int pr = 0; pr < WGM; ++pr) {
+    if (pr > 0) __syncthreads();
+    if (wm == pr) {
+      const int cr = (lane >> 4) * 4, cc = lane & 15;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          Cs[(wm * WTM + i * 16 + cr + q) * CST + wn * WTN + j * 16 + cc] = acc[i][j][q];
-  }
-  __syncthreads();
-  constexpr int CPRO = BN / 8, NOUT = BM * CPRO;
-  for (int c = tid; c < NOUT; c += NTHREADS) {
-    const int r = c / CPRO, cn = (c - r * CPRO) * 8;
-    float v[8];
-    const float* src = Cs + r * CST + cn;
+          for (int q = 0; q < 4; ++q)
+            Cs[(i * 16 + cr + q) * CST + wn * WTN + j * 16 + cc] = acc[i][j][q];
+    }
+    __syncthreads();
+    for (int c = tid; c < NOUT; c += NTHREADS) {
+      const int r = c / CPRO, cn = (c - r * CPRO) * 8;
+      float v[8];
+      const float* src = Cs + r * CST + cn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = src[i];
-    ep(m0 + r, n0 + cn, g, s, v);
+      for (int i = 0; i < 8; ++i) v[i] = src[i];
+      ep(m0 + pr * WTM + r, n0 + cn, g, s, v);
+    }
   }
 }
 

@@ -32,7 +32,7 @@ static inline void rec_stop(const KTimer* kt, hipStream_t st) { if (kt) hipEvent
 // =========================================================================
 // GEMM launches
 // =========================================================================
-template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP>
+template <typename T, int BM, int BN, int WGM, int WGN, int ST = 2, class AL, class BL, class EP>
 static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
                            int splits, hipStream_t st, const KTimer* kt = nullptr) {
   GemmGrid gg;
@@ -45,7 +45,7 @@ static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int 
   gg.groups = groups;
   dim3 grid(gg.tiles_m * gg.tiles_n * groups * gg.splits);
   rec_start(kt, st);
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP>), grid, dim3(NTHREADS), 0, st, al, bl,
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP, ST>), grid, dim3(NTHREADS), 0, st, al, bl,
                      ep, gg);
   rec_stop(kt, st);
   return hipGetLastError();
@@ -132,16 +132,24 @@ hipError_t conv1_w_s2d(DType dt, const void* w, void* out, hipStream_t st) {
 static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
 
 template <typename T>
+struct Conv1FwdFn {
+  const void* xs; int Nimg; const void* ws2d; const void* b1; void* y; hipStream_t st; const KTimer* kt;
+  template <int BM, int BN, int WGM, int WGN>
+  hipError_t operator()() const {
+    Im2colLd<T, BM> a;
+    a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
+    RowsLd<T, BN> b;
+    b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
+    EpBiasRelu<T> e;
+    e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
+    return run_gemm<T, BM, BN, WGM, WGN>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
+  }
+};
+
+template <typename T>
 static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
                               hipStream_t st, const KTimer* kt) {
-  constexpr int BM = 128, BN = 96;
-  Im2colLd<T, BM> a;
-  a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
-  RowsLd<T, BN> b;
-  b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
-  EpBiasRelu<T> e;
-  e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
-  return run_gemm<T, BM, BN, 2, 2>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
+  return by_tile<T>(Nimg * 3025, 96, 1, Conv1FwdFn<T>{xs, Nimg, ws2d, b1, y, st, kt});
 }
 
 hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
@@ -150,22 +158,53 @@ hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const
                     : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, st, kt);
 }
 
-// Picks the n-tile for an output width N: 128 when it divides, else 96, else
-// 48 (four waves stacked along m), else 128 with a ragged last tile.
+// Tile for an implicit-GEMM convolution with M output rows, N columns per
+// group.  n-tile: 128 when it divides N, else 96, else 48 (four waves stacked
+// along m), else 128 with a ragged last tile.  m-tile (bf16): the one of 96,
+// 128, 192 whose tiles finish in the fewest rounds of the 512 workgroups the
+// chip holds at once (two per CU), weighted slightly towards taller tiles,
+// which reuse each B slice over more rows.
+constexpr int RESIDENT_WG = 512;
+static int pick_bm(int M, int N, int BN, int groups) {
+  const int cand[3] = {96, 128, 192};
+  const float weight[3] = {1.10f, 1.0f, 0.95f};
+  int best = 128;
+  float best_cost = 3.0e38f;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t tiles = (int64_t)cdiv(M, cand[i]) * cdiv(N, BN) * groups;
+    const float cost = (float)((tiles + RESIDENT_WG - 1) / RESIDENT_WG) * cand[i] * weight[i];
+    if (cost < best_cost) { best_cost = cost; best = cand[i]; }
+  }
+  return best;
+}
+
+template <int BN, class Fn>
+static hipError_t by_bm(int bm, Fn&& fn) {
+  switch (bm) {
+    case 96: return fn.template operator()<96, BN, 2, 2>();
+    case 192: return fn.template operator()<192, BN, 2, 2>();
+    default: return fn.template operator()<128, BN, 2, 2>();
+  }
+}
+
 template <typename T, class Fn>
-static hipError_t by_bn(int N, Fn&& fn) {
-  if (N % 128 == 0) return fn.template operator()<128, 2, 2>();
-  if (N % 96 == 0) return fn.template operator()<96, 2, 2>();
-  if (N % 48 == 0 && N <= 96) return fn.template operator()<48, 4, 1>();
-  return fn.template operator()<128, 2, 2>();
+static hipError_t by_tile(int M, int N, int groups, Fn&& fn) {
+  const bool bn128 = N % 128 == 0 || (N % 96 != 0 && !(N % 48 == 0 && N <= 96));
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (bn128) return by_bm<128>(pick_bm(M, N, 128, groups), fn);
+    if (N % 96 == 0) return by_bm<96>(pick_bm(M, N, 96, groups), fn);
+  } else {
+    if (bn128) return fn.template operator()<128, 128, 2, 2>();
+    if (N % 96 == 0) return fn.template operator()<128, 96, 2, 2>();
+  }
+  return fn.template operator()<128, 48, 4, 1>();
 }
 
 template <typename T>
 struct ConvFwdFn {
   ConvShape s; const void* x; const void* wr; const void* b; void* y; hipStream_t st; const KTimer* kt;
-  template <int BN, int WGM, int WGN>
+  template <int BM, int BN, int WGM, int WGN>
   hipError_t operator()() const {
-    constexpr int BM = 128;
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
     Im2colLd<T, BM> a;
     a.p = (const T*)x;
@@ -183,17 +222,17 @@ struct ConvFwdFn {
 hipError_t conv_fwd(DType dt, const ConvShape& s, const void* x, const void* wr, const void* b, void* y,
                     hipStream_t st, const KTimer* kt) {
   const int Cog = s.Cout / s.groups;
-  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st, kt}; return by_bn<bf16>(Cog, f); }
+  const int M = s.Nimg * s.Ho * s.Wo;
+  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st, kt}; return by_tile<bf16>(M, Cog, s.groups, f); }
   ConvFwdFn<float> f{s, x, wr, b, y, st, kt};
-  return by_bn<float>(Cog, f);
+  return by_tile<float>(M, Cog, s.groups, f);
 }
 
 template <typename T>
 struct ConvDgradFn {
   ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; hipStream_t st; const KTimer* kt;
-  template <int BN, int WGM, int WGN>
+  template <int BM, int BN, int WGM, int WGN>
   hipError_t operator()() const {
-    constexpr int BM = 128;
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
     // dX = stride-1 convolution of dY with flipped, transposed weights, pad K-1-p
     Im2colLd<T, BM> a;
@@ -213,9 +252,10 @@ hipError_t conv_dgrad(DType dt, const ConvShape& s, const void* dy, const void* 
                       void* dx, hipStream_t st, const KTimer* kt) {
   if (s.stride != 1) return hipErrorInvalidValue;
   const int Cig = s.Cin / s.groups;
-  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st, kt}; return by_bn<bf16>(Cig, f); }
+  const int M = s.Nimg * s.H * s.W;
+  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st, kt}; return by_tile<bf16>(M, Cig, s.groups, f); }
   ConvDgradFn<float> f{s, dy, wt, mask, dx, st, kt};
-  return by_bn<float>(Cig, f);
+  return by_tile<float>(M, Cig, s.groups, f);
 }
 
 // ---- weight gradients: split-K partials, then an ordered reduction
@@ -364,6 +404,9 @@ hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float
 }
 
 // ---- fully-connected layers
+// FC layers at small batch stream their weights from HBM; split-K spreads
+// that over the CUs.  (More LDS stages per workgroup measured no faster.)
+template <typename T> static constexpr int fc_stages() { return 2; }
 static int fc_splits(int M, int N, int K) {
   const int tiles = cdiv(M, 128) * cdiv(N, 128);
   int want = cdiv(256, tiles);
@@ -437,7 +480,7 @@ static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, co
   bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, O, K, 1, S, st, kt);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2, fc_stages<T>()>(a, bl, e, M, O, K, 1, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O,
                      (const T*)b, ep, (const T*)nullptr, (T*)y, y_f32);
@@ -463,7 +506,7 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
   bl.p = (const T*)w; bl.ld = K; bl.rows = K; bl.K = O; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = K; e.M = M; e.N = K; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2>(a, bl, e, M, K, O, 1, S, st, kt);
+  hipError_t err = run_gemm<T, BM, BN, 2, 2, fc_stages<T>()>(a, bl, e, M, K, O, 1, S, st, kt);
   if (err != hipSuccess) return err;
   FcEpi none{};
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K,
