@@ -30,6 +30,10 @@ CONV = {  # name: (Cin, Cout, k, Ho, grouped)
     "CONV4": (384, 384, 3, 13, True), "CONV5": (384, 256, 3, 13, True),
 }
 N_PARAMS_SINGLE = 62_378_344
+FC = {"FC6": (9216, 4096), "FC7": (4096, 4096), "FC8": (4096, 1000)}
+# tensors the stand-alone SGD kernel updates: conv weights and all 16 biases
+# (the FC weights are updated inside their weight-gradient GEMM)
+SGD_ELEMS = N_PARAMS_SINGLE - sum(fin * fout for fin, fout in FC.values())
 
 
 def conv_flops(name, n, groups):
@@ -47,13 +51,14 @@ def kernel_work(kt, n, groups):
     if layer.startswith("CONV") and op in ("FWD", "WGRAD", "DGRAD"):
         return "mfma", conv_flops(layer, n, groups)
     if kt.startswith("FC"):
-        fin, fout = {"FC6": (9216, 4096), "FC7": (4096, 4096), "FC8": (4096, 1000)}[layer]
+        fin, fout = FC[layer]
         # weight streaming bound at this batch: weights + activations once
         if op == "FWD":
             return "hbm", e * (fin * fout + n * fin + n * fout)
         if op == "DGRAD":
             return "hbm", e * (fin * fout + n * fout + n * fin)
-        return "hbm", e * (n * fout + n * fin) + 4 * fin * fout          # WGRAD: fp32 dW
+        # WGRAD with the SGD update fused: activations in; fp32 w, v in and out; bf16 w out
+        return "hbm", e * (n * fout + n * fin) + 18 * fin * fout
     act = {"55x96": n * 55 * 55 * 96, "27x96": n * 27 * 27 * 96, "27x256": n * 27 * 27 * 256,
            "13x256": n * 13 * 13 * 256, "6x256": n * 6 * 6 * 256}
     table = {
@@ -66,7 +71,7 @@ def kernel_work(kt, n, groups):
         "POOL1_BWD": (e + 1) * act["27x96"] + e * act["55x96"],
         "POOL2_BWD": (e + 1) * act["13x256"] + e * act["27x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
-        "SGD": 22 * N_PARAMS_SINGLE,
+        "SGD": 22 * SGD_ELEMS,
     }
     return "hbm", float(table[kt])
 

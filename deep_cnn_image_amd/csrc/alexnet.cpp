@@ -136,7 +136,12 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   return ALEXNET_OK;
 }
 
-int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st, const Timers& T) {
+// Backward pass.  The FC weight gradients are applied to (master, momentum,
+// work) of that layer inside their GEMM, after the layer's data gradient has
+// read the old working weights; every other gradient lands in the workspace
+// for the multi-tensor update that follows.
+int enqueue_backward(const Plan& p, void* const* work, float* const* master, float* const* momentum,
+                     const SgdHyper& hy, void* ws, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -153,20 +158,20 @@ int enqueue_backward(const Plan& p, void* const* work, void* ws, hipStream_t st,
   // FC8: dh7 = dz W8 * [drop7 > 0]   (drop7 > 0 <=> kept and ReLU active)
   HIPCHK(fc_dgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), work[14], tp(ws, p, T_DROP7), tp(ws, p, T_DFC7),
                   part, p.part_bytes, st, T(ALEXNET_KT_FC8_DGRAD)));
-  HIPCHK(fc_wgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), gw(7), st,
-                  T(ALEXNET_KT_FC8_WGRAD)));
+  HIPCHK(fc_wgrad_sgd(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), hy, master[14],
+                      momentum[14], work[14], st, T(ALEXNET_KT_FC8_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DLOGITS), N, 1000, gb(7), cs, st));
   // FC7
   HIPCHK(fc_dgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), work[12], tp(ws, p, T_DROP6), tp(ws, p, T_DFC6),
                   part, p.part_bytes, st, T(ALEXNET_KT_FC7_DGRAD)));
-  HIPCHK(fc_wgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), gw(6), st,
-                  T(ALEXNET_KT_FC7_WGRAD)));
+  HIPCHK(fc_wgrad_sgd(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), hy, master[12],
+                      momentum[12], work[12], st, T(ALEXNET_KT_FC7_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DFC7), N, 4096, gb(6), cs, st));
   // FC6 -> gradient w.r.t. the flattened pool5 output
   HIPCHK(fc_dgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), work[10], nullptr, tp(ws, p, T_DFLAT), part,
                   p.part_bytes, st, T(ALEXNET_KT_FC6_DGRAD)));
-  HIPCHK(fc_wgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), gw(5), st,
-                  T(ALEXNET_KT_FC6_WGRAD)));
+  HIPCHK(fc_wgrad_sgd(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), hy, master[10],
+                      momentum[10], work[10], st, T(ALEXNET_KT_FC6_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DFC6), N, 4096, gb(5), cs, st));
   // pool5 backward * ReLU5'
   HIPCHK(pool_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
@@ -306,18 +311,21 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
                  (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
     return ALEXNET_E_HIP;
   if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
-  if ((r = enqueue_backward(p, work, ws, st, T)) != ALEXNET_OK) return r;
+  const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
+  if ((r = enqueue_backward(p, work, master, momentum, hy, ws, st, T)) != ALEXNET_OK) return r;
+  // the remaining tensors: conv weights and all biases (FC weights are done)
   TensorSet ts;
   for (int i = 0; i < 8; ++i) {
+    const bool fused = i >= 5;
     ts.master[2 * i] = master[2 * i];
     ts.master[2 * i + 1] = master[2 * i + 1];
     ts.mom[2 * i] = momentum[2 * i];
     ts.mom[2 * i + 1] = momentum[2 * i + 1];
-    ts.grad[2 * i] = (const float*)tp(ws, p, T_GW1 + i);
+    ts.grad[2 * i] = fused ? nullptr : (const float*)tp(ws, p, T_GW1 + i);
     ts.grad[2 * i + 1] = (const float*)tp(ws, p, T_GB1 + i);
     ts.work[2 * i] = work[2 * i];
     ts.work[2 * i + 1] = work[2 * i + 1];
-    ts.n[2 * i] = p.net.wcount[i];
+    ts.n[2 * i] = fused ? 0 : p.net.wcount[i];
     ts.n[2 * i + 1] = p.net.bcount[i];
   }
   if (sgd(dt, ts, lr, momentum_coef, weight_decay, st, T(ALEXNET_KT_SGD)) != hipSuccess) return ALEXNET_E_HIP;

@@ -20,6 +20,15 @@ __device__ __forceinline__ bf16 f2bf(float f) {
   return (bf16)(u >> 16);
 }
 
+// One SGD-with-momentum step on an element (paper form, lr inside v):
+//   v <- mom * v - wd * lr * w - lr * g,   w <- w + v
+// written with explicit fmas so that every kernel that applies it (the
+// multi-tensor update and the fused weight-gradient epilogue) rounds alike.
+__device__ __forceinline__ void sgd_elem(float& w, float& v, float g, float mom, float wdlr, float lr) {
+  v = fmaf(mom, v, -fmaf(lr, g, wdlr * w));
+  w = w + v;
+}
+
 template <typename T> struct Num;
 template <> struct Num<float> {
   static __device__ __forceinline__ float load(float v) { return v; }

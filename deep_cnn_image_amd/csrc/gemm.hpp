@@ -726,6 +726,16 @@ struct EpF32 {
   }
 };
 
+// Epilogue functors may declare `static constexpr bool prefetches = true`,
+// a `State`, `State prefetch(m, n)` and `apply(m, n, v, state)`.
+template <class EP, class = void>
+struct EpPrefetch { static constexpr bool value = false; struct State {}; };
+template <class EP>
+struct EpPrefetch<EP, std::void_t<typename EP::State>> {
+  static constexpr bool value = EP::prefetches;
+  using State = typename EP::State;
+};
+
 // ------------------------------------------------------------------ MFMA steps
 template <typename T, int FM, int FN, class LA, class LB> struct Mma;
 
@@ -909,8 +919,21 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   // 8-column runs to the epilogue functor.
   float* Cs = reinterpret_cast<float*>(smem);
   constexpr int CPRO = BN / 8, NOUT = WTM * CPRO;
+  // Functors that read memory per output chunk (EpPrefetch) issue those
+  // reads for all of this thread's chunks before the staging, so they are in
+  // flight while the accumulators go through LDS.
+  constexpr bool PRE = EpPrefetch<EP>::value && NOUT % NTHREADS == 0;
+  constexpr int CH = PRE ? NOUT / NTHREADS : 1;
 #pragma unroll 1
   for (int pr = 0; pr < WGM; ++pr) {
+    typename EpPrefetch<EP>::State pre[CH];
+    if constexpr (PRE) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + i * NTHREADS, r = c / CPRO, cn = (c - r * CPRO) * 8;
+        pre[i] = ep.prefetch(m0 + pr * WTM + r, n0 + cn);
+      }
+    }
     if (pr > 0) __syncthreads();
     if (wm == pr) {
       const int cr = (lane >> 4) * 4, cc = lane & 15;
@@ -923,13 +946,25 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
             Cs[(i * 16 + cr + q) * CST + wn * WTN + j * 16 + cc] = acc[i][j][q];
     }
     __syncthreads();
-    for (int c = tid; c < NOUT; c += NTHREADS) {
-      const int r = c / CPRO, cn = (c - r * CPRO) * 8;
-      float v[8];
-      const float* src = Cs + r * CST + cn;
+    if constexpr (PRE) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = src[i];
-      ep(m0 + pr * WTM + r, n0 + cn, g, s, v);
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + i * NTHREADS, r = c / CPRO, cn = (c - r * CPRO) * 8;
+        float v[8];
+        const float* src = Cs + r * CST + cn;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = src[q];
+        ep.apply(m0 + pr * WTM + r, n0 + cn, v, pre[i]);
+      }
+    } else {
+      for (int c = tid; c < NOUT; c += NTHREADS) {
+        const int r = c / CPRO, cn = (c - r * CPRO) * 8;
+        float v[8];
+        const float* src = Cs + r * CST + cn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+        ep(m0 + pr * WTM + r, n0 + cn, g, s, v);
+      }
     }
   }
 }

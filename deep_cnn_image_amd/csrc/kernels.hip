@@ -520,23 +520,63 @@ hipError_t fc_dgrad(DType dt, int M, int K, int O, const void* dy, const void* w
                     : fc_dgrad_t<float>(M, K, O, dy, w, mask, dx, part, part_bytes, st, kt);
 }
 
+// Epilogue of the FC weight-gradient GEMM: the fp32 gradient of 8 weights
+// w[m][n .. n+7] goes straight into the SGD update of master w, momentum v
+// and working copy wb (same element update as the multi-tensor kernel).
+// w and v are fetched ahead (prefetch) while the accumulators are staged.
 template <typename T>
-static hipError_t fc_wgrad_t(int M, int K, int O, const void* dy, const void* x, float* gw,
-                             hipStream_t st, const KTimer* kt) {
+struct EpSgd {
+  static constexpr bool prefetches = true;
+  struct State { float4 w0, w1, v0, v1; };
+  float* w; float* v; T* wb; int ldo, M, N; SgdHyper h;
+  __device__ __forceinline__ State prefetch(int m, int n) const {
+    State st{};
+    if (m < M && n < N) {
+      const int64_t o = (int64_t)m * ldo + n;
+      st.w0 = *reinterpret_cast<const float4*>(w + o);
+      st.w1 = *reinterpret_cast<const float4*>(w + o + 4);
+      st.v0 = *reinterpret_cast<const float4*>(v + o);
+      st.v1 = *reinterpret_cast<const float4*>(v + o + 4);
+    }
+    return st;
+  }
+  __device__ __forceinline__ void apply(int m, int n, const float* g, const State& st) const {
+    if (m >= M || n >= N) return;
+    const int64_t o = (int64_t)m * ldo + n;
+    float wv[8] = {st.w0.x, st.w0.y, st.w0.z, st.w0.w, st.w1.x, st.w1.y, st.w1.z, st.w1.w};
+    float vv[8] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w, st.v1.x, st.v1.y, st.v1.z, st.v1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sgd_elem(wv[i], vv[i], g[i], h.mom, h.wdlr, h.lr);
+    *reinterpret_cast<float4*>(w + o) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+    *reinterpret_cast<float4*>(w + o + 4) = make_float4(wv[4], wv[5], wv[6], wv[7]);
+    *reinterpret_cast<float4*>(v + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+    *reinterpret_cast<float4*>(v + o + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
+    Pack8<T>::store(wb + o, wv);
+  }
+  // per-chunk form (used when a tile's chunk count does not split evenly)
+  __device__ __forceinline__ void operator()(int m, int n, int, int, const float* g) const {
+    apply(m, n, g, prefetch(m, n));
+  }
+};
+
+template <typename T>
+static hipError_t fc_wgrad_sgd_t(int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,
+                                 float* w, float* v, void* wb, hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
+  if (K % 8) return hipErrorInvalidValue;
   ColsLd<T, BM> a;
   a.p = (const T*)dy; a.ld = O; a.rows = O; a.K = M; a.gstride = 0;
   ColsLd<T, BN> bl;
   bl.p = (const T*)x; bl.ld = K; bl.rows = K; bl.K = M; bl.gstride = 0;
-  EpF32 e;
-  e.out = gw; e.ldo = K; e.M = O; e.N = K; e.splits = 1;
+  EpSgd<T> e;
+  e.w = w; e.v = v; e.wb = (T*)wb; e.ldo = K; e.M = O; e.N = K; e.h = h;
   return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st, kt);
 }
 
-hipError_t fc_wgrad(DType dt, int M, int K, int O, const void* dy, const void* x, float* gw,
-                    hipStream_t st, const KTimer* kt) {
-  return dt == BF16 ? fc_wgrad_t<bf16>(M, K, O, dy, x, gw, st, kt)
-                    : fc_wgrad_t<float>(M, K, O, dy, x, gw, st, kt);
+hipError_t fc_wgrad_sgd(DType dt, int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,
+                        float* w, float* v, void* wb, hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? fc_wgrad_sgd_t<bf16>(M, K, O, dy, x, h, w, v, wb, st, kt)
+                    : fc_wgrad_sgd_t<float>(M, K, O, dy, x, h, w, v, wb, st, kt);
 }
 
 // =========================================================================
@@ -1039,11 +1079,10 @@ __global__ void k_multi(MultiArgs a) {
   if (SGD) {
     float4 v = *reinterpret_cast<const float4*>(a.v[ti] + e);
     const float4 g = *reinterpret_cast<const float4*>(a.g[ti] + e);
-    v.x = a.mom * v.x - a.wdlr * w.x - a.lr * g.x;
-    v.y = a.mom * v.y - a.wdlr * w.y - a.lr * g.y;
-    v.z = a.mom * v.z - a.wdlr * w.z - a.lr * g.z;
-    v.w = a.mom * v.w - a.wdlr * w.w - a.lr * g.w;
-    w.x += v.x; w.y += v.y; w.z += v.z; w.w += v.w;
+    sgd_elem(w.x, v.x, g.x, a.mom, a.wdlr, a.lr);
+    sgd_elem(w.y, v.y, g.y, a.mom, a.wdlr, a.lr);
+    sgd_elem(w.z, v.z, g.z, a.mom, a.wdlr, a.lr);
+    sgd_elem(w.w, v.w, g.w, a.mom, a.wdlr, a.lr);
     *reinterpret_cast<float4*>(a.v[ti] + e) = v;
     *reinterpret_cast<float4*>(a.w[ti] + e) = w;
   }

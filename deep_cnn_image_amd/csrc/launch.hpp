@@ -88,9 +88,12 @@ hipError_t fc_dgrad(DType, int M, int K, int O, const void* dy, const void* w, c
                     void* dx, float* part, size_t part_bytes, hipStream_t,
                       const KTimer* kt = nullptr);
 // dW[O][K] fp32 = dy^T x
-hipError_t fc_wgrad(DType, int M, int K, int O, const void* dy, const void* x, float* gw,
-                    hipStream_t,
-                      const KTimer* kt = nullptr);
+// SGD hyper-parameters as the update uses them (wdlr = weight decay * lr).
+struct SgdHyper { float lr, mom, wdlr; };
+// FC weight gradient dW = dY^T X, applied at once to the layer's fp32 master
+// weights w, momentum v and working copy wb (sgd_elem); dW is not stored.
+hipError_t fc_wgrad_sgd(DType, int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,
+                        float* w, float* v, void* wb, hipStream_t, const KTimer* kt = nullptr);
 size_t fc_fwd_part_bytes(int M, int K, int O);
 size_t fc_dgrad_part_bytes(int M, int K, int O);
 

@@ -141,16 +141,15 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
     nhwc(T_DLRN1, 55, 96, dt);
     nhwc(T_DCONV1, 55, 96, dt);
     for (int i = 0; i < 8; ++i) {
-      TapDesc& w = p->tap[T_GW1 + i];
-      w.buf = a.take((size_t)net.wcount[i] * 4);
+      // FC weight gradients are applied inside their GEMM (never stored):
+      // no gw6..gw8 taps.
       if (i < 5) {
+        TapDesc& w = p->tap[T_GW1 + i];
+        w.buf = a.take((size_t)net.wcount[i] * 4);
         const ConvShape& c = net.conv[i];
         w.shape[0] = c.Cout; w.shape[1] = c.Cin / c.groups; w.shape[2] = c.K; w.shape[3] = c.K;
-      } else {
-        const int fin[3] = {9216, 4096, 4096}, fout[3] = {4096, 4096, 1000};
-        w.shape[0] = fout[i - 5]; w.shape[1] = fin[i - 5]; w.shape[2] = 1; w.shape[3] = 1;
+        w.dtype = ALEXNET_F32; w.layout = 2; w.present = true;
       }
-      w.dtype = ALEXNET_F32; w.layout = 2; w.present = true;
       TapDesc& b = p->tap[T_GB1 + i];
       b.buf = a.take((size_t)net.bcount[i] * 4);
       b.shape[0] = net.bcount[i]; b.shape[1] = 1; b.shape[2] = 1; b.shape[3] = 1;

@@ -120,7 +120,12 @@ int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16]
  *                undefined loss and gradient but never an out-of-bounds access
  *   loss         one fp32 (device), the batch-mean cross-entropy
  *   probs        optional [batch][1000] fp32 softmax output (may be null)
- * The gradients stay in the workspace (taps) until the next call. */
+ * The three FC weight tensors are updated inside the GEMM that forms their
+ * gradient, after that layer's data gradient has read the old working
+ * weights, so every tensor still sees the gradient of the pre-step weights;
+ * those gradients are never stored.  The conv weight gradients and all bias
+ * gradients stay in the workspace (taps gw1..gw5, gb1..gb8) until the next
+ * call; gw6..gw8 do not exist (alexnet_tap returns ALEXNET_E_ARG). */
 int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
                        void* const work[16], const void* x, const int32_t* labels, float lr,
                        float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,

@@ -140,9 +140,13 @@ def test_tap_shapes_follow_the_layer_list():
     assert get("conv3") == (2, 13, 13, 384) and get("conv5") == (2, 13, 13, 256)
     assert get("pool5") == (2, 9216, 1, 1) and get("logits") == (2, 1000, 1, 1)
     assert get("gw2") == (256, 48, 5, 5) and get("gw4") == (384, 192, 3, 3)
-    assert get("gw3") == (384, 256, 3, 3) and get("gw6") == (4096, 9216, 1, 1)
+    assert get("gw3") == (384, 256, 3, 3) and get("gb6") == (4096, 1, 1, 1)
     with pytest.raises(B.AlexNetError):
         B.alexnet_tap(c, B.MODE_FORWARD, ids["gw1"])
+    # FC weight gradients are applied inside their GEMM: never stored
+    for name in ("gw6", "gw7", "gw8"):
+        with pytest.raises(B.AlexNetError):
+            B.alexnet_tap(c, B.MODE_TRAIN, ids[name])
 
 
 def test_kernel_ids_match_header():

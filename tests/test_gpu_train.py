@@ -52,9 +52,17 @@ def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None):
     torch.cuda.synchronize()
     r.update(sess=sess, loss=float(loss.item()), probs=host(probs), master=[host(m) for m in master],
              mom=[host(v) for v in mom], work=[w.clone() for w in work],
-             gw=[host(sess.tap(f"gw{i + 1}")) for i in range(8)],
+             gw=[host(sess.tap(f"gw{i + 1}")) for i in range(5)],
              gb=[host(sess.tap(f"gb{i + 1}")).ravel() for i in range(8)],
              taps={k: sess.tap(k).clone() for k in TAPS})
+    # The FC weight gradients are applied inside their GEMM and never stored;
+    # recover them from the momentum update v1 = mu v0 - wd lr w0 - lr g
+    # (fp32 coefficients as the library forms them).
+    lr32, mu32 = np.float32(HYPER["lr"]), np.float32(HYPER["momentum_coef"])
+    wdlr32 = np.float32(np.float32(HYPER["weight_decay"]) * lr32)
+    for i in range(5, 8):
+        w0, v0, v1 = (np.asarray(a[2 * i], np.float64) for a in (r["master0"], r["mom0"], r["mom"]))
+        r["gw"].append((float(mu32) * v0 - float(wdlr32) * w0 - v1) / float(lr32))
     return r
 
 
