@@ -63,10 +63,10 @@ def kernel_work(kt, n, groups):
            "13x256": n * 13 * 13 * 256, "6x256": n * 6 * 6 * 256}
     table = {
         "S2D": e * (n * 3 * 227 * 227 + n * 57 * 57 * 48),
-        "LRN1_FWD": 2 * e * act["55x96"], "LRN2_FWD": 2 * e * act["27x256"],
+        # LRN + max-pool fused: LRN input read once, pooled values and argmax written
+        "LRNPOOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
+        "LRNPOOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
         "LRN1_BWD": 3 * e * act["55x96"], "LRN2_BWD": 3 * e * act["27x256"],
-        "POOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
-        "POOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
         "POOL1_BWD": (e + 1) * act["27x96"] + e * act["55x96"],
         "POOL2_BWD": (e + 1) * act["13x256"] + e * act["27x256"],

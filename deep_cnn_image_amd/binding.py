@@ -28,8 +28,8 @@ EXPORTED = (
 
 # alexnet_kernel ids (kernel-timing hooks)
 KERNELS = (
-    "S2D", "CONV1_FWD", "CONV2_FWD", "CONV3_FWD", "CONV4_FWD", "CONV5_FWD", "LRN1_FWD", "LRN2_FWD",
-    "POOL1_FWD", "POOL2_FWD", "POOL5_FWD", "FC6_FWD", "FC7_FWD", "FC8_FWD", "FC8_DGRAD", "FC7_DGRAD",
+    "S2D", "CONV1_FWD", "CONV2_FWD", "CONV3_FWD", "CONV4_FWD", "CONV5_FWD", "LRNPOOL1_FWD",
+    "LRNPOOL2_FWD", "POOL5_FWD", "FC6_FWD", "FC7_FWD", "FC8_FWD", "FC8_DGRAD", "FC7_DGRAD",
     "FC6_DGRAD", "FC8_WGRAD", "FC7_WGRAD", "FC6_WGRAD", "POOL5_BWD", "CONV5_WGRAD", "CONV4_WGRAD",
     "CONV3_WGRAD", "CONV2_WGRAD", "CONV1_WGRAD", "CONV5_DGRAD", "CONV4_DGRAD", "CONV3_DGRAD",
     "CONV2_DGRAD", "POOL2_BWD", "LRN2_BWD", "POOL1_BWD", "LRN1_BWD", "SGD",
@@ -40,7 +40,7 @@ KT = {name: i + 1 for i, name in enumerate(KERNELS)}
 class Cfg(C.Structure):
     _fields_ = [("batch", C.c_int32), ("groups", C.c_int32), ("dtype", C.c_int32),
                 ("lrn_n", C.c_int32), ("lrn_k", C.c_float), ("lrn_alpha", C.c_float),
-                ("lrn_beta", C.c_float), ("dropout_p", C.c_float)]
+                ("lrn_beta", C.c_float), ("dropout_p", C.c_float), ("lrn_taps", C.c_int32)]
 
 
 class Timer(C.Structure):
@@ -125,9 +125,10 @@ def status_string(status: int) -> str:
     return lib().alexnet_status_string(status).decode()
 
 
-def alexnet_default_cfg(batch: int, groups: int = 1, dtype: int = BF16) -> Cfg:
+def alexnet_default_cfg(batch: int, groups: int = 1, dtype: int = BF16, lrn_taps: bool = False) -> Cfg:
     cfg = Cfg()
     lib().alexnet_default_cfg(C.byref(cfg), batch, groups, dtype)
+    cfg.lrn_taps = 1 if lrn_taps else 0
     return cfg
 
 

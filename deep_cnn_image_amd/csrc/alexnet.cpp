@@ -93,16 +93,14 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   HIPCHK(conv1_s2d(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
   HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st,
                    T(ALEXNET_KT_CONV1_FWD)));
-  HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_LRN1), (int64_t)N * 55 * 55, 96, c.lrn_k, c.lrn_alpha,
-                 c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN1_FWD)));
-  HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1), N, 55, 55, 96, 0,
-                  st, T(ALEXNET_KT_POOL1_FWD)));
+  HIPCHK(lrn_pool_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1),
+                      c.lrn_taps ? tp(ws, p, T_LRN1) : nullptr, N, 55, 55, 96, c.lrn_k, c.lrn_alpha, c.lrn_beta,
+                      c.lrn_n, st, T(ALEXNET_KT_LRNPOOL1_FWD)));
   HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), st,
                   T(ALEXNET_KT_CONV2_FWD)));
-  HIPCHK(lrn_fwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_LRN2), (int64_t)N * 27 * 27, 256, c.lrn_k,
-                 c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN2_FWD)));
-  HIPCHK(pool_fwd(dt, tp(ws, p, T_LRN2), tp(ws, p, T_POOL2), (uint8_t*)tp(ws, p, T_ARG2), N, 27, 27, 256, 0,
-                  st, T(ALEXNET_KT_POOL2_FWD)));
+  HIPCHK(lrn_pool_fwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_POOL2), (uint8_t*)tp(ws, p, T_ARG2),
+                      c.lrn_taps ? tp(ws, p, T_LRN2) : nullptr, N, 27, 27, 256, c.lrn_k, c.lrn_alpha, c.lrn_beta,
+                      c.lrn_n, st, T(ALEXNET_KT_LRNPOOL2_FWD)));
   HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), st,
                   T(ALEXNET_KT_CONV3_FWD)));
   HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), st,
@@ -239,6 +237,7 @@ void alexnet_default_cfg(alexnet_cfg* cfg, int32_t batch, int32_t groups, int32_
   cfg->lrn_alpha = 1e-4f;
   cfg->lrn_beta = 0.75f;
   cfg->dropout_p = 0.5f;
+  cfg->lrn_taps = 0;
 }
 
 size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode) {

@@ -473,12 +473,15 @@ struct DmaKO {
   bool cok;
   __device__ void setup(int r0, int g, int kb) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    rs = buf_rsrc(p + (int64_t)g * gstride, (uint32_t)(((int64_t)(K - 1) * ld + rows) * 2));
+    // descriptor based at k-row kb: offsets stay within this split's range
+    const int64_t span = ((int64_t)(K - 1 - kb) * ld + rows) * 2;
+    rs = buf_rsrc(p + (int64_t)g * gstride + (int64_t)kb * ld, (uint32_t)(span < 0x7FFFFFFF ? span : 0x7FFFFFFF));
     const int col = r0 + TrSlots::granule(wave, lane) * 8;
     cok = col < rows;
-    kr = kb + TrSlots::krow(wave, 0, lane);
+    const int k0 = TrSlots::krow(wave, 0, lane);
+    kr = kb + k0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) off[i] = (uint32_t)(((int64_t)(kr + 16 * i) * ld + col) * 2);
+    for (int i = 0; i < NI; ++i) off[i] = (uint32_t)(((int64_t)(k0 + 16 * i) * ld + col) * 2);
   }
   __device__ __forceinline__ void issue(bf16* s) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

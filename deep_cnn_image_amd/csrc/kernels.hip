@@ -638,14 +638,16 @@ __device__ __forceinline__ void load24(const T* px, int c0, int C, float* v) {
   }
 }
 
-// One thread per pixel and run of 8 channels; window half-width H and the
-// beta == 3/4 case are compile-time, so every loop below unrolls completely.
-// With beta == 3/4: r = rsqrt(S), S^-beta = r sqrt(r), S^(-beta-1) = S^-beta r^2.
+// LRN kernels take the window half-width H and the beta == 3/4 case as
+// compile-time parameters, so every loop below unrolls completely.
+// S = k + alpha * sum >= k > 0 is a normal number, so the hardware reciprocal
+// square root and square root (about 1 ulp each) need no range scaling:
+// with beta == 3/4, r = rsq(S), S^-beta = r sqrt(r), S^(-beta-1) = S^-beta r^2.
 template <bool B075>
 __device__ __forceinline__ void lrn_pows(float S, float beta, float& p, float& q) {
   if (B075) {
-    const float r = rsqrtf(S);
-    p = r * sqrtf(r);
+    const float r = __builtin_amdgcn_rsqf(S);
+    p = r * __builtin_amdgcn_sqrtf(r);
     q = p * r * r;
   } else {
     p = exp2f(-beta * log2f(S));
@@ -653,17 +655,9 @@ __device__ __forceinline__ void lrn_pows(float S, float beta, float& p, float& q
   }
 }
 
-template <typename T, int H, bool B075>
-__global__ void k_lrn_fwd(const T* __restrict__ a, T* __restrict__ b, uint32_t total, int C, float k,
-                          float alpha, float beta) {
-  const uint32_t t = blockIdx.x * TPB + threadIdx.x;
-  if (t >= total) return;
-  const uint32_t cpp = (uint32_t)C >> 3;
-  const uint32_t pix = t / cpp;
-  const int c0 = (int)(t - pix * cpp) * 8;
-  float v[24];
-  load24(a + (size_t)pix * C, c0, C, v);
-  float o[8];
+// LRN of 8 channels c0 .. c0+7 of one pixel; v holds channels c0-8 .. c0+15.
+template <int H, bool B075>
+__device__ __forceinline__ void lrn8(const float* v, float k, float alpha, float beta, float* o) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float s = 0.f;
@@ -673,7 +667,109 @@ __global__ void k_lrn_fwd(const T* __restrict__ a, T* __restrict__ b, uint32_t t
     lrn_pows<B075>(k + alpha * s, beta, p, q);
     o[i] = v[8 + i] * p;
   }
-  Pack8<T>::store(b + (size_t)pix * C + c0, o);
+}
+
+// LRN followed by the overlapping 3x3 / stride-2 max-pool with argmax, fused:
+// the LRN output is stored only in LDS (rounded to T exactly as a stored
+// tensor would be), so pooled values and argmax equal those of the two
+// separate steps.  One workgroup per (image n, pooled row i) over input rows
+// 2i .. 2i+2 (Hin = 2 Ho + 1), which are one contiguous run of 3 W C
+// elements:
+//   1. the run is copied into LDS with direct-to-LDS loads (one wait);
+//   2. each thread normalises its (row, column, 8-channel) units from LDS into
+//      registers, and after a barrier writes them back in place;
+//   3. the pooled row and its argmax are taken from LDS.
+// `dbg`, if not null, receives the LRN output (rows 2i, 2i+1, and the last
+// row from the last workgroup of an image).  Workgroups are remapped so that
+// the rows of one image, which share an input row, run on one XCD.
+constexpr int LRNPOOL_LDS = 3 * 27 * 256;   // elements: max over the two layers (3 x W x C)
+constexpr int LRNPOOL_TPB = 512;
+constexpr int LRNPOOL_UPT = 6;              // units per thread: ceil(3 W C / 8 / 512) <= 6
+template <typename T, int H, bool B075, int Win, int C>
+__global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ a, T* __restrict__ y,
+                                                          uint8_t* __restrict__ arg, T* __restrict__ dbg,
+                                                          float k, float alpha, float beta) {
+  constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho;
+  static_assert(3 * Win * C <= LRNPOOL_LDS && C % 8 == 0, "fused LRN/pool geometry");
+  static_assert(3 * Win * C / 8 <= LRNPOOL_UPT * LRNPOOL_TPB, "units per thread");
+  constexpr int LDS_BYTES = ((LRNPOOL_LDS * (int)sizeof(T) + 1023) / 1024) * 1024;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  T* rows = reinterpret_cast<T*>(lds);
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
+  const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
+  const int n = b / Ho, i = b - n * Ho;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int cpp = C >> 3, rowu = Win * cpp, units = 3 * rowu;
+  // 1. rows 2i .. 2i+2 -> LDS (1 KB per wave instruction; past the image reads as zero)
+  {
+    const size_t img = (size_t)Hin * Win * C;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + n * img, (uint32_t)(img * sizeof(T)));
+    const uint32_t base = (uint32_t)((size_t)2 * i * Win * C * sizeof(T));
+    constexpr int nins = (3 * Win * C * (int)sizeof(T) + 1023) / 1024;
+    for (int j = wave; j < nins; j += LRNPOOL_TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
+                                               (int)(base + j * 1024 + lane * 16), 0, 0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  // 2. LRN of this thread's units into registers, then back into LDS
+  const bool last = i == Ho - 1;
+  float o[LRNPOOL_UPT][8];
+#pragma unroll
+  for (int t = 0; t < LRNPOOL_UPT; ++t) {
+    const int u = tid + t * LRNPOOL_TPB;
+    if (u < units) {
+      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
+      float v[24];
+#pragma unroll
+      for (int h = 0; h < 3; ++h) {
+        const int cc = c0 + (h - 1) * 8;
+        if (cc >= 0 && cc < C) Pack8<T>::load(rows + pix * C + cc, v + h * 8);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[h * 8 + e] = 0.f;
+        }
+      }
+      lrn8<H, B075>(v, k, alpha, beta, o[t]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < LRNPOOL_UPT; ++t) {
+    const int u = tid + t * LRNPOOL_TPB;
+    if (u < units) {
+      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
+      Pack8<T>::store(rows + pix * C + c0, o[t]);
+      const int rr = pix / Win;
+      if (dbg && (rr < 2 || last)) {
+        const size_t g = (((size_t)n * Hin + 2 * i) * Win + pix) * C + c0;
+        Pack8<T>::store(dbg + g, o[t]);
+      }
+    }
+  }
+  __syncthreads();
+  // 3. pool: window rows 0..2 of LDS, columns 2j .. 2j+2
+  for (int u = tid; u < Wo * cpp; u += LRNPOOL_TPB) {
+    const int j = u / cpp, c0 = (u - j * cpp) * 8;
+    float best[8], v[8];
+    uint32_t bi[8];
+    Pack8<T>::load(rows + (2 * j) * C + c0, best);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bi[e] = 0;
+#pragma unroll
+    for (int d = 1; d < 9; ++d) {
+      const int dy = d / 3, dx = d % 3;
+      Pack8<T>::load(rows + (dy * Win + 2 * j + dx) * C + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
+    }
+    const size_t og = (((size_t)n * Ho + i) * Wo + j) * C + c0;
+    Pack8<T>::store(y + og, best);
+    *reinterpret_cast<uint2*>(arg + og) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
+                                                     bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
+  }
 }
 
 // Backward of LRN fused with the preceding ReLU's mask [a > 0]:
@@ -731,13 +827,14 @@ static hipError_t lrn_dispatch(int half, float beta, Fn&& fn) {
 #undef AX_LRN_CASE
 }
 
-template <typename T>
-struct LrnFwdFn {
-  const void* a; void* b; uint32_t total; int C; float k, alpha, beta; hipStream_t st;
+template <typename T, int Win, int C>
+struct LrnPoolFn {
+  const void* a; void* y; uint8_t* arg; void* dbg; int N; float k, alpha, beta; hipStream_t st;
   template <int H, bool B075>
   hipError_t operator()() const {
-    hipLaunchKernelGGL((k_lrn_fwd<T, H, B075>), grid1d(total), dim3(TPB), 0, st, (const T*)a, (T*)b, total, C,
-                       k, alpha, beta);
+    constexpr int Ho = (Win - 1) / 2;
+    hipLaunchKernelGGL((k_lrn_pool<T, H, B075, Win, C>), dim3(N * Ho), dim3(LRNPOOL_TPB), 0, st, (const T*)a,
+                       (T*)y, arg, (T*)dbg, k, alpha, beta);
     return hipGetLastError();
   }
 };
@@ -752,14 +849,19 @@ struct LrnBwdFn {
   }
 };
 
-hipError_t lrn_fwd(DType dt, const void* a, void* b, int64_t npix, int C, float k, float alpha, float beta,
-                   int n, hipStream_t st, const KTimer* kt) {
-  const int64_t total = npix * (C / 8);
-  if (total >= (int64_t)1 << 31) return hipErrorInvalidValue;
+hipError_t lrn_pool_fwd(DType dt, const void* a, void* y, uint8_t* arg, void* dbg, int N, int H, int W, int C,
+                        float k, float alpha, float beta, int n, hipStream_t st, const KTimer* kt) {
+  // the two layers of the network: 55 x 55 x 96 and 27 x 27 x 256
+  const int layer = (H == 55 && W == 55 && C == 96) ? 1 : (H == 27 && W == 27 && C == 256) ? 2 : 0;
+  if (!layer) return hipErrorInvalidValue;
   rec_start(kt, st);
-  const hipError_t e = dt == BF16
-      ? lrn_dispatch(n / 2, beta, LrnFwdFn<bf16>{a, b, (uint32_t)total, C, k, alpha, beta, st})
-      : lrn_dispatch(n / 2, beta, LrnFwdFn<float>{a, b, (uint32_t)total, C, k, alpha, beta, st});
+  hipError_t e;
+  if (layer == 1)
+    e = dt == BF16 ? lrn_dispatch(n / 2, beta, LrnPoolFn<bf16, 55, 96>{a, y, arg, dbg, N, k, alpha, beta, st})
+                   : lrn_dispatch(n / 2, beta, LrnPoolFn<float, 55, 96>{a, y, arg, dbg, N, k, alpha, beta, st});
+  else
+    e = dt == BF16 ? lrn_dispatch(n / 2, beta, LrnPoolFn<bf16, 27, 256>{a, y, arg, dbg, N, k, alpha, beta, st})
+                   : lrn_dispatch(n / 2, beta, LrnPoolFn<float, 27, 256>{a, y, arg, dbg, N, k, alpha, beta, st});
   rec_stop(kt, st);
   return e;
 }

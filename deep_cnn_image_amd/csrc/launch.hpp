@@ -98,9 +98,10 @@ size_t fc_fwd_part_bytes(int M, int K, int O);
 size_t fc_dgrad_part_bytes(int M, int K, int O);
 
 // ---- bandwidth-bound layers (NHWC, C % 8 == 0)
-hipError_t lrn_fwd(DType, const void* a, void* b, int64_t npix, int C, float k, float alpha,
-                   float beta, int n, hipStream_t,
-                      const KTimer* kt = nullptr);
+// LRN then 3x3 / stride-2 max-pool with argmax in one pass over the input;
+// `dbg` (may be null) also receives the LRN output.
+hipError_t lrn_pool_fwd(DType, const void* a, void* y, uint8_t* arg, void* dbg, int N, int H, int W, int C,
+                        float k, float alpha, float beta, int n, hipStream_t, const KTimer* kt = nullptr);
 hipError_t lrn_bwd(DType, const void* a, const void* g, void* da, int64_t npix, int C, float k,
                    float alpha, float beta, int n, hipStream_t,
                       const KTimer* kt = nullptr);

@@ -66,6 +66,7 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
   if (cfg->batch < 1 || cfg->batch > maxb) return ALEXNET_E_SHAPE;
   // LRN window: odd, half-width <= 4 (the backward kernel's reach)
   if (cfg->lrn_n < 1 || cfg->lrn_n > 9 || (cfg->lrn_n & 1) == 0) return ALEXNET_E_ARG;
+  if (cfg->lrn_taps != 0 && cfg->lrn_taps != 1) return ALEXNET_E_ARG;
   if (!(cfg->lrn_k > 0.f) || !(cfg->lrn_alpha >= 0.f) || !(cfg->lrn_beta >= 0.f)) return ALEXNET_E_ARG;
   if (!(cfg->dropout_p >= 0.f && cfg->dropout_p < 1.f)) return ALEXNET_E_ARG;
 
@@ -106,11 +107,11 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
   };
 
   nhwc(T_CONV1, 55, 96, dt);
-  nhwc(T_LRN1, 55, 96, dt);
+  if (cfg->lrn_taps) nhwc(T_LRN1, 55, 96, dt);
   nhwc(T_POOL1, 27, 96, dt);
   nhwc(T_ARG1, 27, 96, ALEXNET_U8);
   nhwc(T_CONV2, 27, 256, dt);
-  nhwc(T_LRN2, 27, 256, dt);
+  if (cfg->lrn_taps) nhwc(T_LRN2, 27, 256, dt);
   nhwc(T_POOL2, 13, 256, dt);
   nhwc(T_ARG2, 13, 256, ALEXNET_U8);
   nhwc(T_CONV3, 13, 384, dt);

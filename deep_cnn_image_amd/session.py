@@ -31,8 +31,8 @@ class Session:
     """One configuration (batch, groups, dtype, mode) with its workspace."""
 
     def __init__(self, batch: int, groups: int = 1, dtype: int = B.BF16, mode: int = B.MODE_FORWARD,
-                 device: str = "cuda:0"):
-        self.cfg = B.alexnet_default_cfg(batch, groups, dtype)
+                 device: str = "cuda:0", lrn_taps: bool = False):
+        self.cfg = B.alexnet_default_cfg(batch, groups, dtype, lrn_taps)
         self.mode = mode
         self.dtype = dtype
         self.device = torch.device(device)

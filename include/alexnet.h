@@ -79,10 +79,13 @@ typedef struct {
   float lrn_alpha;   /* 1e-4, multiplies the window sum of squares directly            */
   float lrn_beta;    /* 0.75                                                           */
   float dropout_p;   /* 0.5: training drop probability; inference scales by 1 - p      */
+  int32_t lrn_taps;  /* 0: LRN and the max-pool after it run fused and the LRN outputs
+                        are never stored; 1: they are also stored as taps lrn1, lrn2
+                        (for layer-by-layer checks; results are identical)          */
 } alexnet_cfg;
 
 /* Fills *cfg with the pages' constants: k = 2, n = 5, alpha = 1e-4,
- * beta = 0.75, dropout p = 0.5. */
+ * beta = 0.75, dropout p = 0.5; lrn_taps = 0. */
 void alexnet_default_cfg(alexnet_cfg* cfg, int32_t batch, int32_t groups, int32_t dtype);
 
 /* Workspace bytes for one call in `mode`; 0 if cfg is invalid.  Host only. */
@@ -156,8 +159,9 @@ typedef enum {
   ALEXNET_KT_S2D = 1,          /* layer-1 input staging (4x4 pixel blocks)      */
   ALEXNET_KT_CONV1_FWD, ALEXNET_KT_CONV2_FWD, ALEXNET_KT_CONV3_FWD, ALEXNET_KT_CONV4_FWD,
   ALEXNET_KT_CONV5_FWD,
-  ALEXNET_KT_LRN1_FWD, ALEXNET_KT_LRN2_FWD,
-  ALEXNET_KT_POOL1_FWD, ALEXNET_KT_POOL2_FWD, ALEXNET_KT_POOL5_FWD,
+  ALEXNET_KT_LRNPOOL1_FWD,     /* LRN1 + pool1 (one fused kernel)                */
+  ALEXNET_KT_LRNPOOL2_FWD,     /* LRN2 + pool2                                   */
+  ALEXNET_KT_POOL5_FWD,
   ALEXNET_KT_FC6_FWD, ALEXNET_KT_FC7_FWD, ALEXNET_KT_FC8_FWD,
   ALEXNET_KT_FC8_DGRAD, ALEXNET_KT_FC7_DGRAD, ALEXNET_KT_FC6_DGRAD,
   ALEXNET_KT_FC8_WGRAD, ALEXNET_KT_FC7_WGRAD, ALEXNET_KT_FC6_WGRAD,

@@ -38,7 +38,7 @@ def test_default_cfg_holds_page_constants():
 
 @pytest.mark.parametrize("field,value", [("batch", 0), ("batch", -1), ("batch", 5000), ("groups", 3),
                                          ("groups", 0), ("dtype", 7), ("lrn_n", 4), ("lrn_n", 11),
-                                         ("lrn_k", 0.0), ("dropout_p", 1.0)])
+                                         ("lrn_k", 0.0), ("dropout_p", 1.0), ("lrn_taps", 2)])
 def test_invalid_cfg_gives_zero_workspace(field, value):
     c = B.alexnet_default_cfg(4, 1, B.BF16)
     setattr(c, field, value)
@@ -147,6 +147,18 @@ def test_tap_shapes_follow_the_layer_list():
     for name in ("gw6", "gw7", "gw8"):
         with pytest.raises(B.AlexNetError):
             B.alexnet_tap(c, B.MODE_TRAIN, ids[name])
+
+
+def test_lrn_taps_only_on_request():
+    ids = B.tap_ids()
+    for mode in (B.MODE_FORWARD, B.MODE_TRAIN):
+        c = B.alexnet_default_cfg(2, 1, B.BF16)
+        assert c.lrn_taps == 0
+        with pytest.raises(B.AlexNetError):
+            B.alexnet_tap(c, mode, ids["lrn1"])
+        c = B.alexnet_default_cfg(2, 1, B.BF16, lrn_taps=True)
+        assert B.alexnet_tap(c, mode, ids["lrn1"])[1] == (2, 55, 55, 96)
+        assert B.alexnet_tap(c, mode, ids["lrn2"])[1] == (2, 27, 27, 256)
 
 
 def test_kernel_ids_match_header():

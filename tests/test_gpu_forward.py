@@ -22,15 +22,16 @@ FWD_TAPS = ("conv1", "lrn1", "pool1", "arg1", "conv2", "lrn2", "pool2", "arg2", 
             "conv5", "pool5", "arg5", "drop6", "drop7", "logits")
 
 
-def run_forward(syn, dtype, mode=B.MODE_FORWARD, batch=None):
+def run_forward(syn, dtype, mode=B.MODE_FORWARD, batch=None, lrn_taps=True):
     n = syn.x.shape[0] if batch is None else batch
-    say(f"[gpu] forward mode={mode} batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed}")
-    sess = Session(n, syn.groups, dtype, mode, DEV)
+    say(f"[gpu] forward mode={mode} batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed} "
+        f"lrn_taps={lrn_taps}")
+    sess = Session(n, syn.groups, dtype, mode, DEV, lrn_taps=lrn_taps)
     params = sess.upload_params(syn.weights, syn.biases)
     x = to_device(syn.x, dtype, DEV)
     probs = sess.forward(params, x)
     torch.cuda.synchronize()
-    g = {name: sess.tap(name).clone() for name in FWD_TAPS}
+    g = {name: sess.tap(name).clone() for name in FWD_TAPS if lrn_taps or not name.startswith("lrn")}
     if mode == B.MODE_TENVIEW:
         g["view_probs"] = sess.tap("view_probs").clone()
     g["probs"] = probs.clone()
@@ -143,6 +144,17 @@ def test_tenview_small(orc):
     assert e_views <= TOL_BF16 and e_mean <= TOL_BF16
     vp = flat(g["view_probs"]).reshape(2, 10, 1000)
     np.testing.assert_allclose(host(g["probs"]), vp.sum(1) / 10.0, rtol=1e-6, atol=1e-9)
+
+
+def test_fused_lrn_pool_equals_stored_path():
+    """The default forward (LRN and max-pool fused, LRN output never stored)
+    gives bit-identical pooled values, argmax and probabilities."""
+    syn = I.config_inputs(2, batch=3)
+    a = run_forward(syn, B.BF16, lrn_taps=True)
+    b = run_forward(syn, B.BF16, lrn_taps=False)
+    for k in b:
+        assert torch.equal(a[k].view(torch.uint8) if a[k].dtype != torch.uint8 else a[k],
+                           b[k].view(torch.uint8) if b[k].dtype != torch.uint8 else b[k]), k
 
 
 def test_forward_is_deterministic():

@@ -28,10 +28,10 @@ TAPS = ("conv1", "lrn1", "pool1", "arg1", "conv2", "lrn2", "pool2", "arg2", "con
 HYPER = dict(lr=0.01, momentum_coef=0.9, weight_decay=5e-4)
 
 
-def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None):
+def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None, lrn_taps=True):
     n = syn.x.shape[0]
-    say(f"[gpu] train batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed} step={step}")
-    sess = Session(n, syn.groups, dtype, B.MODE_TRAIN, DEV)
+    say(f"[gpu] train batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed} step={step} lrn_taps={lrn_taps}")
+    sess = Session(n, syn.groups, dtype, B.MODE_TRAIN, DEV, lrn_taps=lrn_taps)
     master = params_f32(syn.master_w, syn.biases)
     if v0 is None:
         mom = [torch.zeros_like(m) for m in master]
@@ -54,7 +54,7 @@ def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None):
              mom=[host(v) for v in mom], work=[w.clone() for w in work],
              gw=[host(sess.tap(f"gw{i + 1}")) for i in range(5)],
              gb=[host(sess.tap(f"gb{i + 1}")).ravel() for i in range(8)],
-             taps={k: sess.tap(k).clone() for k in TAPS})
+             taps={k: sess.tap(k).clone() for k in TAPS if lrn_taps or not k.startswith("lrn")})
     # The FC weight gradients are applied inside their GEMM and never stored;
     # recover them from the momentum update v1 = mu v0 - wd lr w0 - lr g
     # (fp32 coefficients as the library forms them).
@@ -275,6 +275,18 @@ def test_fp32_train_step_small(orc):
     assert max(ew) <= 1e-4
     assert abs(r["loss"] - o["loss"]) / abs(o["loss"]) <= 1e-5
     check_sgd(r, syn)
+
+
+def test_train_step_fused_lrn_pool_equals_stored_path():
+    """Training with LRN and max-pool fused (the default) updates every tensor
+    bit-identically to the path that also stores the LRN outputs."""
+    syn = I.config_inputs(4, batch=2)
+    a = run_train(syn, lrn_taps=True)
+    b = run_train(syn, lrn_taps=False)
+    assert a["loss"] == b["loss"]
+    for j in range(16):
+        assert np.array_equal(a["master"][j], b["master"][j]) and np.array_equal(a["mom"][j], b["mom"][j]), j
+        assert torch.equal(a["work"][j].view(torch.uint8), b["work"][j].view(torch.uint8)), j
 
 
 def test_train_step_is_deterministic():
