@@ -66,10 +66,10 @@ def kernel_work(kt, n, groups):
         # LRN + max-pool fused: LRN input read once, pooled values and argmax written
         "LRNPOOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
         "LRNPOOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
-        "LRN1_BWD": 3 * e * act["55x96"], "LRN2_BWD": 3 * e * act["27x256"],
+        # pool, LRN and ReLU backward fused: pooled gradient, argmax and LRN input read, da written
+        "POOLLRN1_BWD": (e + 1) * act["27x96"] + 2 * e * act["55x96"],
+        "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"],
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
-        "POOL1_BWD": (e + 1) * act["27x96"] + e * act["55x96"],
-        "POOL2_BWD": (e + 1) * act["13x256"] + e * act["27x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
         "SGD": 22 * SGD_ELEMS,
     }

@@ -191,10 +191,9 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       tp(ws, p, din[i]), st, T(ktd[i])));
   }
   // pool2 -> LRN2 -> ReLU2
-  HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), nullptr, tp(ws, p, T_DLRN2), N,
-                  27, 27, 256, 0, st, T(ALEXNET_KT_POOL2_BWD)));
-  HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_DLRN2), tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256,
-                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN2_BWD)));
+  HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), tp(ws, p, T_CONV2),
+                      tp(ws, p, T_DCONV2), c.lrn_taps ? tp(ws, p, T_DLRN2) : nullptr, N, 27, 27, 256, c.lrn_k,
+                      c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN2_BWD)));
   {
     const ConvShape& s = net.conv[1];
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st,
@@ -204,10 +203,9 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       T(ALEXNET_KT_CONV2_DGRAD)));
   }
   // pool1 -> LRN1 -> ReLU1, then layer-1 weight gradient (no input gradient)
-  HIPCHK(pool_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), nullptr, tp(ws, p, T_DLRN1), N,
-                  55, 55, 96, 0, st, T(ALEXNET_KT_POOL1_BWD)));
-  HIPCHK(lrn_bwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_DLRN1), tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96,
-                 c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_LRN1_BWD)));
+  HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), tp(ws, p, T_CONV1),
+                      tp(ws, p, T_DCONV1), c.lrn_taps ? tp(ws, p, T_DLRN1) : nullptr, N, 55, 55, 96, c.lrn_k,
+                      c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
   HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st,
                      T(ALEXNET_KT_CONV1_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96, gb(0), cs, st));

@@ -772,21 +772,14 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
   }
 }
 
-// Backward of LRN fused with the preceding ReLU's mask [a > 0]:
+// Backward of LRN fused with the preceding ReLU's mask [a > 0], for channels
+// c0 .. c0+7 of one pixel:
 //   da_j = g_j S_j^-beta - 2 alpha beta a_j sum_{|i-j| <= H} g_i a_i S_i^(-beta-1)
-// The 8 + 2H channels c0-H .. c0+7+H carry the per-channel terms; a is needed
-// over c0-2H .. c0+7+2H (inside c0-8 .. c0+15 for H <= 4).
-template <typename T, int H, bool B075>
-__global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* __restrict__ da,
-                          uint32_t total, int C, float k, float alpha, float beta) {
-  const uint32_t t = blockIdx.x * TPB + threadIdx.x;
-  if (t >= total) return;
-  const uint32_t cpp = (uint32_t)C >> 3;
-  const uint32_t pix = t / cpp;
-  const int c0 = (int)(t - pix * cpp) * 8;
-  float av[24], gv[24];
-  load24(a + (size_t)pix * C, c0, C, av);
-  load24(g + (size_t)pix * C, c0, C, gv);
+// av holds a over c0-8 .. c0+15 and gv holds g over the same channels (only
+// c0-H .. c0+7+H of g and c0-2H .. c0+7+2H of a are used; H <= 4).
+template <int H, bool B075>
+__device__ __forceinline__ void lrn_bwd8(const float* av, const float* gv, float k, float alpha, float beta,
+                                         float* o) {
   constexpr int NR = 8 + 2 * H;
   float pb[NR], tt[NR];
 #pragma unroll
@@ -800,7 +793,6 @@ __global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* _
     pb[r] = p;
     tt[r] = gv[rel] * av[rel] * q;
   }
-  float o[8];
   const float c2 = 2.f * alpha * beta;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -811,7 +803,106 @@ __global__ void k_lrn_bwd(const T* __restrict__ a, const T* __restrict__ g, T* _
     const float d = gv[8 + i] * pb[i + H] - c2 * aj * cross;
     o[i] = aj > 0.f ? d : 0.f;
   }
-  Pack8<T>::store(da + (size_t)pix * C + c0, o);
+}
+
+// Max-pool backward (3x3 / stride 2, argmax codes dy*3+dx) for channels
+// c0 .. c0+7 of input pixel (n, h, w): the sum, over the windows (i, j) that
+// contain the pixel and whose argmax is it, of dy[n][i][j] -- windows in
+// row-major order -- rounded to T as a stored gradient would be.
+template <typename T>
+__device__ __forceinline__ void pool_bwd8(const T* __restrict__ dy, const uint8_t* __restrict__ arg, int n, int h,
+                                          int w, int c0, int C, int Ho, int Wo, float* out) {
+  const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
+  const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int i = i0; i <= i1; ++i)
+    for (int j = j0; j <= j1; ++j) {
+      const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
+      const size_t op = (((size_t)n * Ho + i) * Wo + j) * C + c0;
+      const uint2 am = *reinterpret_cast<const uint2*>(arg + op);
+      float g[8];
+      Pack8<T>::load(dy + op, g);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+        if (b == code) acc[q] += g[q];
+      }
+    }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) out[q] = Num<T>::load(Num<T>::store(acc[q]));
+}
+
+// Max-pool backward, LRN backward and the ReLU mask in one pass.  One
+// workgroup per input row (image n, row h) of a Win x C layer:
+//   1. the row of the LRN input a is copied into LDS (direct-to-LDS loads)
+//      while each thread forms the pooled gradient g (w.r.t. the LRN output)
+//      of its (column, 8-channel) units, rounded as a stored gradient would
+//      be, into a second LDS row;
+//   2. each unit's LRN backward reads its channel neighbours of a and g from
+//      LDS, applies the ReLU mask and writes da.
+// da therefore equals that of the separate steps.  `dbg`, if not null,
+// receives g.
+constexpr int POOLLRN_UPT = 4;   // units per thread: Win * C / 8 / 256 <= 4
+template <typename T, int H, bool B075, int Win, int C>
+__global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
+                                                      const T* __restrict__ a, T* __restrict__ da,
+                                                      T* __restrict__ dbg, float k, float alpha, float beta) {
+  constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, cpp = C / 8, units = Win * cpp;
+  static_assert(units <= POOLLRN_UPT * TPB && C % 8 == 0, "pool/LRN backward geometry");
+  constexpr int ROW_BYTES = ((Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
+  __shared__ __attribute__((aligned(16))) char lds[2 * ROW_BYTES];
+  T* arow = reinterpret_cast<T*>(lds);
+  T* grow = reinterpret_cast<T*>(lds + ROW_BYTES);
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
+  const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
+  const int n = b / Hin, h = b - n * Hin;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t row0 = ((size_t)n * Hin + h) * Win * C;   // element offset of the row
+  {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + row0, (uint32_t)(Win * C * sizeof(T)));
+    constexpr int nins = ROW_BYTES / 1024;
+    for (int j = wave; j < nins; j += TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16, j * 1024 + lane * 16, 0,
+                                               0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < POOLLRN_UPT; ++t) {
+    const int u = tid + t * TPB;
+    if (u < units) {
+      const int w = u / cpp, c0 = (u - w * cpp) * 8;
+      float g[8];
+      pool_bwd8<T>(dy, arg, n, h, w, c0, C, Ho, Wo, g);
+      Pack8<T>::store(grow + w * C + c0, g);
+      if (dbg) Pack8<T>::store(dbg + row0 + w * C + c0, g);
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < POOLLRN_UPT; ++t) {
+    const int u = tid + t * TPB;
+    if (u < units) {
+      const int w = u / cpp, c0 = (u - w * cpp) * 8;
+      float av[24], gv[24];
+#pragma unroll
+      for (int hh = 0; hh < 3; ++hh) {
+        const int cc = c0 + (hh - 1) * 8;
+        if (cc >= 0 && cc < C) {
+          Pack8<T>::load(arow + w * C + cc, av + hh * 8);
+          Pack8<T>::load(grow + w * C + cc, gv + hh * 8);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { av[hh * 8 + e] = 0.f; gv[hh * 8 + e] = 0.f; }
+        }
+      }
+      float o[8];
+      lrn_bwd8<H, B075>(av, gv, k, alpha, beta, o);
+      Pack8<T>::store(da + row0 + w * C + c0, o);
+    }
+  }
 }
 
 // Calls fn.operator()<H, B075>() for the window half-width and beta.
@@ -838,13 +929,14 @@ struct LrnPoolFn {
     return hipGetLastError();
   }
 };
-template <typename T>
-struct LrnBwdFn {
-  const void* a; const void* g; void* da; uint32_t total; int C; float k, alpha, beta; hipStream_t st;
+template <typename T, int Win, int C>
+struct PoolLrnBwdFn {
+  const void* dy; const uint8_t* arg; const void* a; void* da; void* dbg; int N; float k, alpha, beta;
+  hipStream_t st;
   template <int H, bool B075>
   hipError_t operator()() const {
-    hipLaunchKernelGGL((k_lrn_bwd<T, H, B075>), grid1d(total), dim3(TPB), 0, st, (const T*)a, (const T*)g,
-                       (T*)da, total, C, k, alpha, beta);
+    hipLaunchKernelGGL((k_pool_lrn_bwd<T, H, B075, Win, C>), dim3(N * Win), dim3(TPB), 0, st, (const T*)dy, arg,
+                       (const T*)a, (T*)da, (T*)dbg, k, alpha, beta);
     return hipGetLastError();
   }
 };
@@ -865,14 +957,22 @@ hipError_t lrn_pool_fwd(DType dt, const void* a, void* y, uint8_t* arg, void* db
   rec_stop(kt, st);
   return e;
 }
-hipError_t lrn_bwd(DType dt, const void* a, const void* gr, void* da, int64_t npix, int C, float k,
-                   float alpha, float beta, int n, hipStream_t st, const KTimer* kt) {
-  const int64_t total = npix * (C / 8);
-  if (total >= (int64_t)1 << 31) return hipErrorInvalidValue;
+
+
+hipError_t pool_lrn_bwd(DType dt, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg, int N,
+                        int H, int W, int C, float k, float alpha, float beta, int n, hipStream_t st,
+                        const KTimer* kt) {
+  // the two layers of the network: 55 x 55 x 96 and 27 x 27 x 256
+  const int layer = (H == 55 && W == 55 && C == 96) ? 1 : (H == 27 && W == 27 && C == 256) ? 2 : 0;
+  if (!layer) return hipErrorInvalidValue;
   rec_start(kt, st);
-  const hipError_t e = dt == BF16
-      ? lrn_dispatch(n / 2, beta, LrnBwdFn<bf16>{a, gr, da, (uint32_t)total, C, k, alpha, beta, st})
-      : lrn_dispatch(n / 2, beta, LrnBwdFn<float>{a, gr, da, (uint32_t)total, C, k, alpha, beta, st});
+  hipError_t e;
+  if (layer == 1)
+    e = dt == BF16 ? lrn_dispatch(n / 2, beta, PoolLrnBwdFn<bf16, 55, 96>{dy, arg, a, da, dbg, N, k, alpha, beta, st})
+                   : lrn_dispatch(n / 2, beta, PoolLrnBwdFn<float, 55, 96>{dy, arg, a, da, dbg, N, k, alpha, beta, st});
+  else
+    e = dt == BF16 ? lrn_dispatch(n / 2, beta, PoolLrnBwdFn<bf16, 27, 256>{dy, arg, a, da, dbg, N, k, alpha, beta, st})
+                   : lrn_dispatch(n / 2, beta, PoolLrnBwdFn<float, 27, 256>{dy, arg, a, da, dbg, N, k, alpha, beta, st});
   rec_stop(kt, st);
   return e;
 }

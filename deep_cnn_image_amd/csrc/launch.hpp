@@ -102,9 +102,12 @@ size_t fc_dgrad_part_bytes(int M, int K, int O);
 // `dbg` (may be null) also receives the LRN output.
 hipError_t lrn_pool_fwd(DType, const void* a, void* y, uint8_t* arg, void* dbg, int N, int H, int W, int C,
                         float k, float alpha, float beta, int n, hipStream_t, const KTimer* kt = nullptr);
-hipError_t lrn_bwd(DType, const void* a, const void* g, void* da, int64_t npix, int C, float k,
-                   float alpha, float beta, int n, hipStream_t,
-                      const KTimer* kt = nullptr);
+// Max-pool backward, LRN backward and the preceding ReLU's mask in one pass:
+// dy (pooled gradient) and arg -> da w.r.t. the LRN input a.  `dbg` (may be
+// null) also receives the gradient w.r.t. the LRN output.
+hipError_t pool_lrn_bwd(DType, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg, int N,
+                        int H, int W, int C, float k, float alpha, float beta, int n, hipStream_t,
+                        const KTimer* kt = nullptr);
 // 3x3/s2 max-pool; flat_out: y written [N][C*Ho*Wo] in (c,h,w) order
 hipError_t pool_fwd(DType, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C,
                     int flat_out, hipStream_t,

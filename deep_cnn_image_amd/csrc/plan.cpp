@@ -136,10 +136,10 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
     nhwc(T_DCONV4, 13, 384, dt);
     nhwc(T_DCONV3, 13, 384, dt);
     nhwc(T_DIN3, 13, 256, dt);
-    nhwc(T_DLRN2, 27, 256, dt);
+    if (cfg->lrn_taps) nhwc(T_DLRN2, 27, 256, dt);
     nhwc(T_DCONV2, 27, 256, dt);
     nhwc(T_DIN2, 27, 96, dt);
-    nhwc(T_DLRN1, 55, 96, dt);
+    if (cfg->lrn_taps) nhwc(T_DLRN1, 55, 96, dt);
     nhwc(T_DCONV1, 55, 96, dt);
     for (int i = 0; i < 8; ++i) {
       // FC weight gradients are applied inside their GEMM (never stored):

@@ -79,9 +79,10 @@ typedef struct {
   float lrn_alpha;   /* 1e-4, multiplies the window sum of squares directly            */
   float lrn_beta;    /* 0.75                                                           */
   float dropout_p;   /* 0.5: training drop probability; inference scales by 1 - p      */
-  int32_t lrn_taps;  /* 0: LRN and the max-pool after it run fused and the LRN outputs
-                        are never stored; 1: they are also stored as taps lrn1, lrn2
-                        (for layer-by-layer checks; results are identical)          */
+  int32_t lrn_taps;  /* 0: LRN and the max-pool after it run fused (forward and
+                        backward) and the LRN outputs and their gradients are never
+                        stored; 1: they are also stored as taps lrn1, lrn2, dlrn1,
+                        dlrn2 (for layer-by-layer checks; results are identical)    */
 } alexnet_cfg;
 
 /* Fills *cfg with the pages' constants: k = 2, n = 5, alpha = 1e-4,
@@ -169,7 +170,8 @@ typedef enum {
   ALEXNET_KT_CONV5_WGRAD, ALEXNET_KT_CONV4_WGRAD, ALEXNET_KT_CONV3_WGRAD, ALEXNET_KT_CONV2_WGRAD,
   ALEXNET_KT_CONV1_WGRAD,
   ALEXNET_KT_CONV5_DGRAD, ALEXNET_KT_CONV4_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV2_DGRAD,
-  ALEXNET_KT_POOL2_BWD, ALEXNET_KT_LRN2_BWD, ALEXNET_KT_POOL1_BWD, ALEXNET_KT_LRN1_BWD,
+  ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
+  ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
   ALEXNET_KT_SGD,
   ALEXNET_KT_COUNT
 } alexnet_kernel;

@@ -159,6 +159,12 @@ def test_lrn_taps_only_on_request():
         c = B.alexnet_default_cfg(2, 1, B.BF16, lrn_taps=True)
         assert B.alexnet_tap(c, mode, ids["lrn1"])[1] == (2, 55, 55, 96)
         assert B.alexnet_tap(c, mode, ids["lrn2"])[1] == (2, 27, 27, 256)
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    for name in ("dlrn1", "dlrn2"):
+        with pytest.raises(B.AlexNetError):
+            B.alexnet_tap(c, B.MODE_TRAIN, ids[name])
+    c = B.alexnet_default_cfg(2, 1, B.BF16, lrn_taps=True)
+    assert B.alexnet_tap(c, B.MODE_TRAIN, ids["dlrn1"])[1] == (2, 55, 55, 96)
 
 
 def test_kernel_ids_match_header():

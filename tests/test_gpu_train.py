@@ -54,7 +54,7 @@ def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None, lrn_taps=True):
              mom=[host(v) for v in mom], work=[w.clone() for w in work],
              gw=[host(sess.tap(f"gw{i + 1}")) for i in range(5)],
              gb=[host(sess.tap(f"gb{i + 1}")).ravel() for i in range(8)],
-             taps={k: sess.tap(k).clone() for k in TAPS if lrn_taps or not k.startswith("lrn")})
+             taps={k: sess.tap(k).clone() for k in TAPS if lrn_taps or not k.startswith(("lrn", "dlrn"))})
     # The FC weight gradients are applied inside their GEMM and never stored;
     # recover them from the momentum update v1 = mu v0 - wd lr w0 - lr g
     # (fp32 coefficients as the library forms them).
