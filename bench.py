@@ -76,6 +76,32 @@ def kernel_work(kt, n, groups):
     return "hbm", float(table[kt])
 
 
+def kernel_source_sha256():
+    """sha256 over the HIP kernel sources (name + bytes, sorted): the identity
+    of the build that HBM counters in profiles/ were taken on."""
+    import hashlib
+    d = os.path.join(ROOT, "deep_cnn_image_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (two rocprofv3
+    --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None if
+    the counters were taken on other kernel sources or another kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel") != kernel or t.get("source_sha256") != kernel_source_sha256():
+        return None
+    return int(t["read_bytes"] + t["write_bytes"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,7 +245,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if kind == "mfma" else PEAK_HBM_GBS
     roofline = {"kernel": dominant, "bound": kind, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s" if kind == "mfma" else "GB/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "avg_launch_us": round(dom_ms * 1e3, 2),
+                "traffic": measured_traffic(dominant), "avg_launch_us": round(dom_ms * 1e3, 2),
                 "work_per_launch": work}
 
     rec = {

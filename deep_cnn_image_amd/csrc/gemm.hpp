@@ -383,17 +383,23 @@ struct DmaKC {
   }
 };
 
-// Direct-to-LDS version of LdIm2col for bf16 (same row and k decomposition).
+// Direct-to-LDS version of LdIm2col for bf16 (same row decomposition).  Two
+// k orders: tap-major, k = (kh, kw, ci) as LdIm2col; or, with `blocked` (Cg a
+// multiple of BK), channel-blocked k = (ci / BK, kh, kw, ci % BK), where each
+// k-slice is one tap of one 64-channel block.  The blocked order revisits a
+// block's input rows for every tap before moving on, which keeps a channel
+// block of the rows a wave of workgroups touches resident in L2 for wide
+// inputs; the weights must be laid out in the same order.
 template <int R>
 struct DmaIm2col {
   static constexpr bool DMA = true;
   using Layout = LayoutKC<bf16>;
   using Slots = DmaSlots<R>;
   static constexpr int NI = Slots::NI;
-  const bf16* p; ConvGeom cg; int M; int K;
+  const bf16* p; ConvGeom cg; int M; int K; bool blocked = false;
   __amdgpu_buffer_rsrc_t rs;
   int hb[NI], wb[NI], pix[NI];   // pix: element offset of input pixel (hb, wb) of the row's image
-  int kc, kh, kw, ci;
+  int kc, kh, kw, ci;            // blocked: kh, kw uniform, ci = block base + this lane's granule
   __device__ void setup(int r0, int g, int kb) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = cg.Ho * cg.Wo;
@@ -411,12 +417,30 @@ struct DmaIm2col {
         pix[i] = ((n * cg.H + hb[i]) * cg.W + wb[i]) * cg.Ctot + g * cg.Cg;
       }
     }
-    kc = kb + Slots::granule(lane, wave & 1) * 8;
-    const int tap = kc / cg.Cg;
-    ci = kc - tap * cg.Cg; kh = tap / cg.KW; kw = tap - kh * cg.KW;
+    const int gcol = Slots::granule(lane, wave & 1) * 8;
+    kc = kb + gcol;
+    if (blocked) {
+      const int kt = kb / BK, taps = cg.KH * cg.KW;
+      const int blk = kt / taps, tap = kt - blk * taps;
+      kh = tap / cg.KW; kw = tap - kh * cg.KW; ci = blk * BK + gcol;
+    } else {
+      const int tap = kc / cg.Cg;
+      ci = kc - tap * cg.Cg; kh = tap / cg.KW; kw = tap - kh * cg.KW;
+    }
   }
   __device__ __forceinline__ void issue(bf16* s) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (blocked) {   // K = Cg * KH * KW is a multiple of BK: no k tail
+      const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int hi = hb[i] + kh, wi = wb[i] + kw;
+        const bool ok = ((unsigned)hi < (unsigned)cg.H) & ((unsigned)wi < (unsigned)cg.W);
+        dma16(rs, ok ? (uint32_t)(pix[i] + tapoff) * 2u : BUF_OOB, s + Slots::slot(wave, i) * 8 * BK);
+      }
+      if (++kw == cg.KW) { kw = 0; if (++kh == cg.KH) { kh = 0; ci += BK; } }
+      return;
+    }
     const bool kok = kc < K;
     const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
 #pragma unroll

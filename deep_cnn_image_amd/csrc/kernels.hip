@@ -23,6 +23,10 @@ template <typename T, int R>
 using ColsLd = std::conditional_t<std::is_same<T, bf16>::value, DmaKO<R>, LdKO<T, R>>;
 template <typename T, int R>
 using WgradBLd = std::conditional_t<std::is_same<T, bf16>::value, DmaWgradB<R>, LdWgradB<T, R>>;
+// channel-blocked k order (direct-to-LDS im2col only; see DmaIm2col)
+template <int R> static void set_blocked(DmaIm2col<R>& a, bool b) { a.blocked = b; }
+template <typename T, int R> static void set_blocked(LdIm2col<T, R>&, bool) {}
+bool im2col_blocked(DType dt, int Cg);
 
 static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
 
@@ -207,6 +211,7 @@ struct ConvFwdFn {
   hipError_t operator()() const {
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
     Im2colLd<T, BM> a;
+    set_blocked(a, im2col_blocked(std::is_same<T, bf16>::value ? BF16 : F32, Cig));
     a.p = (const T*)x;
     a.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
     a.M = s.Nimg * s.Ho * s.Wo;
@@ -236,6 +241,7 @@ struct ConvDgradFn {
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
     // dX = stride-1 convolution of dY with flipped, transposed weights, pad K-1-p
     Im2colLd<T, BM> a;
+    set_blocked(a, im2col_blocked(std::is_same<T, bf16>::value ? BF16 : F32, Cog));
     a.p = (const T*)dy;
     a.cg = ConvGeom{s.Ho, s.Wo, s.Cout, Cog, s.K, s.K, 1, s.K - 1 - s.pad, s.H, s.W};
     a.M = s.Nimg * s.H * s.W;
@@ -582,41 +588,68 @@ hipError_t fc_wgrad_sgd(DType dt, int M, int K, int O, const void* dy, const voi
 // =========================================================================
 // Weight re-layouts
 // =========================================================================
+// Forward weights [co][ci][kh][kw] -> GEMM rows [co][k] in the loader's k order:
+// k = (kh, kw, ci), or with `blocked` k = (ci / 64, kh, kw, ci % 64).
 template <typename T>
-__global__ void k_w_khwc(const T* __restrict__ w, T* __restrict__ o, int Cout, int Cg, int K) {
+__global__ void k_w_khwc(const T* __restrict__ w, T* __restrict__ o, int Cout, int Cg, int K, int blocked) {
   const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
   if (i >= (int64_t)Cout * Cg * K * K) return;
-  int t = (int)i;
-  const int ci = t % Cg; t /= Cg;
-  const int kw = t % K; t /= K;
-  const int kh = t % K;
-  const int co = t / K;
+  int t = (int)i, ci, kh, kw, co;
+  if (blocked) {
+    const int c0 = t % GEMM_BK; t /= GEMM_BK;
+    kw = t % K; t /= K;
+    kh = t % K; t /= K;
+    const int nblk = Cg / GEMM_BK;
+    ci = (t % nblk) * GEMM_BK + c0;
+    co = t / nblk;
+  } else {
+    ci = t % Cg; t /= Cg;
+    kw = t % K; t /= K;
+    kh = t % K;
+    co = t / K;
+  }
   o[i] = w[(((int64_t)co * Cg + ci) * K + kh) * K + kw];
 }
 
+// Data-gradient weights: rows [g][ci], k over (flipped tap, output channel
+// col of the group) in the loader's order: k = (kh, kw, col), or with
+// `blocked` k = (col / 64, kh, kw, col % 64).
 template <typename T>
-__global__ void k_w_dgrad(const T* __restrict__ w, T* __restrict__ o, int G, int Cog, int Cig, int K) {
+__global__ void k_w_dgrad(const T* __restrict__ w, T* __restrict__ o, int G, int Cog, int Cig, int K,
+                          int blocked) {
   const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
   if (i >= (int64_t)G * Cig * K * K * Cog) return;
-  int t = (int)i;
-  const int col = t % Cog; t /= Cog;
-  const int kw = t % K; t /= K;
-  const int kh = t % K; t /= K;
+  int t = (int)i, col, kh, kw;
+  if (blocked) {
+    const int c0 = t % GEMM_BK; t /= GEMM_BK;
+    kw = t % K; t /= K;
+    kh = t % K; t /= K;
+    const int nblk = Cog / GEMM_BK;
+    col = (t % nblk) * GEMM_BK + c0; t /= nblk;
+  } else {
+    col = t % Cog; t /= Cog;
+    kw = t % K; t /= K;
+    kh = t % K; t /= K;
+  }
   const int ci = t % Cig;
   const int g = t / Cig;
   o[i] = w[((((int64_t)g * Cog + col) * Cig + ci) * K + (K - 1 - kh)) * K + (K - 1 - kw)];
 }
 
+bool im2col_blocked(DType dt, int Cg) { return dt == BF16 && Cg % GEMM_BK == 0; }
+
 hipError_t w_khwc(DType dt, const void* w, void* out, int Cout, int Cg, int K, hipStream_t st) {
   const dim3 g = grid1d((int64_t)Cout * Cg * K * K);
-  if (dt == BF16) hipLaunchKernelGGL((k_w_khwc<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, Cout, Cg, K);
-  else hipLaunchKernelGGL((k_w_khwc<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, Cout, Cg, K);
+  const int blk = im2col_blocked(dt, Cg) ? 1 : 0;
+  if (dt == BF16) hipLaunchKernelGGL((k_w_khwc<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, Cout, Cg, K, blk);
+  else hipLaunchKernelGGL((k_w_khwc<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, Cout, Cg, K, blk);
   return hipGetLastError();
 }
 hipError_t w_dgrad(DType dt, const void* w, void* out, int G, int Cog, int Cig, int K, hipStream_t st) {
   const dim3 g = grid1d((int64_t)G * Cig * K * K * Cog);
-  if (dt == BF16) hipLaunchKernelGGL((k_w_dgrad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, G, Cog, Cig, K);
-  else hipLaunchKernelGGL((k_w_dgrad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, G, Cog, Cig, K);
+  const int blk = im2col_blocked(dt, Cog) ? 1 : 0;
+  if (dt == BF16) hipLaunchKernelGGL((k_w_dgrad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, G, Cog, Cig, K, blk);
+  else hipLaunchKernelGGL((k_w_dgrad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, G, Cog, Cig, K, blk);
   return hipGetLastError();
 }
 
