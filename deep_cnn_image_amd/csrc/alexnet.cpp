@@ -107,8 +107,8 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
                   T(ALEXNET_KT_CONV4_FWD)));
   HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), st,
                   T(ALEXNET_KT_CONV5_FWD)));
-  HIPCHK(pool_fwd(dt, tp(ws, p, T_CONV5), tp(ws, p, T_POOL5), (uint8_t*)tp(ws, p, T_ARG5), N, 13, 13, 256, 1,
-                  st, T(ALEXNET_KT_POOL5_FWD)));
+  HIPCHK(pool5_fwd(dt, tp(ws, p, T_CONV5), tp(ws, p, T_POOL5), (uint8_t*)tp(ws, p, T_ARG5), N, 13, 13, 256, st,
+                   T(ALEXNET_KT_POOL5_FWD)));
 
   FcEpi ep{};
   ep.relu = 1;
@@ -172,8 +172,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       momentum[10], work[10], st, T(ALEXNET_KT_FC6_WGRAD)));
   HIPCHK(colsum(dt, tp(ws, p, T_DFC6), N, 4096, gb(5), cs, st));
   // pool5 backward * ReLU5'
-  HIPCHK(pool_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
-                  tp(ws, p, T_DCONV5), N, 13, 13, 256, 1, st, T(ALEXNET_KT_POOL5_BWD)));
+  HIPCHK(pool5_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
+                   tp(ws, p, T_DCONV5), N, 13, 13, 256, st, T(ALEXNET_KT_POOL5_BWD)));
   // conv5, conv4, conv3
   const int din[5] = {-1, T_DIN2, T_DIN3, T_DCONV3, T_DCONV4};
   const int dz[5] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5};

@@ -1014,56 +1014,72 @@ hipError_t pool_lrn_bwd(DType dt, const void* dy, const uint8_t* arg, const void
 // Overlapping max-pool 3x3 / stride 2, NHWC, with argmax (dy*3 + dx of the
 // first maximum in a row-major scan of the window)
 // =========================================================================
-template <typename T, bool FLAT>
-__global__ void k_pool_fwd(const T* __restrict__ x, T* __restrict__ y, uint8_t* __restrict__ arg, int N,
-                           int H, int W, int C, int Ho, int Wo) {
-  const int cpp = C >> 3;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (t >= (int64_t)N * Ho * Wo * cpp) return;
-  const int64_t pix = t / cpp;
-  const int c0 = (int)(t - pix * cpp) * 8;
-  const int wo = (int)(pix % Wo);
-  const int ho = (int)((pix / Wo) % Ho);
-  const int n = (int)(pix / ((int64_t)Wo * Ho));
-  float best[8], v[8];
-  uint32_t bi[8];
-  const T* base = x + (((int64_t)n * H + 2 * ho) * W + 2 * wo) * C + c0;
-  Pack8<T>::load(base, best);
+// Pool 5: max-pool whose output is flattened in (c, h, w) order for FC6.
+// One workgroup per (image n, 128-channel block): pooled values go to LDS as
+// [c][h*Wo+w], which is exactly the block's contiguous run of the flat output.
+constexpr int POOL5_CB = 128;   // channels per workgroup
+constexpr int POOL5_P = 64;     // max pooled positions (Ho * Wo)
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_pool5_fwd(const T* __restrict__ x, T* __restrict__ y,
+                                                   uint8_t* __restrict__ arg, int H, int W, int C, int Ho,
+                                                   int Wo) {
+  __shared__ __attribute__((aligned(16))) T ly[POOL5_CB * POOL5_P];
+  const int nblk = C / POOL5_CB, n = blockIdx.x / nblk, cb = blockIdx.x - n * nblk;
+  const int P = Ho * Wo, units = P * (POOL5_CB / 8);
+  for (int u = threadIdx.x; u < units; u += TPB) {
+    const int pos = u / (POOL5_CB / 8), ch8 = u - pos * (POOL5_CB / 8);
+    const int i = pos / Wo, j = pos - i * Wo, c0 = cb * POOL5_CB + ch8 * 8;
+    const T* base = x + (((size_t)n * H + 2 * i) * W + 2 * j) * C + c0;
+    float best[8], v[8];
+    uint32_t bi[8];
+    Pack8<T>::load(base, best);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bi[i] = 0;
+    for (int e = 0; e < 8; ++e) bi[e] = 0;
 #pragma unroll
-  for (int d = 1; d < 9; ++d) {
-    const int dy = d / 3, dx = d % 3;
-    Pack8<T>::load(base + ((int64_t)dy * W + dx) * C, v);
+    for (int d = 1; d < 9; ++d) {
+      const int dy = d / 3, dx = d % 3;
+      Pack8<T>::load(base + ((size_t)dy * W + dx) * C, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (v[i] > best[i]) { best[i] = v[i]; bi[i] = d; }
+      for (int e = 0; e < 8; ++e)
+        if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
+    }
+    *reinterpret_cast<uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0) =
+        make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
+                   bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ly[(ch8 * 8 + e) * P + pos] = Num<T>::store(best[e]);
   }
-  const uint32_t lo = bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24);
-  const uint32_t hi = bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24);
-  *reinterpret_cast<uint2*>(arg + pix * C + c0) = make_uint2(lo, hi);
-  if (FLAT) {
-    T* yo = y + (int64_t)n * C * Ho * Wo + ho * Wo + wo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) yo[(int64_t)(c0 + i) * Ho * Wo] = Num<T>::store(best[i]);
-  } else {
-    Pack8<T>::store(y + pix * C + c0, best);
-  }
+  __syncthreads();
+  // the block's run of the flat output: POOL5_CB * P elements, 16-byte chunks
+  T* out = y + (size_t)n * C * P + (size_t)cb * POOL5_CB * P;
+  constexpr int V = 16 / sizeof(T);
+  for (int q = threadIdx.x; q < POOL5_CB * P / V; q += TPB)
+    *reinterpret_cast<uint4*>(out + q * V) = *reinterpret_cast<const uint4*>(ly + q * V);
 }
 
-template <typename T, bool FLAT>
-__global__ void k_pool_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
-                           const T* __restrict__ mask, T* __restrict__ dx, int N, int H, int W, int C,
-                           int Ho, int Wo) {
-  const int cpp = C >> 3;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (t >= (int64_t)N * H * W * cpp) return;
-  const int64_t pix = t / cpp;
-  const int c0 = (int)(t - pix * cpp) * 8;
-  const int w = (int)(pix % W);
-  const int h = (int)((pix / W) % H);
-  const int n = (int)(pix / ((int64_t)W * H));
-  // windows (i, j) with 2i <= h <= 2i + 2 and 2j <= w <= 2j + 2
+// Pool-5 backward from the flat (c, h, w) gradient, times the ReLU mask of
+// the pool input [mask > 0]: one workgroup per (image n, 128-channel block,
+// input row h).  The block's run of the flat gradient is transposed into LDS
+// as [h*Wo+w][c]; each thread then sums, for one (column, 8-channel) unit, the
+// windows whose argmax is the pixel (windows in row-major order).
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_pool5_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
+                                                   const T* __restrict__ mask, T* __restrict__ dx, int H, int W,
+                                                   int C, int Ho, int Wo) {
+  constexpr int LS = POOL5_CB + 8;   // padded row: the transposing writes spread over banks
+  __shared__ __attribute__((aligned(16))) T lg[POOL5_P * LS];
+  const int nblk = C / POOL5_CB;
+  const int h = blockIdx.x % H, nc = blockIdx.x / H, n = nc / nblk, cb = nc - n * nblk;
+  const int P = Ho * Wo;
+  const T* src = dy + (size_t)n * C * P + (size_t)cb * POOL5_CB * P;
+  for (int e = threadIdx.x; e < POOL5_CB * P; e += TPB) {
+    const int c = e / P, pos = e - c * P;
+    lg[pos * LS + c] = src[e];
+  }
+  __syncthreads();
+  const int ch8 = threadIdx.x % (POOL5_CB / 8), w = threadIdx.x / (POOL5_CB / 8);
+  if (w >= W) return;
+  const int c0 = cb * POOL5_CB + ch8 * 8;
   const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
   const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
   float acc[8];
@@ -1072,59 +1088,49 @@ __global__ void k_pool_bwd(const T* __restrict__ dy, const uint8_t* __restrict__
   for (int i = i0; i <= i1; ++i)
     for (int j = j0; j <= j1; ++j) {
       const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
-      const int64_t op = ((int64_t)n * Ho + i) * Wo + j;
-      const uint2 am = *reinterpret_cast<const uint2*>(arg + op * C + c0);
+      const uint2 am = *reinterpret_cast<const uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0);
       float g[8];
-      if (FLAT) {
-        const T* gp = dy + (int64_t)n * C * Ho * Wo + i * Wo + j;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) g[q] = Num<T>::load(gp[(int64_t)(c0 + q) * Ho * Wo]);
-      } else {
-        Pack8<T>::load(dy + op * C + c0, g);
-      }
+      Pack8<T>::load(lg + (i * Wo + j) * LS + ch8 * 8, g);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
         if (b == code) acc[q] += g[q];
       }
     }
-  if (mask) {
-    float mk[8];
-    Pack8<T>::load(mask + pix * C + c0, mk);
+  const size_t o = (((size_t)n * H + h) * W + w) * C + c0;
+  float mk[8];
+  Pack8<T>::load(mask + o, mk);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
-  }
-  Pack8<T>::store(dx + pix * C + c0, acc);
+  for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
+  Pack8<T>::store(dx + o, acc);
 }
 
-hipError_t pool_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C, int flat,
-                    hipStream_t st, const KTimer* kt) {
-  const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
-  const dim3 g = grid1d((int64_t)N * Ho * Wo * (C / 8));
+static bool pool5_shape_ok(int H, int W, int C, int& Ho, int& Wo) {
+  Ho = (H - 3) / 2 + 1; Wo = (W - 3) / 2 + 1;
+  return C % POOL5_CB == 0 && Ho * Wo <= POOL5_P && W * (POOL5_CB / 8) <= TPB &&
+         (POOL5_CB * Ho * Wo) % 8 == 0;
+}
+
+hipError_t pool5_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C, hipStream_t st,
+                     const KTimer* kt) {
+  int Ho, Wo;
+  if (!pool5_shape_ok(H, W, C, Ho, Wo)) return hipErrorInvalidValue;
+  const dim3 g(N * (C / POOL5_CB));
   rec_start(kt, st);
-  if (dt == BF16) {
-    if (flat) hipLaunchKernelGGL((k_pool_fwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
-    else hipLaunchKernelGGL((k_pool_fwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, N, H, W, C, Ho, Wo);
-  } else {
-    if (flat) hipLaunchKernelGGL((k_pool_fwd<float, true>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
-    else hipLaunchKernelGGL((k_pool_fwd<float, false>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, N, H, W, C, Ho, Wo);
-  }
+  if (dt == BF16) hipLaunchKernelGGL((k_pool5_fwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)y, arg, H, W, C, Ho, Wo);
+  else hipLaunchKernelGGL((k_pool5_fwd<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)y, arg, H, W, C, Ho, Wo);
   rec_stop(kt, st);
   return hipGetLastError();
 }
 
-hipError_t pool_bwd(DType dt, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N, int H,
-                    int W, int C, int flat, hipStream_t st, const KTimer* kt) {
-  const int Ho = (H - 3) / 2 + 1, Wo = (W - 3) / 2 + 1;
-  const dim3 g = grid1d((int64_t)N * H * W * (C / 8));
+hipError_t pool5_bwd(DType dt, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N, int H,
+                     int W, int C, hipStream_t st, const KTimer* kt) {
+  int Ho, Wo;
+  if (!pool5_shape_ok(H, W, C, Ho, Wo) || !mask) return hipErrorInvalidValue;
+  const dim3 g(N * (C / POOL5_CB) * H);
   rec_start(kt, st);
-  if (dt == BF16) {
-    if (flat) hipLaunchKernelGGL((k_pool_bwd<bf16, true>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
-    else hipLaunchKernelGGL((k_pool_bwd<bf16, false>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, N, H, W, C, Ho, Wo);
-  } else {
-    if (flat) hipLaunchKernelGGL((k_pool_bwd<float, true>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
-    else hipLaunchKernelGGL((k_pool_bwd<float, false>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, N, H, W, C, Ho, Wo);
-  }
+  if (dt == BF16) hipLaunchKernelGGL((k_pool5_bwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, H, W, C, Ho, Wo);
+  else hipLaunchKernelGGL((k_pool5_bwd<float>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, H, W, C, Ho, Wo);
   rec_stop(kt, st);
   return hipGetLastError();
 }
@@ -1143,6 +1149,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int SOFTMAX_MAX_O = 1024;
 template <typename T, bool CE>
 __global__ void k_softmax(const float* __restrict__ z, const int32_t* __restrict__ labels,
                           float* __restrict__ p, T* __restrict__ dz, float* __restrict__ rowloss, int M,
@@ -1150,31 +1157,49 @@ __global__ void k_softmax(const float* __restrict__ z, const int32_t* __restrict
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
   if (row >= M) return;
+  // the row is read once into registers (O <= SOFTMAX_MAX_O)
   const float* zr = z + (int64_t)row * O;
+  float v[SOFTMAX_MAX_O / 64];
+#pragma unroll
+  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
+    const int i = lane + 64 * q;
+    v[q] = i < O ? zr[i] : -INFINITY;
+  }
   float mx = -INFINITY;
-  for (int i = lane; i < O; i += 64) mx = fmaxf(mx, zr[i]);
+#pragma unroll
+  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) mx = fmaxf(mx, v[q]);
   mx = wave_max(mx);
   float s = 0.f;
-  for (int i = lane; i < O; i += 64) s += expf(zr[i] - mx);
+#pragma unroll
+  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
+    v[q] = lane + 64 * q < O ? expf(v[q] - mx) : 0.f;
+    s += v[q];
+  }
   s = wave_sum(s);
   const float inv = 1.f / s;
   int y = 0;
   if (CE) { y = labels[row]; y = y < 0 ? 0 : (y >= O ? O - 1 : y); }
-  for (int i = lane; i < O; i += 64) {
-    const float pi = expf(zr[i] - mx) * inv;
-    if (p) p[(int64_t)row * O + i] = pi;
-    if (CE) dz[(int64_t)row * O + i] = Num<T>::store((pi - (i == y ? 1.f : 0.f)) / (float)M);
+#pragma unroll
+  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
+    const int i = lane + 64 * q;
+    if (i < O) {
+      const float pi = v[q] * inv;
+      if (p) p[(int64_t)row * O + i] = pi;
+      if (CE) dz[(int64_t)row * O + i] = Num<T>::store((pi - (i == y ? 1.f : 0.f)) / (float)M);
+    }
   }
   if (CE && lane == 0) rowloss[row] = -(zr[y] - mx - logf(s));
 }
 
 hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t st) {
+  if (O > SOFTMAX_MAX_O) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_softmax<float, false>), dim3(cdiv(M, TPB / 64)), dim3(TPB), 0, st, z,
                      (const int32_t*)nullptr, p, (float*)nullptr, (float*)nullptr, M, O);
   return hipGetLastError();
 }
 hipError_t softmax_ce(DType dt, const float* z, const int32_t* labels, float* p, void* dz, float* rowloss,
                       int M, int O, hipStream_t st) {
+  if (O > SOFTMAX_MAX_O) return hipErrorInvalidValue;
   const dim3 g(cdiv(M, TPB / 64));
   if (dt == BF16) hipLaunchKernelGGL((k_softmax<bf16, true>), g, dim3(TPB), 0, st, z, labels, p, (bf16*)dz, rowloss, M, O);
   else hipLaunchKernelGGL((k_softmax<float, true>), g, dim3(TPB), 0, st, z, labels, p, (float*)dz, rowloss, M, O);
@@ -1214,22 +1239,26 @@ hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t st) {
 }
 
 // =========================================================================
-// Column sums (bias gradients) of a [rows][C] matrix, C % 8 == 0.  Pass 1:
-// block b sums its contiguous row range; each thread owns one 8-column chunk
-// and a fixed subset of the rows, and the block combines those in a fixed
-// order.  Pass 2: one wavefront per column adds the per-block partials with a
-// fixed butterfly.  No atomics: the result does not depend on timing.
+// Column sums
 // =========================================================================
-static constexpr int COLSUM_CW = 2048;   // columns per block (256 chunks of 8)
-
-static int colsum_blocks(int64_t rows) {
-  int64_t rb = (rows + 511) / 512;
-  if (rb < 32) rb = 32;
-  return (int)((rows + rb - 1) / rb);
+// Column sums of a row-major [rows][C] tensor (bias gradients: sum of dY over
+// all pixels of the batch), in fp32, deterministic: block (b, j) sums rows
+// [b*rb, (b+1)*rb) of columns [j*512, (j+1)*512) -- each thread a run of 8
+// columns over every L-th row, L = 256 / (columns / 8), four rows in flight --
+// and combines its L partial sums in a fixed order.  With one row block the
+// result goes straight to `out`; otherwise a second pass adds the row blocks
+// in order.
+static constexpr int COLSUM_CW = 512;
+static int colsum_blocks(int64_t rows, int C) {
+  const int ct = cdiv(C, COLSUM_CW);
+  int64_t nb = (1024 + ct - 1) / ct;                 // about 1024 workgroups
+  nb = std::min<int64_t>(nb, (rows + 15) / 16);      // at least 16 rows per block
+  return (int)std::max<int64_t>(nb, 1);
 }
 
 template <typename T>
-__global__ void k_colsum1(const T* __restrict__ x, int64_t rows, int C, int64_t rb, float* __restrict__ part) {
+__global__ void __launch_bounds__(TPB) k_colsum1(const T* __restrict__ x, int64_t rows, int C, int64_t rb,
+                                                 float* __restrict__ part) {
   __shared__ float sh[TPB][9];
   const int c0 = blockIdx.y * COLSUM_CW;
   const int w = min(COLSUM_CW, C - c0);
@@ -1240,9 +1269,20 @@ __global__ void k_colsum1(const T* __restrict__ x, int64_t rows, int C, int64_t 
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   if (rl < nrl) {
-    for (int64_t r = r0 + rl; r < r1; r += nrl) {
+    const T* base = x + c0 + cc * 8;
+    int64_t r = r0 + rl;
+    for (; r + 3 * nrl < r1; r += 4 * nrl) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Pack8<T>::load(base + (r + u * nrl) * C, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+    }
+    for (; r < r1; r += nrl) {
       float v[8];
-      Pack8<T>::load(x + r * C + c0 + cc * 8, v);
+      Pack8<T>::load(base + r * C, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
@@ -1270,17 +1310,18 @@ __global__ void k_colsum2(const float* __restrict__ part, int nb, int C, float* 
 }
 
 size_t colsum_scratch_bytes(int64_t rows, int C) {
-  return (size_t)colsum_blocks(rows) * C * sizeof(float);
+  return (size_t)colsum_blocks(rows, C) * C * sizeof(float);
 }
 
 hipError_t colsum(DType dt, const void* x, int64_t rows, int C, float* out, float* scratch, hipStream_t st) {
   if (C % 8) return hipErrorInvalidValue;
-  const int nb = colsum_blocks(rows);
+  const int nb = colsum_blocks(rows, C);
   const int64_t rb = (rows + nb - 1) / nb;
   const dim3 g1(nb, cdiv(C, COLSUM_CW));
-  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, rb, scratch);
-  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, rb, scratch);
-  hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB / 64)), dim3(TPB), 0, st, scratch, nb, C, out);
+  float* dst = nb == 1 ? out : scratch;
+  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, rb, dst);
+  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, rb, dst);
+  if (nb > 1) hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB / 64)), dim3(TPB), 0, st, scratch, nb, C, out);
   return hipGetLastError();
 }
 

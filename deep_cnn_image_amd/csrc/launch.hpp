@@ -109,13 +109,12 @@ hipError_t pool_lrn_bwd(DType, const void* dy, const uint8_t* arg, const void* a
                         int H, int W, int C, float k, float alpha, float beta, int n, hipStream_t,
                         const KTimer* kt = nullptr);
 // 3x3/s2 max-pool; flat_out: y written [N][C*Ho*Wo] in (c,h,w) order
-hipError_t pool_fwd(DType, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C,
-                    int flat_out, hipStream_t,
-                      const KTimer* kt = nullptr);
-// gather-form backward; flat_dy: dy is [N][C*Ho*Wo] in (c,h,w) order; mask optional
-hipError_t pool_bwd(DType, const void* dy, const uint8_t* arg, const void* mask, void* dx, int N,
-                    int H, int W, int C, int flat_dy, hipStream_t,
-                      const KTimer* kt = nullptr);
+// Pool 5 (3x3 / stride 2) with its output flattened in (c, h, w) order for
+// FC6, and its backward times the ReLU mask of the pool input.  C % 128 == 0.
+hipError_t pool5_fwd(DType, const void* x, void* y_flat, uint8_t* arg, int N, int H, int W, int C, hipStream_t,
+                     const KTimer* kt = nullptr);
+hipError_t pool5_bwd(DType, const void* dy_flat, const uint8_t* arg, const void* mask, void* dx, int N, int H,
+                     int W, int C, hipStream_t, const KTimer* kt = nullptr);
 
 // ---- softmax, loss, ten-view mean, column sums
 hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t);
