@@ -29,17 +29,18 @@ CONV = {  # name: (Cin, Cout, k, Ho, grouped)
     "CONV1": (3, 96, 11, 55, False), "CONV2": (96, 256, 5, 27, True), "CONV3": (256, 384, 3, 13, False),
     "CONV4": (384, 384, 3, 13, True), "CONV5": (384, 256, 3, 13, True),
 }
-N_PARAMS_SINGLE = 62_378_344
 FC = {"FC6": (9216, 4096), "FC7": (4096, 4096), "FC8": (4096, 1000)}
-# tensors the stand-alone SGD kernel updates: conv weights and all 16 biases
-# (the FC weights are updated inside their weight-gradient GEMM)
-SGD_ELEMS = N_PARAMS_SINGLE - sum(fin * fout for fin, fout in FC.values())
 
 
 def conv_flops(name, n, groups):
     cin, cout, k, ho, grouped = CONV[name]
     g = groups if grouped else 1
     return 2.0 * cout * (cin // g) * k * k * n * ho * ho
+
+
+def conv_wcount(name, groups):
+    cin, cout, k, _, grouped = CONV[name]
+    return cout * (cin // (groups if grouped else 1)) * k * k
 
 
 def kernel_work(kt, n, groups):
@@ -71,7 +72,16 @@ def kernel_work(kt, n, groups):
         "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"],
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
-        "SGD": 22 * SGD_ELEMS,
+        # the stand-alone SGD kernel updates the conv weights only (FC weights are
+        # updated inside their weight-gradient GEMM, biases with their gradient)
+        "SGD": 22 * sum(conv_wcount(c, groups) for c in CONV),
+        # bias gradients: every layer's output gradient read once (the partial
+        # sums and the 22 B per bias of the update are below 0.1%)
+        "BIAS": e * (act["55x96"] + act["27x256"] + 2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
+        # weight re-layouts of a training step: each OIHW source read once; the
+        # layer-1 block layout, and the forward and data-gradient copies of
+        # conv2..5, written once
+        "WPREP": e * (96 * 3 * 11 * 11 + 96 * 432 + 3 * sum(conv_wcount(c, groups) for c in CONV if c != "CONV1")),
     }
     return "hbm", float(table[kt])
 

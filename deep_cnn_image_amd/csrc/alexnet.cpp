@@ -81,11 +81,20 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   const int N = p.N;
   const alexnet_cfg& c = p.cfg;
 
-  // weights into the layouts the GEMM loaders read
-  HIPCHK(conv1_w_s2d(dt, prm[0], at(ws, p.w1s), st));
-  for (int i = 1; i < 5; ++i) {
-    const ConvShape& s = net.conv[i];
-    HIPCHK(w_khwc(dt, prm[2 * i], at(ws, p.wr[i]), s.Cout, s.Cin / s.groups, s.K, st));
+  // weights into the layouts the GEMM loaders read (for a training step also
+  // the data-gradient layouts of the backward pass), one launch
+  {
+    WeightPrep jobs[WPREP_MAX];
+    int nj = 0;
+    jobs[nj++] = WeightPrep{WPREP_W1S, prm[0], at(ws, p.w1s), 96, 3, 11, 1};
+    for (int i = 1; i < 5; ++i) {
+      const ConvShape& s = net.conv[i];
+      jobs[nj++] = WeightPrep{WPREP_KHWC, prm[2 * i], at(ws, p.wr[i]), s.Cout, s.Cin / s.groups, s.K, s.groups};
+      if (train)
+        jobs[nj++] =
+            WeightPrep{WPREP_DGRAD, prm[2 * i], at(ws, p.wt[i]), s.Cout, s.Cin / s.groups, s.K, s.groups};
+    }
+    HIPCHK(prep_weights(dt, jobs, nj, st, T(ALEXNET_KT_WPREP)));
   }
 
   const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
@@ -149,28 +158,21 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   auto gw = [&](int i) { return (float*)tp(ws, p, T_GW1 + i); };
   auto gb = [&](int i) { return (float*)tp(ws, p, T_GB1 + i); };
 
-  for (int i = 1; i < 5; ++i) {
-    const ConvShape& s = net.conv[i];
-    HIPCHK(w_dgrad(dt, work[2 * i], at(ws, p.wt[i]), s.groups, s.Cout / s.groups, s.Cin / s.groups, s.K, st));
-  }
   // FC8: dh7 = dz W8 * [drop7 > 0]   (drop7 > 0 <=> kept and ReLU active)
   HIPCHK(fc_dgrad(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), work[14], tp(ws, p, T_DROP7), tp(ws, p, T_DFC7),
                   part, p.part_bytes, st, T(ALEXNET_KT_FC8_DGRAD)));
   HIPCHK(fc_wgrad_sgd(dt, N, 4096, 1000, tp(ws, p, T_DLOGITS), tp(ws, p, T_DROP7), hy, master[14],
                       momentum[14], work[14], st, T(ALEXNET_KT_FC8_WGRAD)));
-  HIPCHK(colsum(dt, tp(ws, p, T_DLOGITS), N, 1000, gb(7), cs, st));
   // FC7
   HIPCHK(fc_dgrad(dt, N, 4096, 4096, tp(ws, p, T_DFC7), work[12], tp(ws, p, T_DROP6), tp(ws, p, T_DFC6),
                   part, p.part_bytes, st, T(ALEXNET_KT_FC7_DGRAD)));
   HIPCHK(fc_wgrad_sgd(dt, N, 4096, 4096, tp(ws, p, T_DFC7), tp(ws, p, T_DROP6), hy, master[12],
                       momentum[12], work[12], st, T(ALEXNET_KT_FC7_WGRAD)));
-  HIPCHK(colsum(dt, tp(ws, p, T_DFC7), N, 4096, gb(6), cs, st));
   // FC6 -> gradient w.r.t. the flattened pool5 output
   HIPCHK(fc_dgrad(dt, N, 9216, 4096, tp(ws, p, T_DFC6), work[10], nullptr, tp(ws, p, T_DFLAT), part,
                   p.part_bytes, st, T(ALEXNET_KT_FC6_DGRAD)));
   HIPCHK(fc_wgrad_sgd(dt, N, 9216, 4096, tp(ws, p, T_DFC6), tp(ws, p, T_POOL5), hy, master[10],
                       momentum[10], work[10], st, T(ALEXNET_KT_FC6_WGRAD)));
-  HIPCHK(colsum(dt, tp(ws, p, T_DFC6), N, 4096, gb(5), cs, st));
   // pool5 backward * ReLU5'
   HIPCHK(pool5_bwd(dt, tp(ws, p, T_DFLAT), (const uint8_t*)tp(ws, p, T_ARG5), tp(ws, p, T_CONV5),
                    tp(ws, p, T_DCONV5), N, 13, 13, 256, st, T(ALEXNET_KT_POOL5_BWD)));
@@ -186,7 +188,6 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), st, T(ktw[i])));
-    HIPCHK(colsum(dt, tp(ws, p, dz[i]), (int64_t)N * s.Ho * s.Wo, s.Cout, gb(i), cs, st));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
                       tp(ws, p, din[i]), st, T(ktd[i])));
   }
@@ -198,7 +199,6 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
     const ConvShape& s = net.conv[1];
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st,
                       T(ALEXNET_KT_CONV2_WGRAD)));
-    HIPCHK(colsum(dt, tp(ws, p, T_DCONV2), (int64_t)N * 27 * 27, 256, gb(1), cs, st));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st,
                       T(ALEXNET_KT_CONV2_DGRAD)));
   }
@@ -208,7 +208,17 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
   HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st,
                      T(ALEXNET_KT_CONV1_WGRAD)));
-  HIPCHK(colsum(dt, tp(ws, p, T_DCONV1), (int64_t)N * 55 * 55, 96, gb(0), cs, st));
+  // bias gradients of all eight layers, and their SGD update
+  {
+    const int dys[8] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5, T_DFC6, T_DFC7, T_DLOGITS};
+    BiasJob jobs[8];
+    for (int i = 0; i < 8; ++i) {
+      const int64_t rows = i < 5 ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo : N;
+      jobs[i] = BiasJob{tp(ws, p, dys[i]), rows, (int)net.bcount[i], gb(i), master[2 * i + 1],
+                        momentum[2 * i + 1], work[2 * i + 1]};
+    }
+    HIPCHK(bias_grads_sgd(dt, jobs, 8, hy, cs, st, T(ALEXNET_KT_BIAS)));
+  }
   return ALEXNET_OK;
 }
 
@@ -310,7 +320,7 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
   if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
   const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
   if ((r = enqueue_backward(p, work, master, momentum, hy, ws, st, T)) != ALEXNET_OK) return r;
-  // the remaining tensors: conv weights and all biases (FC weights are done)
+  // the remaining tensors: conv weights (FC weights and all biases are done)
   TensorSet ts;
   for (int i = 0; i < 8; ++i) {
     const bool fused = i >= 5;
@@ -323,7 +333,7 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
     ts.work[2 * i] = work[2 * i];
     ts.work[2 * i + 1] = work[2 * i + 1];
     ts.n[2 * i] = fused ? 0 : p.net.wcount[i];
-    ts.n[2 * i + 1] = p.net.bcount[i];
+    ts.n[2 * i + 1] = 0;
   }
   if (sgd(dt, ts, lr, momentum_coef, weight_decay, st, T(ALEXNET_KT_SGD)) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;

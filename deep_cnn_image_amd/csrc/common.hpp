@@ -13,11 +13,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16 h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest, ties to even: gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32), one per pair in f2bf2.
+__device__ __forceinline__ bf16 f2bf(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
+// two floats -> a packed bf16 pair, a in the low half
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // One SGD-with-momentum step on an element (paper form, lr inside v):
@@ -54,7 +58,7 @@ template <> struct Pack8<bf16> {
   static __device__ __forceinline__ void store(bf16* p, const float* v) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = f2bf2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };

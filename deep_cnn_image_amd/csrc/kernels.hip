@@ -71,67 +71,80 @@ __device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, i
   flip = v >= 5;
 }
 
-// One workgroup per (image, block row): stage the 12 input rows (3 channels x
-// 4 rows, 228 columns with the last one zero) in LDS, then write the 57 x 48
-// values of the block row contiguously.  Ten-view mode: image n is view n % 10
-// of source n / 10 (227x227 crop at the view's offset, mirrored for views 5..9).
+// One workgroup per (image, block row).  The 12 input rows it needs (3
+// channels x 4 rows) are copied into LDS as whole 16-byte chunks: image rows
+// start at any element (227 is odd), so each row's copy begins at the chunk
+// boundary below its first element and the row sits in LDS at that shift.
+// The 57 x 48 values of the block row are then written as 16-byte runs.
+// Ten-view mode: image n is view n % 10 of source n / 10 (227x227 crop at the
+// view's offset, mirrored for views 5..9).  `total` is the element count of x;
+// a chunk that would cross its end is read element by element.
 template <typename T>
-__global__ void k_s2d(const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws, int tenview) {
-  __shared__ T rows[12][228];
+__global__ void __launch_bounds__(TPB) k_s2d(const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws,
+                                             int tenview, int64_t total) {
+  constexpr int V = 16 / (int)sizeof(T);                // elements per chunk
+  constexpr int RCH = (V + 225) / V + 1;                // chunks per staged row (span of 227 at shift < V)
+  constexpr int RS = RCH * V;                           // LDS row stride, elements
+  __shared__ __attribute__((aligned(16))) T rows[12 * RS];
+  __shared__ int shift[12];
   const int n = blockIdx.x / S2D_B, bh = blockIdx.x - n * S2D_B;
   int y0 = 0, x0 = 0, flip = 0;
-  const T* img;
+  int64_t img;
   if (tenview) {
     tenview_offset(n % 10, Hs - 227, y0, x0, flip);
-    img = x + (int64_t)(n / 10) * 3 * Hs * Ws;
+    img = (int64_t)(n / 10) * 3 * Hs * Ws;
   } else {
-    img = x + (int64_t)n * 3 * Hs * Ws;
+    img = (int64_t)n * 3 * Hs * Ws;
   }
-  for (int i = threadIdx.x; i < 12 * 228; i += TPB) {
-    const int r = i / 228, xc = i - r * 228;
+  for (int i = threadIdx.x; i < 12 * RCH; i += TPB) {
+    const int r = i / RCH, ch = i - r * RCH;
     const int c = r >> 2, yc = 4 * bh + (r & 3);
-    T v = T(0);
-    if (yc < 227 && xc < 227) {
-      const int sx = flip ? x0 + 226 - xc : x0 + xc;
-      v = img[((int64_t)c * Hs + y0 + yc) * Ws + sx];
+    if (yc >= 227) continue;                             // below the image: never read
+    const int64_t first = img + ((int64_t)c * Hs + y0 + yc) * Ws + x0;   // element of column 0
+    const int64_t e0 = (first & ~(int64_t)(V - 1)) + (int64_t)ch * V;
+    if (ch == 0) shift[r] = (int)(first & (V - 1));
+    if (e0 > first + 226) continue;                      // past the row's last chunk
+    uint4 q;
+    if (e0 + V <= total) {
+      q = *reinterpret_cast<const uint4*>(x + e0);
+    } else {
+      T e[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) e[j] = e0 + j < total ? x[e0 + j] : T(0);
+      q = pack_u4(e);
     }
-    rows[r][xc] = v;
+    *reinterpret_cast<uint4*>(rows + r * RS + ch * V) = q;
   }
   __syncthreads();
   T* out = xs + (int64_t)blockIdx.x * S2D_B * S2D_C;
-  for (int i = threadIdx.x; i < S2D_B * S2D_C; i += TPB) {
-    const int bw = i / S2D_C, q = i - bw * S2D_C;
-    const int c = q >> 4, dh = (q >> 2) & 3, dw = q & 3;
-    out[i] = rows[c * 4 + dh][4 * bw + dw];
+  for (int i = threadIdx.x; i < S2D_B * S2D_C / V; i += TPB) {
+    const int bw = (i * V) / S2D_C, q0 = i * V - bw * S2D_C;
+    T e[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int q = q0 + j, c = q >> 4, dh = (q >> 2) & 3, dw = q & 3;
+      const int r = c * 4 + dh, yc = 4 * bh + dh, xc = 4 * bw + dw;
+      T v = T(0);
+      if (yc < 227 && xc < 227) v = rows[r * RS + shift[r] + (flip ? 226 - xc : xc)];
+      e[j] = v;
+    }
+    *reinterpret_cast<uint4*>(out + i * V) = pack_u4(e);
   }
-}
-
-template <typename T>
-__global__ void k_w1_s2d(const T* __restrict__ w, T* __restrict__ o) {
-  const int i = blockIdx.x * TPB + threadIdx.x;
-  if (i >= 96 * S2D_K) return;
-  const int co = i / S2D_K, r = i - co * S2D_K;
-  const int tap = r / S2D_C, q = r - tap * S2D_C;
-  const int kh = (tap / 3) * 4 + ((q >> 2) & 3), kw = (tap % 3) * 4 + (q & 3), c = q >> 4;
-  o[i] = (kh < 11 && kw < 11) ? w[((co * 3 + c) * 11 + kh) * 11 + kw] : T(0);
 }
 
 hipError_t conv1_s2d(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs,
                      hipStream_t st, const KTimer* kt) {
   const dim3 g(Nimg * S2D_B);
+  const int64_t total = (int64_t)(tenview ? Nimg / 10 : Nimg) * 3 * Hs * Ws;
   rec_start(kt, st);
-  if (dt == BF16) hipLaunchKernelGGL((k_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview);
-  else hipLaunchKernelGGL((k_s2d<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)xs, Hs, Ws, tenview);
+  if (dt == BF16)
+    hipLaunchKernelGGL((k_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview, total);
+  else
+    hipLaunchKernelGGL((k_s2d<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)xs, Hs, Ws, tenview, total);
   rec_stop(kt, st);
   return hipGetLastError();
 }
 
-hipError_t conv1_w_s2d(DType dt, const void* w, void* out, hipStream_t st) {
-  const dim3 g = grid1d(96 * S2D_K);
-  if (dt == BF16) hipLaunchKernelGGL((k_w1_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out);
-  else hipLaunchKernelGGL((k_w1_s2d<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out);
-  return hipGetLastError();
-}
 
 static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
 
@@ -588,68 +601,119 @@ hipError_t fc_wgrad_sgd(DType dt, int M, int K, int O, const void* dy, const voi
 // =========================================================================
 // Weight re-layouts
 // =========================================================================
-// Forward weights [co][ci][kh][kw] -> GEMM rows [co][k] in the loader's k order:
-// k = (kh, kw, ci), or with `blocked` k = (ci / 64, kh, kw, ci % 64).
-template <typename T>
-__global__ void k_w_khwc(const T* __restrict__ w, T* __restrict__ o, int Cout, int Cg, int K, int blocked) {
-  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (i >= (int64_t)Cout * Cg * K * K) return;
-  int t = (int)i, ci, kh, kw, co;
-  if (blocked) {
-    const int c0 = t % GEMM_BK; t /= GEMM_BK;
-    kw = t % K; t /= K;
-    kh = t % K; t /= K;
-    const int nblk = Cg / GEMM_BK;
-    ci = (t % nblk) * GEMM_BK + c0;
-    co = t / nblk;
-  } else {
-    ci = t % Cg; t /= Cg;
-    kw = t % K; t /= K;
-    kh = t % K;
-    co = t / K;
-  }
-  o[i] = w[(((int64_t)co * Cg + ci) * K + kh) * K + kw];
-}
+// All in one launch.  Jobs:
+//   W1S    layer 1 over 4x4 pixel blocks: W'[co][kh'][kw'][c*16+dh*4+dw] =
+//          W[co][c][4kh'+dh][4kw'+dw], zero where 4kh'+dh or 4kw'+dw >= 11;
+//          one output element per thread;
+//   KHWC   forward rows [co], k = (tap, ci), or with `blocked`
+//          k = (ci / 64, tap, ci % 64), tap = kh*K + kw; one thread per source
+//          row (co, ci) of K*K taps, consecutive threads on consecutive ci;
+//   DGRAD  data-gradient rows [g][ci], k over (flipped tap, output channel col
+//          of the group): k = (tap, col), or with `blocked`
+//          k = (col / 64, tap, col % 64); one thread per (g, ci, col),
+//          consecutive threads on consecutive col.
+// Stores of neighbouring threads are therefore contiguous in every job.
+struct PrepArgs {
+  const void* src[WPREP_MAX];
+  void* dst[WPREP_MAX];
+  int kind[WPREP_MAX], Cog[WPREP_MAX], Cig[WPREP_MAX], K[WPREP_MAX], blocked[WPREP_MAX], count[WPREP_MAX];
+  int bstart[WPREP_MAX + 1];   // first block of each job
+  int n;
+};
 
-// Data-gradient weights: rows [g][ci], k over (flipped tap, output channel
-// col of the group) in the loader's order: k = (kh, kw, col), or with
-// `blocked` k = (col / 64, kh, kw, col % 64).
 template <typename T>
-__global__ void k_w_dgrad(const T* __restrict__ w, T* __restrict__ o, int G, int Cog, int Cig, int K,
-                          int blocked) {
-  const int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  if (i >= (int64_t)G * Cig * K * K * Cog) return;
-  int t = (int)i, col, kh, kw;
-  if (blocked) {
-    const int c0 = t % GEMM_BK; t /= GEMM_BK;
-    kw = t % K; t /= K;
-    kh = t % K; t /= K;
-    const int nblk = Cog / GEMM_BK;
-    col = (t % nblk) * GEMM_BK + c0; t /= nblk;
-  } else {
-    col = t % Cog; t /= Cog;
-    kw = t % K; t /= K;
-    kh = t % K; t /= K;
+__global__ void __launch_bounds__(TPB) k_prep_weights(PrepArgs a) {
+  const int bid = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < WPREP_MAX; ++q) j += (q < a.n && bid >= a.bstart[q]) ? 1 : 0;
+  const int i = (bid - a.bstart[j]) * TPB + threadIdx.x;
+  if (i >= a.count[j]) return;
+  const T* __restrict__ src = static_cast<const T*>(a.src[j]);
+  T* __restrict__ dst = static_cast<T*>(a.dst[j]);
+  const int kind = a.kind[j];
+  if (kind == WPREP_W1S) {
+    const int co = i / S2D_K, r = i - co * S2D_K;
+    const int tap = r / S2D_C, q = r - tap * S2D_C;
+    const int kh = (tap / 3) * 4 + ((q >> 2) & 3), kw = (tap % 3) * 4 + (q & 3), c = q >> 4;
+    dst[i] = (kh < 11 && kw < 11) ? src[((co * 3 + c) * 11 + kh) * 11 + kw] : T(0);
+    return;
   }
-  const int ci = t % Cig;
-  const int g = t / Cig;
-  o[i] = w[((((int64_t)g * Cog + col) * Cig + ci) * K + (K - 1 - kh)) * K + (K - 1 - kw)];
+  const int K = a.K[j], KK = K * K, blocked = a.blocked[j];
+  if (kind == WPREP_KHWC) {
+    const int Cg = a.Cig[j];
+    const int co = i / Cg, ci = i - co * Cg;
+    const T* s = src + (int64_t)i * KK;                      // W[co][ci][.][.]
+    int64_t o, ostep;
+    if (blocked) {
+      o = ((int64_t)(co * (Cg / GEMM_BK) + ci / GEMM_BK) * KK) * GEMM_BK + (ci % GEMM_BK);
+      ostep = GEMM_BK;
+    } else {
+      o = (int64_t)co * KK * Cg + ci;
+      ostep = Cg;
+    }
+    for (int tap = 0; tap < KK; ++tap) dst[o + tap * ostep] = s[tap];
+    return;
+  }
+  // DGRAD
+  const int Cog = a.Cog[j], Cig = a.Cig[j];
+  const int col = i % Cog, rest = i / Cog, ci = rest % Cig, g = rest / Cig;
+  const T* s = src + ((int64_t)(g * Cog + col) * Cig + ci) * KK;   // W[g*Cog+col][ci][.][.]
+  int64_t o, ostep;
+  if (blocked) {
+    o = ((int64_t)((g * Cig + ci) * (Cog / GEMM_BK) + col / GEMM_BK) * KK) * GEMM_BK + (col % GEMM_BK);
+    ostep = GEMM_BK;
+  } else {
+    o = (int64_t)(g * Cig + ci) * KK * Cog + col;
+    ostep = Cog;
+  }
+  // output tap (kh, kw) takes the flipped source tap (K-1-kh, K-1-kw): KK-1-tap
+  for (int tap = 0; tap < KK; ++tap) dst[o + tap * ostep] = s[KK - 1 - tap];
 }
 
 bool im2col_blocked(DType dt, int Cg) { return dt == BF16 && Cg % GEMM_BK == 0; }
 
-hipError_t w_khwc(DType dt, const void* w, void* out, int Cout, int Cg, int K, hipStream_t st) {
-  const dim3 g = grid1d((int64_t)Cout * Cg * K * K);
-  const int blk = im2col_blocked(dt, Cg) ? 1 : 0;
-  if (dt == BF16) hipLaunchKernelGGL((k_w_khwc<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, Cout, Cg, K, blk);
-  else hipLaunchKernelGGL((k_w_khwc<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, Cout, Cg, K, blk);
-  return hipGetLastError();
-}
-hipError_t w_dgrad(DType dt, const void* w, void* out, int G, int Cog, int Cig, int K, hipStream_t st) {
-  const dim3 g = grid1d((int64_t)G * Cig * K * K * Cog);
-  const int blk = im2col_blocked(dt, Cog) ? 1 : 0;
-  if (dt == BF16) hipLaunchKernelGGL((k_w_dgrad<bf16>), g, dim3(TPB), 0, st, (const bf16*)w, (bf16*)out, G, Cog, Cig, K, blk);
-  else hipLaunchKernelGGL((k_w_dgrad<float>), g, dim3(TPB), 0, st, (const float*)w, (float*)out, G, Cog, Cig, K, blk);
+hipError_t prep_weights(DType dt, const WeightPrep* jobs, int n, hipStream_t st, const KTimer* kt) {
+  if (n < 1 || n > WPREP_MAX) return hipErrorInvalidValue;
+  PrepArgs a = {};
+  a.n = n;
+  int blocks = 0;
+  for (int j = 0; j < n; ++j) {
+    const WeightPrep& w = jobs[j];
+    int64_t count;
+    a.src[j] = w.src;
+    a.dst[j] = w.dst;
+    a.kind[j] = w.kind;
+    a.K[j] = w.K;
+    switch (w.kind) {
+      case WPREP_W1S:
+        count = (int64_t)S2D_W_ELEMS;
+        break;
+      case WPREP_KHWC:   // Cig = input channels per group; one thread per (co, ci)
+        a.Cig[j] = w.Cig;
+        a.blocked[j] = im2col_blocked(dt, w.Cig) ? 1 : 0;
+        count = (int64_t)w.Cout * w.Cig;
+        break;
+      case WPREP_DGRAD:  // one thread per (g, ci, col)
+        if (w.G < 1 || w.Cout % w.G) return hipErrorInvalidValue;
+        a.Cog[j] = w.Cout / w.G;
+        a.Cig[j] = w.Cig;
+        a.blocked[j] = im2col_blocked(dt, a.Cog[j]) ? 1 : 0;
+        count = (int64_t)w.Cout * w.Cig;
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    if (count > (int64_t)1 << 30) return hipErrorInvalidValue;
+    a.count[j] = (int)count;
+    a.bstart[j] = blocks;
+    blocks += (int)cdiv(count, TPB);
+  }
+  a.bstart[n] = blocks;
+  rec_start(kt, st);
+  if (dt == BF16) hipLaunchKernelGGL((k_prep_weights<bf16>), dim3(blocks), dim3(TPB), 0, st, a);
+  else hipLaunchKernelGGL((k_prep_weights<float>), dim3(blocks), dim3(TPB), 0, st, a);
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -725,7 +789,7 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
   constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho;
   static_assert(3 * Win * C <= LRNPOOL_LDS && C % 8 == 0, "fused LRN/pool geometry");
   static_assert(3 * Win * C / 8 <= LRNPOOL_UPT * LRNPOOL_TPB, "units per thread");
-  constexpr int LDS_BYTES = ((LRNPOOL_LDS * (int)sizeof(T) + 1023) / 1024) * 1024;
+  constexpr int LDS_BYTES = ((3 * Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   T* rows = reinterpret_cast<T*>(lds);
   const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
@@ -839,28 +903,33 @@ __device__ __forceinline__ void lrn_bwd8(const float* av, const float* gv, float
 }
 
 // Max-pool backward (3x3 / stride 2, argmax codes dy*3+dx) for channels
-// c0 .. c0+7 of input pixel (n, h, w): the sum, over the windows (i, j) that
-// contain the pixel and whose argmax is it, of dy[n][i][j] -- windows in
-// row-major order -- rounded to T as a stored gradient would be.
-template <typename T>
-__device__ __forceinline__ void pool_bwd8(const T* __restrict__ dy, const uint8_t* __restrict__ arg, int n, int h,
-                                          int w, int c0, int C, int Ho, int Wo, float* out) {
-  const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
+// c0 .. c0+7 of input pixel (h, w): the sum, over the windows (i, j) that
+// contain the pixel and whose argmax is it, of dy[i][j] -- windows in
+// row-major order -- rounded to T as a stored gradient would be.  dyL / argL
+// hold pooled rows ilo .. ihi of the image (at most two), [row][j][c].
+template <typename T, int C>
+__device__ __forceinline__ void pool_bwd8_lds(const T* dyL, const uint8_t* argL, int h, int w, int c0, int ilo,
+                                              int ihi, int Wo, float* out) {
   const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int i = i0; i <= i1; ++i)
-    for (int j = j0; j <= j1; ++j) {
-      const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
-      const size_t op = (((size_t)n * Ho + i) * Wo + j) * C + c0;
-      const uint2 am = *reinterpret_cast<const uint2*>(arg + op);
-      float g[8];
-      Pack8<T>::load(dy + op, g);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
-        if (b == code) acc[q] += g[q];
+  for (int di = 0; di < 2; ++di)
+#pragma unroll
+    for (int dj = 0; dj < 2; ++dj) {
+      const int i = ilo + di, j = j0 + dj;
+      if (i <= ihi && j <= j1) {
+        const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
+        const int off = (di * Wo + j) * C + c0;
+        const uint2 am = *reinterpret_cast<const uint2*>(argL + off);
+        float g[8];
+        Pack8<T>::load(dyL + off, g);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t bq = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+          if (bq == code) acc[q] += g[q];
+        }
       }
     }
 #pragma unroll
@@ -869,11 +938,13 @@ __device__ __forceinline__ void pool_bwd8(const T* __restrict__ dy, const uint8_
 
 // Max-pool backward, LRN backward and the ReLU mask in one pass.  One
 // workgroup per input row (image n, row h) of a Win x C layer:
-//   1. the row of the LRN input a is copied into LDS (direct-to-LDS loads)
-//      while each thread forms the pooled gradient g (w.r.t. the LRN output)
-//      of its (column, 8-channel) units, rounded as a stored gradient would
-//      be, into a second LDS row;
-//   2. each unit's LRN backward reads its channel neighbours of a and g from
+//   1. the row of the LRN input a, and the one or two pooled rows of dy and
+//      argmax whose windows cover row h, are copied into LDS with
+//      direct-to-LDS loads, all issued before one wait;
+//   2. each thread forms the pooled gradient g (w.r.t. the LRN output) of its
+//      (column, 8-channel) units from LDS, rounded as a stored gradient would
+//      be, into a third LDS row;
+//   3. each unit's LRN backward reads its channel neighbours of a and g from
 //      LDS, applies the ReLU mask and writes da.
 // da therefore equals that of the separate steps.  `dbg`, if not null,
 // receives g.
@@ -884,22 +955,40 @@ __global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, 
                                                       T* __restrict__ dbg, float k, float alpha, float beta) {
   constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, cpp = C / 8, units = Win * cpp;
   static_assert(units <= POOLLRN_UPT * TPB && C % 8 == 0, "pool/LRN backward geometry");
-  constexpr int ROW_BYTES = ((Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
-  __shared__ __attribute__((aligned(16))) char lds[2 * ROW_BYTES];
+  constexpr int KB = 1024;
+  constexpr int ROW_BYTES = (Win * C * (int)sizeof(T) + KB - 1) / KB * KB;
+  constexpr int DY_BYTES = (2 * Wo * C * (int)sizeof(T) + KB - 1) / KB * KB;
+  constexpr int ARG_BYTES = (2 * Wo * C + KB - 1) / KB * KB;
+  __shared__ __attribute__((aligned(16))) char lds[2 * ROW_BYTES + DY_BYTES + ARG_BYTES];
   T* arow = reinterpret_cast<T*>(lds);
   T* grow = reinterpret_cast<T*>(lds + ROW_BYTES);
+  const T* dyL = reinterpret_cast<const T*>(lds + 2 * ROW_BYTES);
+  const uint8_t* argL = reinterpret_cast<const uint8_t*>(lds + 2 * ROW_BYTES + DY_BYTES);
   const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
   const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
   const int n = b / Hin, h = b - n * Hin;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t row0 = ((size_t)n * Hin + h) * Win * C;   // element offset of the row
+  // pooled rows whose windows (rows 2i .. 2i+2) contain row h
+  const int ilo = h >= 2 ? (h - 1) / 2 : 0, ihi = min(h / 2, Ho - 1);
   {
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + row0, (uint32_t)(Win * C * sizeof(T)));
-    constexpr int nins = ROW_BYTES / 1024;
-    for (int j = wave; j < nins; j += TPB / 64)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16, j * 1024 + lane * 16, 0,
-                                               0, 0);
+    // descriptors bound each copy to its rows; the rest of an LDS region reads zero
+    const size_t prow = ((size_t)n * Ho + ilo) * Wo * C;
+    const uint32_t pel = (uint32_t)((ihi - ilo + 1) * Wo * C);
+    const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a + row0, (uint32_t)(Win * C * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dy + prow, pel * (uint32_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(arg + prow, pel);
+    for (int j = wave; j < ROW_BYTES / KB; j += TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(lds + j * KB), 16, j * KB + lane * 16, 0, 0, 0);
+    for (int j = wave; j < DY_BYTES / KB; j += TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(lds + 2 * ROW_BYTES + j * KB), 16,
+                                               j * KB + lane * 16, 0, 0, 0);
+    for (int j = wave; j < ARG_BYTES / KB; j += TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void_t*)(lds + 2 * ROW_BYTES + DY_BYTES + j * KB), 16,
+                                               j * KB + lane * 16, 0, 0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < POOLLRN_UPT; ++t) {
@@ -907,12 +996,11 @@ __global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, 
     if (u < units) {
       const int w = u / cpp, c0 = (u - w * cpp) * 8;
       float g[8];
-      pool_bwd8<T>(dy, arg, n, h, w, c0, C, Ho, Wo, g);
+      pool_bwd8_lds<T, C>(dyL, argL, h, w, c0, ilo, ihi, Wo, g);
       Pack8<T>::store(grow + w * C + c0, g);
       if (dbg) Pack8<T>::store(dbg + row0 + w * C + c0, g);
     }
   }
-  wait_vmcnt<0>();
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < POOLLRN_UPT; ++t) {
@@ -1256,15 +1344,16 @@ static int colsum_blocks(int64_t rows, int C) {
   return (int)std::max<int64_t>(nb, 1);
 }
 
+// Column sums of one (row block, column tile) of x[rows][C]: part[rowblock][c].
 template <typename T>
-__global__ void __launch_bounds__(TPB) k_colsum1(const T* __restrict__ x, int64_t rows, int C, int64_t rb,
-                                                 float* __restrict__ part) {
+__device__ __forceinline__ void colsum_block(const T* __restrict__ x, int64_t rows, int C, int64_t rb,
+                                             int rowblock, int ctile, float* __restrict__ part) {
   __shared__ float sh[TPB][9];
-  const int c0 = blockIdx.y * COLSUM_CW;
+  const int c0 = ctile * COLSUM_CW;
   const int w = min(COLSUM_CW, C - c0);
   const int cpr = w >> 3, nrl = TPB / cpr;
   const int t = threadIdx.x, cc = t % cpr, rl = t / cpr;
-  const int64_t r0 = (int64_t)blockIdx.x * rb, r1 = min(r0 + rb, rows);
+  const int64_t r0 = (int64_t)rowblock * rb, r1 = min(r0 + rb, rows);
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -1294,34 +1383,123 @@ __global__ void __launch_bounds__(TPB) k_colsum1(const T* __restrict__ x, int64_
     const int q = col >> 3, e = col & 7;
     float s = 0.f;
     for (int j = 0; j < nrl; ++j) s += sh[j * cpr + q][e];
-    part[(int64_t)blockIdx.x * C + c0 + col] = s;
+    part[(int64_t)rowblock * C + c0 + col] = s;
   }
 }
 
-__global__ void k_colsum2(const float* __restrict__ part, int nb, int C, float* __restrict__ out) {
+// Bias gradients of several layers, each the column sum of the layer's output
+// gradient dy[rows][C] over its N*H*W rows, followed by the SGD update of the
+// bias, in two launches:
+//   1. every (layer, row block, column tile) block writes one partial row;
+//   2. one wave per bias element sums that element's partials in block order,
+//      stores the gradient and updates the bias (fp32 master, momentum, and
+//      working copy).
+struct BiasArgs1 {
+  const void* x[BIAS_MAX];
+  float* part[BIAS_MAX];
+  int64_t rows[BIAS_MAX], rb[BIAS_MAX];
+  int C[BIAS_MAX], nb[BIAS_MAX];
+  int bstart[BIAS_MAX + 1];
+  int n;
+};
+struct BiasArgs2 {
+  const float* part[BIAS_MAX];
+  float* grad[BIAS_MAX];
+  float* w[BIAS_MAX];
+  float* v[BIAS_MAX];
+  void* wb[BIAS_MAX];
+  int nb[BIAS_MAX];
+  int cstart[BIAS_MAX + 1];   // first bias element of each layer
+  int n;
+  float lr, mom, wdlr;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_bias_colsum(BiasArgs1 a) {
+  const int bid = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < BIAS_MAX; ++q) j += (q < a.n && bid >= a.bstart[q]) ? 1 : 0;
+  const int local = bid - a.bstart[j];
+  const int ctile = local / a.nb[j], rowblock = local - ctile * a.nb[j];
+  colsum_block<T>(static_cast<const T*>(a.x[j]), a.rows[j], a.C[j], a.rb[j], rowblock, ctile, a.part[j]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_bias_sgd(BiasArgs2 a) {
   const int lane = threadIdx.x & 63;
-  const int col = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
-  if (col >= C) return;
+  const int e = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
+  if (e >= a.cstart[a.n]) return;
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < BIAS_MAX; ++q) j += (q < a.n && e >= a.cstart[q]) ? 1 : 0;
+  const int col = e - a.cstart[j], C = a.cstart[j + 1] - a.cstart[j];
+  const float* part = a.part[j];
   float s = 0.f;
-  for (int b = lane; b < nb; b += 64) s += part[(int64_t)b * C + col];
+  for (int b = lane; b < a.nb[j]; b += 64) s += part[(int64_t)b * C + col];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (lane == 0) out[col] = s;
+  if (lane == 0) {
+    a.grad[j][col] = s;
+    float w = a.w[j][col], v = a.v[j][col];
+    sgd_elem(w, v, s, a.mom, a.wdlr, a.lr);
+    a.w[j][col] = w;
+    a.v[j][col] = v;
+    if (sizeof(T) == 2) static_cast<bf16*>(a.wb[j])[col] = f2bf(w);
+    else static_cast<float*>(a.wb[j])[col] = w;
+  }
 }
 
-size_t colsum_scratch_bytes(int64_t rows, int C) {
-  return (size_t)colsum_blocks(rows, C) * C * sizeof(float);
+size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n) {
+  size_t b = 0;
+  for (int j = 0; j < n; ++j) b += (size_t)colsum_blocks(jobs[j].rows, jobs[j].C) * jobs[j].C * sizeof(float);
+  return b;
 }
 
-hipError_t colsum(DType dt, const void* x, int64_t rows, int C, float* out, float* scratch, hipStream_t st) {
-  if (C % 8) return hipErrorInvalidValue;
-  const int nb = colsum_blocks(rows, C);
-  const int64_t rb = (rows + nb - 1) / nb;
-  const dim3 g1(nb, cdiv(C, COLSUM_CW));
-  float* dst = nb == 1 ? out : scratch;
-  if (dt == BF16) hipLaunchKernelGGL((k_colsum1<bf16>), g1, dim3(TPB), 0, st, (const bf16*)x, rows, C, rb, dst);
-  else hipLaunchKernelGGL((k_colsum1<float>), g1, dim3(TPB), 0, st, (const float*)x, rows, C, rb, dst);
-  if (nb > 1) hipLaunchKernelGGL(k_colsum2, dim3(cdiv(C, TPB / 64)), dim3(TPB), 0, st, scratch, nb, C, out);
+hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch,
+                          hipStream_t st, const KTimer* kt) {
+  if (n < 1 || n > BIAS_MAX) return hipErrorInvalidValue;
+  BiasArgs1 a1 = {};
+  BiasArgs2 a2 = {};
+  a1.n = a2.n = n;
+  int blocks = 0, cols = 0;
+  float* part = scratch;
+  for (int j = 0; j < n; ++j) {
+    const BiasJob& b = jobs[j];
+    if (b.C % 8 || b.rows < 1) return hipErrorInvalidValue;
+    const int nb = colsum_blocks(b.rows, b.C);
+    a1.x[j] = b.dy;
+    a1.part[j] = part;
+    a1.rows[j] = b.rows;
+    a1.rb[j] = (b.rows + nb - 1) / nb;
+    a1.C[j] = b.C;
+    a1.nb[j] = nb;
+    a1.bstart[j] = blocks;
+    blocks += nb * cdiv(b.C, COLSUM_CW);
+    a2.part[j] = part;
+    a2.grad[j] = b.grad;
+    a2.w[j] = b.w;
+    a2.v[j] = b.v;
+    a2.wb[j] = b.wb;
+    a2.nb[j] = nb;
+    a2.cstart[j] = cols;
+    cols += b.C;
+    part += (size_t)nb * b.C;
+  }
+  a1.bstart[n] = blocks;
+  a2.cstart[n] = cols;
+  a2.lr = hy.lr;
+  a2.mom = hy.mom;
+  a2.wdlr = hy.wdlr;
+  rec_start(kt, st);
+  if (dt == BF16) {
+    hipLaunchKernelGGL((k_bias_colsum<bf16>), dim3(blocks), dim3(TPB), 0, st, a1);
+    hipLaunchKernelGGL((k_bias_sgd<bf16>), dim3(cdiv(cols, TPB / 64)), dim3(TPB), 0, st, a2);
+  } else {
+    hipLaunchKernelGGL((k_bias_colsum<float>), dim3(blocks), dim3(TPB), 0, st, a1);
+    hipLaunchKernelGGL((k_bias_sgd<float>), dim3(cdiv(cols, TPB / 64)), dim3(TPB), 0, st, a2);
+  }
+  rec_stop(kt, st);
   return hipGetLastError();
 }
 
@@ -1364,8 +1542,8 @@ __global__ void k_multi(MultiArgs a) {
   }
   T* o = reinterpret_cast<T*>(a.wb[ti]) + e;
   if (sizeof(T) == 2) {
-    const uint32_t lo = (uint32_t)f2bf(w.x) | ((uint32_t)f2bf(w.y) << 16);
-    const uint32_t hi = (uint32_t)f2bf(w.z) | ((uint32_t)f2bf(w.w) << 16);
+    const uint32_t lo = f2bf2(w.x, w.y);
+    const uint32_t hi = f2bf2(w.z, w.w);
     *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
   } else {
     *reinterpret_cast<float4*>(o) = w;

@@ -34,10 +34,18 @@ struct ConvShape {
   int Nimg, H, W, Cin, Cout, K, stride, pad, groups, Ho, Wo;
 };
 
-// ---- weight re-layouts (per call; weights change every training step)
-hipError_t w_khwc(DType, const void* w_oihw, void* out, int Cout, int Cg, int K, hipStream_t);
-hipError_t w_dgrad(DType, const void* w_oihw, void* out, int G, int Coutg, int Cing, int K,
-                   hipStream_t);
+// ---- weight re-layouts (per call; weights change every training step), all
+// in one launch.  src is an OIHW tensor of Cout x Cig x K x K (Cig = input
+// channels per group), G the group count.
+enum { WPREP_W1S = 0, WPREP_KHWC = 1, WPREP_DGRAD = 2 };
+constexpr int WPREP_MAX = 9;
+struct WeightPrep {
+  int kind;
+  const void* src;
+  void* dst;
+  int Cout, Cig, K, G;
+};
+hipError_t prep_weights(DType, const WeightPrep* jobs, int n, hipStream_t, const KTimer* kt = nullptr);
 
 // ---- convolutions (bf16 MFMA or fp32 MFMA, fp32 accumulate)
 // Layer 1 runs as a 3x3 stride-1 convolution over 4x4 pixel blocks:
@@ -47,7 +55,6 @@ constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
 constexpr size_t S2D_W_ELEMS = 96 * 432;
 hipError_t conv1_s2d(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs, hipStream_t,
                       const KTimer* kt = nullptr);
-hipError_t conv1_w_s2d(DType, const void* w_oihw, void* ws, hipStream_t);
 // y NHWC [N][55][55][96] = relu(conv1 + b)
 hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t,
                       const KTimer* kt = nullptr);
@@ -122,10 +129,23 @@ hipError_t softmax_ce(DType, const float* z, const int32_t* labels, float* p, vo
                       float* rowloss, int M, int O, hipStream_t);
 hipError_t mean_reduce(const float* v, int n, float* out, hipStream_t);
 hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t);
-// out[c] = sum over rows of x[rows][C] (fp32), via `scratch` (colsum_scratch_bytes)
-hipError_t colsum(DType, const void* x, int64_t rows, int C, float* out, float* scratch,
-                  hipStream_t);
-size_t colsum_scratch_bytes(int64_t rows, int C);
+// Bias gradients of up to BIAS_MAX layers, grad[c] = sum over the rows of
+// dy[rows][C] (fp32), each followed by the SGD update of the bias (w, v fp32
+// in place; wb the working copy in the compute type).  Partial sums go to
+// `scratch` (bias_grad_scratch_bytes).
+constexpr int BIAS_MAX = 8;
+struct BiasJob {
+  const void* dy;
+  int64_t rows;
+  int C;
+  float* grad;
+  float* w;
+  float* v;
+  void* wb;
+};
+size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n);
+hipError_t bias_grads_sgd(DType, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch, hipStream_t,
+                          const KTimer* kt = nullptr);
 
 // ---- optimizer, casts, dropout mask
 struct TensorSet {

@@ -162,12 +162,13 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
     part = mx(part, fc_dgrad_part_bytes(N, 9216, 4096));
     part = mx(part, conv1_wgrad_part_bytes(N));
     for (int i = 1; i < 5; ++i) part = mx(part, conv_wgrad_part_bytes(net.conv[i]));
-    for (int i = 0; i < 5; ++i) {
-      const ConvShape& c = net.conv[i];
-      cs = mx(cs, colsum_scratch_bytes((int64_t)N * c.Ho * c.Wo, c.Cout));
+    // bias-gradient partials of all eight layers at once
+    BiasJob bj[8] = {};
+    for (int i = 0; i < 8; ++i) {
+      bj[i].rows = i < 5 ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo : N;
+      bj[i].C = (int)net.bcount[i];
     }
-    cs = mx(cs, colsum_scratch_bytes(N, 4096));
-    cs = mx(cs, colsum_scratch_bytes(N, 1000));
+    cs = bias_grad_scratch_bytes(bj, 8);
   }
   p->part = a.take(part);
   p->part_bytes = part;

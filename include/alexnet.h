@@ -173,6 +173,8 @@ typedef enum {
   ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
   ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
   ALEXNET_KT_SGD,
+  ALEXNET_KT_WPREP,            /* every weight re-layout of the call, one launch */
+  ALEXNET_KT_BIAS,             /* all bias gradients + their SGD (two launches)  */
   ALEXNET_KT_COUNT
 } alexnet_kernel;
 
