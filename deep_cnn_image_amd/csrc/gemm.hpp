@@ -160,6 +160,7 @@ struct DmaSlots {
   static constexpr int NSLOT = R / 8, NI = (NSLOT + 3) / 4;
   static __device__ __forceinline__ int slot(int wave, int i) {
     const int j = wave + 4 * i;
+    if constexpr (NSLOT % 4 == 0) return j;   // wave < 4: always in range
     return j < NSLOT ? j : j - 4;
   }
   // k granule (of 8) that `lane` fetches for a slot of parity `odd`
@@ -830,10 +831,17 @@ struct Mma<float, FM, FN, LA, LB> {
 };
 
 // ------------------------------------------------------------------ kernel
+// bf16 tiles (up to 192 x 128) run two workgroups per CU, two waves per SIMD;
+// one workgroup per CU with larger tiles measured slower (less latency
+// hiding).  fp32 tiles run one workgroup per CU.
+template <typename T, int BM, int BN>
+constexpr int gemm_waves_per_simd() { return sizeof(T) == 2 ? 2 : 1; }
+template <typename T, int BM, int BN>
+constexpr int gemm_default_stages() { return 2; }
+
 template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP, int ST = 2>
-// bf16 kernels are held to two waves per SIMD (two workgroups per CU), which
-// the tile sizes and the grid sizing assume.
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd<T, BM, BN>(), gemm_waves_per_simd<T, BM, BN>())))
 k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   static_assert(WGM * WGN == 4, "four waves");
   using LA = typename AL::Layout;
@@ -899,7 +907,7 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
       for (int p = 0; p < ST - 1; ++p)
         if (kt0 + p < kt1) { al.issue(As + p * A_EL); bl.issue(Bs + p * B_EL); }
       using MM = Mma<T, FM, FN, LA, LB>;
-      auto step = [&](auto cur_c, int kt) {
+      auto step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         const int ahead = kt1 - 1 - kt;   // slices issued after this one: min(ahead, ST - 2)
         wait_ahead<OPS, ST - 2>(ahead);
@@ -919,8 +927,9 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
       };
       int kt = kt0;
       for (; kt + ST - 1 < kt1; kt += ST)
-        unroll_steps(std::make_integer_sequence<int, ST>{}, [&](auto i) { step(i, kt + decltype(i)::value); });
-      unroll_steps(std::make_integer_sequence<int, ST - 1>{}, [&](auto i) {
+        unroll_steps(std::make_integer_sequence<int, ST>{},
+                     [&](auto i) __attribute__((always_inline)) { step(i, kt + decltype(i)::value); });
+      unroll_steps(std::make_integer_sequence<int, ST - 1>{}, [&](auto i) __attribute__((always_inline)) {
         if (kt + decltype(i)::value < kt1) step(i, kt + decltype(i)::value);
       });
     }

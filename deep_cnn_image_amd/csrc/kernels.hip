@@ -36,9 +36,11 @@ static inline void rec_stop(const KTimer* kt, hipStream_t st) { if (kt) hipEvent
 // =========================================================================
 // GEMM launches
 // =========================================================================
-template <typename T, int BM, int BN, int WGM, int WGN, int ST = 2, class AL, class BL, class EP>
+// ST = 0: the tile's default LDS stage count.
+template <typename T, int BM, int BN, int WGM, int WGN, int ST0 = 0, class AL, class BL, class EP>
 static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
                            int splits, hipStream_t st, const KTimer* kt = nullptr) {
+  constexpr int ST = ST0 ? ST0 : gemm_default_stages<T, BM, BN>();
   GemmGrid gg;
   gg.M = M; gg.N = N; gg.K = K;
   gg.tiles_m = cdiv(M, BM);
@@ -424,13 +426,22 @@ hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float
 
 // ---- fully-connected layers
 // FC layers at small batch stream their weights from HBM; split-K spreads
-// that over the CUs.  (More LDS stages per workgroup measured no faster.)
-template <typename T> static constexpr int fc_stages() { return 2; }
+// that over the CUs in one round of at most one workgroup per CU, and bf16
+// splits of 6 or more k-slices keep three slices in flight (four LDS stages,
+// 128 KB) to cover the HBM latency.
 static int fc_splits(int M, int N, int K) {
   const int tiles = cdiv(M, 128) * cdiv(N, 128);
-  int want = cdiv(256, tiles);
-  if (want > 8) want = 8;
+  int want = 256 / tiles;
+  if (want > 16) want = 16;
   return eff_splits(K, want);
+}
+template <typename T, class AL, class BL>
+static hipError_t fc_gemm(const AL& a, const BL& b, const EpF32& e, int M, int N, int K, int S, hipStream_t st,
+                          const KTimer* kt) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (cdiv(cdiv(K, GEMM_BK), S) >= 6) return run_gemm<T, 128, 128, 2, 2, 4>(a, b, e, M, N, K, 1, S, st, kt);
+  }
+  return run_gemm<T, 128, 128, 2, 2, 2>(a, b, e, M, N, K, 1, S, st, kt);
 }
 size_t fc_fwd_part_bytes(int M, int K, int O) {
   return (size_t)fc_splits(M, O, K) * M * O * sizeof(float);
@@ -499,7 +510,7 @@ static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, co
   bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2, fc_stages<T>()>(a, bl, e, M, O, K, 1, S, st, kt);
+  hipError_t err = fc_gemm<T>(a, bl, e, M, O, K, S, st, kt);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O,
                      (const T*)b, ep, (const T*)nullptr, (T*)y, y_f32);
@@ -525,7 +536,7 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
   bl.p = (const T*)w; bl.ld = K; bl.rows = K; bl.K = O; bl.gstride = 0;
   EpF32 e;
   e.out = part; e.ldo = K; e.M = M; e.N = K; e.splits = S;
-  hipError_t err = run_gemm<T, BM, BN, 2, 2, fc_stages<T>()>(a, bl, e, M, K, O, 1, S, st, kt);
+  hipError_t err = fc_gemm<T>(a, bl, e, M, K, O, S, st, kt);
   if (err != hipSuccess) return err;
   FcEpi none{};
   hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K,
@@ -606,13 +617,16 @@ hipError_t fc_wgrad_sgd(DType dt, int M, int K, int O, const void* dy, const voi
 //          W[co][c][4kh'+dh][4kw'+dw], zero where 4kh'+dh or 4kw'+dw >= 11;
 //          one output element per thread;
 //   KHWC   forward rows [co], k = (tap, ci), or with `blocked`
-//          k = (ci / 64, tap, ci % 64), tap = kh*K + kw; one thread per source
-//          row (co, ci) of K*K taps, consecutive threads on consecutive ci;
+//          k = (ci / 64, tap, ci % 64), tap = kh*K + kw: one workgroup per co
+//          copies the co slice (Cg*K*K contiguous elements) into LDS and
+//          writes it back permuted (the destination slice is contiguous too);
 //   DGRAD  data-gradient rows [g][ci], k over (flipped tap, output channel col
 //          of the group): k = (tap, col), or with `blocked`
-//          k = (col / 64, tap, col % 64); one thread per (g, ci, col),
-//          consecutive threads on consecutive col.
-// Stores of neighbouring threads are therefore contiguous in every job.
+//          k = (col / 64, tap, col % 64): a 64 x 64 tile transpose through LDS
+//          of (64 output channels col) x (64 consecutive (ci, tap) entries).
+// Reads and writes of neighbouring threads are contiguous in every job.
+constexpr int WPREP_T = 64;                              // DGRAD tile edge
+constexpr int WPREP_LDS_ELEMS = 4160;                    // >= max(Cg*K*K) = 3456 and 64 x 65
 struct PrepArgs {
   const void* src[WPREP_MAX];
   void* dst[WPREP_MAX];
@@ -623,52 +637,67 @@ struct PrepArgs {
 
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_prep_weights(PrepArgs a) {
-  const int bid = blockIdx.x;
+  __shared__ T tile[WPREP_LDS_ELEMS];
+  const int bid = blockIdx.x, tid = threadIdx.x;
   int j = 0;
 #pragma unroll
   for (int q = 1; q < WPREP_MAX; ++q) j += (q < a.n && bid >= a.bstart[q]) ? 1 : 0;
-  const int i = (bid - a.bstart[j]) * TPB + threadIdx.x;
-  if (i >= a.count[j]) return;
+  const int local = bid - a.bstart[j];
   const T* __restrict__ src = static_cast<const T*>(a.src[j]);
   T* __restrict__ dst = static_cast<T*>(a.dst[j]);
   const int kind = a.kind[j];
   if (kind == WPREP_W1S) {
+    const int i = local * TPB + tid;
+    if (i >= a.count[j]) return;
     const int co = i / S2D_K, r = i - co * S2D_K;
     const int tap = r / S2D_C, q = r - tap * S2D_C;
     const int kh = (tap / 3) * 4 + ((q >> 2) & 3), kw = (tap % 3) * 4 + (q & 3), c = q >> 4;
     dst[i] = (kh < 11 && kw < 11) ? src[((co * 3 + c) * 11 + kh) * 11 + kw] : T(0);
     return;
   }
-  const int K = a.K[j], KK = K * K, blocked = a.blocked[j];
+  const int KK = a.K[j] * a.K[j], blocked = a.blocked[j];
   if (kind == WPREP_KHWC) {
-    const int Cg = a.Cig[j];
-    const int co = i / Cg, ci = i - co * Cg;
-    const T* s = src + (int64_t)i * KK;                      // W[co][ci][.][.]
-    int64_t o, ostep;
-    if (blocked) {
-      o = ((int64_t)(co * (Cg / GEMM_BK) + ci / GEMM_BK) * KK) * GEMM_BK + (ci % GEMM_BK);
-      ostep = GEMM_BK;
-    } else {
-      o = (int64_t)co * KK * Cg + ci;
-      ostep = Cg;
+    const int Cg = a.Cig[j], n = Cg * KK, co = local;
+    const T* s = src + (int64_t)co * n;
+    for (int e = tid; e < n; e += TPB) tile[e] = s[e];
+    __syncthreads();
+    T* d = dst + (int64_t)co * n;
+    for (int o = tid; o < n; o += TPB) {
+      int ci, tap;
+      if (blocked) {
+        const int t2 = o / GEMM_BK;
+        tap = t2 % KK;
+        ci = (t2 / KK) * GEMM_BK + (o - t2 * GEMM_BK);
+      } else {
+        tap = o / Cg;
+        ci = o - tap * Cg;
+      }
+      d[o] = tile[ci * KK + tap];
     }
-    for (int tap = 0; tap < KK; ++tap) dst[o + tap * ostep] = s[tap];
     return;
   }
-  // DGRAD
-  const int Cog = a.Cog[j], Cig = a.Cig[j];
-  const int col = i % Cog, rest = i / Cog, ci = rest % Cig, g = rest / Cig;
-  const T* s = src + ((int64_t)(g * Cog + col) * Cig + ci) * KK;   // W[g*Cog+col][ci][.][.]
-  int64_t o, ostep;
-  if (blocked) {
-    o = ((int64_t)((g * Cig + ci) * (Cog / GEMM_BK) + col / GEMM_BK) * KK) * GEMM_BK + (col % GEMM_BK);
-    ostep = GEMM_BK;
-  } else {
-    o = (int64_t)(g * Cig + ci) * KK * Cog + col;
-    ostep = Cog;
+  // DGRAD: tile (g, col block, e block), e = ci*KK + tap over W[g*Cog + col][ci][tap]
+  const int Cog = a.Cog[j], Cig = a.Cig[j], nE = Cig * KK;
+  const int ncb = (Cog + WPREP_T - 1) / WPREP_T, neb = (nE + WPREP_T - 1) / WPREP_T;
+  const int g = local / (ncb * neb), rem = local - g * ncb * neb;
+  const int col0 = (rem / neb) * WPREP_T, e0 = (rem % neb) * WPREP_T;
+  for (int idx = tid; idx < WPREP_T * WPREP_T; idx += TPB) {
+    const int c = idx / WPREP_T, e = idx - c * WPREP_T;
+    if (col0 + c < Cog && e0 + e < nE)
+      tile[c * (WPREP_T + 1) + e] = src[(int64_t)(g * Cog + col0 + c) * nE + e0 + e];
   }
-  // output tap (kh, kw) takes the flipped source tap (K-1-kh, K-1-kw): KK-1-tap
-  for (int tap = 0; tap < KK; ++tap) dst[o + tap * ostep] = s[KK - 1 - tap];
+  __syncthreads();
+  const int nblk = Cog / GEMM_BK;
+  for (int idx = tid; idx < WPREP_T * WPREP_T; idx += TPB) {
+    const int e = idx / WPREP_T, c = idx - e * WPREP_T;
+    const int col = col0 + c, ee = e0 + e;
+    if (col >= Cog || ee >= nE) continue;
+    const int ci = ee / KK, tapo = KK - 1 - (ee - ci * KK);   // output tap takes the flipped source tap
+    int64_t o;
+    if (blocked) o = (((int64_t)(g * Cig + ci) * nblk + col / GEMM_BK) * KK + tapo) * GEMM_BK + (col % GEMM_BK);
+    else o = ((int64_t)(g * Cig + ci) * KK + tapo) * Cog + col;
+    dst[o] = tile[c * (WPREP_T + 1) + e];
+  }
 }
 
 bool im2col_blocked(DType dt, int Cg) { return dt == BF16 && Cg % GEMM_BK == 0; }
@@ -689,25 +718,26 @@ hipError_t prep_weights(DType dt, const WeightPrep* jobs, int n, hipStream_t st,
       case WPREP_W1S:
         count = (int64_t)S2D_W_ELEMS;
         break;
-      case WPREP_KHWC:   // Cig = input channels per group; one thread per (co, ci)
+      case WPREP_KHWC:   // Cig = input channels per group; one workgroup per co
+        if (w.Cig * w.K * w.K > WPREP_LDS_ELEMS) return hipErrorInvalidValue;
         a.Cig[j] = w.Cig;
         a.blocked[j] = im2col_blocked(dt, w.Cig) ? 1 : 0;
-        count = (int64_t)w.Cout * w.Cig;
+        count = w.Cout;
         break;
-      case WPREP_DGRAD:  // one thread per (g, ci, col)
+      case WPREP_DGRAD:  // one workgroup per 64 x 64 tile
         if (w.G < 1 || w.Cout % w.G) return hipErrorInvalidValue;
         a.Cog[j] = w.Cout / w.G;
         a.Cig[j] = w.Cig;
         a.blocked[j] = im2col_blocked(dt, a.Cog[j]) ? 1 : 0;
-        count = (int64_t)w.Cout * w.Cig;
+        count = (int64_t)w.G * cdiv(a.Cog[j], WPREP_T) * cdiv((int64_t)w.Cig * w.K * w.K, WPREP_T);
         break;
       default:
         return hipErrorInvalidValue;
     }
     if (count > (int64_t)1 << 30) return hipErrorInvalidValue;
-    a.count[j] = (int)count;
+    a.count[j] = (int)count;   // W1S: elements; KHWC, DGRAD: workgroups
     a.bstart[j] = blocks;
-    blocks += (int)cdiv(count, TPB);
+    blocks += w.kind == WPREP_W1S ? cdiv(count, TPB) : (int)count;
   }
   a.bstart[n] = blocks;
   rec_start(kt, st);
@@ -766,109 +796,6 @@ __device__ __forceinline__ void lrn8(const float* v, float k, float alpha, float
   }
 }
 
-// LRN followed by the overlapping 3x3 / stride-2 max-pool with argmax, fused:
-// the LRN output is stored only in LDS (rounded to T exactly as a stored
-// tensor would be), so pooled values and argmax equal those of the two
-// separate steps.  One workgroup per (image n, pooled row i) over input rows
-// 2i .. 2i+2 (Hin = 2 Ho + 1), which are one contiguous run of 3 W C
-// elements:
-//   1. the run is copied into LDS with direct-to-LDS loads (one wait);
-//   2. each thread normalises its (row, column, 8-channel) units from LDS into
-//      registers, and after a barrier writes them back in place;
-//   3. the pooled row and its argmax are taken from LDS.
-// `dbg`, if not null, receives the LRN output (rows 2i, 2i+1, and the last
-// row from the last workgroup of an image).  Workgroups are remapped so that
-// the rows of one image, which share an input row, run on one XCD.
-constexpr int LRNPOOL_LDS = 3 * 27 * 256;   // elements: max over the two layers (3 x W x C)
-constexpr int LRNPOOL_TPB = 512;
-constexpr int LRNPOOL_UPT = 6;              // units per thread: ceil(3 W C / 8 / 512) <= 6
-template <typename T, int H, bool B075, int Win, int C>
-__global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ a, T* __restrict__ y,
-                                                          uint8_t* __restrict__ arg, T* __restrict__ dbg,
-                                                          float k, float alpha, float beta) {
-  constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho;
-  static_assert(3 * Win * C <= LRNPOOL_LDS && C % 8 == 0, "fused LRN/pool geometry");
-  static_assert(3 * Win * C / 8 <= LRNPOOL_UPT * LRNPOOL_TPB, "units per thread");
-  constexpr int LDS_BYTES = ((3 * Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  T* rows = reinterpret_cast<T*>(lds);
-  const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
-  const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
-  const int n = b / Ho, i = b - n * Ho;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int cpp = C >> 3, rowu = Win * cpp, units = 3 * rowu;
-  // 1. rows 2i .. 2i+2 -> LDS (1 KB per wave instruction; past the image reads as zero)
-  {
-    const size_t img = (size_t)Hin * Win * C;
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + n * img, (uint32_t)(img * sizeof(T)));
-    const uint32_t base = (uint32_t)((size_t)2 * i * Win * C * sizeof(T));
-    constexpr int nins = (3 * Win * C * (int)sizeof(T) + 1023) / 1024;
-    for (int j = wave; j < nins; j += LRNPOOL_TPB / 64)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
-                                               (int)(base + j * 1024 + lane * 16), 0, 0, 0);
-    wait_vmcnt<0>();
-    __syncthreads();
-  }
-  // 2. LRN of this thread's units into registers, then back into LDS
-  const bool last = i == Ho - 1;
-  float o[LRNPOOL_UPT][8];
-#pragma unroll
-  for (int t = 0; t < LRNPOOL_UPT; ++t) {
-    const int u = tid + t * LRNPOOL_TPB;
-    if (u < units) {
-      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
-      float v[24];
-#pragma unroll
-      for (int h = 0; h < 3; ++h) {
-        const int cc = c0 + (h - 1) * 8;
-        if (cc >= 0 && cc < C) Pack8<T>::load(rows + pix * C + cc, v + h * 8);
-        else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[h * 8 + e] = 0.f;
-        }
-      }
-      lrn8<H, B075>(v, k, alpha, beta, o[t]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < LRNPOOL_UPT; ++t) {
-    const int u = tid + t * LRNPOOL_TPB;
-    if (u < units) {
-      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
-      Pack8<T>::store(rows + pix * C + c0, o[t]);
-      const int rr = pix / Win;
-      if (dbg && (rr < 2 || last)) {
-        const size_t g = (((size_t)n * Hin + 2 * i) * Win + pix) * C + c0;
-        Pack8<T>::store(dbg + g, o[t]);
-      }
-    }
-  }
-  __syncthreads();
-  // 3. pool: window rows 0..2 of LDS, columns 2j .. 2j+2
-  for (int u = tid; u < Wo * cpp; u += LRNPOOL_TPB) {
-    const int j = u / cpp, c0 = (u - j * cpp) * 8;
-    float best[8], v[8];
-    uint32_t bi[8];
-    Pack8<T>::load(rows + (2 * j) * C + c0, best);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bi[e] = 0;
-#pragma unroll
-    for (int d = 1; d < 9; ++d) {
-      const int dy = d / 3, dx = d % 3;
-      Pack8<T>::load(rows + (dy * Win + 2 * j + dx) * C + c0, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
-    }
-    const size_t og = (((size_t)n * Ho + i) * Wo + j) * C + c0;
-    Pack8<T>::store(y + og, best);
-    *reinterpret_cast<uint2*>(arg + og) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
-                                                     bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
-  }
-}
-
 // Backward of LRN fused with the preceding ReLU's mask [a > 0], for channels
 // c0 .. c0+7 of one pixel:
 //   da_j = g_j S_j^-beta - 2 alpha beta a_j sum_{|i-j| <= H} g_i a_i S_i^(-beta-1)
@@ -899,6 +826,266 @@ __device__ __forceinline__ void lrn_bwd8(const float* av, const float* gv, float
     const float aj = av[8 + i];
     const float d = gv[8 + i] * pb[i + H] - c2 * aj * cross;
     o[i] = aj > 0.f ? d : 0.f;
+  }
+}
+
+// bf16 halves of a packed pair, and the pair's sum of squares in one
+// v_dot2_f32_bf16 (the products of bf16 values are exact in fp32).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf_sq2(uint32_t w) {
+  const bf16x2_t a = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(a, a, 0.f, false);
+}
+
+// LRN of channels c0 .. c0+7 of pixel px (C channels, c0 % 8 == 0).  For bf16
+// and the 5-channel window the window sums are built from pair sums of
+// squares of the packed data: channel c's window c-2 .. c+2 is two pairs and
+// one single.
+template <typename T, int H, bool B075, int C>
+__device__ __forceinline__ void lrn_unit(const T* px, int c0, float k, float alpha, float beta, float* o) {
+  if constexpr (std::is_same<T, bf16>::value && H == 2) {
+    uint32_t W[6];   // W[j] = channels (c0 - 2 + 2j, c0 - 1 + 2j)
+    W[0] = c0 >= 8 ? *reinterpret_cast<const uint32_t*>(px + c0 - 2) : 0u;
+    const uint4 q = *reinterpret_cast<const uint4*>(px + c0);
+    W[1] = q.x; W[2] = q.y; W[3] = q.z; W[4] = q.w;
+    W[5] = c0 + 8 < C ? *reinterpret_cast<const uint32_t*>(px + c0 + 8) : 0u;
+    float Q[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) Q[j] = bf_sq2(W[j]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float ae = bf_lo(W[m + 2]), ao = bf_hi(W[m]);
+      const float se = fmaf(ae, ae, Q[m] + Q[m + 1]);      // channels c0+2m-2 .. c0+2m+2
+      const float so = fmaf(ao, ao, Q[m + 1] + Q[m + 2]);  // channels c0+2m-1 .. c0+2m+3
+      float p, unused;
+      lrn_pows<B075>(k + alpha * se, beta, p, unused);
+      o[2 * m] = bf_lo(W[m + 1]) * p;
+      lrn_pows<B075>(k + alpha * so, beta, p, unused);
+      o[2 * m + 1] = bf_hi(W[m + 1]) * p;
+    }
+  } else {
+    float v[24];
+#pragma unroll
+    for (int h = 0; h < 3; ++h) {
+      const int cc = c0 + (h - 1) * 8;
+      if (cc >= 0 && cc < C) Pack8<T>::load(px + cc, v + h * 8);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[h * 8 + e] = 0.f;
+      }
+    }
+    lrn8<H, B075>(v, k, alpha, beta, o);
+  }
+}
+
+// LRN backward with the ReLU mask for channels c0 .. c0+7 of one pixel: apx
+// holds the LRN input a and gpx the gradient g w.r.t. the LRN output.
+template <typename T, int H, bool B075, int C>
+__device__ __forceinline__ void lrn_bwd_unit(const T* apx, const T* gpx, int c0, float k, float alpha, float beta,
+                                             float* o) {
+  if constexpr (std::is_same<T, bf16>::value && H == 2) {
+    uint32_t A[8];   // A[j] = a over channels (c0 - 4 + 2j, c0 - 3 + 2j)
+    uint32_t G[6];   // G[j] = g over channels (c0 - 2 + 2j, c0 - 1 + 2j)
+    if (c0 >= 8) {
+      const uint2 l = *reinterpret_cast<const uint2*>(apx + c0 - 4);
+      A[0] = l.x; A[1] = l.y;
+      G[0] = *reinterpret_cast<const uint32_t*>(gpx + c0 - 2);
+    } else {
+      A[0] = A[1] = G[0] = 0u;
+    }
+    const uint4 aq = *reinterpret_cast<const uint4*>(apx + c0);
+    const uint4 gq = *reinterpret_cast<const uint4*>(gpx + c0);
+    A[2] = aq.x; A[3] = aq.y; A[4] = aq.z; A[5] = aq.w;
+    G[1] = gq.x; G[2] = gq.y; G[3] = gq.z; G[4] = gq.w;
+    if (c0 + 8 < C) {
+      const uint2 h = *reinterpret_cast<const uint2*>(apx + c0 + 8);
+      A[6] = h.x; A[7] = h.y;
+      G[5] = *reinterpret_cast<const uint32_t*>(gpx + c0 + 8);
+    } else {
+      A[6] = A[7] = G[5] = 0u;
+    }
+    float Q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Q[j] = bf_sq2(A[j]);
+    // positions r = 0..11: channels c0 - 2 + r (the reach of the 8 outputs' windows)
+    float pb[12], tt[12];
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      const int j = r >> 1;
+      float s, ac, gc;
+      if ((r & 1) == 0) {
+        const float x = bf_lo(A[j + 2]);
+        s = fmaf(x, x, Q[j] + Q[j + 1]);
+        ac = bf_lo(A[j + 1]);
+        gc = bf_lo(G[j]);
+      } else {
+        const float x = bf_hi(A[j]);
+        s = fmaf(x, x, Q[j + 1] + Q[j + 2]);
+        ac = bf_hi(A[j + 1]);
+        gc = bf_hi(G[j]);
+      }
+      float p, qq;
+      lrn_pows<B075>(k + alpha * s, beta, p, qq);
+      pb[r] = p;
+      tt[r] = gc * ac * qq;
+    }
+    const float c2 = 2.f * alpha * beta;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float cross = 0.f;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) cross += tt[i + j];
+      const uint32_t aw = A[2 + (i >> 1)], gw = G[1 + (i >> 1)];
+      const float aj = (i & 1) ? bf_hi(aw) : bf_lo(aw), gj = (i & 1) ? bf_hi(gw) : bf_lo(gw);
+      const float d = gj * pb[i + 2] - c2 * aj * cross;
+      o[i] = aj > 0.f ? d : 0.f;
+    }
+  } else {
+    float av[24], gv[24];
+#pragma unroll
+    for (int hh = 0; hh < 3; ++hh) {
+      const int cc = c0 + (hh - 1) * 8;
+      if (cc >= 0 && cc < C) {
+        Pack8<T>::load(apx + cc, av + hh * 8);
+        Pack8<T>::load(gpx + cc, gv + hh * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { av[hh * 8 + e] = 0.f; gv[hh * 8 + e] = 0.f; }
+      }
+    }
+    lrn_bwd8<H, B075>(av, gv, k, alpha, beta, o);
+  }
+}
+
+// LRN followed by the overlapping 3x3 / stride-2 max-pool with argmax, fused:
+// the LRN output is kept only in LDS (rounded to T exactly as a stored tensor
+// would be), so pooled values and argmax equal those of the two separate
+// steps.  One workgroup per (image n, pair of pooled rows i0 = 2 p, i0 + 1)
+// over input rows 2 i0 .. 2 i0 + 4 (Hin = 2 Ho + 1; the last pair of an odd Ho
+// has one pooled row and three input rows), one contiguous run of NHWC:
+//   1. the run is copied into LDS with direct-to-LDS loads (one wait);
+//   2. each thread normalises its (row, column, 8-channel) units from LDS into
+//      registers and, after a barrier, writes them back in place -- rows 0..2
+//      and then rows 3..4, to bound the registers held;
+//   3. the pooled rows and their argmax are taken from LDS.
+// For bf16 the window maximum is taken on integer keys (value bits << 16 |
+// 15 - d): the inputs are ReLU outputs, so every LRN output is >= +0 and its
+// bf16 bits order as its value, and the key's low bits make the first of equal
+// maxima in row-major scan order win, as in the float comparison.
+// `dbg`, if not null, receives the LRN output of the rows the workgroup owns
+// (2 i0 .. 2 i0 + 3, and the image's last row).  Workgroups are remapped so
+// that the pairs of one image, which share an input row, run on one XCD.
+constexpr int LRNPOOL_TPB = 512;
+
+template <typename T, int H, bool B075, int Win, int C, int R0, int R1>
+__device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, T* __restrict__ dbg, size_t dbg_row0, int own_last,
+                                              float k, float alpha, float beta) {
+  constexpr int cpp = C / 8, rowu = Win * cpp;
+  constexpr int UPT = ((R1 - R0) * rowu + LRNPOOL_TPB - 1) / LRNPOOL_TPB;
+  const int tid = threadIdx.x;
+  const int units = (min(R1, nrows) - R0) * rowu;
+  float o[UPT][8];
+#pragma unroll
+  for (int t = 0; t < UPT; ++t) {
+    const int u = tid + t * LRNPOOL_TPB;
+    if (u < units) {
+      const int pix = R0 * Win + u / cpp, c0 = (u % cpp) * 8;
+      lrn_unit<T, H, B075, C>(rows + pix * C, c0, k, alpha, beta, o[t]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < UPT; ++t) {
+    const int u = tid + t * LRNPOOL_TPB;
+    if (u < units) {
+      const int pix = R0 * Win + u / cpp, c0 = (u % cpp) * 8;
+      Pack8<T>::store(rows + pix * C + c0, o[t]);
+      const int rr = pix / Win;
+      if (dbg && (rr < 4 || own_last)) Pack8<T>::store(dbg + dbg_row0 + (size_t)pix * C + c0, o[t]);
+    }
+  }
+}
+
+template <typename T, int H, bool B075, int Win, int C>
+__global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ a, T* __restrict__ y,
+                                                          uint8_t* __restrict__ arg, T* __restrict__ dbg,
+                                                          float k, float alpha, float beta) {
+  constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, NP = (Ho + 1) / 2;
+  static_assert(C % 8 == 0 && Hin == 2 * Ho + 1, "fused LRN/pool geometry");
+  constexpr int LDS_BYTES = ((5 * Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  T* rows = reinterpret_cast<T*>(lds);
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
+  const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
+  const int n = b / NP, i0 = (b - n * NP) * 2;
+  const int npool = min(2, Ho - i0), nrows = 2 * npool + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int cpp = C >> 3;
+  const size_t img = (size_t)Hin * Win * C;
+  // 1. input rows 2 i0 .. 2 i0 + nrows - 1 -> LDS (1 KB per wave instruction; past the image reads as zero)
+  {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + n * img, (uint32_t)(img * sizeof(T)));
+    const uint32_t base = (uint32_t)((size_t)2 * i0 * Win * C * sizeof(T));
+    const int nins = (nrows * Win * C * (int)sizeof(T) + 1023) / 1024;
+    for (int j = wave; j < nins; j += LRNPOOL_TPB / 64)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
+                                               (int)(base + j * 1024 + lane * 16), 0, 0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  // 2. LRN in place, rows 0..2 then 3..4
+  const size_t dbg_row0 = ((size_t)n * Hin + 2 * i0) * Win * C;
+  const int own_last = 2 * i0 + nrows == Hin;
+  lrn_pool_rows<T, H, B075, Win, C, 0, 3>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
+  if (nrows > 3) lrn_pool_rows<T, H, B075, Win, C, 3, 5>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
+  __syncthreads();
+  // 3. pool: pooled row i0 + ii from LDS rows 2 ii .. 2 ii + 2, columns 2j .. 2j+2
+  for (int u = tid; u < npool * Wo * cpp; u += LRNPOOL_TPB) {
+    const int ii = u / (Wo * cpp), ju = u - ii * (Wo * cpp);
+    const int j = ju / cpp, c0 = (ju - j * cpp) * 8;
+    const T* px = rows + ((2 * ii) * Win + 2 * j) * C + c0;
+    const size_t og = (((size_t)n * Ho + i0 + ii) * Wo + j) * C + c0;
+    uint32_t bi[8];
+    if constexpr (std::is_same<T, bf16>::value) {
+      uint32_t key[8];
+#pragma unroll
+      for (int d = 0; d < 9; ++d) {
+        const int dy = d / 3, dx = d % 3;
+        const uint4 qv = *reinterpret_cast<const uint4*>(px + (dy * Win + dx) * C);
+        const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t code = 15u - (uint32_t)d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t klo = (w[e] << 16) | code, khi = (w[e] & 0xFFFF0000u) | code;
+          key[2 * e] = d == 0 ? klo : max(key[2 * e], klo);
+          key[2 * e + 1] = d == 0 ? khi : max(key[2 * e + 1], khi);
+        }
+      }
+      uint32_t ow[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ow[e] = (key[2 * e] >> 16) | (key[2 * e + 1] & 0xFFFF0000u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bi[e] = 15u - (key[e] & 15u);
+      *reinterpret_cast<uint4*>(y + og) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    } else {
+      float best[8], v[8];
+      Pack8<T>::load(px, best);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bi[e] = 0;
+#pragma unroll
+      for (int d = 1; d < 9; ++d) {
+        const int dy = d / 3, dx = d % 3;
+        Pack8<T>::load(px + (dy * Win + dx) * C, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
+      }
+      Pack8<T>::store(y + og, best);
+    }
+    *reinterpret_cast<uint2*>(arg + og) = make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
+                                                     bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
   }
 }
 
@@ -1007,20 +1194,8 @@ __global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, 
     const int u = tid + t * TPB;
     if (u < units) {
       const int w = u / cpp, c0 = (u - w * cpp) * 8;
-      float av[24], gv[24];
-#pragma unroll
-      for (int hh = 0; hh < 3; ++hh) {
-        const int cc = c0 + (hh - 1) * 8;
-        if (cc >= 0 && cc < C) {
-          Pack8<T>::load(arow + w * C + cc, av + hh * 8);
-          Pack8<T>::load(grow + w * C + cc, gv + hh * 8);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { av[hh * 8 + e] = 0.f; gv[hh * 8 + e] = 0.f; }
-        }
-      }
       float o[8];
-      lrn_bwd8<H, B075>(av, gv, k, alpha, beta, o);
+      lrn_bwd_unit<T, H, B075, C>(arow + w * C, grow + w * C, c0, k, alpha, beta, o);
       Pack8<T>::store(da + row0 + w * C + c0, o);
     }
   }
@@ -1045,7 +1220,8 @@ struct LrnPoolFn {
   template <int H, bool B075>
   hipError_t operator()() const {
     constexpr int Ho = (Win - 1) / 2;
-    hipLaunchKernelGGL((k_lrn_pool<T, H, B075, Win, C>), dim3(N * Ho), dim3(LRNPOOL_TPB), 0, st, (const T*)a,
+    hipLaunchKernelGGL((k_lrn_pool<T, H, B075, Win, C>), dim3(N * ((Ho + 1) / 2)), dim3(LRNPOOL_TPB), 0, st,
+                       (const T*)a,
                        (T*)y, arg, (T*)dbg, k, alpha, beta);
     return hipGetLastError();
   }
@@ -1337,9 +1513,11 @@ hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t st) {
 // result goes straight to `out`; otherwise a second pass adds the row blocks
 // in order.
 static constexpr int COLSUM_CW = 512;
+// Row blocks per layer: all layers' blocks run in one launch, so 256 per
+// layer fill the chip, and each bias element then sums at most 256 partials.
 static int colsum_blocks(int64_t rows, int C) {
   const int ct = cdiv(C, COLSUM_CW);
-  int64_t nb = (1024 + ct - 1) / ct;                 // about 1024 workgroups
+  int64_t nb = (256 + ct - 1) / ct;
   nb = std::min<int64_t>(nb, (rows + 15) / 16);      // at least 16 rows per block
   return (int)std::max<int64_t>(nb, 1);
 }
@@ -1436,6 +1614,7 @@ __global__ void __launch_bounds__(TPB) k_bias_sgd(BiasArgs2 a) {
   const int col = e - a.cstart[j], C = a.cstart[j + 1] - a.cstart[j];
   const float* part = a.part[j];
   float s = 0.f;
+#pragma unroll 4
   for (int b = lane; b < a.nb[j]; b += 64) s += part[(int64_t)b * C + col];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
