@@ -72,9 +72,6 @@ def kernel_work(kt, n, groups):
         "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"],
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
-        # the stand-alone SGD kernel updates the conv weights only (FC weights are
-        # updated inside their weight-gradient GEMM, biases with their gradient)
-        "SGD": 22 * sum(conv_wcount(c, groups) for c in CONV),
         # bias gradients: every layer's output gradient read once (the partial
         # sums and the 22 B per bias of the update are below 0.1%)
         "BIAS": e * (act["55x96"] + act["27x256"] + 2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),

@@ -143,10 +143,14 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   return ALEXNET_OK;
 }
 
-// Backward pass.  The FC weight gradients are applied to (master, momentum,
-// work) of that layer inside their GEMM, after the layer's data gradient has
-// read the old working weights; every other gradient lands in the workspace
-// for the multi-tensor update that follows.
+// Backward pass, with the SGD update of every tensor folded in:
+//  - FC weights inside their weight-gradient GEMM, after the layer's data
+//    gradient has read the old working weights;
+//  - conv weights as their split-K gradient is reduced; the layer's data
+//    gradient reads the data-gradient copy prepared from the old weights at
+//    the start of the step;
+//  - biases with their gradients, in the last two launches.
+// Every gradient except the FC weights' also lands in the workspace (taps).
 int enqueue_backward(const Plan& p, void* const* work, float* const* master, float* const* momentum,
                      const SgdHyper& hy, void* ws, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
@@ -187,7 +191,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       ALEXNET_KT_CONV5_DGRAD};
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), st, T(ktw[i])));
+    const SgdTarget u{master[2 * i], momentum[2 * i], work[2 * i], hy};
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), &u, st, T(ktw[i])));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
                       tp(ws, p, din[i]), st, T(ktd[i])));
   }
@@ -197,7 +202,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN2_BWD)));
   {
     const ConvShape& s = net.conv[1];
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), st,
+    const SgdTarget u{master[2], momentum[2], work[2], hy};
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), &u, st,
                       T(ALEXNET_KT_CONV2_WGRAD)));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st,
                       T(ALEXNET_KT_CONV2_DGRAD)));
@@ -206,8 +212,11 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), tp(ws, p, T_CONV1),
                       tp(ws, p, T_DCONV1), c.lrn_taps ? tp(ws, p, T_DLRN1) : nullptr, N, 55, 55, 96, c.lrn_k,
                       c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
-  HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), st,
-                     T(ALEXNET_KT_CONV1_WGRAD)));
+  {
+    const SgdTarget u{master[0], momentum[0], work[0], hy};
+    HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), &u, st,
+                       T(ALEXNET_KT_CONV1_WGRAD)));
+  }
   // bias gradients of all eight layers, and their SGD update
   {
     const int dys[8] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5, T_DFC6, T_DFC7, T_DLOGITS};
@@ -320,22 +329,6 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
   if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
   const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
   if ((r = enqueue_backward(p, work, master, momentum, hy, ws, st, T)) != ALEXNET_OK) return r;
-  // the remaining tensors: conv weights (FC weights and all biases are done)
-  TensorSet ts;
-  for (int i = 0; i < 8; ++i) {
-    const bool fused = i >= 5;
-    ts.master[2 * i] = master[2 * i];
-    ts.master[2 * i + 1] = master[2 * i + 1];
-    ts.mom[2 * i] = momentum[2 * i];
-    ts.mom[2 * i + 1] = momentum[2 * i + 1];
-    ts.grad[2 * i] = fused ? nullptr : (const float*)tp(ws, p, T_GW1 + i);
-    ts.grad[2 * i + 1] = (const float*)tp(ws, p, T_GB1 + i);
-    ts.work[2 * i] = work[2 * i];
-    ts.work[2 * i + 1] = work[2 * i + 1];
-    ts.n[2 * i] = fused ? 0 : p.net.wcount[i];
-    ts.n[2 * i + 1] = 0;
-  }
-  if (sgd(dt, ts, lr, momentum_coef, weight_decay, st, T(ALEXNET_KT_SGD)) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;
 }
 

@@ -304,13 +304,62 @@ size_t conv1_wgrad_part_bytes(int Nimg) {
 //   r = (kh*KW + kw)*Cg + ci                                  (mode 1)
 //   r = ((kh/4)*3 + kw/4)*48 + ci*16 + (kh%4)*4 + kw%4        (mode 2: layer 1, space-to-depth;
 //                                                               r outside the 11x11 taps is dropped)
-// A block covers 32 runs of four consecutive r (16-byte coalesced loads along
-// the partial rows) with 8 split groups: group j sums splits j, j+8, ... in
-// order, then the 8 group sums are added in order of j.  Needs Np % 4 == 0.
+// followed, when w is not null, by the SGD update of those weights: fp32
+// master w and momentum v in place, working copy wb (the same element update
+// as every other SGD path).
+//
+// Mode 1, k_wgrad_finish: one workgroup (16 waves) per output channel co.  It sums the S
+// partial rows of co (Np = KH*KW*Cg values each, 16-byte loads, splits in
+// order) into an LDS row, then walks the channel's OIHW slice in order, so
+// the gradient, w, v and wb are read and written contiguously.
+constexpr int WF_TPB = 1024;   // 16 waves per output channel keep enough loads in flight
+template <typename T>
+__global__ void __launch_bounds__(WF_TPB) k_wgrad_finish(const float* __restrict__ part, int S, int Mg, int Np,
+                                                      int Cg, int KH, int KW, float* __restrict__ gw,
+                                                      float* __restrict__ w, float* __restrict__ v,
+                                                      T* __restrict__ wb, float lr, float mom, float wdlr) {
+  extern __shared__ float4 row4[];
+  float* row = reinterpret_cast<float*>(row4);
+  const int co = blockIdx.x, g = co / Mg, col = co - g * Mg;
+  const float4* p = reinterpret_cast<const float4*>(part + ((int64_t)g * S * Mg + col) * Np);
+  const int64_t ss4 = (int64_t)Mg * Np / 4;
+  for (int q = threadIdx.x; q < Np / 4; q += WF_TPB) {
+    float4 acc = p[q];
+#pragma unroll 4
+    for (int s = 1; s < S; ++s) {
+      const float4 x = p[s * ss4 + q];
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    row4[q] = acc;
+  }
+  __syncthreads();
+  const int taps = KH * KW;
+  const int64_t base = (int64_t)co * Np;   // OIHW slice of co (Cg*KH*KW == Np)
+  for (int o = threadIdx.x; o < Np; o += WF_TPB) {
+    const int ci = o / taps, t = o - ci * taps;
+    const float gv = row[t * Cg + ci];      // (kh*KW + kw)*Cg + ci with t = kh*KW + kw
+    gw[base + o] = gv;
+    if (w) {
+      float ww = w[base + o], vv = v[base + o];
+      sgd_elem(ww, vv, gv, mom, wdlr, lr);
+      w[base + o] = ww;
+      v[base + o] = vv;
+      wb[base + o] = Num<T>::store(ww);
+    }
+  }
+}
+
+// Mode 2 (layer 1: 96 channels, many splits), k_wgrad_reduce: a block covers
+// 32 runs of four consecutive r (16-byte coalesced loads along the partial
+// rows) with 8 split groups: group j sums splits j, j+8, ... in order, then
+// the 8 group sums are added in order of j.  Needs Np % 4 == 0.
 constexpr int WR_Q = 32, WR_G = TPB / WR_Q;
+template <typename T>
 __global__ void __launch_bounds__(TPB) k_wgrad_reduce(const float* __restrict__ part, int G, int S, int Mg,
                                                       int Np, int Cg, int KH, int KW, int mode,
-                                                      float* __restrict__ gw) {
+                                                      float* __restrict__ gw, float* __restrict__ w,
+                                                      float* __restrict__ v, T* __restrict__ wb, float lr,
+                                                      float mom, float wdlr) {
   __shared__ float4 red[WR_G][WR_Q];
   const int qd = threadIdx.x % WR_Q, j = threadIdx.x / WR_Q;
   const int64_t t = (int64_t)blockIdx.x * WR_Q + qd;
@@ -337,7 +386,7 @@ __global__ void __launch_bounds__(TPB) k_wgrad_reduce(const float* __restrict__ 
     const float4 q = red[jj][qd];
     a[0] += q.x; a[1] += q.y; a[2] += q.z; a[3] += q.w;
   }
-  float* out = gw + (int64_t)co * Cg * KH * KW;
+  const int64_t base = (int64_t)co * Cg * KH * KW;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = r0 + i;
@@ -350,15 +399,25 @@ __global__ void __launch_bounds__(TPB) k_wgrad_reduce(const float* __restrict__ 
       const int tp = r / Cg;
       ci = r - tp * Cg; kh = tp / KW; kw = tp - kh * KW;
     }
-    out[(ci * KH + kh) * KW + kw] = a[i];
+    const int64_t e = base + (ci * KH + kh) * KW + kw;
+    gw[e] = a[i];
+    if (w) {
+      float ww = w[e], vv = v[e];
+      sgd_elem(ww, vv, a[i], mom, wdlr, lr);
+      w[e] = ww;
+      v[e] = vv;
+      wb[e] = Num<T>::store(ww);
+    }
   }
 }
 
 static dim3 wgrad_reduce_grid(int64_t outputs4) { return dim3((unsigned)((outputs4 + WR_Q - 1) / WR_Q)); }
+static const SgdTarget kNoSgd{nullptr, nullptr, nullptr, {0.f, 0.f, 0.f}};
 
 template <typename T>
 static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x, float* part,
-                               size_t part_bytes, float* gw, hipStream_t st, const KTimer* kt) {
+                               size_t part_bytes, float* gw, const SgdTarget& u, hipStream_t st,
+                               const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
   const int N = s.K * s.K * Cig, P = s.Nimg * s.Ho * s.Wo;
@@ -384,20 +443,22 @@ static hipError_t conv_wgrad_t(const ConvShape& s, const void* dy, const void* x
     err = run_gemm<T, BM, BN, 2, 2>(a, b, e, Cog, N, P, s.groups, S, st, kt);
   }
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid((int64_t)s.Cout * N / 4), dim3(TPB), 0, st, part,
-                     s.groups, S, Cog, N, Cig, s.K, s.K, 1, gw);
+  if (N % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_wgrad_finish<T>), dim3(s.Cout), dim3(WF_TPB), N * sizeof(float), st, part, S, Cog, N, Cig,
+                     s.K, s.K, gw, u.w, u.v, (T*)u.wb, u.hy.lr, u.hy.mom, u.hy.wdlr);
   return hipGetLastError();
 }
 
 hipError_t conv_wgrad(DType dt, const ConvShape& s, const void* dy, const void* x, float* part,
-                      size_t part_bytes, float* gw, hipStream_t st, const KTimer* kt) {
-  return dt == BF16 ? conv_wgrad_t<bf16>(s, dy, x, part, part_bytes, gw, st, kt)
-                    : conv_wgrad_t<float>(s, dy, x, part, part_bytes, gw, st, kt);
+                      size_t part_bytes, float* gw, const SgdTarget* u, hipStream_t st, const KTimer* kt) {
+  const SgdTarget& t = u ? *u : kNoSgd;
+  return dt == BF16 ? conv_wgrad_t<bf16>(s, dy, x, part, part_bytes, gw, t, st, kt)
+                    : conv_wgrad_t<float>(s, dy, x, part, part_bytes, gw, t, st, kt);
 }
 
 template <typename T>
 static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                                float* gw, hipStream_t st, const KTimer* kt) {
+                                float* gw, const SgdTarget& u, hipStream_t st, const KTimer* kt) {
   constexpr int BM = 128, BN = 128;
   const int N = S2D_K, P = Nimg * 3025;
   const int S = wgrad_splits(cdiv(96, BM) * cdiv(N, BN), P);
@@ -413,15 +474,16 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   b.p = (const T*)xs; b.cg = conv1_geom(); b.rows = N; b.P = P;
   err = run_gemm<T, BM, BN, 2, 2>(a, b, e, 96, N, P, 1, S, st, kt);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_wgrad_reduce, wgrad_reduce_grid(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3, 11, 11, 2,
-                     gw);
+  hipLaunchKernelGGL((k_wgrad_reduce<T>), wgrad_reduce_grid(96 * N / 4), dim3(TPB), 0, st, part, 1, S, 96, N, 3,
+                     11, 11, 2, gw, u.w, u.v, (T*)u.wb, u.hy.lr, u.hy.mom, u.hy.wdlr);
   return hipGetLastError();
 }
 
 hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                       float* gw, hipStream_t st, const KTimer* kt) {
-  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, st, kt)
-                    : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, st, kt);
+                       float* gw, const SgdTarget* u, hipStream_t st, const KTimer* kt) {
+  const SgdTarget& t = u ? *u : kNoSgd;
+  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, t, st, kt)
+                    : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, t, st, kt);
 }
 
 // ---- fully-connected layers

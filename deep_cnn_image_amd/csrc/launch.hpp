@@ -66,13 +66,19 @@ hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, cons
 hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, const void* mask,
                       void* dx, hipStream_t,
                       const KTimer* kt = nullptr);
+// SGD hyper-parameters: learning rate, momentum, weight decay times learning rate.
+struct SgdHyper { float lr, mom, wdlr; };
+// Optional SGD applied to a weight gradient as it is reduced: fp32 master w and
+// momentum v (same layout as the gradient) in place, working copy wb in the
+// compute type; w == nullptr: gradient only.
+struct SgdTarget { float* w; float* v; void* wb; SgdHyper hy; };
 // fp32 weight gradient (OIHW) of layers 2-5; `part` is split-K scratch
 hipError_t conv_wgrad(DType, const ConvShape&, const void* dy, const void* x, float* part,
-                      size_t part_bytes, float* gw, hipStream_t,
+                      size_t part_bytes, float* gw, const SgdTarget* sgd, hipStream_t,
                       const KTimer* kt = nullptr);
 // fp32 weight gradient (OIHW) of layer 1 from the space-to-depth input xs
 hipError_t conv1_wgrad(DType, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
-                       float* gw, hipStream_t,
+                       float* gw, const SgdTarget* sgd, hipStream_t,
                       const KTimer* kt = nullptr);
 size_t conv_wgrad_part_bytes(const ConvShape&);
 size_t conv1_wgrad_part_bytes(int Nimg);
@@ -96,7 +102,6 @@ hipError_t fc_dgrad(DType, int M, int K, int O, const void* dy, const void* w, c
                       const KTimer* kt = nullptr);
 // dW[O][K] fp32 = dy^T x
 // SGD hyper-parameters as the update uses them (wdlr = weight decay * lr).
-struct SgdHyper { float lr, mom, wdlr; };
 // FC weight gradient dW = dY^T X, applied at once to the layer's fp32 master
 // weights w, momentum v and working copy wb (sgd_elem); dW is not stored.
 hipError_t fc_wgrad_sgd(DType, int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,

@@ -124,12 +124,15 @@ int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16]
  *                undefined loss and gradient but never an out-of-bounds access
  *   loss         one fp32 (device), the batch-mean cross-entropy
  *   probs        optional [batch][1000] fp32 softmax output (may be null)
- * The three FC weight tensors are updated inside the GEMM that forms their
- * gradient, after that layer's data gradient has read the old working
- * weights, so every tensor still sees the gradient of the pre-step weights;
- * those gradients are never stored.  The conv weight gradients and all bias
- * gradients stay in the workspace (taps gw1..gw5, gb1..gb8) until the next
- * call; gw6..gw8 do not exist (alexnet_tap returns ALEXNET_E_ARG). */
+ * Each tensor is updated as soon as its gradient is complete: the three FC
+ * weight tensors inside the GEMM that forms their gradient (after that layer's
+ * data gradient has read the old working weights), the conv weights as their
+ * split-K gradient is reduced (the data gradients read a copy of the old
+ * weights made at the start of the step), the biases with their gradients.
+ * Every gradient is therefore that of the pre-step weights.  The conv weight
+ * gradients and all bias gradients stay in the workspace (taps gw1..gw5,
+ * gb1..gb8) until the next call; the FC weight gradients are never stored and
+ * gw6..gw8 do not exist (alexnet_tap returns ALEXNET_E_ARG). */
 int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
                        void* const work[16], const void* x, const int32_t* labels, float lr,
                        float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
@@ -172,7 +175,6 @@ typedef enum {
   ALEXNET_KT_CONV5_DGRAD, ALEXNET_KT_CONV4_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV2_DGRAD,
   ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
   ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
-  ALEXNET_KT_SGD,
   ALEXNET_KT_WPREP,            /* every weight re-layout of the call, one launch */
   ALEXNET_KT_BIAS,             /* all bias gradients + their SGD (two launches)  */
   ALEXNET_KT_COUNT
