@@ -43,7 +43,7 @@ def conv_wcount(name, groups):
     return cout * (cin // (groups if grouped else 1)) * k * k
 
 
-def kernel_work(kt, n, groups):
+def kernel_work(kt, n, groups, train=True):
     """Algorithmic work of one launch: ("mfma", FLOP) or ("hbm", bytes).
     Bytes count each input read once and each output written once (bf16
     activations, uint8 argmax, fp32 optimizer state)."""
@@ -63,7 +63,11 @@ def kernel_work(kt, n, groups):
     act = {"55x96": n * 55 * 55 * 96, "27x96": n * 27 * 27 * 96, "27x256": n * 27 * 27 * 256,
            "13x256": n * 13 * 13 * 256, "6x256": n * 6 * 6 * 256}
     table = {
-        "S2D": e * (n * 3 * 227 * 227 + n * 57 * 57 * 48),
+        # layer-1 input staging, and in the same launch the weight re-layouts:
+        # each OIHW source read once; the layer-1 block layout, the forward copies
+        # of conv2..5 and, for a training step, their data-gradient copies written
+        "S2D": e * (n * 3 * 227 * 227 + n * 57 * 57 * 48 + 96 * 3 * 11 * 11 + 96 * 432
+                    + (3 if train else 2) * sum(conv_wcount(c, groups) for c in CONV if c != "CONV1")),
         # LRN + max-pool fused: LRN input read once, pooled values and argmax written
         "LRNPOOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
         "LRNPOOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
@@ -75,10 +79,6 @@ def kernel_work(kt, n, groups):
         # bias gradients: every layer's output gradient read once (the partial
         # sums and the 22 B per bias of the update are below 0.1%)
         "BIAS": e * (act["55x96"] + act["27x256"] + 2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
-        # weight re-layouts of a training step: each OIHW source read once; the
-        # layer-1 block layout, and the forward and data-gradient copies of
-        # conv2..5, written once
-        "WPREP": e * (96 * 3 * 11 * 11 + 96 * 432 + 3 * sum(conv_wcount(c, groups) for c in CONV if c != "CONV1")),
     }
     return "hbm", float(table[kt])
 
@@ -233,8 +233,8 @@ def main():
         del fs
 
     # ---------------------------------------------------------------- fractions of roofline
-    def frac(nm, ms, groups=1):
-        kind, work = kernel_work(nm, n, groups)
+    def frac(nm, ms, groups=1, train=True):
+        kind, work = kernel_work(nm, n, groups, train)
         if kind == "mfma":
             return {"bound": "mfma", "TFLOP/s": round(work / (ms * 1e-3) / 1e12, 1),
                     "frac": round(work / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "us": round(ms * 1e3, 2)}
@@ -279,7 +279,7 @@ def main():
                               "ms": round(fwd["two_tower"] * 1e3, 4)},
         "train_conv_mfma_frac": round(conv_train_flops / (conv_train_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels_train": kernels_train,
-        "kernels_forward": {nm: frac(nm, ms) for nm, ms in fwd_kernels["single"].items()},
+        "kernels_forward": {nm: frac(nm, ms, train=False) for nm, ms in fwd_kernels["single"].items()},
         "roofline": roofline,
     }
 

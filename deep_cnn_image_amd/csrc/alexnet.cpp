@@ -94,12 +94,11 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
         jobs[nj++] =
             WeightPrep{WPREP_DGRAD, prm[2 * i], at(ws, p.wt[i]), s.Cout, s.Cin / s.groups, s.K, s.groups};
     }
-    HIPCHK(prep_weights(dt, jobs, nj, st, T(ALEXNET_KT_WPREP)));
+    // together with the layer-1 input staging
+    const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
+    const int hs = tenview ? 256 : 227;
+    HIPCHK(stage_inputs(dt, jobs, nj, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
   }
-
-  const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
-  const int hs = tenview ? 256 : 227;
-  HIPCHK(conv1_s2d(dt, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
   HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st,
                    T(ALEXNET_KT_CONV1_FWD)));
   HIPCHK(lrn_pool_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1),

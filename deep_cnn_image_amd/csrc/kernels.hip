@@ -82,14 +82,14 @@ __device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, i
 // view's offset, mirrored for views 5..9).  `total` is the element count of x;
 // a chunk that would cross its end is read element by element.
 template <typename T>
-__global__ void __launch_bounds__(TPB) k_s2d(const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws,
-                                             int tenview, int64_t total) {
+__device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws,
+                                          int tenview, int64_t total) {
   constexpr int V = 16 / (int)sizeof(T);                // elements per chunk
   constexpr int RCH = (V + 225) / V + 1;                // chunks per staged row (span of 227 at shift < V)
   constexpr int RS = RCH * V;                           // LDS row stride, elements
   __shared__ __attribute__((aligned(16))) T rows[12 * RS];
   __shared__ int shift[12];
-  const int n = blockIdx.x / S2D_B, bh = blockIdx.x - n * S2D_B;
+  const int n = blk / S2D_B, bh = blk - n * S2D_B;
   int y0 = 0, x0 = 0, flip = 0;
   int64_t img;
   if (tenview) {
@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(TPB) k_s2d(const T* __restrict__ x, T* __restr
     *reinterpret_cast<uint4*>(rows + r * RS + ch * V) = q;
   }
   __syncthreads();
-  T* out = xs + (int64_t)blockIdx.x * S2D_B * S2D_C;
+  T* out = xs + (int64_t)blk * S2D_B * S2D_C;
   for (int i = threadIdx.x; i < S2D_B * S2D_C / V; i += TPB) {
     const int bw = (i * V) / S2D_C, q0 = i * V - bw * S2D_C;
     T e[V];
@@ -134,18 +134,6 @@ __global__ void __launch_bounds__(TPB) k_s2d(const T* __restrict__ x, T* __restr
   }
 }
 
-hipError_t conv1_s2d(DType dt, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs,
-                     hipStream_t st, const KTimer* kt) {
-  const dim3 g(Nimg * S2D_B);
-  const int64_t total = (int64_t)(tenview ? Nimg / 10 : Nimg) * 3 * Hs * Ws;
-  rec_start(kt, st);
-  if (dt == BF16)
-    hipLaunchKernelGGL((k_s2d<bf16>), g, dim3(TPB), 0, st, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview, total);
-  else
-    hipLaunchKernelGGL((k_s2d<float>), g, dim3(TPB), 0, st, (const float*)x, (float*)xs, Hs, Ws, tenview, total);
-  rec_stop(kt, st);
-  return hipGetLastError();
-}
 
 
 static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
@@ -698,9 +686,9 @@ struct PrepArgs {
 };
 
 template <typename T>
-__global__ void __launch_bounds__(TPB) k_prep_weights(PrepArgs a) {
-  __shared__ T tile[WPREP_LDS_ELEMS];
-  const int bid = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void prep_block(int bid, const PrepArgs& a) {
+  __shared__ __attribute__((aligned(16))) T tile[WPREP_LDS_ELEMS];
+  const int tid = threadIdx.x;
   int j = 0;
 #pragma unroll
   for (int q = 1; q < WPREP_MAX; ++q) j += (q < a.n && bid >= a.bstart[q]) ? 1 : 0;
@@ -718,53 +706,82 @@ __global__ void __launch_bounds__(TPB) k_prep_weights(PrepArgs a) {
     return;
   }
   const int KK = a.K[j] * a.K[j], blocked = a.blocked[j];
+  constexpr int V = 16 / (int)sizeof(T);   // elements per 16-byte access
   if (kind == WPREP_KHWC) {
+    // n = Cg*K*K is a multiple of V (host-checked): 16-byte copies in and out
     const int Cg = a.Cig[j], n = Cg * KK, co = local;
     const T* s = src + (int64_t)co * n;
-    for (int e = tid; e < n; e += TPB) tile[e] = s[e];
+    for (int e = tid * V; e < n; e += TPB * V) *reinterpret_cast<uint4*>(tile + e) = *reinterpret_cast<const uint4*>(s + e);
     __syncthreads();
     T* d = dst + (int64_t)co * n;
-    for (int o = tid; o < n; o += TPB) {
-      int ci, tap;
-      if (blocked) {
-        const int t2 = o / GEMM_BK;
-        tap = t2 % KK;
-        ci = (t2 / KK) * GEMM_BK + (o - t2 * GEMM_BK);
-      } else {
-        tap = o / Cg;
-        ci = o - tap * Cg;
+    for (int o0 = tid * V; o0 < n; o0 += TPB * V) {
+      T v[V];
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const int o = o0 + q;
+        int ci, tap;
+        if (blocked) {
+          const int t2 = o / GEMM_BK;
+          tap = t2 % KK;
+          ci = (t2 / KK) * GEMM_BK + (o - t2 * GEMM_BK);
+        } else {
+          tap = o / Cg;
+          ci = o - tap * Cg;
+        }
+        v[q] = tile[ci * KK + tap];
       }
-      d[o] = tile[ci * KK + tap];
+      *reinterpret_cast<uint4*>(d + o0) = pack_u4(v);
     }
     return;
   }
-  // DGRAD: tile (g, col block, e block), e = ci*KK + tap over W[g*Cog + col][ci][tap]
+  // DGRAD: tile (g, col block, e block), e = ci*KK + tap over W[g*Cog + col][ci][tap];
+  // Cog and Cig*KK are multiples of V (host-checked), so every 16-byte access is whole
   const int Cog = a.Cog[j], Cig = a.Cig[j], nE = Cig * KK;
   const int ncb = (Cog + WPREP_T - 1) / WPREP_T, neb = (nE + WPREP_T - 1) / WPREP_T;
   const int g = local / (ncb * neb), rem = local - g * ncb * neb;
   const int col0 = (rem / neb) * WPREP_T, e0 = (rem % neb) * WPREP_T;
-  for (int idx = tid; idx < WPREP_T * WPREP_T; idx += TPB) {
-    const int c = idx / WPREP_T, e = idx - c * WPREP_T;
-    if (col0 + c < Cog && e0 + e < nE)
-      tile[c * (WPREP_T + 1) + e] = src[(int64_t)(g * Cog + col0 + c) * nE + e0 + e];
+  constexpr int VPR = WPREP_T / V;   // 16-byte pieces per tile row
+  for (int idx = tid; idx < WPREP_T * VPR; idx += TPB) {
+    const int c = idx / VPR, e = (idx - c * VPR) * V;
+    if (col0 + c < Cog && e0 + e < nE) {
+      T v[V];
+      unpack_u4(*reinterpret_cast<const uint4*>(src + (int64_t)(g * Cog + col0 + c) * nE + e0 + e), v);
+#pragma unroll
+      for (int q = 0; q < V; ++q) tile[c * (WPREP_T + 1) + e + q] = v[q];
+    }
   }
   __syncthreads();
   const int nblk = Cog / GEMM_BK;
-  for (int idx = tid; idx < WPREP_T * WPREP_T; idx += TPB) {
-    const int e = idx / WPREP_T, c = idx - e * WPREP_T;
+  for (int idx = tid; idx < WPREP_T * VPR; idx += TPB) {
+    const int e = idx / VPR, c = (idx - e * VPR) * V;
     const int col = col0 + c, ee = e0 + e;
     if (col >= Cog || ee >= nE) continue;
     const int ci = ee / KK, tapo = KK - 1 - (ee - ci * KK);   // output tap takes the flipped source tap
+    T v[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) v[q] = tile[(c + q) * (WPREP_T + 1) + e];
     int64_t o;
     if (blocked) o = (((int64_t)(g * Cig + ci) * nblk + col / GEMM_BK) * KK + tapo) * GEMM_BK + (col % GEMM_BK);
     else o = ((int64_t)(g * Cig + ci) * KK + tapo) * Cog + col;
-    dst[o] = tile[c * (WPREP_T + 1) + e];
+    *reinterpret_cast<uint4*>(dst + o) = pack_u4(v);
   }
 }
 
 bool im2col_blocked(DType dt, int Cg) { return dt == BF16 && Cg % GEMM_BK == 0; }
 
-hipError_t prep_weights(DType dt, const WeightPrep* jobs, int n, hipStream_t st, const KTimer* kt) {
+// Start of every call, one launch: the weight re-layouts (workgroups below
+// a.bstart[a.n]) and the layer-1 input staging (one workgroup per image and
+// block row after them) are independent of each other.
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_stage(PrepArgs a, const T* __restrict__ x, T* __restrict__ xs, int Hs,
+                                               int Ws, int tenview, int64_t total) {
+  const int prep_blocks = a.bstart[a.n];
+  if ((int)blockIdx.x < prep_blocks) prep_block<T>(blockIdx.x, a);
+  else s2d_block<T>(blockIdx.x - prep_blocks, x, xs, Hs, Ws, tenview, total);
+}
+
+hipError_t stage_inputs(DType dt, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int tenview,
+                        int Nimg, void* xs, hipStream_t st, const KTimer* kt) {
   if (n < 1 || n > WPREP_MAX) return hipErrorInvalidValue;
   PrepArgs a = {};
   a.n = n;
@@ -781,13 +798,13 @@ hipError_t prep_weights(DType dt, const WeightPrep* jobs, int n, hipStream_t st,
         count = (int64_t)S2D_W_ELEMS;
         break;
       case WPREP_KHWC:   // Cig = input channels per group; one workgroup per co
-        if (w.Cig * w.K * w.K > WPREP_LDS_ELEMS) return hipErrorInvalidValue;
+        if (w.Cig * w.K * w.K > WPREP_LDS_ELEMS || (w.Cig * w.K * w.K) % 8) return hipErrorInvalidValue;
         a.Cig[j] = w.Cig;
         a.blocked[j] = im2col_blocked(dt, w.Cig) ? 1 : 0;
         count = w.Cout;
         break;
       case WPREP_DGRAD:  // one workgroup per 64 x 64 tile
-        if (w.G < 1 || w.Cout % w.G) return hipErrorInvalidValue;
+        if (w.G < 1 || w.Cout % w.G || (w.Cout / w.G) % 8 || (w.Cig * w.K * w.K) % 8) return hipErrorInvalidValue;
         a.Cog[j] = w.Cout / w.G;
         a.Cig[j] = w.Cig;
         a.blocked[j] = im2col_blocked(dt, a.Cog[j]) ? 1 : 0;
@@ -802,9 +819,14 @@ hipError_t prep_weights(DType dt, const WeightPrep* jobs, int n, hipStream_t st,
     blocks += w.kind == WPREP_W1S ? cdiv(count, TPB) : (int)count;
   }
   a.bstart[n] = blocks;
+  const int64_t total = (int64_t)(tenview ? Nimg / 10 : Nimg) * 3 * Hs * Ws;
+  const dim3 g(blocks + Nimg * S2D_B);
   rec_start(kt, st);
-  if (dt == BF16) hipLaunchKernelGGL((k_prep_weights<bf16>), dim3(blocks), dim3(TPB), 0, st, a);
-  else hipLaunchKernelGGL((k_prep_weights<float>), dim3(blocks), dim3(TPB), 0, st, a);
+  if (dt == BF16)
+    hipLaunchKernelGGL((k_stage<bf16>), g, dim3(TPB), 0, st, a, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview, total);
+  else
+    hipLaunchKernelGGL((k_stage<float>), g, dim3(TPB), 0, st, a, (const float*)x, (float*)xs, Hs, Ws, tenview,
+                       total);
   rec_stop(kt, st);
   return hipGetLastError();
 }
@@ -1341,10 +1363,53 @@ hipError_t pool_lrn_bwd(DType dt, const void* dy, const uint8_t* arg, const void
 // first maximum in a row-major scan of the window)
 // =========================================================================
 // Pool 5: max-pool whose output is flattened in (c, h, w) order for FC6.
-// One workgroup per (image n, 128-channel block): pooled values go to LDS as
-// [c][h*Wo+w], which is exactly the block's contiguous run of the flat output.
-constexpr int POOL5_CB = 128;   // channels per workgroup
+// One workgroup per (image n, 32-channel block): one thread per (position,
+// 8-channel) unit takes its window's maximum and argmax; the pooled values go
+// to LDS as [c][h*Wo+w], which is exactly the block's contiguous run of the
+// flat output.  For bf16 the maximum is taken on integer keys (value bits <<
+// 16 | 15 - d), valid because the input is a ReLU output (every value >= +0,
+// so bf16 bits order as values); equal maxima resolve to the first in
+// row-major scan order, as in the float comparison.
+constexpr int POOL5_CB = 32;    // channels per workgroup
 constexpr int POOL5_P = 64;     // max pooled positions (Ho * Wo)
+
+// max/argmax of the 3x3 window at px (row stride W*C elements) for 8 channels
+template <typename T>
+__device__ __forceinline__ void pool_window8(const T* px, int64_t rs, int C, float* best, uint32_t* bi) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    uint32_t key[8];
+#pragma unroll
+    for (int d = 0; d < 9; ++d) {
+      const uint4 q = *reinterpret_cast<const uint4*>(px + (d / 3) * rs + (d % 3) * C);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      const uint32_t code = 15u - (uint32_t)d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t klo = (w[e] << 16) | code, khi = (w[e] & 0xFFFF0000u) | code;
+        key[2 * e] = d == 0 ? klo : max(key[2 * e], klo);
+        key[2 * e + 1] = d == 0 ? khi : max(key[2 * e + 1], khi);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      best[e] = __uint_as_float(key[e] & 0xFFFF0000u);
+      bi[e] = 15u - (key[e] & 15u);
+    }
+  } else {
+    float v[8];
+    Pack8<T>::load(px, best);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bi[e] = 0;
+#pragma unroll
+    for (int d = 1; d < 9; ++d) {
+      Pack8<T>::load(px + (d / 3) * rs + (d % 3) * C, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_pool5_fwd(const T* __restrict__ x, T* __restrict__ y,
                                                    uint8_t* __restrict__ arg, int H, int W, int C, int Ho,
@@ -1352,23 +1417,13 @@ __global__ void __launch_bounds__(TPB) k_pool5_fwd(const T* __restrict__ x, T* _
   __shared__ __attribute__((aligned(16))) T ly[POOL5_CB * POOL5_P];
   const int nblk = C / POOL5_CB, n = blockIdx.x / nblk, cb = blockIdx.x - n * nblk;
   const int P = Ho * Wo, units = P * (POOL5_CB / 8);
-  for (int u = threadIdx.x; u < units; u += TPB) {
+  const int u = threadIdx.x;
+  if (u < units) {
     const int pos = u / (POOL5_CB / 8), ch8 = u - pos * (POOL5_CB / 8);
     const int i = pos / Wo, j = pos - i * Wo, c0 = cb * POOL5_CB + ch8 * 8;
-    const T* base = x + (((size_t)n * H + 2 * i) * W + 2 * j) * C + c0;
-    float best[8], v[8];
+    float best[8];
     uint32_t bi[8];
-    Pack8<T>::load(base, best);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bi[e] = 0;
-#pragma unroll
-    for (int d = 1; d < 9; ++d) {
-      const int dy = d / 3, dx = d % 3;
-      Pack8<T>::load(base + ((size_t)dy * W + dx) * C, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
-    }
+    pool_window8<T>(x + (((size_t)n * H + 2 * i) * W + 2 * j) * C + c0, (int64_t)W * C, C, best, bi);
     *reinterpret_cast<uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0) =
         make_uint2(bi[0] | (bi[1] << 8) | (bi[2] << 16) | (bi[3] << 24),
                    bi[4] | (bi[5] << 8) | (bi[6] << 16) | (bi[7] << 24));
@@ -1384,56 +1439,74 @@ __global__ void __launch_bounds__(TPB) k_pool5_fwd(const T* __restrict__ x, T* _
 }
 
 // Pool-5 backward from the flat (c, h, w) gradient, times the ReLU mask of
-// the pool input [mask > 0]: one workgroup per (image n, 128-channel block,
-// input row h).  The block's run of the flat gradient is transposed into LDS
-// as [h*Wo+w][c]; each thread then sums, for one (column, 8-channel) unit, the
-// windows whose argmax is the pixel (windows in row-major order).
+// the pool input [mask > 0]: one workgroup per (image n, 32-channel block).
+// The block's run of the flat gradient (POOL5_CB * P values) is read once in
+// 4-element pieces and transposed into LDS as [h*Wo+w][c]; each thread then
+// sums, for its (row, column, 8-channel) units, the windows whose argmax is
+// the pixel (windows in row-major order).
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_pool5_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
                                                    const T* __restrict__ mask, T* __restrict__ dx, int H, int W,
                                                    int C, int Ho, int Wo) {
   constexpr int LS = POOL5_CB + 8;   // padded row: the transposing writes spread over banks
   __shared__ __attribute__((aligned(16))) T lg[POOL5_P * LS];
-  const int nblk = C / POOL5_CB;
-  const int h = blockIdx.x % H, nc = blockIdx.x / H, n = nc / nblk, cb = nc - n * nblk;
+  const int nblk = C / POOL5_CB, n = blockIdx.x / nblk, cb = blockIdx.x - n * nblk;
   const int P = Ho * Wo;
   const T* src = dy + (size_t)n * C * P + (size_t)cb * POOL5_CB * P;
-  for (int e = threadIdx.x; e < POOL5_CB * P; e += TPB) {
-    const int c = e / P, pos = e - c * P;
-    lg[pos * LS + c] = src[e];
+  for (int e4 = threadIdx.x; e4 < POOL5_CB * P / 4; e4 += TPB) {
+    T v[4];
+    if constexpr (sizeof(T) == 2) {
+      const uint2 q = *reinterpret_cast<const uint2*>(src + e4 * 4);
+      v[0] = (T)(q.x & 0xFFFFu); v[1] = (T)(q.x >> 16); v[2] = (T)(q.y & 0xFFFFu); v[3] = (T)(q.y >> 16);
+    } else {
+      const float4 q = *reinterpret_cast<const float4*>(src + e4 * 4);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = e4 * 4 + k, c = e / P, pos = e - c * P;
+      lg[pos * LS + c] = v[k];
+    }
   }
   __syncthreads();
-  const int ch8 = threadIdx.x % (POOL5_CB / 8), w = threadIdx.x / (POOL5_CB / 8);
-  if (w >= W) return;
-  const int c0 = cb * POOL5_CB + ch8 * 8;
-  const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
-  const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
-  float acc[8];
+  constexpr int CPP = POOL5_CB / 8;
+  for (int u = threadIdx.x; u < H * W * CPP; u += TPB) {
+    const int hw = u / CPP, ch8 = u - hw * CPP, h = hw / W, w = hw - h * W;
+    const int c0 = cb * POOL5_CB + ch8 * 8;
+    const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
+    const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
+    float acc[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int i = i0; i <= i1; ++i)
-    for (int j = j0; j <= j1; ++j) {
-      const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
-      const uint2 am = *reinterpret_cast<const uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0);
-      float g[8];
-      Pack8<T>::load(lg + (i * Wo + j) * LS + ch8 * 8, g);
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
-        if (b == code) acc[q] += g[q];
+    for (int di = 0; di < 2; ++di)
+#pragma unroll
+      for (int dj = 0; dj < 2; ++dj) {
+        const int i = i0 + di, j = j0 + dj;
+        if (i <= i1 && j <= j1) {
+          const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
+          const uint2 am = *reinterpret_cast<const uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0);
+          float g[8];
+          Pack8<T>::load(lg + (i * Wo + j) * LS + ch8 * 8, g);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+            if (b == code) acc[q] += g[q];
+          }
+        }
       }
-    }
-  const size_t o = (((size_t)n * H + h) * W + w) * C + c0;
-  float mk[8];
-  Pack8<T>::load(mask + o, mk);
+    const size_t o = (((size_t)n * H + h) * W + w) * C + c0;
+    float mk[8];
+    Pack8<T>::load(mask + o, mk);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
-  Pack8<T>::store(dx + o, acc);
+    for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
+    Pack8<T>::store(dx + o, acc);
+  }
 }
 
 static bool pool5_shape_ok(int H, int W, int C, int& Ho, int& Wo) {
   Ho = (H - 3) / 2 + 1; Wo = (W - 3) / 2 + 1;
-  return C % POOL5_CB == 0 && Ho * Wo <= POOL5_P && W * (POOL5_CB / 8) <= TPB &&
+  return C % POOL5_CB == 0 && Ho * Wo <= POOL5_P && Ho * Wo * (POOL5_CB / 8) <= TPB &&
          (POOL5_CB * Ho * Wo) % 8 == 0;
 }
 
@@ -1453,7 +1526,7 @@ hipError_t pool5_bwd(DType dt, const void* dy, const uint8_t* arg, const void* m
                      int W, int C, hipStream_t st, const KTimer* kt) {
   int Ho, Wo;
   if (!pool5_shape_ok(H, W, C, Ho, Wo) || !mask) return hipErrorInvalidValue;
-  const dim3 g(N * (C / POOL5_CB) * H);
+  const dim3 g(N * (C / POOL5_CB));
   rec_start(kt, st);
   if (dt == BF16) hipLaunchKernelGGL((k_pool5_bwd<bf16>), g, dim3(TPB), 0, st, (const bf16*)dy, arg, (const bf16*)mask, (bf16*)dx, H, W, C, Ho, Wo);
   else hipLaunchKernelGGL((k_pool5_bwd<float>), g, dim3(TPB), 0, st, (const float*)dy, arg, (const float*)mask, (float*)dx, H, W, C, Ho, Wo);

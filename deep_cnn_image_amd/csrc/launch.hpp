@@ -45,7 +45,10 @@ struct WeightPrep {
   void* dst;
   int Cout, Cig, K, G;
 };
-hipError_t prep_weights(DType, const WeightPrep* jobs, int n, hipStream_t, const KTimer* kt = nullptr);
+// One launch: the weight re-layouts `jobs` and the layer-1 input staging
+// (xs from the NCHW images x, or the crops of the ten-view sources).
+hipError_t stage_inputs(DType, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int tenview,
+                        int Nimg, void* xs, hipStream_t, const KTimer* kt = nullptr);
 
 // ---- convolutions (bf16 MFMA or fp32 MFMA, fp32 accumulate)
 // Layer 1 runs as a 3x3 stride-1 convolution over 4x4 pixel blocks:
@@ -53,8 +56,7 @@ hipError_t prep_weights(DType, const WeightPrep* jobs, int n, hipStream_t, const
 // mirrored), ws [96][432] from the OIHW weights.
 constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
 constexpr size_t S2D_W_ELEMS = 96 * 432;
-hipError_t conv1_s2d(DType, const void* x, int Hs, int Ws, int tenview, int Nimg, void* xs, hipStream_t,
-                      const KTimer* kt = nullptr);
+
 // y NHWC [N][55][55][96] = relu(conv1 + b)
 hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t,
                       const KTimer* kt = nullptr);

@@ -160,7 +160,8 @@ int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t ro
  * kernel alone, not its split-K reduction.  A kernel the call does not launch
  * records nothing.  timers may be NULL when n_timers is 0. */
 typedef enum {
-  ALEXNET_KT_S2D = 1,          /* layer-1 input staging (4x4 pixel blocks)      */
+  ALEXNET_KT_S2D = 1,          /* layer-1 input staging (4x4 pixel blocks) and all
+                                  weight re-layouts of the call, one launch      */
   ALEXNET_KT_CONV1_FWD, ALEXNET_KT_CONV2_FWD, ALEXNET_KT_CONV3_FWD, ALEXNET_KT_CONV4_FWD,
   ALEXNET_KT_CONV5_FWD,
   ALEXNET_KT_LRNPOOL1_FWD,     /* LRN1 + pool1 (one fused kernel)                */
@@ -175,7 +176,6 @@ typedef enum {
   ALEXNET_KT_CONV5_DGRAD, ALEXNET_KT_CONV4_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV2_DGRAD,
   ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
   ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
-  ALEXNET_KT_WPREP,            /* every weight re-layout of the call, one launch */
   ALEXNET_KT_BIAS,             /* all bias gradients + their SGD (two launches)  */
   ALEXNET_KT_COUNT
 } alexnet_kernel;
