@@ -781,6 +781,22 @@ struct Mma<bf16, FM, FN, LA, LB> {
       for (int j = 0; j < FN; ++j) f.b[s][j] = LB::frag(Bs, rb + j * 16, s * 32, lane);
     }
   }
+  // One 32-deep k-step of the slice.
+  struct Half { bf16x8_t a[FM], b[FN]; };
+  static __device__ __forceinline__ void read_half(const bf16* As, int ra, const bf16* Bs, int rb, int kk,
+                                                   Half& h, int lane) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) h.a[i] = LA::frag(As, ra + i * 16, kk, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) h.b[j] = LB::frag(Bs, rb + j * 16, kk, lane);
+  }
+  static __device__ __forceinline__ void mul_half(const Half& h, f32x4_t (&acc)[FM][FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h.a[i], h.b[j], acc[i][j], 0, 0, 0);
+  }
   static __device__ __forceinline__ void mul(const Frags& f, f32x4_t (&acc)[FM][FN]) {
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s)
@@ -838,6 +854,14 @@ template <typename T, int BM, int BN>
 constexpr int gemm_waves_per_simd() { return sizeof(T) == 2 ? 2 : 1; }
 template <typename T, int BM, int BN>
 constexpr int gemm_default_stages() { return 2; }
+// Read-ahead schedule (see k_gemm) for k-contiguous LDS tiles with wave tiles
+// of up to 18 fragments, where it measured faster; the slice-at-a-time
+// schedule elsewhere (it measured faster with transposing fragment reads and
+// with 96 x 64 wave tiles).
+template <class LA, class LB, int FM, int FN>
+constexpr bool gemm_read_ahead() {
+  return std::is_same<LA, LayoutKC<bf16>>::value && std::is_same<LB, LayoutKC<bf16>>::value && FM * FN <= 18;
+}
 
 template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP, int ST = 2>
 __global__ void __launch_bounds__(NTHREADS)
@@ -890,23 +914,66 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
 
   static_assert(AL::DMA == BL::DMA, "both operands direct-to-LDS or neither");
   if constexpr (AL::DMA) {
-    // ST LDS buffers; slice kt lands in buffer (kt - kt0) % ST and up to
-    // ST - 1 slices are in flight.  At the top of an iteration a wave waits
-    // until its own loads of slice kt have landed (loads complete in order,
-    // so it may leave the later slices outstanding); the barrier then
-    // publishes the slice from every wave and guarantees that all waves are
-    // done with the buffer read one iteration earlier, which the slice
-    // ST - 1 ahead then overwrites while the matrix cores work.  Fragments of
-    // the current slice are read into registers before those loads are
-    // issued, so no LDS read has to wait for them.  The loop is unrolled by ST
-    // so that buffer offsets are compile-time constants.
-    if (kt0 < kt1) {
-      constexpr int OPS = AL::NI + BL::NI;   // loads per wave per slice
+    // ST LDS buffers, slice kt in buffer (kt - kt0) % ST.  Both schedules
+    // unroll the loop by ST so that buffer offsets are compile-time constants.
+    using MM = Mma<T, FM, FN, LA, LB>;
+    constexpr int OPS = AL::NI + BL::NI;   // loads per wave per slice
+    constexpr bool RA = gemm_read_ahead<LA, LB, FM, FN>();
+    if constexpr (RA) {
+      // Read-ahead: slice kt sits in buffer (kt - kt0) % ST and up to ST
+      // slices are in flight.  Each k-step's fragments are read while the
+      // matrix cores multiply the previous k-step's, so no product waits on
+      // an LDS read issued just before it.  Between the two k-steps of a
+      // slice a wave waits for its own loads of the next slice, and the
+      // barrier publishes that slice from every wave; it also marks this
+      // slice's buffer as read by all waves, so the loads of slice kt + ST
+      // are issued into it right away.
+      if (kt0 < kt1) {
+        static_assert((ST - 1) * OPS < 64, "vmcnt range");
+        const int ra = wm * WTM, rb = wn * WTN;
+#pragma unroll
+        for (int p = 0; p < ST; ++p)
+          if (kt0 + p < kt1) { al.issue(As + p * A_EL); bl.issue(Bs + p * B_EL); }
+        wait_ahead<OPS, ST - 1>(kt1 - 1 - kt0);
+        lds_barrier();
+        typename MM::Half h0, h1;
+        MM::read_half(As, ra, Bs, rb, 0, h0, lane);
+        auto step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
+          constexpr int CUR = decltype(cur_c)::value;
+          constexpr int NXT = (CUR + 1) % ST;
+          MM::read_half(As + CUR * A_EL, ra, Bs + CUR * B_EL, rb, 32, h1, lane);
+          MM::mul_half(h0, acc);
+          __builtin_amdgcn_sched_barrier(0);
+          const bool more = kt + 1 < kt1;
+          if (more) wait_ahead<OPS, ST - 2>(kt1 - 2 - kt);
+          lds_barrier();
+          if (kt + ST < kt1) { al.issue(As + CUR * A_EL); bl.issue(Bs + CUR * B_EL); }
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) MM::read_half(As + NXT * A_EL, ra, Bs + NXT * B_EL, rb, 0, h0, lane);
+          MM::mul_half(h1, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = kt0;
+        for (; kt + ST - 1 < kt1; kt += ST)
+          unroll_steps(std::make_integer_sequence<int, ST>{},
+                       [&](auto i) __attribute__((always_inline)) { step(i, kt + decltype(i)::value); });
+        unroll_steps(std::make_integer_sequence<int, ST - 1>{}, [&](auto i) __attribute__((always_inline)) {
+          if (kt + decltype(i)::value < kt1) step(i, kt + decltype(i)::value);
+        });
+      }
+    } else if (kt0 < kt1) {
+      // Slice-at-a-time: up to ST - 1 slices in flight.  At the top of an
+      // iteration a wave waits until its own loads of slice kt have landed
+      // (loads complete in order, so it may leave the later slices
+      // outstanding); the barrier then publishes the slice from every wave and
+      // guarantees that all waves are done with the buffer read one iteration
+      // earlier, which the slice ST - 1 ahead then overwrites while the matrix
+      // cores work.  All fragments of the slice are read into registers before
+      // those loads are issued, so no LDS read has to wait for them.
       static_assert((ST - 2) * OPS < 64, "vmcnt range");
 #pragma unroll
       for (int p = 0; p < ST - 1; ++p)
         if (kt0 + p < kt1) { al.issue(As + p * A_EL); bl.issue(Bs + p * B_EL); }
-      using MM = Mma<T, FM, FN, LA, LB>;
       auto step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         const int ahead = kt1 - 1 - kt;   // slices issued after this one: min(ahead, ST - 2)
