@@ -43,6 +43,17 @@ template <> struct Num<bf16> {
   static __device__ __forceinline__ bf16 store(float v) { return f2bf(v); }
 };
 
+// 16-byte store marked non-temporal: the line is written back without being
+// kept dirty in the last-level (Infinity) cache, so later streaming reads do
+// not have to evict it first.  For data that is not read again soon.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt16(void* p, uint4 q) {
+  __builtin_nontemporal_store((u32x4_t){q.x, q.y, q.z, q.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_nt16(void* p, float4 q) {
+  st_nt16(p, make_uint4(__float_as_uint(q.x), __float_as_uint(q.y), __float_as_uint(q.z), __float_as_uint(q.w)));
+}
+
 // Eight consecutive elements of T as floats, from / to one or two 16-byte words.
 template <typename T> struct Pack8;
 template <> struct Pack8<bf16> {
@@ -61,6 +72,12 @@ template <> struct Pack8<bf16> {
     for (int i = 0; i < 4; ++i) w[i] = f2bf2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+  static __device__ __forceinline__ void store_nt(bf16* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f2bf2(v[2 * i], v[2 * i + 1]);
+    st_nt16(p, make_uint4(w[0], w[1], w[2], w[3]));
+  }
 };
 template <> struct Pack8<float> {
   static __device__ __forceinline__ void load(const float* p, float* v) {
@@ -72,6 +89,10 @@ template <> struct Pack8<float> {
   static __device__ __forceinline__ void store(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ void store_nt(float* p, const float* v) {
+    st_nt16(p, make_float4(v[0], v[1], v[2], v[3]));
+    st_nt16(p + 4, make_float4(v[4], v[5], v[6], v[7]));
   }
 };
 

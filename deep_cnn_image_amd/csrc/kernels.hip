@@ -627,11 +627,11 @@ struct EpSgd {
     float vv[8] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w, st.v1.x, st.v1.y, st.v1.z, st.v1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) sgd_elem(wv[i], vv[i], g[i], h.mom, h.wdlr, h.lr);
-    *reinterpret_cast<float4*>(w + o) = make_float4(wv[0], wv[1], wv[2], wv[3]);
-    *reinterpret_cast<float4*>(w + o + 4) = make_float4(wv[4], wv[5], wv[6], wv[7]);
-    *reinterpret_cast<float4*>(v + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-    *reinterpret_cast<float4*>(v + o + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
-    Pack8<T>::store(wb + o, wv);
+    // Nothing reads these before the next step: non-temporal stores keep the
+    // last-level cache clean for the streaming reads of the layers that follow.
+    Pack8<float>::store_nt(w + o, wv);
+    Pack8<float>::store_nt(v + o, vv);
+    Pack8<T>::store_nt(wb + o, wv);
   }
   // per-chunk form (used when a tile's chunk count does not split evenly)
   __device__ __forceinline__ void operator()(int m, int n, int, int, const float* g) const {
