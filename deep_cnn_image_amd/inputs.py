@@ -16,6 +16,17 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
 
 bf16 values are produced from float32 by round-to-nearest-even on the bit
 pattern; the float32 copy of a bf16 tensor holds exactly the bf16 value.
+
+Augmentation workload (``augment_inputs``, its own stream of ``seed``):
+  1. sources z ~ N(0, 1), float32 [N, 3, Hs, Ws], mixed across the colour
+     channels by the fixed matrix AUG_MIX = R diag(AUG_SPREAD) (R a rotation
+     by fixed angles), so the RGB covariance of the sources is close to
+     R diag(AUG_SPREAD^2) R^T with well separated eigenvalues, as in natural
+     images, where one colour component dominates;
+  2. per image: crop offsets y0 in [0, Hs - 227], x0 in [0, Ws - 227] and a
+     mirror flag, uniform; colour draws alpha ~ N(0, 0.1) (the pages'
+     standard deviation), float32 [N, 3];
+  3. labels uniform in [0, 1000).
 """
 from __future__ import annotations
 
@@ -123,3 +134,45 @@ def config_inputs(cfg: int, batch: Optional[int] = None) -> Synthetic:
     n = c["batch"] if batch is None else batch
     image = SOURCE if c["mode"] == "tenview" else IMAGE
     return synthetic(c["seed"], n, c["groups"], c["bf16"], image=image)
+
+
+# ---------------------------------------------------------------- augmentation
+AUG_SPREAD = (1.0, 0.45, 0.2)
+AUG_ALPHA_STD = 0.1
+
+
+def _rotation(a: float, b: float, c: float) -> np.ndarray:
+    ca, sa, cb, sb, cc, sc = np.cos(a), np.sin(a), np.cos(b), np.sin(b), np.cos(c), np.sin(c)
+    rz = np.array([[ca, -sa, 0], [sa, ca, 0], [0, 0, 1]])
+    ry = np.array([[cb, 0, sb], [0, 1, 0], [-sb, 0, cb]])
+    rx = np.array([[1, 0, 0], [0, cc, -sc], [0, sc, cc]])
+    return rz @ ry @ rx
+
+
+AUG_MIX = (_rotation(0.5, -0.7, 0.3) @ np.diag(AUG_SPREAD)).astype(np.float32)
+
+
+@dataclass
+class AugInputs:
+    seed: int
+    bf16: bool
+    src: np.ndarray       # float32 [N, 3, Hs, Ws] (bf16-exact when bf16)
+    crop: np.ndarray      # int32 [N, 3]: y0, x0, flip
+    alpha: np.ndarray     # float32 [N, 3]
+    labels: np.ndarray    # int32 [N]
+
+
+def augment_inputs(seed: int, batch: int, src_h: int = SOURCE, src_w: int = SOURCE,
+                   bf16: bool = True) -> AugInputs:
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((batch, 3, src_h, src_w), dtype=np.float32)
+    src = np.einsum("cd,ndhw->nchw", AUG_MIX, z).astype(np.float32)
+    y0 = rng.integers(0, src_h - IMAGE + 1, size=batch)
+    x0 = rng.integers(0, src_w - IMAGE + 1, size=batch)
+    flip = rng.integers(0, 2, size=batch)
+    crop = np.stack([y0, x0, flip], axis=1).astype(np.int32)
+    alpha = (rng.standard_normal((batch, 3)) * AUG_ALPHA_STD).astype(np.float32)
+    labels = rng.integers(0, CLASSES, size=batch, dtype=np.int32)
+    if bf16:
+        src = round_bf16(src)
+    return AugInputs(seed, bf16, src, crop, alpha, labels)

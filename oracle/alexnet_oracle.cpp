@@ -479,6 +479,42 @@ void orc_tenview_crop(const double* src, int N, int C, int S, int P, double* out
     }
 }
 
+/* ------------------------------------------------------------------------ *
+ * Training-time augmentation (paper-graph-ui "Data Augmentation", Form 1:
+ * random patches and their horizontal reflections; Form 2: PCA-based colour
+ * intensity jittering; the paper's section 4.1).  Image n is the P x P patch
+ * of source n (side Hs x Ws) whose top-left corner is (y0, x0), mirrored
+ * left-right (x -> P-1-x) when flip != 0, and every pixel of channel c gets
+ *     sum_i eigvec[c*3 + i] * alpha[n*3 + i] * eigval[i]
+ * added: the principal components weighted by the image's draws times their
+ * eigenvalues, the same vector for every pixel of the image.  crop[n*3 ..]
+ * holds (y0, x0, flip); offsets outside the source are clamped into it (the
+ * library's stated rule for out-of-range draws; the pages draw only valid
+ * ones).
+ * Pinned by: identity case (P = Hs = Ws, zero offsets, no flip, alpha 0),
+ * mirror twice, the ten-view crops as special cases, constant images.
+ * ------------------------------------------------------------------------ */
+void orc_augment(const double* src, int N, int C, int Hs, int Ws, const int32_t* crop, const double* alpha,
+                 const double* eigvec, const double* eigval, int P, double* out) {
+#pragma omp parallel for
+  for (int n = 0; n < N; ++n) {
+    int y0 = crop[n * 3], x0 = crop[n * 3 + 1];
+    const bool flip = crop[n * 3 + 2] != 0;
+    y0 = y0 < 0 ? 0 : (y0 > Hs - P ? Hs - P : y0);
+    x0 = x0 < 0 ? 0 : (x0 > Ws - P ? Ws - P : x0);
+    for (int c = 0; c < C; ++c) {
+      double shift = 0.0;
+      for (int i = 0; i < 3; ++i) shift += eigvec[c * 3 + i] * alpha[n * 3 + i] * eigval[i];
+      for (int y = 0; y < P; ++y)
+        for (int x = 0; x < P; ++x) {
+          const int sx = flip ? (P - 1 - x) : x;
+          out[(((size_t)n * C + c) * P + y) * P + x] =
+              src[(((size_t)n * C + c) * Hs + y0 + y) * Ws + x0 + sx] + shift;
+        }
+    }
+  }
+}
+
 /* Mean of the ten views' softmax outputs for each source image. */
 void orc_view_mean(const double* p, int N, int O, double* out) {
   for (int n = 0; n < N; ++n)

@@ -47,6 +47,7 @@ def _load():
         "orc_dropout_mask": [C.c_uint64, C.c_uint64, _i, _i, _i, C.c_double, _U8],
         "orc_tenview_crop": [_D, _i, _i, _i, _i, _D],
         "orc_view_mean": [_D, _i, _i, _D],
+        "orc_augment": [_D, _i, _i, _i, _i, _I32, _D, _D, _D, _i, _D],
         "orc_num_threads": [],
     }
     for name, args in sig.items():
@@ -230,3 +231,44 @@ def view_mean(p):
     out = np.empty((M // 10, O), np.float64)
     _load().orc_view_mean(_p(p), M // 10, O, _p(out))
     return out
+
+
+def augment(src, crop, alpha, eigvec, eigval, patch=227):
+    """Augmented patches of src [N][3][Hs][Ws] (see orc_augment)."""
+    src = _d(src)
+    N, Cc, Hs, Ws = src.shape
+    crop = np.ascontiguousarray(crop, dtype=np.int32).reshape(N, 3)
+    out = np.empty((N, Cc, patch, patch), np.float64)
+    _load().orc_augment(_p(src), N, Cc, Hs, Ws, _p(crop, _I32), _p(_d(alpha).reshape(N, 3)),
+                        _p(_d(eigvec).reshape(3, 3)), _p(_d(eigval).reshape(3)), patch, _p(out))
+    return out
+
+
+def rgb_pca(images):
+    """Principal components of the RGB values of every pixel of images [n][3][h][w]
+    (paper-graph-ui "Data Augmentation", Form 2, steps 1-2; the paper's
+    section 4.1): the 3 x 3 covariance of the pixels' RGB vectors (the mean of
+    the outer products of the centred vectors, dividing by the pixel count),
+    then its eigenvectors and eigenvalues.  Sums are plain float64 sums over
+    all pixels; the eigen-decomposition is LAPACK's
+    symmetric solver (numpy.linalg.eigh).  Returned in descending order of
+    eigenvalue, each eigenvector (column i of the 3 x 3 result) signed so that
+    its largest-magnitude entry is positive (the first such entry on a tie).
+    Pinned by: images built from orthogonal patterns with an exactly known
+    covariance, and brute force on a tiny image."""
+    x = _d(images)
+    n, c, h, w = x.shape
+    assert c == 3
+    pix = np.moveaxis(x, 1, -1).reshape(-1, 3)       # one RGB vector per pixel
+    P = pix.shape[0]
+    mean = pix.sum(axis=0) / P
+    d = pix - mean                                    # centred RGB vectors
+    cov = d.T @ d / P
+    lam, vec = np.linalg.eigh(cov)
+    order = np.argsort(-lam, kind="stable")
+    lam, vec = lam[order], vec[:, order]
+    for i in range(3):
+        big = int(np.argmax(np.abs(vec[:, i])))
+        if vec[big, i] < 0:
+            vec[:, i] = -vec[:, i]
+    return lam, vec, cov
