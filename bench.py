@@ -176,7 +176,7 @@ def main():
 
     # diagnostic pass (untimed): every kernel bracketed by its own events
     diag_steps = 3
-    names = list(B.KERNELS)
+    names = [k for k in B.KERNELS if k != "RGB_PCA"]   # every kernel of the training step
     evs = [new_events(len(names)) for _ in range(diag_steps)]
     for d in range(diag_steps):
         train(step, [(B.KT[nm], evs[d][j][0].cuda_event, evs[d][j][1].cuda_event)
@@ -201,7 +201,51 @@ def main():
     train_s = (time.perf_counter() - t0) / args.steps
     dom_ms = sum(a.elapsed_time(b) for a, b in tev) / args.steps
     final_loss = float(loss.item())
-    del sess
+
+    # ---------------------------------------------------------------- augmented training step
+    # Same step fed by the section-4.1 augmentation: 227x227 patches of 256x256
+    # sources with mirror flags and PCA colour shifts, read by the layer-1
+    # staging.  The principal components come from alexnet_rgb_pca on the batch.
+    aug_in = I.augment_inputs(5, n)
+    src = to_device(aug_in.src, B.BF16, dev)
+    crop = torch.from_numpy(aug_in.crop).to(dev)
+    alpha = torch.from_numpy(aug_in.alpha).to(dev)
+    eigval = torch.empty(3, dtype=torch.float32, device=dev)
+    eigvec = torch.empty(9, dtype=torch.float32, device=dev)
+    pca_ws_bytes = B.alexnet_rgb_pca_workspace_bytes()
+    pca_ws = torch.empty(pca_ws_bytes, dtype=torch.uint8, device=dev)
+    hs, ws_ = aug_in.src.shape[2], aug_in.src.shape[3]
+
+    def pca(timers=()):
+        B.alexnet_rgb_pca_timed(sess.cfg, src, n, hs, ws_, eigval, eigvec, pca_ws, pca_ws_bytes, stream,
+                                list(timers))
+
+    for _ in range(args.warmup):
+        pca()
+    pev = new_events(args.steps)
+    for i in range(args.steps):
+        pca([(B.KT["RGB_PCA"], pev[i][0].cuda_event, pev[i][1].cuda_event)])
+    torch.cuda.synchronize()
+    pca_ms = sum(a.elapsed_time(b) for a, b in pev) / args.steps
+    aug = B.augment(crop, alpha, eigval, eigvec)
+
+    def train_aug(i, timers=()):
+        B.alexnet_train_step_augmented_timed(sess.cfg, master, mom, work, src, hs, ws_, aug, labels, h["lr"],
+                                             h["momentum"], h["weight_decay"], h["dropout_seed"], i, loss, None,
+                                             sess.ws, sess.ws_bytes, stream, list(timers))
+
+    for _ in range(args.warmup):
+        train_aug(step); step += 1
+    sev = new_events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        train_aug(step, [(B.KT["S2D"], sev[i][0].cuda_event, sev[i][1].cuda_event)])
+        step += 1
+    torch.cuda.synchronize()
+    aug_s = (time.perf_counter() - t0) / args.steps
+    aug_stage_ms = sum(a.elapsed_time(b) for a, b in sev) / args.steps
+    del sess, src, pca_ws
 
     # ---------------------------------------------------------------- forward passes
     fwd = {}
@@ -240,6 +284,12 @@ def main():
                     "frac": round(work / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "us": round(ms * 1e3, 2)}
         return {"bound": "hbm", "GB/s": round(work / (ms * 1e-3) / 1e9, 1),
                 "frac": round(work / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2)}
+
+    def frac_pca(ms):
+        # one read of every source pixel; the 9 fp64 moments per workgroup are negligible
+        b = n * 3 * hs * ws_ * 2
+        return {"bound": "hbm", "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "us": round(ms * 1e3, 2)}
 
     kernels_train = {nm: frac(nm, ms) for nm, ms in per_kernel.items()}
     conv_fwd_flops = sum(conv_flops(c, n, 1) for c in CONV)
@@ -281,6 +331,12 @@ def main():
         "kernels_train": kernels_train,
         "kernels_forward": {nm: frac(nm, ms, train=False) for nm, ms in fwd_kernels["single"].items()},
         "roofline": roofline,
+        "train_augmented": {
+            "images_per_s": round(n / aug_s, 1), "ms": round(aug_s * 1e3, 4),
+            "workload": "the training step on 227x227 patches of 3x256x256 sources (random offsets, mirror "
+                        "flags, PCA colour shifts with alpha ~ N(0, 0.1)), staged straight from the sources",
+            "staging": frac("S2D", aug_stage_ms)},
+        "rgb_pca": dict(frac_pca(pca_ms), images=n, size=f"3x{hs}x{ws_}"),
     }
 
     if args.copy_calibration:

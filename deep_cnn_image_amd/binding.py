@@ -23,7 +23,9 @@ EXPORTED = (
     "alexnet_default_cfg", "alexnet_workspace_bytes", "alexnet_forward", "alexnet_forward_tenview",
     "alexnet_train_step", "alexnet_cast_weights", "alexnet_dropout_mask", "alexnet_tap",
     "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string", "alexnet_forward_timed",
-    "alexnet_train_step_timed",
+    "alexnet_train_step_timed", "alexnet_augment_images", "alexnet_train_step_augmented",
+    "alexnet_train_step_augmented_timed", "alexnet_rgb_pca_workspace_bytes", "alexnet_rgb_pca",
+    "alexnet_rgb_pca_timed",
 )
 
 # alexnet_kernel ids (kernel-timing hooks)
@@ -32,7 +34,7 @@ KERNELS = (
     "LRNPOOL2_FWD", "POOL5_FWD", "FC6_FWD", "FC7_FWD", "FC8_FWD", "FC8_DGRAD", "FC7_DGRAD",
     "FC6_DGRAD", "FC8_WGRAD", "FC7_WGRAD", "FC6_WGRAD", "POOL5_BWD", "CONV5_WGRAD", "CONV4_WGRAD",
     "CONV3_WGRAD", "CONV2_WGRAD", "CONV1_WGRAD", "CONV5_DGRAD", "CONV4_DGRAD", "CONV3_DGRAD",
-    "CONV2_DGRAD", "POOLLRN2_BWD", "POOLLRN1_BWD", "BIAS",
+    "CONV2_DGRAD", "POOLLRN2_BWD", "POOLLRN1_BWD", "BIAS", "RGB_PCA",
 )
 KT = {name: i + 1 for i, name in enumerate(KERNELS)}
 
@@ -45,6 +47,17 @@ class Cfg(C.Structure):
 
 class Timer(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("start", C.c_void_p), ("stop", C.c_void_p)]
+
+
+class Augment(C.Structure):
+    """alexnet_augment: device addresses of crop [N][3] int32, alpha [N][3],
+    eigval [3] and eigvec [3][3] (fp32)."""
+    _fields_ = [("crop", C.c_void_p), ("alpha", C.c_void_p), ("eigval", C.c_void_p),
+                ("eigvec", C.c_void_p)]
+
+
+def augment(crop, alpha, eigval, eigvec) -> Augment:
+    return Augment(_ptr(crop) or None, _ptr(alpha) or None, _ptr(eigval) or None, _ptr(eigvec) or None)
 
 
 class AlexNetError(RuntimeError):
@@ -83,6 +96,21 @@ def lib():
                                            C.c_float, C.c_uint64, C.c_uint64, vp, vp, vp, C.c_size_t,
                                            vp, tp, C.c_int32]
     L.alexnet_train_step_timed.restype = C.c_int
+    augp = C.POINTER(Augment)
+    L.alexnet_augment_images.argtypes = [cfgp, vp, C.c_int32, C.c_int32, augp, vp, vp]
+    L.alexnet_augment_images.restype = C.c_int
+    L.alexnet_train_step_augmented.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, C.c_int32, C.c_int32, augp,
+                                               vp, C.c_float, C.c_float, C.c_float, C.c_uint64, C.c_uint64,
+                                               vp, vp, vp, C.c_size_t, vp]
+    L.alexnet_train_step_augmented.restype = C.c_int
+    L.alexnet_train_step_augmented_timed.argtypes = L.alexnet_train_step_augmented.argtypes + [tp, C.c_int32]
+    L.alexnet_train_step_augmented_timed.restype = C.c_int
+    L.alexnet_rgb_pca_workspace_bytes.argtypes = []
+    L.alexnet_rgb_pca_workspace_bytes.restype = C.c_size_t
+    L.alexnet_rgb_pca.argtypes = [cfgp, vp, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, C.c_size_t, vp]
+    L.alexnet_rgb_pca.restype = C.c_int
+    L.alexnet_rgb_pca_timed.argtypes = L.alexnet_rgb_pca.argtypes + [tp, C.c_int32]
+    L.alexnet_rgb_pca_timed.restype = C.c_int
     L.alexnet_cast_weights.argtypes = [cfgp, _PTR16, _PTR16, vp]
     L.alexnet_cast_weights.restype = C.c_int
     L.alexnet_dropout_mask.argtypes = [C.c_uint64, C.c_uint64, C.c_int32, C.c_int32, C.c_int32,
@@ -181,6 +209,54 @@ def alexnet_train_step_timed(cfg, master, momentum, work, x, labels, lr, momentu
                                        weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None,
                                        _ptr(ws) or None, ws_bytes, _ptr(stream) or None, arr, n)
     return _check(s, "alexnet_train_step_timed") if check else s
+
+
+def alexnet_augment_images(cfg, src, src_h, src_w, aug: Augment, x, stream=0, check=True) -> int:
+    s = lib().alexnet_augment_images(C.byref(cfg), _ptr(src) or None, src_h, src_w,
+                                     C.byref(aug) if aug is not None else None, _ptr(x) or None,
+                                     _ptr(stream) or None)
+    return _check(s, "alexnet_augment_images") if check else s
+
+
+def alexnet_train_step_augmented(cfg, master, momentum, work, src, src_h, src_w, aug: Augment, labels, lr,
+                                 momentum_coef, weight_decay, seed, step, loss, probs, ws, ws_bytes, stream=0,
+                                 check=True) -> int:
+    s = lib().alexnet_train_step_augmented(
+        C.byref(cfg), _ptr16(master), _ptr16(momentum), _ptr16(work), _ptr(src) or None, src_h, src_w,
+        C.byref(aug) if aug is not None else None, _ptr(labels) or None, lr, momentum_coef, weight_decay,
+        seed, step, _ptr(loss) or None, _ptr(probs) or None, _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
+    return _check(s, "alexnet_train_step_augmented") if check else s
+
+
+def alexnet_train_step_augmented_timed(cfg, master, momentum, work, src, src_h, src_w, aug: Augment, labels,
+                                       lr, momentum_coef, weight_decay, seed, step, loss, probs, ws, ws_bytes,
+                                       stream, timers, check=True) -> int:
+    arr, n = _timers(timers)
+    s = lib().alexnet_train_step_augmented_timed(
+        C.byref(cfg), _ptr16(master), _ptr16(momentum), _ptr16(work), _ptr(src) or None, src_h, src_w,
+        C.byref(aug) if aug is not None else None, _ptr(labels) or None, lr, momentum_coef, weight_decay,
+        seed, step, _ptr(loss) or None, _ptr(probs) or None, _ptr(ws) or None, ws_bytes, _ptr(stream) or None,
+        arr, n)
+    return _check(s, "alexnet_train_step_augmented_timed") if check else s
+
+
+def alexnet_rgb_pca_workspace_bytes() -> int:
+    return int(lib().alexnet_rgb_pca_workspace_bytes())
+
+
+def alexnet_rgb_pca(cfg, images, n, h, w, eigval, eigvec, ws, ws_bytes, stream=0, check=True) -> int:
+    s = lib().alexnet_rgb_pca(C.byref(cfg), _ptr(images) or None, n, h, w, _ptr(eigval) or None,
+                              _ptr(eigvec) or None, _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
+    return _check(s, "alexnet_rgb_pca") if check else s
+
+
+def alexnet_rgb_pca_timed(cfg, images, n, h, w, eigval, eigvec, ws, ws_bytes, stream, timers,
+                          check=True) -> int:
+    arr, k = _timers(timers)
+    s = lib().alexnet_rgb_pca_timed(C.byref(cfg), _ptr(images) or None, n, h, w, _ptr(eigval) or None,
+                                    _ptr(eigvec) or None, _ptr(ws) or None, ws_bytes, _ptr(stream) or None,
+                                    arr, k)
+    return _check(s, "alexnet_rgb_pca_timed") if check else s
 
 
 def alexnet_cast_weights(cfg, master, work, stream=0, check=True) -> int:

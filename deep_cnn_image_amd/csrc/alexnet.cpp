@@ -73,9 +73,11 @@ inline char* tp(void* ws, const Plan& p, int id) { return (char*)ws + p.tap[id].
   } while (0)
 
 // Forward pass.  train: dropout masks of (seed, step); else the 1 - p scale.
-// src_hw: 227 (images) or 256 (ten-view sources).
+// x: 227 x 227 images, 256 x 256 ten-view sources (ten-view plan), or, with
+// `aug`, aug_h x aug_w sources of augmented patches.
 int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* ws, bool train,
-                    uint64_t seed, uint64_t step, hipStream_t st, const Timers& T) {
+                    uint64_t seed, uint64_t step, hipStream_t st, const Timers& T,
+                    const AugSrc* aug = nullptr, int aug_h = 0, int aug_w = 0) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -96,8 +98,9 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
     }
     // together with the layer-1 input staging
     const bool tenview = p.mode == ALEXNET_MODE_TENVIEW;
-    const int hs = tenview ? 256 : 227;
-    HIPCHK(stage_inputs(dt, jobs, nj, x, hs, hs, tenview ? 1 : 0, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
+    const int kind = aug ? SRC_AUGMENT : tenview ? SRC_TENVIEW : SRC_IMAGES;
+    const int hs = aug ? aug_h : tenview ? 256 : 227, wsz = aug ? aug_w : hs;
+    HIPCHK(stage_inputs(dt, jobs, nj, x, hs, wsz, kind, aug, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
   }
   HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st,
                    T(ALEXNET_KT_CONV1_FWD)));
@@ -301,11 +304,26 @@ int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16]
   return ALEXNET_OK;
 }
 
-int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
-                             void* const work[16], const void* x, const int32_t* labels, float lr,
-                             float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
-                             float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
-                             const alexnet_timer* timers, int32_t n_timers) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of an augmentation description; the crop offsets are
+// device data, clamped by the kernels.
+int check_augment(const alexnet_augment* aug, int32_t src_h, int32_t src_w, AugSrc* out) {
+  if (!aug || !aug->crop || !aug->alpha || !aug->eigval || !aug->eigvec) return ALEXNET_E_NULL;
+  if (!aligned(aug->crop, 4) || !aligned(aug->alpha, 4) || !aligned(aug->eigval, 4) || !aligned(aug->eigvec, 4))
+    return ALEXNET_E_ALIGN;
+  if (src_h < 227 || src_w < 227 || src_h > 8192 || src_w > 8192) return ALEXNET_E_SHAPE;
+  *out = AugSrc{aug->crop, aug->alpha, aug->eigvec, aug->eigval};
+  return ALEXNET_OK;
+}
+
+int train_step_impl(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                    void* const work[16], const void* x, const AugSrc* aug, int aug_h, int aug_w,
+                    const int32_t* labels, float lr, float momentum_coef, float weight_decay, uint64_t seed,
+                    uint64_t step, float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
+                    const alexnet_timer* timers, int32_t n_timers) {
   Plan p;
   int r = prepare(cfg, ALEXNET_MODE_TRAIN, ws, ws_bytes, &p);
   if (r != ALEXNET_OK) return r;
@@ -321,7 +339,9 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
   const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
-  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st, T)) != ALEXNET_OK) return r;
+  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st, T, aug, aug_h, aug_w)) !=
+      ALEXNET_OK)
+    return r;
   if (softmax_ce(dt, (const float*)tp(ws, p, T_LOGITS), labels, probs, tp(ws, p, T_DLOGITS),
                  (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
     return ALEXNET_E_HIP;
@@ -329,6 +349,86 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], fl
   const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
   if ((r = enqueue_backward(p, work, master, momentum, hy, ws, st, T)) != ALEXNET_OK) return r;
   return ALEXNET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                             void* const work[16], const void* x, const int32_t* labels, float lr,
+                             float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
+                             float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
+                             const alexnet_timer* timers, int32_t n_timers) {
+  return train_step_impl(cfg, master, momentum, work, x, nullptr, 0, 0, labels, lr, momentum_coef, weight_decay,
+                         seed, step, loss, probs, ws, ws_bytes, stream, timers, n_timers);
+}
+
+int alexnet_train_step_augmented_timed(const alexnet_cfg* cfg, float* const master[16],
+                                       float* const momentum[16], void* const work[16], const void* src,
+                                       int32_t src_h, int32_t src_w, const alexnet_augment* aug,
+                                       const int32_t* labels, float lr, float momentum_coef, float weight_decay,
+                                       uint64_t seed, uint64_t step, float* loss, float* probs, void* ws,
+                                       size_t ws_bytes, void* stream, const alexnet_timer* timers,
+                                       int32_t n_timers) {
+  AugSrc a;
+  const int r = check_augment(aug, src_h, src_w, &a);
+  if (r != ALEXNET_OK) return r;
+  return train_step_impl(cfg, master, momentum, work, src, &a, src_h, src_w, labels, lr, momentum_coef,
+                         weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, timers, n_timers);
+}
+
+int alexnet_train_step_augmented(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                                 void* const work[16], const void* src, int32_t src_h, int32_t src_w,
+                                 const alexnet_augment* aug, const int32_t* labels, float lr, float momentum_coef,
+                                 float weight_decay, uint64_t seed, uint64_t step, float* loss, float* probs,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  return alexnet_train_step_augmented_timed(cfg, master, momentum, work, src, src_h, src_w, aug, labels, lr,
+                                            momentum_coef, weight_decay, seed, step, loss, probs, ws, ws_bytes,
+                                            stream, nullptr, 0);
+}
+
+int alexnet_augment_images(const alexnet_cfg* cfg, const void* src, int32_t src_h, int32_t src_w,
+                           const alexnet_augment* aug, void* x, void* stream) {
+  Plan p;
+  int r = make_plan(cfg, ALEXNET_MODE_TRAIN, &p);
+  if (r != ALEXNET_OK) return r;
+  AugSrc a;
+  if ((r = check_augment(aug, src_h, src_w, &a)) != ALEXNET_OK) return r;
+  if (!src || !x) return ALEXNET_E_NULL;
+  if (!aligned(src, 16) || !aligned(x, 16)) return ALEXNET_E_ALIGN;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
+  return augment_images(dt, src, src_h, src_w, a, cfg->batch, x, (hipStream_t)stream) == hipSuccess
+             ? ALEXNET_OK
+             : ALEXNET_E_HIP;
+}
+
+size_t alexnet_rgb_pca_workspace_bytes(void) { return rgb_pca_scratch_bytes(); }
+
+int alexnet_rgb_pca_timed(const alexnet_cfg* cfg, const void* images, int32_t n, int32_t h, int32_t w,
+                          float* eigval, float* eigvec, void* ws, size_t ws_bytes, void* stream,
+                          const alexnet_timer* timers, int32_t n_timers) {
+  if (!cfg || !images || !eigval || !eigvec || !ws) return ALEXNET_E_NULL;
+  if (cfg->dtype != ALEXNET_F32 && cfg->dtype != ALEXNET_BF16) return ALEXNET_E_DTYPE;
+  if (n < 1 || h < 1 || w < 1 || (int64_t)n * h * w > ((int64_t)1 << 40)) return ALEXNET_E_SHAPE;
+  if (!aligned(images, 16) || !aligned(eigval, 4) || !aligned(eigvec, 4) || !aligned(ws, 256))
+    return ALEXNET_E_ALIGN;
+  if (ws_bytes < rgb_pca_scratch_bytes()) return ALEXNET_E_WORKSPACE;
+  Timers T;
+  int r = load_timers(timers, n_timers, &T);
+  if (r != ALEXNET_OK) return r;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
+  return rgb_pca(dt, images, n, h, w, eigval, eigvec, ws, (hipStream_t)stream, T(ALEXNET_KT_RGB_PCA)) ==
+                 hipSuccess
+             ? ALEXNET_OK
+             : ALEXNET_E_HIP;
+}
+
+int alexnet_rgb_pca(const alexnet_cfg* cfg, const void* images, int32_t n, int32_t h, int32_t w, float* eigval,
+                    float* eigvec, void* ws, size_t ws_bytes, void* stream) {
+  return alexnet_rgb_pca_timed(cfg, images, n, h, w, eigval, eigvec, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],

@@ -73,17 +73,42 @@ __device__ __forceinline__ void tenview_offset(int v, int d, int& y0, int& x0, i
   flip = v >= 5;
 }
 
+// Training-time augmentation (ImageNet Classification with Deep
+// Convolutional Neural Networks, section 4.1): the patch of source n and its
+// mirror flag, and the RGB shift added to every pixel of the image, the
+// principal components weighted by the image's draws alpha times the
+// eigenvalues.  Crop offsets outside the source are clamped into it.
+__device__ __forceinline__ void aug_patch(const AugSrc& a, int n, int Hs, int Ws, int& y0, int& x0, int& flip) {
+  const int32_t* c = a.crop + 3 * n;
+  y0 = min(max(c[0], 0), Hs - 227);
+  x0 = min(max(c[1], 0), Ws - 227);
+  flip = c[2] != 0;
+}
+__device__ __forceinline__ float aug_shift(const AugSrc& a, int n, int ch) {
+  const float* al = a.alpha + 3 * n;
+  const float* p = a.eigvec + 3 * ch;
+  float s = p[0] * (al[0] * a.eigval[0]);
+  s = fmaf(p[1], al[1] * a.eigval[1], s);
+  s = fmaf(p[2], al[2] * a.eigval[2], s);
+  return s;
+}
+// pixel value plus shift, rounded once to T
+template <typename T>
+__device__ __forceinline__ T aug_value(T v, float shift) { return Num<T>::store(Num<T>::load(v) + shift); }
+
 // One workgroup per (image, block row).  The 12 input rows it needs (3
 // channels x 4 rows) are copied into LDS as whole 16-byte chunks: image rows
 // start at any element (227 is odd), so each row's copy begins at the chunk
 // boundary below its first element and the row sits in LDS at that shift.
 // The 57 x 48 values of the block row are then written as 16-byte runs.
-// Ten-view mode: image n is view n % 10 of source n / 10 (227x227 crop at the
-// view's offset, mirrored for views 5..9).  `total` is the element count of x;
-// a chunk that would cross its end is read element by element.
+// Ten-view sources: image n is view n % 10 of source n / 10 (227x227 crop at
+// the view's offset, mirrored for views 5..9).  Augmented sources: image n is
+// the patch of source n given by `aug`, with its RGB shift.  `total` is the
+// element count of x; a chunk that would cross its end is read element by
+// element.
 template <typename T>
 __device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* __restrict__ xs, int Hs, int Ws,
-                                          int tenview, int64_t total) {
+                                          int kind, const AugSrc& aug, int64_t total) {
   constexpr int V = 16 / (int)sizeof(T);                // elements per chunk
   constexpr int RCH = (V + 225) / V + 1;                // chunks per staged row (span of 227 at shift < V)
   constexpr int RS = RCH * V;                           // LDS row stride, elements
@@ -92,10 +117,16 @@ __device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* _
   const int n = blk / S2D_B, bh = blk - n * S2D_B;
   int y0 = 0, x0 = 0, flip = 0;
   int64_t img;
-  if (tenview) {
+  float rgb[3] = {0.f, 0.f, 0.f};
+  if (kind == SRC_TENVIEW) {
     tenview_offset(n % 10, Hs - 227, y0, x0, flip);
     img = (int64_t)(n / 10) * 3 * Hs * Ws;
   } else {
+    if (kind == SRC_AUGMENT) {
+      aug_patch(aug, n, Hs, Ws, y0, x0, flip);
+#pragma unroll
+      for (int c = 0; c < 3; ++c) rgb[c] = aug_shift(aug, n, c);
+    }
     img = (int64_t)n * 3 * Hs * Ws;
   }
   for (int i = threadIdx.x; i < 12 * RCH; i += TPB) {
@@ -127,7 +158,10 @@ __device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* _
       const int q = q0 + j, c = q >> 4, dh = (q >> 2) & 3, dw = q & 3;
       const int r = c * 4 + dh, yc = 4 * bh + dh, xc = 4 * bw + dw;
       T v = T(0);
-      if (yc < 227 && xc < 227) v = rows[r * RS + shift[r] + (flip ? 226 - xc : xc)];
+      if (yc < 227 && xc < 227) {
+        v = rows[r * RS + shift[r] + (flip ? 226 - xc : xc)];
+        if (kind == SRC_AUGMENT) v = aug_value(v, rgb[c]);
+      }
       e[j] = v;
     }
     *reinterpret_cast<uint4*>(out + i * V) = pack_u4(e);
@@ -774,15 +808,18 @@ bool im2col_blocked(DType dt, int Cg) { return dt == BF16 && Cg % GEMM_BK == 0; 
 // block row after them) are independent of each other.
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_stage(PrepArgs a, const T* __restrict__ x, T* __restrict__ xs, int Hs,
-                                               int Ws, int tenview, int64_t total) {
+                                               int Ws, int kind, AugSrc aug, int64_t total) {
   const int prep_blocks = a.bstart[a.n];
   if ((int)blockIdx.x < prep_blocks) prep_block<T>(blockIdx.x, a);
-  else s2d_block<T>(blockIdx.x - prep_blocks, x, xs, Hs, Ws, tenview, total);
+  else s2d_block<T>(blockIdx.x - prep_blocks, x, xs, Hs, Ws, kind, aug, total);
 }
 
-hipError_t stage_inputs(DType dt, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int tenview,
-                        int Nimg, void* xs, hipStream_t st, const KTimer* kt) {
+hipError_t stage_inputs(DType dt, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int kind,
+                        const AugSrc* aug, int Nimg, void* xs, hipStream_t st, const KTimer* kt) {
   if (n < 1 || n > WPREP_MAX) return hipErrorInvalidValue;
+  if (kind != SRC_IMAGES && kind != SRC_TENVIEW && kind != SRC_AUGMENT) return hipErrorInvalidValue;
+  if (kind == SRC_AUGMENT && (!aug || Hs < 227 || Ws < 227)) return hipErrorInvalidValue;
+  const AugSrc ag = kind == SRC_AUGMENT ? *aug : AugSrc{nullptr, nullptr, nullptr, nullptr};
   PrepArgs a = {};
   a.n = n;
   int blocks = 0;
@@ -819,14 +856,206 @@ hipError_t stage_inputs(DType dt, const WeightPrep* jobs, int n, const void* x, 
     blocks += w.kind == WPREP_W1S ? cdiv(count, TPB) : (int)count;
   }
   a.bstart[n] = blocks;
-  const int64_t total = (int64_t)(tenview ? Nimg / 10 : Nimg) * 3 * Hs * Ws;
+  const int64_t total = (int64_t)(kind == SRC_TENVIEW ? Nimg / 10 : Nimg) * 3 * Hs * Ws;
   const dim3 g(blocks + Nimg * S2D_B);
   rec_start(kt, st);
   if (dt == BF16)
-    hipLaunchKernelGGL((k_stage<bf16>), g, dim3(TPB), 0, st, a, (const bf16*)x, (bf16*)xs, Hs, Ws, tenview, total);
-  else
-    hipLaunchKernelGGL((k_stage<float>), g, dim3(TPB), 0, st, a, (const float*)x, (float*)xs, Hs, Ws, tenview,
+    hipLaunchKernelGGL((k_stage<bf16>), g, dim3(TPB), 0, st, a, (const bf16*)x, (bf16*)xs, Hs, Ws, kind, ag,
                        total);
+  else
+    hipLaunchKernelGGL((k_stage<float>), g, dim3(TPB), 0, st, a, (const float*)x, (float*)xs, Hs, Ws, kind, ag,
+                       total);
+  rec_stop(kt, st);
+  return hipGetLastError();
+}
+
+// The augmented patches as NCHW images, one thread per output element (the
+// same per-element arithmetic as the staging above).
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_augment(const T* __restrict__ src, int Hs, int Ws, AugSrc aug,
+                                                 int64_t total, T* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (e >= total) return;
+  constexpr int P = 227 * 227;
+  const int n = (int)(e / (3 * P));
+  const int rem = (int)(e - (int64_t)n * 3 * P);
+  const int c = rem / P, yx = rem - c * P, y = yx / 227, xo = yx - y * 227;
+  int y0, x0, flip;
+  aug_patch(aug, n, Hs, Ws, y0, x0, flip);
+  const int xi = x0 + (flip ? 226 - xo : xo);
+  const T v = src[(((int64_t)n * 3 + c) * Hs + y0 + y) * Ws + xi];
+  out[e] = aug_value(v, aug_shift(aug, n, c));
+}
+
+hipError_t augment_images(DType dt, const void* src, int Hs, int Ws, const AugSrc& aug, int Nimg, void* x_out,
+                          hipStream_t st) {
+  if (Hs < 227 || Ws < 227 || Nimg < 0) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)Nimg * 3 * 227 * 227;
+  if (total == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL((k_augment<bf16>), grid1d(total), dim3(TPB), 0, st, (const bf16*)src, Hs, Ws, aug, total,
+                       (bf16*)x_out);
+  else
+    hipLaunchKernelGGL((k_augment<float>), grid1d(total), dim3(TPB), 0, st, (const float*)src, Hs, Ws, aug, total,
+                       (float*)x_out);
+  return hipGetLastError();
+}
+
+// ---- principal components of the RGB values (section 4.1: the 3 x 3
+// covariance of the RGB values of all pixels, its eigenvectors and
+// eigenvalues).  Pass 1: PCA_BLOCKS workgroups each accumulate, in fp64, the
+// nine moments sum r, g, b and sum rr, rg, rb, gg, gb, bb over a grid-stride
+// range of pixels, reduced in the workgroup in a fixed tree order.  (For bf16
+// inputs every product and partial sum is exact in fp64.)  Pass 2: one
+// workgroup sums the partials in a fixed order, forms the covariance
+// (E[x x^T] - mean mean^T; the fp64 moments keep the cancellation harmless
+// unless the mean exceeds the spread by ~10^4) and diagonalises it.
+constexpr int PCA_BLOCKS = 256;
+size_t rgb_pca_scratch_bytes() { return (size_t)PCA_BLOCKS * 9 * sizeof(double); }
+
+// in-place fixed-order tree sum of v[0..TPB) in LDS; result in v[0]
+__device__ __forceinline__ void tree_sum(double* v) {
+  for (int w = TPB / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) v[threadIdx.x] += v[threadIdx.x + w];
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void rgb_accumulate(double (&m)[9], double r, double g, double bl) {
+  m[0] += r; m[1] += g; m[2] += bl;
+  m[3] += r * r; m[4] += r * g; m[5] += r * bl;
+  m[6] += g * g; m[7] += g * bl; m[8] += bl * bl;
+}
+
+// Planes whose size is a multiple of 8 are read as runs of 8 pixels (one
+// 16-byte load per channel for bf16) so that many loads are in flight; other
+// sizes pixel by pixel.
+template <typename T>
+__global__ void __launch_bounds__(TPB) k_rgb_moments(const T* __restrict__ src, int64_t HW, int64_t P,
+                                                     double* __restrict__ part) {
+  __shared__ double red[9][TPB];
+  double m[9] = {0., 0., 0., 0., 0., 0., 0., 0., 0.};
+  const int64_t stride = (int64_t)gridDim.x * TPB;
+  if (HW % 8 == 0) {
+    const int64_t runs = P / 8;
+#pragma unroll 2
+    for (int64_t c = (int64_t)blockIdx.x * TPB + threadIdx.x; c < runs; c += stride) {
+      const int64_t p = c * 8, img = p / HW, q = p - img * HW;
+      const T* b = src + img * 3 * HW + q;
+      float r[8], g[8], bl[8];
+      Pack8<T>::load(b, r);
+      Pack8<T>::load(b + HW, g);
+      Pack8<T>::load(b + 2 * HW, bl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rgb_accumulate(m, r[i], g[i], bl[i]);
+    }
+  } else {
+    for (int64_t p = (int64_t)blockIdx.x * TPB + threadIdx.x; p < P; p += stride) {
+      const int64_t img = p / HW, q = p - img * HW;
+      const T* b = src + img * 3 * HW + q;
+      rgb_accumulate(m, Num<T>::load(b[0]), Num<T>::load(b[HW]), Num<T>::load(b[2 * HW]));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 9; ++k) red[k][threadIdx.x] = m[k];
+  __syncthreads();
+  for (int w = TPB / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < 9) part[blockIdx.x * 9 + threadIdx.x] = red[threadIdx.x][0];
+}
+
+// Cyclic Jacobi eigenvalue iteration on a symmetric 3 x 3 matrix a (row
+// major): each rotation in the (p, q) plane, with t = tan(phi) the smaller
+// root of t^2 + 2 theta t - 1 = 0, theta = (a_qq - a_pp) / (2 a_pq), zeroes
+// a_pq; the rotations accumulate in v.  Sweeps stop when the off-diagonal
+// mass is negligible against the diagonal (at most 50 sweeps).
+__device__ void jacobi3(double a[3][3], double v[3][3]) {
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) v[i][j] = i == j ? 1. : 0.;
+  const int P[3] = {0, 0, 1}, Q[3] = {1, 2, 2};
+  for (int sweep = 0; sweep < 50; ++sweep) {
+    const double off = a[0][1] * a[0][1] + a[0][2] * a[0][2] + a[1][2] * a[1][2];
+    const double dia = a[0][0] * a[0][0] + a[1][1] * a[1][1] + a[2][2] * a[2][2];
+    if (off <= 1e-34 * dia || off == 0.) break;
+    for (int k = 0; k < 3; ++k) {
+      const int p = P[k], q = Q[k];
+      const double apq = a[p][q];
+      if (apq == 0.) continue;
+      const double theta = (a[q][q] - a[p][p]) / (2. * apq);
+      double t = 1. / (fabs(theta) + sqrt(theta * theta + 1.));
+      if (fabs(theta) > 1e150) t = 0.5 / fabs(theta);
+      if (theta < 0.) t = -t;
+      const double c = 1. / sqrt(t * t + 1.), s = t * c;
+      a[p][p] -= t * apq;
+      a[q][q] += t * apq;
+      a[p][q] = a[q][p] = 0.;
+      const int r = 3 - p - q;   // the remaining index
+      const double arp = a[r][p], arq = a[r][q];
+      a[r][p] = a[p][r] = c * arp - s * arq;
+      a[r][q] = a[q][r] = s * arp + c * arq;
+      for (int i = 0; i < 3; ++i) {
+        const double vip = v[i][p], viq = v[i][q];
+        v[i][p] = c * vip - s * viq;
+        v[i][q] = s * vip + c * viq;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(TPB) k_rgb_pca_finish(const double* __restrict__ part, int nblk, int64_t P,
+                                                        float* __restrict__ eigval, float* __restrict__ eigvec) {
+  __shared__ double red[TPB];
+  __shared__ double mom[9];
+  for (int k = 0; k < 9; ++k) {
+    double acc = 0.;   // partials t, t + TPB, ... in order, then the tree
+    for (int b = threadIdx.x; b < nblk; b += TPB) acc += part[b * 9 + k];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    tree_sum(red);
+    if (threadIdx.x == 0) mom[k] = red[0];
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  const double inv = 1. / (double)P;
+  const double mean[3] = {mom[0] * inv, mom[1] * inv, mom[2] * inv};
+  const int idx[3][3] = {{3, 4, 5}, {4, 6, 7}, {5, 7, 8}};
+  double a[3][3], v[3][3];
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) a[i][j] = mom[idx[i][j]] * inv - mean[i] * mean[j];
+  jacobi3(a, v);
+  // eigenvalues in descending order, ties keep the lower index first
+  int ord[3] = {0, 1, 2};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2 - i; ++j)
+      if (a[ord[j + 1]][ord[j + 1]] > a[ord[j]][ord[j]]) { const int t = ord[j]; ord[j] = ord[j + 1]; ord[j + 1] = t; }
+  for (int i = 0; i < 3; ++i) {
+    const int k = ord[i];
+    int big = 0;
+    for (int r = 1; r < 3; ++r)
+      if (fabs(v[r][k]) > fabs(v[big][k])) big = r;
+    const double sg = v[big][k] < 0. ? -1. : 1.;
+    eigval[i] = (float)a[k][k];
+    for (int r = 0; r < 3; ++r) eigvec[3 * r + i] = (float)(sg * v[r][k]);
+  }
+}
+
+hipError_t rgb_pca(DType dt, const void* src, int n, int H, int W, float* eigval, float* eigvec, void* scratch,
+                   hipStream_t st, const KTimer* kt) {
+  if (n < 1 || H < 1 || W < 1) return hipErrorInvalidValue;
+  const int64_t HW = (int64_t)H * W, P = (int64_t)n * HW;
+  double* part = (double*)scratch;
+  rec_start(kt, st);
+  if (dt == BF16)
+    hipLaunchKernelGGL((k_rgb_moments<bf16>), dim3(PCA_BLOCKS), dim3(TPB), 0, st, (const bf16*)src, HW, P, part);
+  else
+    hipLaunchKernelGGL((k_rgb_moments<float>), dim3(PCA_BLOCKS), dim3(TPB), 0, st, (const float*)src, HW, P, part);
+  hipLaunchKernelGGL(k_rgb_pca_finish, dim3(1), dim3(TPB), 0, st, (const double*)part, PCA_BLOCKS, P, eigval,
+                     eigvec);
   rec_stop(kt, st);
   return hipGetLastError();
 }

@@ -45,10 +45,36 @@ struct WeightPrep {
   void* dst;
   int Cout, Cig, K, G;
 };
+// Training-time augmentation of a batch of Hs x Ws sources (device arrays):
+// image n is the 227 x 227 patch of source n at (y0, x0) = crop[n][0..1]
+// (clamped into the source), mirrored left-right if crop[n][2] != 0, plus the
+// RGB shift sum_i eigvec[c][i] * alpha[n][i] * eigval[i] on channel c.
+struct AugSrc {
+  const int32_t* crop;   // [N][3]
+  const float* alpha;    // [N][3]
+  const float* eigvec;   // [3][3], column i = component i
+  const float* eigval;   // [3]
+};
+// Layer-1 input sources: 227 x 227 images, ten-view crops of 256 x 256
+// sources, or augmented patches of Hs x Ws sources.
+enum { SRC_IMAGES = 0, SRC_TENVIEW = 1, SRC_AUGMENT = 2 };
 // One launch: the weight re-layouts `jobs` and the layer-1 input staging
-// (xs from the NCHW images x, or the crops of the ten-view sources).
-hipError_t stage_inputs(DType, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int tenview,
-                        int Nimg, void* xs, hipStream_t, const KTimer* kt = nullptr);
+// (xs from the NCHW images x, the ten-view crops or the augmented patches;
+// `aug` is read only for SRC_AUGMENT).
+hipError_t stage_inputs(DType, const WeightPrep* jobs, int n, const void* x, int Hs, int Ws, int src_kind,
+                        const AugSrc* aug, int Nimg, void* xs, hipStream_t, const KTimer* kt = nullptr);
+// x_out [N][3][227][227] = the augmented patches (same values stage_inputs
+// stages for SRC_AUGMENT).
+hipError_t augment_images(DType, const void* src, int Hs, int Ws, const AugSrc& aug, int Nimg, void* x_out,
+                          hipStream_t);
+// Principal components of the RGB values of every pixel of n images
+// [n][3][H][W]: covariance (divided by the pixel count) accumulated in fp64,
+// eigen-decomposed by cyclic Jacobi rotations; eigval [3] descending, eigvec
+// [3][3] with column i the unit eigenvector of eigval[i], signed so that its
+// largest-magnitude entry is positive.  `scratch` holds rgb_pca_scratch_bytes().
+size_t rgb_pca_scratch_bytes();
+hipError_t rgb_pca(DType, const void* src, int n, int H, int W, float* eigval, float* eigvec, void* scratch,
+                   hipStream_t, const KTimer* kt = nullptr);
 
 // ---- convolutions (bf16 MFMA or fp32 MFMA, fp32 accumulate)
 // Layer 1 runs as a 3x3 stride-1 convolution over 4x4 pixel blocks:

@@ -138,6 +138,64 @@ int alexnet_train_step(const alexnet_cfg* cfg, float* const master[16], float* c
                        float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
                        float* loss, float* probs, void* ws, size_t ws_bytes, void* stream);
 
+/* Training-time data augmentation (ImageNet Classification with Deep
+ * Convolutional Neural Networks, section 4.1, both forms), fed straight into
+ * the layer-1 input staging of a training step.  Image n of the batch is
+ *   x[n][c][y][x'] = src[n][c][y0 + y][x0 + (flip ? 226 - x' : x')]
+ *                    + sum_i eigvec[c][i] * alpha[n][i] * eigval[i]
+ * for y, x' in [0, 227): a 227 x 227 patch of source n, mirrored left-right
+ * when flip != 0, plus the colour shift along the principal components of the
+ * RGB values (one draw alpha[n][0..2] per image, N(0, 0.1) on the pages).
+ * The shift is formed in fp32 as eigvec[c][0]*(alpha0*eigval0), then two
+ * fused multiply-adds for i = 1, 2; the pixel plus shift is rounded once to
+ * cfg->dtype (round to nearest even for bf16).  The random draws are the
+ * caller's: crop offsets, flips and alpha are inputs.
+ *   crop    device int32 [batch][3]: y0, x0, flip.  Offsets outside
+ *           [0, src_h - 227] x [0, src_w - 227] are clamped into it (never an
+ *           out-of-bounds read).
+ *   alpha   device fp32 [batch][3]
+ *   eigval  device fp32 [3]; eigvec device fp32 [3][3], row c = colour
+ *           channel, column i = component i (as alexnet_rgb_pca writes them) */
+typedef struct {
+  const int32_t* crop;
+  const float* alpha;
+  const float* eigval;
+  const float* eigvec;
+} alexnet_augment;
+
+/* x [batch][3][227][227] cfg->dtype (written) = the augmented patches of
+ * src [batch][3][src_h][src_w] (cfg->dtype), 227 <= src_h, src_w <= 8192.
+ * The same values alexnet_train_step_augmented stages for layer 1. */
+int alexnet_augment_images(const alexnet_cfg* cfg, const void* src, int32_t src_h, int32_t src_w,
+                           const alexnet_augment* aug, void* x, void* stream);
+
+/* alexnet_train_step on the augmented patches of src [batch][3][src_h][src_w]
+ * (cfg->dtype): the patches are read from the sources by the layer-1 input
+ * staging and never stored.  Same workspace (ALEXNET_MODE_TRAIN), outputs and
+ * results as alexnet_train_step on the output of alexnet_augment_images. */
+int alexnet_train_step_augmented(const alexnet_cfg* cfg, float* const master[16],
+                                 float* const momentum[16], void* const work[16], const void* src,
+                                 int32_t src_h, int32_t src_w, const alexnet_augment* aug,
+                                 const int32_t* labels, float lr, float momentum_coef,
+                                 float weight_decay, uint64_t seed, uint64_t step, float* loss,
+                                 float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* Principal components of the RGB values of all pixels of n images
+ * [n][3][h][w] (cfg->dtype; only cfg->dtype is read), the statistic the
+ * colour augmentation uses (section 4.1: the 3 x 3 covariance of the RGB
+ * pixel values, its eigenvectors p_i and eigenvalues lambda_i).  The
+ * covariance divides by the pixel count n*h*w; moments accumulate in fp64
+ * (exact for bf16 inputs), and cyclic Jacobi rotations diagonalise it in fp64.
+ *   eigval  device fp32 [3] (written), descending
+ *   eigvec  device fp32 [3][3] (written), column i the unit eigenvector of
+ *           eigval[i], signed so that its largest-magnitude entry is positive
+ *   ws      device scratch of alexnet_rgb_pca_workspace_bytes(), 256-aligned
+ * Equal eigenvalues leave their eigenvectors' directions to the rotation
+ * sequence; the pages' use of them is unaffected. */
+size_t alexnet_rgb_pca_workspace_bytes(void);
+int alexnet_rgb_pca(const alexnet_cfg* cfg, const void* images, int32_t n, int32_t h, int32_t w,
+                    float* eigval, float* eigvec, void* ws, size_t ws_bytes, void* stream);
+
 /* work[i] <- cfg->dtype copy of master[i] (round to nearest even), all 16
  * tensors.  For fp32 work tensors this is a copy. */
 int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* const work[16],
@@ -177,6 +235,7 @@ typedef enum {
   ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
   ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
   ALEXNET_KT_BIAS,             /* all bias gradients + their SGD (two launches)  */
+  ALEXNET_KT_RGB_PCA,          /* alexnet_rgb_pca: moments + eigen-decomposition */
   ALEXNET_KT_COUNT
 } alexnet_kernel;
 
@@ -195,6 +254,17 @@ int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16],
                              float weight_decay, uint64_t seed, uint64_t step, float* loss,
                              float* probs, void* ws, size_t ws_bytes, void* stream,
                              const alexnet_timer* timers, int32_t n_timers);
+int alexnet_train_step_augmented_timed(const alexnet_cfg* cfg, float* const master[16],
+                                       float* const momentum[16], void* const work[16],
+                                       const void* src, int32_t src_h, int32_t src_w,
+                                       const alexnet_augment* aug, const int32_t* labels, float lr,
+                                       float momentum_coef, float weight_decay, uint64_t seed,
+                                       uint64_t step, float* loss, float* probs, void* ws,
+                                       size_t ws_bytes, void* stream, const alexnet_timer* timers,
+                                       int32_t n_timers);
+int alexnet_rgb_pca_timed(const alexnet_cfg* cfg, const void* images, int32_t n, int32_t h,
+                          int32_t w, float* eigval, float* eigvec, void* ws, size_t ws_bytes,
+                          void* stream, const alexnet_timer* timers, int32_t n_timers);
 
 /* Test and diagnostic access to the tensors a call leaves in its workspace.
  * Host only.  For tap `tap_id` of a call in `mode` with `cfg`, returns its

@@ -185,3 +185,40 @@ def test_timer_validation_before_launch():
     assert f([(B.KT["CONV2_FWD"], 0, FAKE)]) == B.E_NULL
     arr, _ = B._timers([(B.KT["CONV2_FWD"], FAKE, FAKE)])
     assert B.lib().alexnet_forward_timed(C.byref(c), B._ptr16(p), FAKE, FAKE, FAKE, ws, None, arr, -1) == B.E_ARG
+
+
+def test_augment_validation_errors_before_launch():
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    aug = B.Augment(FAKE, FAKE + 256, FAKE + 512, FAKE + 768)
+    f = lambda **kw: B.alexnet_augment_images(kw.get("cfg", c), kw.get("src", FAKE), kw.get("h", 256),
+                                              kw.get("w", 256), kw.get("aug", aug), kw.get("x", FAKE), 0,
+                                              check=False)
+    assert f(aug=None) == B.E_NULL
+    assert f(aug=B.Augment(FAKE, 0, FAKE, FAKE)) == B.E_NULL
+    assert f(aug=B.Augment(FAKE + 2, FAKE, FAKE, FAKE)) == B.E_ALIGN
+    assert f(h=226) == B.E_SHAPE and f(w=100) == B.E_SHAPE and f(h=9000) == B.E_SHAPE
+    assert f(src=0) == B.E_NULL and f(x=0) == B.E_NULL
+    assert f(src=FAKE + 8) == B.E_ALIGN
+    assert f(cfg=B.alexnet_default_cfg(0, 1, B.BF16)) == B.E_SHAPE
+    ws = B.alexnet_workspace_bytes(c, B.MODE_TRAIN)
+    p = fake_params()
+    t = lambda **kw: B.alexnet_train_step_augmented(c, p, p, p, FAKE, kw.get("h", 256), 256, kw.get("aug", aug),
+                                                    FAKE, 0.01, 0.9, 5e-4, 3, 0, FAKE, None, FAKE,
+                                                    kw.get("wsb", ws), 0, check=False)
+    assert t(aug=None) == B.E_NULL
+    assert t(h=200) == B.E_SHAPE
+    assert t(wsb=ws - 256) == B.E_WORKSPACE
+
+
+def test_rgb_pca_validation_errors_before_launch():
+    c = B.alexnet_default_cfg(1, 1, B.BF16)
+    nb = B.alexnet_rgb_pca_workspace_bytes()
+    assert nb >= 9 * 8
+    f = lambda **kw: B.alexnet_rgb_pca(kw.get("cfg", c), kw.get("x", FAKE), kw.get("n", 4), kw.get("h", 8),
+                                       kw.get("w", 8), kw.get("lam", FAKE), kw.get("vec", FAKE),
+                                       kw.get("ws", FAKE), kw.get("wsb", nb), 0, check=False)
+    assert f(n=0) == B.E_SHAPE and f(h=0) == B.E_SHAPE and f(w=-1) == B.E_SHAPE
+    assert f(x=0) == B.E_NULL and f(lam=0) == B.E_NULL and f(vec=0) == B.E_NULL and f(ws=0) == B.E_NULL
+    assert f(wsb=nb - 1) == B.E_WORKSPACE
+    assert f(ws=FAKE + 64) == B.E_ALIGN and f(lam=FAKE + 2) == B.E_ALIGN
+    assert f(cfg=B.alexnet_default_cfg(1, 1, 7)) == B.E_DTYPE
