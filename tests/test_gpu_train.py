@@ -364,3 +364,82 @@ def test_full_batch128_train_step(orc):
         limit = TOL_F32_OUT if k[:2] in ("gw", "gb") else TOL_LAYER_BF16
         assert v <= limit, (k, v)
     check_sgd(r, syn)
+
+
+def test_fp32_three_steps_momentum_carry_and_lr_schedule(orc):
+    """Several training steps in a row, as a training loop runs them: the
+    momentum and master weights carry over in the caller's buffers, the working
+    copies are the ones the previous step refreshed, each step draws its own
+    dropout masks, and the learning rate follows a divide-by-ten schedule
+    (paper-graph-ui "Training Procedure Details").
+
+    Each step is checked against the oracle started from the state the
+    previous GPU step left.  Its forward pass is compared directly.  Its
+    gradients are compared with the oracle's backward pass taken on the GPU
+    step's stored forward state, because a pooling argmax at a near-tie (two
+    window values within fp32 rounding of each other) can fall the other way
+    in fp32 and route one gradient element elsewhere; such differences are
+    counted and required to be near-ties.  The update is then checked
+    element by element against the rule applied to those gradients."""
+    syn = I.synthetic(8, 2, groups=1, bf16=False)
+    # (a rate of 0.01 makes two images' loss blow up by the third step)
+    schedule = [(0, 0.002), (1, 0.002), (2, 0.0002)]
+    say("[gpu] fp32 three-step training, lr schedule", schedule)
+    sess = Session(2, 1, B.F32, B.MODE_TRAIN, DEV)
+    master = params_f32(syn.master_w, syn.biases)
+    mom = [torch.zeros_like(m) for m in master]
+    work = [torch.empty_like(m) for m in master]
+    B.alexnet_cast_weights(sess.cfg, master, work, stream_handle())
+    x = to_device(syn.x, B.F32, DEV)
+    labels = torch.from_numpy(syn.labels.astype(np.int32)).to(DEV)
+    loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+    mu, wd = 0.9, 5e-4
+    for step, lr in schedule:
+        torch.cuda.synchronize()
+        s0 = [host(m) for m in master]
+        v0 = [host(v) for v in mom]
+        sess.train_step(master, mom, work, x, labels, loss, None, lr=lr, momentum_coef=mu,
+                        weight_decay=wd, seed=9, step=step)
+        torch.cuda.synchronize()
+        w0, b0 = s0[0::2], s0[1::2]
+        o = orc.alexnet.forward(w0, b0, syn.x, 1, train=True, seed=9, step=step)
+        got = float(loss.item())
+        h = hostify({k: sess.tap(k) for k in ("conv1", "conv2", "conv3", "conv4", "conv5", "pool1", "pool2",
+                                              "pool5", "arg1", "arg2", "arg5", "drop6", "drop7")})
+        fwd = {k: rel_l2(h[k], o[k]) for k in ("conv1", "pool1", "conv2", "pool2", "conv3", "conv4", "conv5",
+                                              "drop6", "drop7")}
+        say(f"[gpu] step {step} lr {lr}: loss {got:.6f}; forward rel-L2", {k: f"{v:.1e}" for k, v in fwd.items()})
+        assert max(fwd.values()) <= TOL_F32_OUT
+        # argmax differences only at near-ties of the oracle's window values
+        for k, a in (("arg1", "lrn1"), ("arg2", "lrn2"), ("arg5", "conv5")):   # the pooled tensors
+            bad = np.argwhere(h[k] != o[k])
+            say(f"[gpu] step {step} {k}: {len(bad)} of {h[k].size} argmax at near-ties")
+            for n_, c_, i_, j_ in bad:
+                win = np.sort(np.asarray(o[a])[n_, c_, 2 * i_:2 * i_ + 3, 2 * j_:2 * j_ + 3].ravel())
+                assert win[-1] - win[-2] <= 1e-5 * abs(win[-1]), (k, n_, c_, i_, j_)
+        # gradients on the GPU step's own forward state
+        t = {"x": syn.x.astype(np.float64)}
+        for k in ("conv1", "conv2", "conv3", "conv4", "conv5", "pool1", "pool2", "arg1", "arg2", "arg5",
+                  "drop6", "drop7"):
+            t[k] = h[k]
+        t["pool5"] = h["pool5"].reshape(-1, 256, 6, 6)
+        t["flat"] = h["pool5"]
+        t["fc6"], t["fc7"] = h["drop6"], h["drop7"]
+        t["mask6"], t["mask7"] = gpu_masks(2, seed=9, step=step)
+        t["probs"] = orc.softmax(orc.fc(h["drop7"], w0[7], b0[7]))
+        oloss, gw, gb, _ = orc.alexnet.backward(w0, t, syn.labels, 1)
+        assert abs(got - oloss) <= 1e-5 * abs(oloss)
+        # the GPU's gradients, recovered from its update v1 = mu v0 - wd lr w0 - lr g
+        lr32, mu32 = np.float32(lr), np.float32(mu)
+        wdlr32 = np.float64(np.float32(np.float32(wd) * lr32))
+        g = [(float(mu32) * v0[j] - wdlr32 * s0[j] - host(mom[j])) / float(lr32) for j in range(16)]
+        eg = [rel_l2(g[2 * i], gw[i]) for i in range(8)] + [rel_l2(g[2 * i + 1], gb[i]) for i in range(8)]
+        say(f"[gpu] step {step} gradient rel-L2 (weights, biases)", [f"{e:.1e}" for e in eg])
+        assert max(eg[:8]) <= 1e-4
+        # the bias gradients recovered this way carry the fp32 rounding of mu v0 and wd lr b (b ~ 1)
+        assert max(eg[8:]) <= 1e-3
+        # the update itself, element by element: w1 = fl(w0 + v1), working copy = w1
+        for j in range(16):
+            w1 = host(master[j])
+            assert np.array_equal(w1.astype(np.float32), s0[j].astype(np.float32) + host(mom[j]).astype(np.float32)), j
+            assert torch.equal(work[j], master[j]), j
