@@ -450,8 +450,6 @@ int alexnet_cast_weights(const alexnet_cfg* cfg, float* const master[16], void* 
   for (int i = 0; i < 8; ++i) {
     ts.master[2 * i] = master[2 * i];
     ts.master[2 * i + 1] = master[2 * i + 1];
-    ts.mom[2 * i] = ts.mom[2 * i + 1] = nullptr;
-    ts.grad[2 * i] = ts.grad[2 * i + 1] = nullptr;
     ts.work[2 * i] = work[2 * i];
     ts.work[2 * i + 1] = work[2 * i + 1];
     ts.n[2 * i] = p.net.wcount[i];

@@ -26,8 +26,9 @@ __device__ __forceinline__ uint32_t f2bf2(float a, float b) {
 
 // One SGD-with-momentum step on an element (paper form, lr inside v):
 //   v <- mom * v - wd * lr * w - lr * g,   w <- w + v
-// written with explicit fmas so that every kernel that applies it (the
-// multi-tensor update and the fused weight-gradient epilogue) rounds alike.
+// written with explicit fmas so that every kernel that applies it (the FC
+// weight-gradient epilogue, the conv weight-gradient reductions and the bias
+// update) rounds alike.
 __device__ __forceinline__ void sgd_elem(float& w, float& v, float g, float mom, float wdlr, float lr) {
   v = fmaf(mom, v, -fmaf(lr, g, wdlr * w));
   w = w + v;

@@ -636,7 +636,7 @@ hipError_t fc_dgrad(DType dt, int M, int K, int O, const void* dy, const void* w
 
 // Epilogue of the FC weight-gradient GEMM: the fp32 gradient of 8 weights
 // w[m][n .. n+7] goes straight into the SGD update of master w, momentum v
-// and working copy wb (same element update as the multi-tensor kernel).
+// and working copy wb (sgd_elem, as every other tensor's update).
 // w and v are fetched ahead (prefetch) while the accumulators are staged.
 template <typename T>
 struct EpSgd {
@@ -2047,16 +2047,13 @@ hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& 
 }
 
 // =========================================================================
-// SGD with momentum and weight decay over all 16 parameter tensors, and the
-// refresh of the working copies.  Four elements per thread.
+// Working copies of all 16 parameter tensors from their fp32 masters (round
+// to nearest even for bf16), one launch.  Four elements per thread.
 // =========================================================================
-struct MultiArgs {
-  float* w[16];
-  float* v[16];
-  const float* g[16];
+struct CastArgs {
+  const float* w[16];
   void* wb[16];
   int64_t start[17];   // first 4-element chunk of each tensor
-  float lr, mom, wdlr;
 };
 
 __device__ __forceinline__ int find_tensor(const int64_t* start, int64_t c) {
@@ -2066,23 +2063,13 @@ __device__ __forceinline__ int find_tensor(const int64_t* start, int64_t c) {
   return ti;
 }
 
-template <typename T, bool SGD>
-__global__ void k_multi(MultiArgs a) {
+template <typename T>
+__global__ void k_cast_weights(CastArgs a) {
   const int64_t c = (int64_t)blockIdx.x * TPB + threadIdx.x;
   if (c >= a.start[16]) return;
   const int ti = find_tensor(a.start, c);
   const int64_t e = (c - a.start[ti]) * 4;
-  float4 w = *reinterpret_cast<const float4*>(a.w[ti] + e);
-  if (SGD) {
-    float4 v = *reinterpret_cast<const float4*>(a.v[ti] + e);
-    const float4 g = *reinterpret_cast<const float4*>(a.g[ti] + e);
-    sgd_elem(w.x, v.x, g.x, a.mom, a.wdlr, a.lr);
-    sgd_elem(w.y, v.y, g.y, a.mom, a.wdlr, a.lr);
-    sgd_elem(w.z, v.z, g.z, a.mom, a.wdlr, a.lr);
-    sgd_elem(w.w, v.w, g.w, a.mom, a.wdlr, a.lr);
-    *reinterpret_cast<float4*>(a.v[ti] + e) = v;
-    *reinterpret_cast<float4*>(a.w[ti] + e) = w;
-  }
+  const float4 w = *reinterpret_cast<const float4*>(a.w[ti] + e);
   T* o = reinterpret_cast<T*>(a.wb[ti]) + e;
   if (sizeof(T) == 2) {
     const uint32_t lo = f2bf2(w.x, w.y);
@@ -2093,35 +2080,18 @@ __global__ void k_multi(MultiArgs a) {
   }
 }
 
-static hipError_t run_multi(DType dt, const TensorSet& ts, bool sgd, float lr, float mom, float wd,
-                            hipStream_t st, const KTimer* kt = nullptr) {
-  MultiArgs a;
+hipError_t cast_weights(DType dt, const TensorSet& ts, hipStream_t st) {
+  CastArgs a;
   a.start[0] = 0;
   for (int i = 0; i < 16; ++i) {
     if (ts.n[i] % 4) return hipErrorInvalidValue;
-    a.w[i] = ts.master[i]; a.v[i] = ts.mom[i]; a.g[i] = ts.grad[i]; a.wb[i] = ts.work[i];
+    a.w[i] = ts.master[i]; a.wb[i] = ts.work[i];
     a.start[i + 1] = a.start[i] + ts.n[i] / 4;
   }
-  a.lr = lr; a.mom = mom; a.wdlr = wd * lr;
   const dim3 g = grid1d(a.start[16]);
-  rec_start(kt, st);
-  if (dt == BF16) {
-    if (sgd) hipLaunchKernelGGL((k_multi<bf16, true>), g, dim3(TPB), 0, st, a);
-    else hipLaunchKernelGGL((k_multi<bf16, false>), g, dim3(TPB), 0, st, a);
-  } else {
-    if (sgd) hipLaunchKernelGGL((k_multi<float, true>), g, dim3(TPB), 0, st, a);
-    else hipLaunchKernelGGL((k_multi<float, false>), g, dim3(TPB), 0, st, a);
-  }
-  rec_stop(kt, st);
+  if (dt == BF16) hipLaunchKernelGGL((k_cast_weights<bf16>), g, dim3(TPB), 0, st, a);
+  else hipLaunchKernelGGL((k_cast_weights<float>), g, dim3(TPB), 0, st, a);
   return hipGetLastError();
-}
-
-hipError_t sgd(DType dt, const TensorSet& ts, float lr, float mom, float wd, hipStream_t st,
-               const KTimer* kt) {
-  return run_multi(dt, ts, true, lr, mom, wd, st, kt);
-}
-hipError_t cast_weights(DType dt, const TensorSet& ts, hipStream_t st) {
-  return run_multi(dt, ts, false, 0.f, 0.f, 0.f, st);
 }
 
 // =========================================================================

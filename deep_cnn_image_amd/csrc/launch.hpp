@@ -180,16 +180,12 @@ size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n);
 hipError_t bias_grads_sgd(DType, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch, hipStream_t,
                           const KTimer* kt = nullptr);
 
-// ---- optimizer, casts, dropout mask
+// ---- working-copy cast, dropout mask
 struct TensorSet {
-  float* master[16];
-  float* mom[16];
-  const float* grad[16];
+  const float* master[16];
   void* work[16];
   int64_t n[16];
 };
-hipError_t sgd(DType work_dtype, const TensorSet&, float lr, float momentum, float wd, hipStream_t,
-                      const KTimer* kt = nullptr);
 hipError_t cast_weights(DType work_dtype, const TensorSet&, hipStream_t);
 hipError_t dropout_mask(uint64_t seed, uint64_t step, int layer, int rows, int cols,
                         uint32_t thresh, uint8_t* mask, hipStream_t);
