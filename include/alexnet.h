@@ -74,7 +74,7 @@ typedef struct {
   int32_t batch;     /* images per call; ten-view: source images (10 views each). 1..4096 */
   int32_t groups;    /* 1 = single tower; 2 = conv2/conv4/conv5 split in two groups    */
   int32_t dtype;     /* ALEXNET_F32 or ALEXNET_BF16                                    */
-  int32_t lrn_n;     /* LRN window (odd, 1..15), 5 on the pages                        */
+  int32_t lrn_n;     /* LRN window (odd, 1..9), 5 on the pages                         */
   float lrn_k;       /* 2                                                              */
   float lrn_alpha;   /* 1e-4, multiplies the window sum of squares directly            */
   float lrn_beta;    /* 0.75                                                           */
