@@ -443,3 +443,43 @@ def test_fp32_three_steps_momentum_carry_and_lr_schedule(orc):
             w1 = host(master[j])
             assert np.array_equal(w1.astype(np.float32), s0[j].astype(np.float32) + host(mom[j]).astype(np.float32)), j
             assert torch.equal(work[j], master[j]), j
+
+
+@pytest.mark.parametrize("p", [0.3, 0.0, 0.75])
+def test_dropout_probability_other_than_one_half(orc, p):
+    """cfg.dropout_p other than the pages' 0.5: the training step drops
+    exactly the units the Philox rule with threshold floor(p 2^32) drops (the
+    oracle's mask for p), and inference scales the FC6/FC7 outputs by 1 - p."""
+    syn = I.config_inputs(4, batch=2)
+    sess = Session(2, 1, B.BF16, B.MODE_TRAIN, DEV)
+    sess.cfg.dropout_p = p
+    master = params_f32(syn.master_w, syn.biases)
+    mom = [torch.zeros_like(m) for m in master]
+    work = [torch.empty(m.shape, dtype=torch.bfloat16, device=DEV) for m in master]
+    B.alexnet_cast_weights(sess.cfg, master, work, stream_handle())
+    x = to_device(syn.x, B.BF16, DEV)
+    labels = torch.from_numpy(syn.labels.astype(np.int32)).to(DEV)
+    loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+    sess.train_step(master, mom, work, x, labels, loss, None, seed=5, step=7)
+    torch.cuda.synchronize()
+    pf = float(np.float32(p))
+    for layer, tap in ((0, "drop6"), (1, "drop7")):
+        m = orc.dropout_mask(5, 7, layer, 2, 4096, pf)
+        d = flat(sess.tap(tap))
+        assert np.all(d[m == 0] == 0), tap
+        say(f"[gpu] p={p} {tap}: kept {m.mean():.3f}, nonzero outputs only where kept")
+    g = torch.empty((2, 4096), dtype=torch.uint8, device=DEV)
+    B.alexnet_dropout_mask(5, 7, 0, 2, 4096, p, g, stream_handle())
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), orc.dropout_mask(5, 7, 0, 2, 4096, pf))
+    # inference: FC6/FC7 outputs times 1 - p, layer-isolated on the stored FC input
+    fs = Session(2, 1, B.BF16, B.MODE_FORWARD, DEV)
+    fs.cfg.dropout_p = p
+    params = fs.upload_params(syn.weights, syn.biases)
+    fs.forward(params, x)
+    torch.cuda.synchronize()
+    pool5, d6 = flat(fs.tap("pool5")), flat(fs.tap("drop6"))
+    want = (1.0 - pf) * orc.relu(orc.fc(pool5, syn.weights[5], syn.biases[5]))
+    e = rel_l2(d6, want)
+    say(f"[gpu] p={p} inference drop6 rel-L2 {e:.1e}")
+    assert e <= TOL_LAYER_BF16
