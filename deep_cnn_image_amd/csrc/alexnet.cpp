@@ -72,11 +72,20 @@ inline char* tp(void* ws, const Plan& p, int id) { return (char*)ws + p.tap[id].
     if ((x) != hipSuccess) return ALEXNET_E_HIP;   \
   } while (0)
 
+// What the network head produces after FC8: softmax probabilities (probs may
+// be null) and, with labels, the cross-entropy gradient and per-row losses.
+struct Head {
+  const int32_t* labels;
+  float* probs;
+  void* dz;
+  float* rowloss;
+};
+
 // Forward pass.  train: dropout masks of (seed, step); else the 1 - p scale.
 // x: 227 x 227 images, 256 x 256 ten-view sources (ten-view plan), or, with
 // `aug`, aug_h x aug_w sources of augmented patches.
 int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* ws, bool train,
-                    uint64_t seed, uint64_t step, hipStream_t st, const Timers& T,
+                    uint64_t seed, uint64_t step, hipStream_t st, const Timers& T, const Head& head,
                     const AugSrc* aug = nullptr, int aug_h = 0, int aug_w = 0) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
@@ -139,9 +148,8 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   ep.layer = 1;
   HIPCHK(fc_fwd(dt, N, 4096, 4096, tp(ws, p, T_DROP6), prm[12], prm[13], ep, tp(ws, p, T_DROP7), nullptr,
                 part, p.part_bytes, st, T(ALEXNET_KT_FC7_FWD)));
-  FcEpi lin{};
-  HIPCHK(fc_fwd(dt, N, 4096, 1000, tp(ws, p, T_DROP7), prm[14], prm[15], lin, nullptr,
-                (float*)tp(ws, p, T_LOGITS), part, p.part_bytes, st, T(ALEXNET_KT_FC8_FWD)));
+  HIPCHK(fc_head(dt, N, 4096, 1000, tp(ws, p, T_DROP7), prm[14], prm[15], (float*)tp(ws, p, T_LOGITS),
+                 head.labels, head.probs, head.dz, head.rowloss, part, p.part_bytes, st, T(ALEXNET_KT_FC8_FWD)));
   return ALEXNET_OK;
 }
 
@@ -154,7 +162,7 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
 //  - biases with their gradients, in the last two launches.
 // Every gradient except the FC weights' also lands in the workspace (taps).
 int enqueue_backward(const Plan& p, void* const* work, float* const* master, float* const* momentum,
-                     const SgdHyper& hy, void* ws, hipStream_t st, const Timers& T) {
+                     const SgdHyper& hy, float* loss, void* ws, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -228,7 +236,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
       jobs[i] = BiasJob{tp(ws, p, dys[i]), rows, (int)net.bcount[i], gb(i), master[2 * i + 1],
                         momentum[2 * i + 1], work[2 * i + 1]};
     }
-    HIPCHK(bias_grads_sgd(dt, jobs, 8, hy, cs, st, T(ALEXNET_KT_BIAS)));
+    HIPCHK(bias_grads_sgd(dt, jobs, 8, hy, cs, (const float*)tp(ws, p, T_ROWLOSS), N, loss, st,
+                          T(ALEXNET_KT_BIAS)));
   }
   return ALEXNET_OK;
 }
@@ -277,8 +286,9 @@ int alexnet_forward_timed(const alexnet_cfg* cfg, const void* const params[16], 
   if ((r = load_timers(timers, n_timers, &T)) != ALEXNET_OK) return r;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  if ((r = enqueue_forward(p, params, x, ws, false, 0, 0, st, T)) != ALEXNET_OK) return r;
-  if (softmax((const float*)tp(ws, p, T_LOGITS), probs, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
+  if ((r = enqueue_forward(p, params, x, ws, false, 0, 0, st, T, Head{nullptr, probs, nullptr, nullptr})) !=
+      ALEXNET_OK)
+    return r;
   return ALEXNET_OK;
 }
 
@@ -297,9 +307,10 @@ int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16]
   if (!aligned(src, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  if ((r = enqueue_forward(p, params, src, ws, false, 0, 0, st, Timers())) != ALEXNET_OK) return r;
   float* vp = (float*)tp(ws, p, T_VIEWPROBS);
-  if (softmax((const float*)tp(ws, p, T_LOGITS), vp, p.N, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
+  if ((r = enqueue_forward(p, params, src, ws, false, 0, 0, st, Timers(), Head{nullptr, vp, nullptr, nullptr})) !=
+      ALEXNET_OK)
+    return r;
   if (view_mean(vp, probs, cfg->batch, 1000, st) != hipSuccess) return ALEXNET_E_HIP;
   return ALEXNET_OK;
 }
@@ -338,16 +349,12 @@ int train_step_impl(const alexnet_cfg* cfg, float* const master[16], float* cons
   if ((r = load_timers(timers, n_timers, &T)) != ALEXNET_OK) return r;
   if ((r = check_device()) != ALEXNET_OK) return r;
   hipStream_t st = (hipStream_t)stream;
-  const DType dt = cfg->dtype == ALEXNET_BF16 ? BF16 : F32;
-  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st, T, aug, aug_h, aug_w)) !=
-      ALEXNET_OK)
+  const Head head{labels, probs, tp(ws, p, T_DLOGITS), (float*)tp(ws, p, T_ROWLOSS)};
+  if ((r = enqueue_forward(p, (const void* const*)work, x, ws, true, seed, step, st, T, head, aug, aug_h,
+                           aug_w)) != ALEXNET_OK)
     return r;
-  if (softmax_ce(dt, (const float*)tp(ws, p, T_LOGITS), labels, probs, tp(ws, p, T_DLOGITS),
-                 (float*)tp(ws, p, T_ROWLOSS), p.N, 1000, st) != hipSuccess)
-    return ALEXNET_E_HIP;
-  if (mean_reduce((const float*)tp(ws, p, T_ROWLOSS), p.N, loss, st) != hipSuccess) return ALEXNET_E_HIP;
   const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
-  if ((r = enqueue_backward(p, work, master, momentum, hy, ws, st, T)) != ALEXNET_OK) return r;
+  if ((r = enqueue_backward(p, work, master, momentum, hy, loss, ws, st, T)) != ALEXNET_OK) return r;
   return ALEXNET_OK;
 }
 

@@ -1777,79 +1777,100 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int SOFTMAX_MAX_O = 1024;
+// Network head, one workgroup per row m: the FC8 split-K partials summed in
+// split order plus the bias (the logits, stored fp32), then the softmax and,
+// with CE, the cross-entropy gradient (p - onehot(y)) / M and the row's loss
+// -(z_y - max - log sum exp).  Each thread holds 4 consecutive logits.
+constexpr int HEAD_MAX_O = 4 * TPB;
 template <typename T, bool CE>
-__global__ void k_softmax(const float* __restrict__ z, const int32_t* __restrict__ labels,
-                          float* __restrict__ p, T* __restrict__ dz, float* __restrict__ rowloss, int M,
-                          int O) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
-  if (row >= M) return;
-  // the row is read once into registers (O <= SOFTMAX_MAX_O)
-  const float* zr = z + (int64_t)row * O;
-  float v[SOFTMAX_MAX_O / 64];
+__global__ void __launch_bounds__(TPB) k_fc_head(const float* __restrict__ part, int S, int M, int O,
+                                                 const T* __restrict__ bias, float* __restrict__ logits,
+                                                 const int32_t* __restrict__ labels, float* __restrict__ p,
+                                                 T* __restrict__ dz, float* __restrict__ rowloss) {
+  __shared__ float red[TPB / 64];
+  const int m = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n0 = 4 * t;
+  const bool on = n0 < O;
+  float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (on) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float4 q = *reinterpret_cast<const float4*>(part + ((int64_t)s2 * M + m) * O + n0);
+      a[0] += q.x; a[1] += q.y; a[2] += q.z; a[3] += q.w;
+    }
 #pragma unroll
-  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
-    const int i = lane + 64 * q;
-    v[q] = i < O ? zr[i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) v[i] = a[i] + Num<T>::load(bias[n0 + i]);
+    *reinterpret_cast<float4*>(logits + (int64_t)m * O + n0) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) mx = fmaxf(mx, v[q]);
+  // row maximum, then the sum of exponentials: each wave reduces with
+  // shuffles, then the waves' values combine in wave order
+  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
   mx = wave_max(mx);
-  float s = 0.f;
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
 #pragma unroll
-  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
-    v[q] = lane + 64 * q < O ? expf(v[q] - mx) : 0.f;
-    s += v[q];
+  for (int w = 1; w < TPB / 64; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  float e[4], s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e[i] = on ? expf(v[i] - mx) : 0.f;
+    s += e[i];
   }
   s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  s = red[0];
+#pragma unroll
+  for (int w = 1; w < TPB / 64; ++w) s += red[w];
+  if (!on) return;
   const float inv = 1.f / s;
   int y = 0;
-  if (CE) { y = labels[row]; y = y < 0 ? 0 : (y >= O ? O - 1 : y); }
+  if (CE) { y = labels[m]; y = y < 0 ? 0 : (y >= O ? O - 1 : y); }
+  float pr[4];
 #pragma unroll
-  for (int q = 0; q < SOFTMAX_MAX_O / 64; ++q) {
-    const int i = lane + 64 * q;
-    if (i < O) {
-      const float pi = v[q] * inv;
-      if (p) p[(int64_t)row * O + i] = pi;
-      if (CE) dz[(int64_t)row * O + i] = Num<T>::store((pi - (i == y ? 1.f : 0.f)) / (float)M);
+  for (int i = 0; i < 4; ++i) pr[i] = e[i] * inv;
+  if (p) *reinterpret_cast<float4*>(p + (int64_t)m * O + n0) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+  if (CE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dz[(int64_t)m * O + n0 + i] = Num<T>::store((pr[i] - (n0 + i == y ? 1.f : 0.f)) / (float)M);
+      if (n0 + i == y) rowloss[m] = -(v[i] - mx - logf(s));
     }
   }
-  if (CE && lane == 0) rowloss[row] = -(zr[y] - mx - logf(s));
 }
 
-hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t st) {
-  if (O > SOFTMAX_MAX_O) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_softmax<float, false>), dim3(cdiv(M, TPB / 64)), dim3(TPB), 0, st, z,
-                     (const int32_t*)nullptr, p, (float*)nullptr, (float*)nullptr, M, O);
-  return hipGetLastError();
-}
-hipError_t softmax_ce(DType dt, const float* z, const int32_t* labels, float* p, void* dz, float* rowloss,
-                      int M, int O, hipStream_t st) {
-  if (O > SOFTMAX_MAX_O) return hipErrorInvalidValue;
-  const dim3 g(cdiv(M, TPB / 64));
-  if (dt == BF16) hipLaunchKernelGGL((k_softmax<bf16, true>), g, dim3(TPB), 0, st, z, labels, p, (bf16*)dz, rowloss, M, O);
-  else hipLaunchKernelGGL((k_softmax<float, true>), g, dim3(TPB), 0, st, z, labels, p, (float*)dz, rowloss, M, O);
+template <typename T>
+static hipError_t fc_head_t(int M, int K, int O, const void* x, const void* w, const void* b, float* logits,
+                            const int32_t* labels, float* probs, void* dz, float* rowloss, float* part,
+                            size_t part_bytes, hipStream_t st, const KTimer* kt) {
+  constexpr int BM = 128, BN = 128;
+  if (O % 4 || O > HEAD_MAX_O) return hipErrorInvalidValue;
+  const int S = fc_splits(M, O, K);
+  if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  RowsLd<T, BM> a;
+  a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
+  RowsLd<T, BN> bl;
+  bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
+  EpF32 e;
+  e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
+  hipError_t err = fc_gemm<T>(a, bl, e, M, O, K, S, st, kt);
+  if (err != hipSuccess) return err;
+  if (labels)
+    hipLaunchKernelGGL((k_fc_head<T, true>), dim3(M), dim3(TPB), 0, st, part, S, M, O, (const T*)b, logits, labels,
+                       probs, (T*)dz, rowloss);
+  else
+    hipLaunchKernelGGL((k_fc_head<T, false>), dim3(M), dim3(TPB), 0, st, part, S, M, O, (const T*)b, logits,
+                       labels, probs, (T*)nullptr, (float*)nullptr);
   return hipGetLastError();
 }
 
-// out = (sum of v[0..n)) / n, one workgroup, fixed reduction order.
-__global__ void k_mean_reduce(const float* __restrict__ v, int n, float* __restrict__ out) {
-  __shared__ float sh[TPB];
-  float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += TPB) s += v[i];
-  sh[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = TPB / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *out = sh[0] / (float)n;
-}
-hipError_t mean_reduce(const float* v, int n, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_mean_reduce, dim3(1), dim3(TPB), 0, st, v, n, out);
-  return hipGetLastError();
+hipError_t fc_head(DType dt, int M, int K, int O, const void* x, const void* w, const void* b, float* logits,
+                   const int32_t* labels, float* probs, void* dz, float* rowloss, float* part, size_t part_bytes,
+                   hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? fc_head_t<bf16>(M, K, O, x, w, b, logits, labels, probs, dz, rowloss, part, part_bytes, st, kt)
+                    : fc_head_t<float>(M, K, O, x, w, b, logits, labels, probs, dz, rowloss, part, part_bytes, st, kt);
 }
 
 __global__ void k_view_mean(const float* __restrict__ p, float* __restrict__ out, int N, int O) {
@@ -1954,6 +1975,9 @@ struct BiasArgs2 {
   int cstart[BIAS_MAX + 1];   // first bias element of each layer
   int n;
   float lr, mom, wdlr;
+  const float* rowloss;       // optional: loss = mean of rowloss[0..nrow), by one more wave
+  int nrow;
+  float* loss;
 };
 
 template <typename T>
@@ -1971,6 +1995,14 @@ template <typename T>
 __global__ void __launch_bounds__(TPB) k_bias_sgd(BiasArgs2 a) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
+  if (e == a.cstart[a.n] && a.rowloss) {
+    float s = 0.f;
+    for (int r = lane; r < a.nrow; r += 64) s += a.rowloss[r];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) *a.loss = s / (float)a.nrow;
+    return;
+  }
   if (e >= a.cstart[a.n]) return;
   int j = 0;
 #pragma unroll
@@ -2000,10 +2032,13 @@ size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n) {
 }
 
 hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch,
-                          hipStream_t st, const KTimer* kt) {
+                          const float* rowloss, int nrow, float* loss, hipStream_t st, const KTimer* kt) {
   if (n < 1 || n > BIAS_MAX) return hipErrorInvalidValue;
   BiasArgs1 a1 = {};
   BiasArgs2 a2 = {};
+  a2.rowloss = rowloss;
+  a2.nrow = nrow;
+  a2.loss = loss;
   a1.n = a2.n = n;
   int blocks = 0, cols = 0;
   float* part = scratch;
@@ -2037,10 +2072,10 @@ hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& 
   rec_start(kt, st);
   if (dt == BF16) {
     hipLaunchKernelGGL((k_bias_colsum<bf16>), dim3(blocks), dim3(TPB), 0, st, a1);
-    hipLaunchKernelGGL((k_bias_sgd<bf16>), dim3(cdiv(cols, TPB / 64)), dim3(TPB), 0, st, a2);
+    hipLaunchKernelGGL((k_bias_sgd<bf16>), dim3(cdiv(cols + 1, TPB / 64)), dim3(TPB), 0, st, a2);
   } else {
     hipLaunchKernelGGL((k_bias_colsum<float>), dim3(blocks), dim3(TPB), 0, st, a1);
-    hipLaunchKernelGGL((k_bias_sgd<float>), dim3(cdiv(cols, TPB / 64)), dim3(TPB), 0, st, a2);
+    hipLaunchKernelGGL((k_bias_sgd<float>), dim3(cdiv(cols + 1, TPB / 64)), dim3(TPB), 0, st, a2);
   }
   rec_stop(kt, st);
   return hipGetLastError();

@@ -156,11 +156,13 @@ hipError_t pool5_fwd(DType, const void* x, void* y_flat, uint8_t* arg, int N, in
 hipError_t pool5_bwd(DType, const void* dy_flat, const uint8_t* arg, const void* mask, void* dx, int N, int H,
                      int W, int C, hipStream_t, const KTimer* kt = nullptr);
 
-// ---- softmax, loss, ten-view mean, column sums
-hipError_t softmax(const float* z, float* p, int M, int O, hipStream_t);
-hipError_t softmax_ce(DType, const float* z, const int32_t* labels, float* p, void* dz,
-                      float* rowloss, int M, int O, hipStream_t);
-hipError_t mean_reduce(const float* v, int n, float* out, hipStream_t);
+// ---- network head, ten-view mean, column sums
+// FC8 and the softmax: logits[M][O] fp32 = x W^T + b (split-K GEMM), then
+// p = softmax(logits) (p may be null); with labels also dz = (p - onehot)/M
+// in the compute type and rowloss[m] = -log p[m][label].  O % 4 == 0, O <= 1024.
+hipError_t fc_head(DType, int M, int K, int O, const void* x, const void* w, const void* b, float* logits,
+                   const int32_t* labels, float* p, void* dz, float* rowloss, float* part, size_t part_bytes,
+                   hipStream_t, const KTimer* kt = nullptr);
 hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t);
 // Bias gradients of up to BIAS_MAX layers, grad[c] = sum over the rows of
 // dy[rows][C] (fp32), each followed by the SGD update of the bias (w, v fp32
@@ -177,8 +179,9 @@ struct BiasJob {
   void* wb;
 };
 size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n);
-hipError_t bias_grads_sgd(DType, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch, hipStream_t,
-                          const KTimer* kt = nullptr);
+// Also, if rowloss is not null, *loss = mean of rowloss[0..nrow) (fixed order).
+hipError_t bias_grads_sgd(DType, const BiasJob* jobs, int n, const SgdHyper& hy, float* scratch,
+                          const float* rowloss, int nrow, float* loss, hipStream_t, const KTimer* kt = nullptr);
 
 // ---- working-copy cast, dropout mask
 struct TensorSet {
