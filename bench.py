@@ -276,6 +276,46 @@ def main():
         fwd[key] = (time.perf_counter() - t0) / args.steps
         del fs
 
+    # ---------------------------------------------------------------- ten-view inference
+    # 256 sources of 3x256x256; each call runs the forward pass on the 2560
+    # views (four corners and the centre, each also mirrored) and averages
+    # the ten softmax outputs per source.
+    s5 = I.config_inputs(5)
+    n5 = s5.x.shape[0]
+    ts = Session(n5, 1, B.BF16, B.MODE_TENVIEW, dev)
+    params5 = ts.upload_params(s5.weights, s5.biases)
+    src5 = to_device(s5.x, B.BF16, dev)
+    probs5 = torch.empty((n5, 1000), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        B.alexnet_forward_tenview(ts.cfg, params5, src5, probs5, ts.ws, ts.ws_bytes, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        B.alexnet_forward_tenview(ts.cfg, params5, src5, probs5, ts.ws, ts.ws_bytes, stream)
+    torch.cuda.synchronize()
+    tenview_s = (time.perf_counter() - t0) / args.steps
+    del ts, src5, params5
+
+    # ---------------------------------------------------------------- batch-1 fp32 forward (latency)
+    # One image, fp32 weights and activations: each call is waited for on
+    # its own, so the figure is the latency of one call, launches included.
+    s1 = I.config_inputs(1)
+    ls = Session(1, 1, B.F32, B.MODE_FORWARD, dev)
+    params1 = ls.upload_params(s1.weights, s1.biases)
+    x1 = to_device(s1.x, B.F32, dev)
+    probs1 = torch.empty((1, 1000), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        B.alexnet_forward(ls.cfg, params1, x1, probs1, ls.ws, ls.ws_bytes, stream)
+    torch.cuda.synchronize()
+    lat = []
+    for _ in range(max(args.steps, 5)):
+        t0 = time.perf_counter()
+        B.alexnet_forward(ls.cfg, params1, x1, probs1, ls.ws, ls.ws_bytes, stream)
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    lat_s = float(np.median(lat))
+    del ls, params1
+
     # ---------------------------------------------------------------- fractions of roofline
     def frac(nm, ms, groups=1, train=True):
         kind, work = kernel_work(nm, n, groups, train)
@@ -337,6 +377,12 @@ def main():
                         "flags, PCA colour shifts with alpha ~ N(0, 0.1)), staged straight from the sources",
             "staging": frac("S2D", aug_stage_ms)},
         "rgb_pca": dict(frac_pca(pca_ms), images=n, size=f"3x{hs}x{ws_}"),
+        "tenview": {"views_per_s": round(10 * n5 / tenview_s, 1), "source_images_per_s": round(n5 / tenview_s, 1),
+                    "ms": round(tenview_s * 1e3, 4),
+                    "workload": f"{n5} sources of 3x256x256, ten 227x227 views each (bf16, single tower)"},
+        "forward_bs1_fp32": {"latency_ms": round(lat_s * 1e3, 4), "images_per_s": round(1.0 / lat_s, 1),
+                             "workload": "one 3x227x227 image, fp32 weights and activations, single tower; "
+                                         "median of calls each waited for"},
     }
 
     if args.copy_calibration:

@@ -111,22 +111,23 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
     const int hs = aug ? aug_h : tenview ? 256 : 227, wsz = aug ? aug_w : hs;
     HIPCHK(stage_inputs(dt, jobs, nj, x, hs, wsz, kind, aug, N, at(ws, p.xs2d), st, T(ALEXNET_KT_S2D)));
   }
-  HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), st,
+  float* part = (float*)at(ws, p.part);   // split-K partials (small batches, FC layers)
+  HIPCHK(conv1_fwd(dt, at(ws, p.xs2d), N, at(ws, p.w1s), prm[1], tp(ws, p, T_CONV1), part, p.part_bytes, st,
                    T(ALEXNET_KT_CONV1_FWD)));
   HIPCHK(lrn_pool_fwd(dt, tp(ws, p, T_CONV1), tp(ws, p, T_POOL1), (uint8_t*)tp(ws, p, T_ARG1),
                       c.lrn_taps ? tp(ws, p, T_LRN1) : nullptr, N, 55, 55, 96, c.lrn_k, c.lrn_alpha, c.lrn_beta,
                       c.lrn_n, st, T(ALEXNET_KT_LRNPOOL1_FWD)));
-  HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), st,
-                  T(ALEXNET_KT_CONV2_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[1], tp(ws, p, T_POOL1), at(ws, p.wr[1]), prm[3], tp(ws, p, T_CONV2), part,
+                  p.part_bytes, st, T(ALEXNET_KT_CONV2_FWD)));
   HIPCHK(lrn_pool_fwd(dt, tp(ws, p, T_CONV2), tp(ws, p, T_POOL2), (uint8_t*)tp(ws, p, T_ARG2),
                       c.lrn_taps ? tp(ws, p, T_LRN2) : nullptr, N, 27, 27, 256, c.lrn_k, c.lrn_alpha, c.lrn_beta,
                       c.lrn_n, st, T(ALEXNET_KT_LRNPOOL2_FWD)));
-  HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), st,
-                  T(ALEXNET_KT_CONV3_FWD)));
-  HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), st,
-                  T(ALEXNET_KT_CONV4_FWD)));
-  HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), st,
-                  T(ALEXNET_KT_CONV5_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[2], tp(ws, p, T_POOL2), at(ws, p.wr[2]), prm[5], tp(ws, p, T_CONV3), part,
+                  p.part_bytes, st, T(ALEXNET_KT_CONV3_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[3], tp(ws, p, T_CONV3), at(ws, p.wr[3]), prm[7], tp(ws, p, T_CONV4), part,
+                  p.part_bytes, st, T(ALEXNET_KT_CONV4_FWD)));
+  HIPCHK(conv_fwd(dt, net.conv[4], tp(ws, p, T_CONV4), at(ws, p.wr[4]), prm[9], tp(ws, p, T_CONV5), part,
+                  p.part_bytes, st, T(ALEXNET_KT_CONV5_FWD)));
   HIPCHK(pool5_fwd(dt, tp(ws, p, T_CONV5), tp(ws, p, T_POOL5), (uint8_t*)tp(ws, p, T_ARG5), N, 13, 13, 256, st,
                    T(ALEXNET_KT_POOL5_FWD)));
 
@@ -141,7 +142,6 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
     ep.drop = 2;
     ep.scale = 1.f - c.dropout_p;
   }
-  float* part = (float*)at(ws, p.part);
   ep.layer = 0;
   HIPCHK(fc_fwd(dt, N, 9216, 4096, tp(ws, p, T_POOL5), prm[10], prm[11], ep, tp(ws, p, T_DROP6), nullptr,
                 part, p.part_bytes, st, T(ALEXNET_KT_FC6_FWD)));

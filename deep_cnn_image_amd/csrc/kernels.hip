@@ -168,37 +168,6 @@ __device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* _
   }
 }
 
-
-
-static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
-
-template <typename T>
-struct Conv1FwdFn {
-  const void* xs; int Nimg; const void* ws2d; const void* b1; void* y; hipStream_t st; const KTimer* kt;
-  template <int BM, int BN, int WGM, int WGN>
-  hipError_t operator()() const {
-    Im2colLd<T, BM> a;
-    a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
-    RowsLd<T, BN> b;
-    b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
-    EpBiasRelu<T> e;
-    e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
-    return run_gemm<T, BM, BN, WGM, WGN>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
-  }
-};
-
-template <typename T>
-static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
-                              hipStream_t st, const KTimer* kt) {
-  return by_tile<T>(Nimg * 3025, 96, 1, Conv1FwdFn<T>{xs, Nimg, ws2d, b1, y, st, kt});
-}
-
-hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
-                     hipStream_t st, const KTimer* kt) {
-  return dt == BF16 ? conv1_fwd_t<bf16>(xs, Nimg, ws2d, b1, y, st, kt)
-                    : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, st, kt);
-}
-
 // Tile for an implicit-GEMM convolution with M output rows, N columns per
 // group.  n-tile: 128 when it divides N, else 96, else 48 (four waves stacked
 // along m), else 128 with a ragged last tile.  m-tile (bf16): the one of 96,
@@ -228,22 +197,115 @@ static hipError_t by_bm(int bm, Fn&& fn) {
   }
 }
 
+// Tile (BM x BN) that by_tile runs for an M x N (per group) convolution GEMM.
+static void conv_tile(bool bf, int M, int N, int groups, int& bm, int& bn) {
+  const bool bn128 = N % 128 == 0 || (N % 96 != 0 && !(N % 48 == 0 && N <= 96));
+  bn = bn128 ? 128 : N % 96 == 0 ? 96 : 48;
+  bm = bf && bn != 48 ? pick_bm(M, N, bn, groups) : 128;
+}
+
 template <typename T, class Fn>
 static hipError_t by_tile(int M, int N, int groups, Fn&& fn) {
-  const bool bn128 = N % 128 == 0 || (N % 96 != 0 && !(N % 48 == 0 && N <= 96));
+  int bm, bn;
+  conv_tile(std::is_same<T, bf16>::value, M, N, groups, bm, bn);
   if constexpr (std::is_same<T, bf16>::value) {
-    if (bn128) return by_bm<128>(pick_bm(M, N, 128, groups), fn);
-    if (N % 96 == 0) return by_bm<96>(pick_bm(M, N, 96, groups), fn);
+    if (bn == 128) return by_bm<128>(bm, fn);
+    if (bn == 96) return by_bm<96>(bm, fn);
   } else {
-    if (bn128) return fn.template operator()<128, 128, 2, 2>();
-    if (N % 96 == 0) return fn.template operator()<128, 96, 2, 2>();
+    if (bn == 128) return fn.template operator()<128, 128, 2, 2>();
+    if (bn == 96) return fn.template operator()<128, 96, 2, 2>();
   }
   return fn.template operator()<128, 48, 4, 1>();
 }
 
+// ---- split-K for convolutions too small to fill the chip (small batches)
+// With fewer workgroups than CUs, each one's long k loop is the whole run
+// time.  The k range is then split until the chip holds one round of
+// workgroups (512 bf16 ones, two per CU; 256 fp32 ones, whose LDS tiles
+// allow one per CU), each over at least three k-slices for bf16 or one for
+// fp32 (whose slices carry 16 times the matrix-core time).  fp32 partials go
+// to the workspace and k_fc_reduce sums them in split order and applies bias
+// and ReLU.  At batch 128 every layer's tiles alone fill the chip and
+// nothing is split.
+static int conv_split_count(int64_t wgs, int K, bool f32) {
+  if (wgs >= 256) return 1;
+  const int kt = cdiv(K, GEMM_BK);
+  int want = (int)(((f32 ? 256 : 512) + wgs - 1) / wgs);
+  const int cap = f32 ? kt : kt / 3;
+  if (want > cap) want = cap;
+  return eff_splits(K, want);
+}
+
+static int conv_fwd_splits(DType dt, int M, int N, int K, int groups) {
+  int bm, bn;
+  conv_tile(dt == BF16, M, N, groups, bm, bn);
+  return conv_split_count((int64_t)cdiv(M, bm) * cdiv(N, bn) * groups, K, dt == F32);
+}
+
+template <typename T>
+__global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N, int64_t ldo,
+                            const T* __restrict__ bias, FcEpi ep, const T* __restrict__ mask, T* __restrict__ out,
+                            float* __restrict__ out_f32);
+
+// Partials part[g][s][m][n] (n < N per group), then per group the ordered
+// sum + bias + ReLU into out[m * ldo + g * N + n].
+template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL>
+static hipError_t conv_fwd_split(const AL& a, const BL& b, int M, int N, int K, int groups, int S,
+                                 const void* bias, void* y, int64_t ldo, float* part, size_t part_bytes,
+                                 hipStream_t st, const KTimer* kt) {
+  if (N % 4 || (size_t)S * groups * M * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  EpF32 e;
+  e.out = part; e.ldo = N; e.M = M; e.N = N; e.splits = S;
+  rec_start(kt, st);
+  hipError_t err = run_gemm<T, BM, BN, WGM, WGN>(a, b, e, M, N, K, groups, S, st);
+  if (err != hipSuccess) return err;
+  FcEpi ep{};
+  ep.relu = 1;
+  for (int g = 0; g < groups; ++g)
+    hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * N / 4), dim3(TPB), 0, st,
+                       part + (size_t)g * S * M * N, S, M, N, ldo, (const T*)bias + g * N, ep, (const T*)nullptr,
+                       (T*)y + g * N, (float*)nullptr);
+  rec_stop(kt, st);
+  return hipGetLastError();
+}
+
+static ConvGeom conv1_geom() { return ConvGeom{S2D_B, S2D_B, S2D_C, S2D_C, 3, 3, 1, 0, 55, 55}; }
+
+template <typename T>
+struct Conv1FwdFn {
+  const void* xs; int Nimg; const void* ws2d; const void* b1; void* y; float* part; size_t part_bytes;
+  hipStream_t st; const KTimer* kt;
+  template <int BM, int BN, int WGM, int WGN>
+  hipError_t operator()() const {
+    Im2colLd<T, BM> a;
+    a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
+    RowsLd<T, BN> b;
+    b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
+    const int S = conv_split_count(cdiv(a.M, BM) * cdiv(96, BN), S2D_K, std::is_same<T, float>::value);
+    if (S > 1) return conv_fwd_split<T, BM, BN, WGM, WGN>(a, b, a.M, 96, S2D_K, 1, S, b1, y, 96, part,
+                                                          part_bytes, st, kt);
+    EpBiasRelu<T> e;
+    e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
+    return run_gemm<T, BM, BN, WGM, WGN>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
+  }
+};
+
+template <typename T>
+static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y, float* part,
+                              size_t part_bytes, hipStream_t st, const KTimer* kt) {
+  return by_tile<T>(Nimg * 3025, 96, 1, Conv1FwdFn<T>{xs, Nimg, ws2d, b1, y, part, part_bytes, st, kt});
+}
+
+hipError_t conv1_fwd(DType dt, const void* xs, int Nimg, const void* ws2d, const void* b1, void* y, float* part,
+                     size_t part_bytes, hipStream_t st, const KTimer* kt) {
+  return dt == BF16 ? conv1_fwd_t<bf16>(xs, Nimg, ws2d, b1, y, part, part_bytes, st, kt)
+                    : conv1_fwd_t<float>(xs, Nimg, ws2d, b1, y, part, part_bytes, st, kt);
+}
+
 template <typename T>
 struct ConvFwdFn {
-  ConvShape s; const void* x; const void* wr; const void* b; void* y; hipStream_t st; const KTimer* kt;
+  ConvShape s; const void* x; const void* wr; const void* b; void* y; float* part; size_t part_bytes;
+  hipStream_t st; const KTimer* kt;
   template <int BM, int BN, int WGM, int WGN>
   hipError_t operator()() const {
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
@@ -255,6 +317,11 @@ struct ConvFwdFn {
     a.K = s.K * s.K * Cig;
     RowsLd<T, BN> bl;
     bl.p = (const T*)wr; bl.ld = a.K; bl.rows = Cog; bl.K = a.K; bl.gstride = (int64_t)Cog * a.K;
+    const int S = conv_split_count((int64_t)cdiv(a.M, BM) * cdiv(Cog, BN) * s.groups, a.K,
+                                   std::is_same<T, float>::value);
+    if (S > 1)
+      return conv_fwd_split<T, BM, BN, WGM, WGN>(a, bl, a.M, Cog, a.K, s.groups, S, b, y, s.Cout, part,
+                                                 part_bytes, st, kt);
     EpBiasRelu<T> e;
     e.out = (T*)y; e.bias = (const T*)b; e.ldo = s.Cout; e.M = a.M; e.N = Cog;
     return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cog, a.K, s.groups, 1, st, kt);
@@ -262,12 +329,25 @@ struct ConvFwdFn {
 };
 
 hipError_t conv_fwd(DType dt, const ConvShape& s, const void* x, const void* wr, const void* b, void* y,
-                    hipStream_t st, const KTimer* kt) {
+                    float* part, size_t part_bytes, hipStream_t st, const KTimer* kt) {
   const int Cog = s.Cout / s.groups;
   const int M = s.Nimg * s.Ho * s.Wo;
-  if (dt == BF16) { ConvFwdFn<bf16> f{s, x, wr, b, y, st, kt}; return by_tile<bf16>(M, Cog, s.groups, f); }
-  ConvFwdFn<float> f{s, x, wr, b, y, st, kt};
+  if (dt == BF16) {
+    ConvFwdFn<bf16> f{s, x, wr, b, y, part, part_bytes, st, kt};
+    return by_tile<bf16>(M, Cog, s.groups, f);
+  }
+  ConvFwdFn<float> f{s, x, wr, b, y, part, part_bytes, st, kt};
   return by_tile<float>(M, Cog, s.groups, f);
+}
+
+size_t conv_fwd_part_bytes(DType dt, const ConvShape& s) {
+  const int Cog = s.Cout / s.groups, M = s.Nimg * s.Ho * s.Wo, K = s.K * s.K * (s.Cin / s.groups);
+  const int S = conv_fwd_splits(dt, M, Cog, K, s.groups);
+  return S > 1 ? (size_t)S * s.groups * M * Cog * sizeof(float) : 0;
+}
+size_t conv1_fwd_part_bytes(DType dt, int Nimg) {
+  const int S = conv_fwd_splits(dt, Nimg * 3025, 96, S2D_K, 1);
+  return S > 1 ? (size_t)S * Nimg * 3025 * 96 * sizeof(float) : 0;
 }
 
 template <typename T>
@@ -530,14 +610,84 @@ static hipError_t fc_gemm(const AL& a, const BL& b, const EpF32& e, int M, int N
 size_t fc_fwd_part_bytes(int M, int K, int O) {
   return (size_t)fc_splits(M, O, K) * M * O * sizeof(float);
 }
+
+// Forward product of an FC layer for a handful of rows (M <= FC_ROWS_MAX,
+// the batch-1 latency case), where MFMA tiles would be almost all padding
+// and the run is one pass over the weight matrix.  One wave per output o
+// walks row o of W in 8-element runs, lane l starting at 8 l and stepping
+// 512, multiplies them with the same runs of every input row, and sums its
+// lanes in a fixed order: part[m][o] = sum_k x[m][k] W[o][k] in fp32.
+constexpr int FC_ROWS_MAX = 4;
+template <typename T, int MR>
+__global__ void __launch_bounds__(TPB) k_fc_rows(const T* __restrict__ x, const T* __restrict__ w, int K, int O,
+                                                 float* __restrict__ part) {
+  const int o = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (o >= O) return;   // whole waves; no barrier follows
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  const T* wr = w + (int64_t)o * K;
+#pragma unroll 4
+  for (int k = lane * 8; k < K; k += 512) {
+    float wv[8];
+    Pack8<T>::load(wr + k, wv);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float xv[8];
+      Pack8<T>::load(x + (int64_t)m * K + k, xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[m] = fmaf(xv[i], wv[i], acc[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = acc[m];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    if (lane == 0) part[(int64_t)m * O + o] = v;
+  }
+}
+
+// fp32 partial products part[s][m][o] of x W^T, S of them (set here): the
+// MFMA GEMM split S ways over k, or k_fc_rows (S = 1) for a handful of rows.
+template <typename T>
+static hipError_t fc_partials(int M, int K, int O, const void* x, const void* w, float* part, size_t part_bytes,
+                              hipStream_t st, const KTimer* kt, int& S) {
+  if (M <= FC_ROWS_MAX && K % 8 == 0) {
+    S = 1;
+    if ((size_t)M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+    const dim3 grid(cdiv(O, TPB / 64));
+    const T* xp = (const T*)x;
+    const T* wp = (const T*)w;
+    rec_start(kt, st);
+    switch (M) {
+      case 1: hipLaunchKernelGGL((k_fc_rows<T, 1>), grid, dim3(TPB), 0, st, xp, wp, K, O, part); break;
+      case 2: hipLaunchKernelGGL((k_fc_rows<T, 2>), grid, dim3(TPB), 0, st, xp, wp, K, O, part); break;
+      case 3: hipLaunchKernelGGL((k_fc_rows<T, 3>), grid, dim3(TPB), 0, st, xp, wp, K, O, part); break;
+      default: hipLaunchKernelGGL((k_fc_rows<T, 4>), grid, dim3(TPB), 0, st, xp, wp, K, O, part); break;
+    }
+    rec_stop(kt, st);
+    return hipGetLastError();
+  }
+  S = fc_splits(M, O, K);
+  if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  RowsLd<T, 128> a;
+  a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
+  RowsLd<T, 128> bl;
+  bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
+  EpF32 e;
+  e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
+  return fc_gemm<T>(a, bl, e, M, O, K, S, st, kt);
+}
 size_t fc_dgrad_part_bytes(int M, int K, int O) {
   return (size_t)fc_splits(M, K, O) * M * K * sizeof(float);
 }
 
-// out = epi(sum_s part[s][m][n] + b[n]) for 4 consecutive n per thread.
+// out[m * ldo + n] = epi(sum_s part[s][m][n] + b[n]) for 4 consecutive n per
+// thread (ldo = N for the FC layers; mask, if any, has out's layout).
 template <typename T>
-__global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N, const T* __restrict__ bias,
-                            FcEpi ep, const T* __restrict__ mask, T* __restrict__ out,
+__global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N, int64_t ldo,
+                            const T* __restrict__ bias, FcEpi ep, const T* __restrict__ mask, T* __restrict__ out,
                             float* __restrict__ out_f32) {
   const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
   const int64_t total = (int64_t)M * N / 4;
@@ -569,15 +719,16 @@ __global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N,
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] *= ep.scale;
   }
+  const int64_t o = (int64_t)m * ldo + n;
   if (mask) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = Num<T>::load(mask[e0 + i]) > 0.f ? v[i] : 0.f;
+    for (int i = 0; i < 4; ++i) v[i] = Num<T>::load(mask[o + i]) > 0.f ? v[i] : 0.f;
   }
   if (out_f32) {
-    *reinterpret_cast<float4*>(out_f32 + e0) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(out_f32 + o) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[e0 + i] = Num<T>::store(v[i]);
+    for (int i = 0; i < 4; ++i) out[o + i] = Num<T>::store(v[i]);
   }
 }
 
@@ -585,18 +736,10 @@ template <typename T>
 static hipError_t fc_fwd_t(int M, int K, int O, const void* x, const void* w, const void* b,
                            const FcEpi& ep, void* y, float* y_f32, float* part, size_t part_bytes,
                            hipStream_t st, const KTimer* kt) {
-  constexpr int BM = 128, BN = 128;
-  const int S = fc_splits(M, O, K);
-  if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  RowsLd<T, BM> a;
-  a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
-  RowsLd<T, BN> bl;
-  bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
-  EpF32 e;
-  e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
-  hipError_t err = fc_gemm<T>(a, bl, e, M, O, K, S, st, kt);
+  int S = 1;
+  hipError_t err = fc_partials<T>(M, K, O, x, w, part, part_bytes, st, kt, S);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O,
+  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * O / 4), dim3(TPB), 0, st, part, S, M, O, (int64_t)O,
                      (const T*)b, ep, (const T*)nullptr, (T*)y, y_f32);
   return hipGetLastError();
 }
@@ -623,7 +766,7 @@ static hipError_t fc_dgrad_t(int M, int K, int O, const void* dy, const void* w,
   hipError_t err = fc_gemm<T>(a, bl, e, M, K, O, S, st, kt);
   if (err != hipSuccess) return err;
   FcEpi none{};
-  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K,
+  hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * K / 4), dim3(TPB), 0, st, part, S, M, K, (int64_t)K,
                      (const T*)nullptr, none, (const T*)mask, (T*)dx, (float*)nullptr);
   return hipGetLastError();
 }
@@ -1845,17 +1988,9 @@ template <typename T>
 static hipError_t fc_head_t(int M, int K, int O, const void* x, const void* w, const void* b, float* logits,
                             const int32_t* labels, float* probs, void* dz, float* rowloss, float* part,
                             size_t part_bytes, hipStream_t st, const KTimer* kt) {
-  constexpr int BM = 128, BN = 128;
   if (O % 4 || O > HEAD_MAX_O) return hipErrorInvalidValue;
-  const int S = fc_splits(M, O, K);
-  if ((size_t)S * M * O * sizeof(float) > part_bytes) return hipErrorInvalidValue;
-  RowsLd<T, BM> a;
-  a.p = (const T*)x; a.ld = K; a.rows = M; a.K = K; a.gstride = 0;
-  RowsLd<T, BN> bl;
-  bl.p = (const T*)w; bl.ld = K; bl.rows = O; bl.K = K; bl.gstride = 0;
-  EpF32 e;
-  e.out = part; e.ldo = O; e.M = M; e.N = O; e.splits = S;
-  hipError_t err = fc_gemm<T>(a, bl, e, M, O, K, S, st, kt);
+  int S = 1;
+  hipError_t err = fc_partials<T>(M, K, O, x, w, part, part_bytes, st, kt, S);
   if (err != hipSuccess) return err;
   if (labels)
     hipLaunchKernelGGL((k_fc_head<T, true>), dim3(M), dim3(TPB), 0, st, part, S, M, O, (const T*)b, logits, labels,

@@ -83,13 +83,16 @@ hipError_t rgb_pca(DType, const void* src, int n, int H, int W, float* eigval, f
 constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
 constexpr size_t S2D_W_ELEMS = 96 * 432;
 
-// y NHWC [N][55][55][96] = relu(conv1 + b)
-hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, hipStream_t,
-                      const KTimer* kt = nullptr);
-// NHWC conv + bias + ReLU (layers 2-5)
-hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, const void* b, void* y,
-                    hipStream_t,
-                      const KTimer* kt = nullptr);
+// y NHWC [N][55][55][96] = relu(conv1 + b).  part: split-K partials, at
+// least conv1_fwd_part_bytes (0 unless the batch is too small to fill the chip).
+hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, float* part,
+                     size_t part_bytes, hipStream_t, const KTimer* kt = nullptr);
+// NHWC conv + bias + ReLU (layers 2-5); part as for conv1_fwd, at least
+// conv_fwd_part_bytes.
+hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, const void* b, void* y, float* part,
+                    size_t part_bytes, hipStream_t, const KTimer* kt = nullptr);
+size_t conv1_fwd_part_bytes(DType, int Nimg);
+size_t conv_fwd_part_bytes(DType, const ConvShape&);
 // dX (NHWC) = conv^T(dY) * [mask > 0] (mask optional) for stride-1 layers
 hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, const void* mask,
                       void* dx, hipStream_t,

@@ -126,6 +126,9 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
 
   size_t part = mx(mx(fc_fwd_part_bytes(N, 9216, 4096), fc_fwd_part_bytes(N, 4096, 4096)),
                    fc_fwd_part_bytes(N, 4096, 1000));
+  const DType ddt = dt == ALEXNET_BF16 ? BF16 : F32;
+  part = mx(part, conv1_fwd_part_bytes(ddt, N));
+  for (int i = 1; i < 5; ++i) part = mx(part, conv_fwd_part_bytes(ddt, net.conv[i]));
   size_t cs = 0;
   if (train) {
     mat(T_DLOGITS, N, 1000, dt);

@@ -103,6 +103,33 @@ def gpu_masks(n, seed=3, step=0):
     return out
 
 
+def fp32_backward_on_state(orc, syn, h, w0, b0, masks, step_tag):
+    """For an fp32 step: argmax taps of the HIP path may differ from the
+    oracle forward's only at near-ties (two window values within fp32
+    rounding, which either side may take), counted and checked here; then
+    the oracle's backward pass taken on the step's stored forward state h
+    (NCHW / [N, F] host arrays), so both sides route every gradient element
+    through the same argmax.  Returns (loss, grad_w, grad_b)."""
+    o = orc.alexnet.forward(w0, b0, syn.x, 1, train=True, masks=masks)
+    for k, a in (("arg1", "lrn1"), ("arg2", "lrn2"), ("arg5", "conv5")):   # the pooled tensors
+        bad = np.argwhere(h[k] != o[k])
+        say(f"[gpu] {step_tag} {k}: {len(bad)} of {h[k].size} argmax at near-ties")
+        for n_, c_, i_, j_ in bad:
+            win = np.sort(np.asarray(o[a])[n_, c_, 2 * i_:2 * i_ + 3, 2 * j_:2 * j_ + 3].ravel())
+            assert win[-1] - win[-2] <= 1e-5 * abs(win[-1]), (k, n_, c_, i_, j_)
+    t = {"x": syn.x.astype(np.float64)}
+    for k in ("conv1", "conv2", "conv3", "conv4", "conv5", "pool1", "pool2", "arg1", "arg2", "arg5",
+              "drop6", "drop7"):
+        t[k] = h[k]
+    t["pool5"] = h["pool5"].reshape(-1, 256, 6, 6)
+    t["flat"] = h["pool5"]
+    t["fc6"], t["fc7"] = h["drop6"], h["drop7"]       # mask * [h > 0] == [drop > 0]
+    t["mask6"], t["mask7"] = masks
+    t["probs"] = orc.softmax(orc.fc(h["drop7"], w0[7], b0[7]))
+    loss, gw, gb, _ = orc.alexnet.backward(w0, t, syn.labels, 1)
+    return loss, gw, gb
+
+
 def check_sgd(r, syn):
     """Every element of every tensor: v = mu v0 - wd lr w0 - lr g to within fp32
     rounding of the three terms; w = fl(w0 + v) exactly; work = bf16(w)."""
@@ -262,18 +289,26 @@ def test_grouped_train_step_small(orc):
 
 
 def test_fp32_train_step_small(orc):
+    """fp32 step from a non-zero momentum, at a step count above 2^32: the
+    forward pass and loss against the oracle directly, the weight gradients
+    against the oracle's backward pass on the step's stored forward state
+    (pooling argmax differences only at near-ties), and the update."""
     syn = I.synthetic(6, 2, groups=1, bf16=False)
     v0 = [np.random.default_rng(7).standard_normal(a.shape).astype(np.float32) * 1e-3
           for a in sum(([w, b] for w, b in zip(syn.master_w, syn.biases)), [])]
     r = run_train(syn, dtype=B.F32, seed=11, step=2**32 + 5, v0=v0)
-    vw = [v0[2 * i].astype(np.float64) for i in range(8)]
-    vb = [v0[2 * i + 1].astype(np.float64) for i in range(8)]
-    o = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, vw, vb, syn.x,
-                               syn.labels, 1, seed=11, step=2**32 + 5)
-    ew = [rel_l2(r["gw"][i], o["grad_w"][i]) for i in range(8)]
+    h = hostify(r["taps"])
+    masks = gpu_masks(2, seed=11, step=2**32 + 5)
+    o = orc.alexnet.forward(syn.master_w, syn.biases, syn.x, 1, train=True, masks=masks)
+    fwd = {k: rel_l2(h[k], o[k]) for k in ("conv1", "pool1", "conv2", "pool2", "conv3", "conv4", "conv5",
+                                          "drop6", "drop7")}
+    say("[gpu] fp32 forward rel-L2", {k: f"{v:.1e}" for k, v in fwd.items()})
+    assert max(fwd.values()) <= TOL_F32_OUT
+    oloss, gw, _ = fp32_backward_on_state(orc, syn, h, syn.master_w, syn.biases, masks, "fp32 step")
+    ew = [rel_l2(r["gw"][i], gw[i]) for i in range(8)]
     say("[gpu] fp32 grad_w rel-L2:", [f"{x:.2e}" for x in ew])
     assert max(ew) <= 1e-4
-    assert abs(r["loss"] - o["loss"]) / abs(o["loss"]) <= 1e-5
+    assert abs(r["loss"] - oloss) / abs(oloss) <= 1e-5
     check_sgd(r, syn)
 
 
@@ -410,24 +445,9 @@ def test_fp32_three_steps_momentum_carry_and_lr_schedule(orc):
                                               "drop6", "drop7")}
         say(f"[gpu] step {step} lr {lr}: loss {got:.6f}; forward rel-L2", {k: f"{v:.1e}" for k, v in fwd.items()})
         assert max(fwd.values()) <= TOL_F32_OUT
-        # argmax differences only at near-ties of the oracle's window values
-        for k, a in (("arg1", "lrn1"), ("arg2", "lrn2"), ("arg5", "conv5")):   # the pooled tensors
-            bad = np.argwhere(h[k] != o[k])
-            say(f"[gpu] step {step} {k}: {len(bad)} of {h[k].size} argmax at near-ties")
-            for n_, c_, i_, j_ in bad:
-                win = np.sort(np.asarray(o[a])[n_, c_, 2 * i_:2 * i_ + 3, 2 * j_:2 * j_ + 3].ravel())
-                assert win[-1] - win[-2] <= 1e-5 * abs(win[-1]), (k, n_, c_, i_, j_)
         # gradients on the GPU step's own forward state
-        t = {"x": syn.x.astype(np.float64)}
-        for k in ("conv1", "conv2", "conv3", "conv4", "conv5", "pool1", "pool2", "arg1", "arg2", "arg5",
-                  "drop6", "drop7"):
-            t[k] = h[k]
-        t["pool5"] = h["pool5"].reshape(-1, 256, 6, 6)
-        t["flat"] = h["pool5"]
-        t["fc6"], t["fc7"] = h["drop6"], h["drop7"]
-        t["mask6"], t["mask7"] = gpu_masks(2, seed=9, step=step)
-        t["probs"] = orc.softmax(orc.fc(h["drop7"], w0[7], b0[7]))
-        oloss, gw, gb, _ = orc.alexnet.backward(w0, t, syn.labels, 1)
+        oloss, gw, gb = fp32_backward_on_state(orc, syn, h, w0, b0, gpu_masks(2, seed=9, step=step),
+                                               f"step {step}")
         assert abs(got - oloss) <= 1e-5 * abs(oloss)
         # the GPU's gradients, recovered from its update v1 = mu v0 - wd lr w0 - lr g
         lr32, mu32 = np.float32(lr), np.float32(mu)
