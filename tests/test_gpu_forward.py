@@ -117,7 +117,7 @@ def test_fp32_batch1_matches_oracle(orc):
 
 
 # ---------------------------------------------------------------- bf16, small batches
-@pytest.mark.parametrize("cfg,batch", [(2, 3), (3, 2), (2, 1)])
+@pytest.mark.parametrize("cfg,batch", [(2, 3), (3, 2), (2, 1), (2, 4), (2, 5)])
 def test_bf16_small_batch_layerwise_and_end_to_end(orc, cfg, batch):
     syn = I.config_inputs(cfg, batch=batch)
     g = run_forward(syn, B.BF16)
