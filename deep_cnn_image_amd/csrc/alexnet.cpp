@@ -204,7 +204,7 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
     const SgdTarget u{master[2 * i], momentum[2 * i], work[2 * i], hy};
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), &u, st, T(ktw[i])));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
-                      tp(ws, p, din[i]), st, T(ktd[i])));
+                      tp(ws, p, din[i]), part, p.part_bytes, st, T(ktd[i])));
   }
   // pool2 -> LRN2 -> ReLU2
   HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), tp(ws, p, T_CONV2),
@@ -215,8 +215,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
     const SgdTarget u{master[2], momentum[2], work[2], hy};
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), &u, st,
                       T(ALEXNET_KT_CONV2_WGRAD)));
-    HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), st,
-                      T(ALEXNET_KT_CONV2_DGRAD)));
+    HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), part,
+                      p.part_bytes, st, T(ALEXNET_KT_CONV2_DGRAD)));
   }
   // pool1 -> LRN1 -> ReLU1, then layer-1 weight gradient (no input gradient)
   HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), tp(ws, p, T_CONV1),

@@ -224,9 +224,9 @@ static hipError_t by_tile(int M, int N, int groups, Fn&& fn) {
 // workgroups (512 bf16 ones, two per CU; 256 fp32 ones, whose LDS tiles
 // allow one per CU), each over at least three k-slices for bf16 or one for
 // fp32 (whose slices carry 16 times the matrix-core time).  fp32 partials go
-// to the workspace and k_fc_reduce sums them in split order and applies bias
-// and ReLU.  At batch 128 every layer's tiles alone fill the chip and
-// nothing is split.
+// to the workspace and k_fc_reduce sums them in split order and applies the
+// epilogue (bias and ReLU forward, the ReLU mask for a data gradient).  At
+// batch 128 every layer's tiles alone fill the chip and nothing is split.
 static int conv_split_count(int64_t wgs, int K, bool f32) {
   if (wgs >= 256) return 1;
   const int kt = cdiv(K, GEMM_BK);
@@ -236,7 +236,7 @@ static int conv_split_count(int64_t wgs, int K, bool f32) {
   return eff_splits(K, want);
 }
 
-static int conv_fwd_splits(DType dt, int M, int N, int K, int groups) {
+static int conv_gemm_splits(DType dt, int M, int N, int K, int groups) {
   int bm, bn;
   conv_tile(dt == BF16, M, N, groups, bm, bn);
   return conv_split_count((int64_t)cdiv(M, bm) * cdiv(N, bn) * groups, K, dt == F32);
@@ -248,11 +248,12 @@ __global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N,
                             float* __restrict__ out_f32);
 
 // Partials part[g][s][m][n] (n < N per group), then per group the ordered
-// sum + bias + ReLU into out[m * ldo + g * N + n].
+// sum into out[m * ldo + g * N + n]: forward with bias (bias[g * N + n]) and
+// ReLU; data gradient with the mask [mask > 0] (mask laid out as out).
 template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL>
-static hipError_t conv_fwd_split(const AL& a, const BL& b, int M, int N, int K, int groups, int S,
-                                 const void* bias, void* y, int64_t ldo, float* part, size_t part_bytes,
-                                 hipStream_t st, const KTimer* kt) {
+static hipError_t conv_split_k(const AL& a, const BL& b, int M, int N, int K, int groups, int S,
+                               const void* bias, bool relu, const void* mask, void* y, int64_t ldo, float* part,
+                               size_t part_bytes, hipStream_t st, const KTimer* kt) {
   if (N % 4 || (size_t)S * groups * M * N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
   EpF32 e;
   e.out = part; e.ldo = N; e.M = M; e.N = N; e.splits = S;
@@ -260,11 +261,11 @@ static hipError_t conv_fwd_split(const AL& a, const BL& b, int M, int N, int K, 
   hipError_t err = run_gemm<T, BM, BN, WGM, WGN>(a, b, e, M, N, K, groups, S, st);
   if (err != hipSuccess) return err;
   FcEpi ep{};
-  ep.relu = 1;
+  ep.relu = relu ? 1 : 0;
   for (int g = 0; g < groups; ++g)
     hipLaunchKernelGGL((k_fc_reduce<T>), grid1d((int64_t)M * N / 4), dim3(TPB), 0, st,
-                       part + (size_t)g * S * M * N, S, M, N, ldo, (const T*)bias + g * N, ep, (const T*)nullptr,
-                       (T*)y + g * N, (float*)nullptr);
+                       part + (size_t)g * S * M * N, S, M, N, ldo, bias ? (const T*)bias + g * N : nullptr, ep,
+                       mask ? (const T*)mask + g * N : nullptr, (T*)y + g * N, (float*)nullptr);
   rec_stop(kt, st);
   return hipGetLastError();
 }
@@ -282,8 +283,8 @@ struct Conv1FwdFn {
     RowsLd<T, BN> b;
     b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
     const int S = conv_split_count(cdiv(a.M, BM) * cdiv(96, BN), S2D_K, std::is_same<T, float>::value);
-    if (S > 1) return conv_fwd_split<T, BM, BN, WGM, WGN>(a, b, a.M, 96, S2D_K, 1, S, b1, y, 96, part,
-                                                          part_bytes, st, kt);
+    if (S > 1) return conv_split_k<T, BM, BN, WGM, WGN>(a, b, a.M, 96, S2D_K, 1, S, b1, true, nullptr, y, 96, part,
+                                                        part_bytes, st, kt);
     EpBiasRelu<T> e;
     e.out = (T*)y; e.bias = (const T*)b1; e.ldo = 96; e.M = a.M; e.N = 96;
     return run_gemm<T, BM, BN, WGM, WGN>(a, b, e, a.M, 96, S2D_K, 1, 1, st, kt);
@@ -320,8 +321,8 @@ struct ConvFwdFn {
     const int S = conv_split_count((int64_t)cdiv(a.M, BM) * cdiv(Cog, BN) * s.groups, a.K,
                                    std::is_same<T, float>::value);
     if (S > 1)
-      return conv_fwd_split<T, BM, BN, WGM, WGN>(a, bl, a.M, Cog, a.K, s.groups, S, b, y, s.Cout, part,
-                                                 part_bytes, st, kt);
+      return conv_split_k<T, BM, BN, WGM, WGN>(a, bl, a.M, Cog, a.K, s.groups, S, b, true, nullptr, y, s.Cout,
+                                               part, part_bytes, st, kt);
     EpBiasRelu<T> e;
     e.out = (T*)y; e.bias = (const T*)b; e.ldo = s.Cout; e.M = a.M; e.N = Cog;
     return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cog, a.K, s.groups, 1, st, kt);
@@ -342,17 +343,18 @@ hipError_t conv_fwd(DType dt, const ConvShape& s, const void* x, const void* wr,
 
 size_t conv_fwd_part_bytes(DType dt, const ConvShape& s) {
   const int Cog = s.Cout / s.groups, M = s.Nimg * s.Ho * s.Wo, K = s.K * s.K * (s.Cin / s.groups);
-  const int S = conv_fwd_splits(dt, M, Cog, K, s.groups);
+  const int S = conv_gemm_splits(dt, M, Cog, K, s.groups);
   return S > 1 ? (size_t)S * s.groups * M * Cog * sizeof(float) : 0;
 }
 size_t conv1_fwd_part_bytes(DType dt, int Nimg) {
-  const int S = conv_fwd_splits(dt, Nimg * 3025, 96, S2D_K, 1);
+  const int S = conv_gemm_splits(dt, Nimg * 3025, 96, S2D_K, 1);
   return S > 1 ? (size_t)S * Nimg * 3025 * 96 * sizeof(float) : 0;
 }
 
 template <typename T>
 struct ConvDgradFn {
-  ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; hipStream_t st; const KTimer* kt;
+  ConvShape s; const void* dy; const void* wt; const void* mask; void* dx; float* part; size_t part_bytes;
+  hipStream_t st; const KTimer* kt;
   template <int BM, int BN, int WGM, int WGN>
   hipError_t operator()() const {
     const int Cig = s.Cin / s.groups, Cog = s.Cout / s.groups;
@@ -365,6 +367,11 @@ struct ConvDgradFn {
     a.K = s.K * s.K * Cog;
     RowsLd<T, BN> bl;
     bl.p = (const T*)wt; bl.ld = a.K; bl.rows = Cig; bl.K = a.K; bl.gstride = (int64_t)Cig * a.K;
+    const int S = conv_split_count((int64_t)cdiv(a.M, BM) * cdiv(Cig, BN) * s.groups, a.K,
+                                   std::is_same<T, float>::value);
+    if (S > 1)
+      return conv_split_k<T, BM, BN, WGM, WGN>(a, bl, a.M, Cig, a.K, s.groups, S, nullptr, false, mask, dx, s.Cin,
+                                               part, part_bytes, st, kt);
     EpMask<T> e;
     e.out = (T*)dx; e.mask = (const T*)mask; e.ldo = s.Cin; e.M = a.M; e.N = Cig;
     return run_gemm<T, BM, BN, WGM, WGN>(a, bl, e, a.M, Cig, a.K, s.groups, 1, st, kt);
@@ -372,13 +379,22 @@ struct ConvDgradFn {
 };
 
 hipError_t conv_dgrad(DType dt, const ConvShape& s, const void* dy, const void* wt, const void* mask,
-                      void* dx, hipStream_t st, const KTimer* kt) {
+                      void* dx, float* part, size_t part_bytes, hipStream_t st, const KTimer* kt) {
   if (s.stride != 1) return hipErrorInvalidValue;
   const int Cig = s.Cin / s.groups;
   const int M = s.Nimg * s.H * s.W;
-  if (dt == BF16) { ConvDgradFn<bf16> f{s, dy, wt, mask, dx, st, kt}; return by_tile<bf16>(M, Cig, s.groups, f); }
-  ConvDgradFn<float> f{s, dy, wt, mask, dx, st, kt};
+  if (dt == BF16) {
+    ConvDgradFn<bf16> f{s, dy, wt, mask, dx, part, part_bytes, st, kt};
+    return by_tile<bf16>(M, Cig, s.groups, f);
+  }
+  ConvDgradFn<float> f{s, dy, wt, mask, dx, part, part_bytes, st, kt};
   return by_tile<float>(M, Cig, s.groups, f);
+}
+
+size_t conv_dgrad_part_bytes(DType dt, const ConvShape& s) {
+  const int Cig = s.Cin / s.groups, M = s.Nimg * s.H * s.W, K = s.K * s.K * (s.Cout / s.groups);
+  const int S = conv_gemm_splits(dt, M, Cig, K, s.groups);
+  return S > 1 ? (size_t)S * s.groups * M * Cig * sizeof(float) : 0;
 }
 
 // ---- weight gradients: split-K partials, then an ordered reduction

@@ -93,10 +93,11 @@ hipError_t conv_fwd(DType, const ConvShape&, const void* x, const void* wr, cons
                     size_t part_bytes, hipStream_t, const KTimer* kt = nullptr);
 size_t conv1_fwd_part_bytes(DType, int Nimg);
 size_t conv_fwd_part_bytes(DType, const ConvShape&);
-// dX (NHWC) = conv^T(dY) * [mask > 0] (mask optional) for stride-1 layers
+// dX (NHWC) = conv^T(dY) * [mask > 0] (mask optional) for stride-1 layers;
+// part as for conv1_fwd, at least conv_dgrad_part_bytes.
 hipError_t conv_dgrad(DType, const ConvShape&, const void* dy, const void* wt, const void* mask,
-                      void* dx, hipStream_t,
-                      const KTimer* kt = nullptr);
+                      void* dx, float* part, size_t part_bytes, hipStream_t, const KTimer* kt = nullptr);
+size_t conv_dgrad_part_bytes(DType, const ConvShape&);
 // SGD hyper-parameters: learning rate, momentum, weight decay times learning rate.
 struct SgdHyper { float lr, mom, wdlr; };
 // Optional SGD applied to a weight gradient as it is reduced: fp32 master w and

@@ -164,7 +164,10 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
     part = mx(part, fc_dgrad_part_bytes(N, 4096, 4096));
     part = mx(part, fc_dgrad_part_bytes(N, 9216, 4096));
     part = mx(part, conv1_wgrad_part_bytes(N));
-    for (int i = 1; i < 5; ++i) part = mx(part, conv_wgrad_part_bytes(net.conv[i]));
+    for (int i = 1; i < 5; ++i) {
+      part = mx(part, conv_wgrad_part_bytes(net.conv[i]));
+      part = mx(part, conv_dgrad_part_bytes(ddt, net.conv[i]));
+    }
     // bias-gradient partials of all eight layers at once
     BiasJob bj[8] = {};
     for (int i = 0; i < 8; ++i) {
