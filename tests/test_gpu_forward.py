@@ -116,6 +116,19 @@ def test_fp32_batch1_matches_oracle(orc):
     np.testing.assert_allclose(host(g["probs"]).sum(1), 1.0, atol=1e-5)
 
 
+def test_fp32_two_tower_batch2_matches_oracle(orc):
+    """fp32 grouped network at batch 2: the small-batch paths with two groups
+    (split-K partials and their reduction per group, the FC row kernel)."""
+    syn = I.synthetic(12, 2, groups=2, bf16=False)
+    g = run_forward(syn, B.F32)
+    h = hostify(g)
+    layerwise(orc, syn, h, 2, TOL_F32)
+    t = end_to_end(orc, syn, h, 2, TOL_F32)
+    for k in ("arg1", "arg2", "arg5"):      # near-ties may round apart end to end
+        assert np.mean(h[k] == t[k]) >= 0.999, k
+    np.testing.assert_allclose(host(g["probs"]).sum(1), 1.0, atol=1e-5)
+
+
 # ---------------------------------------------------------------- bf16, small batches
 @pytest.mark.parametrize("cfg,batch", [(2, 3), (3, 2), (2, 1), (2, 4), (2, 5)])
 def test_bf16_small_batch_layerwise_and_end_to_end(orc, cfg, batch):
