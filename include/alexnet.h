@@ -214,9 +214,13 @@ int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t ro
 /* Kernel timing (diagnostics).  The *_timed variants behave exactly like
  * the plain calls and additionally record caller-created HIP events
  * (hipEvent_t handles passed as void*) on `stream` immediately before and
- * after the launch of the named kernel; for GEMM layers that is the MFMA
- * kernel alone, not its split-K reduction.  A kernel the call does not launch
- * records nothing.  timers may be NULL when n_timers is 0. */
+ * after the launch of the named kernel; for GEMM layers that is the product
+ * kernel alone (the MFMA GEMM, or for an FC layer of at most 4 rows the row
+ * kernel), not its split-K reduction.  The exception is a convolution split
+ * over k because the batch is too small to fill the chip (never at batch
+ * 128): its events also cover the reduction, which applies its epilogue.  A
+ * kernel the call does not launch records nothing.  timers may be NULL when
+ * n_timers is 0. */
 typedef enum {
   ALEXNET_KT_S2D = 1,          /* layer-1 input staging (4x4 pixel blocks) and all
                                   weight re-layouts of the call, one launch      */
