@@ -124,8 +124,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "layout is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
+              "data parallelism is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -150,7 +150,7 @@ def main():
         return evs
 
     # ---------------------------------------------------------------- training step
-    syn = I.config_inputs(4)
+    syn = I.workload_inputs("train_batch128")
     n = syn.x.shape[0]
     sess = Session(n, 1, B.BF16, B.MODE_TRAIN, dev)
     master = []
@@ -250,8 +250,8 @@ def main():
     # ---------------------------------------------------------------- forward passes
     fwd = {}
     fwd_kernels = {}
-    for cfg, key in ((2, "single"), (3, "two_tower")):
-        s2 = I.config_inputs(cfg)
+    for wl, key in (("bf16_batch128", "single"), ("two_tower_batch128", "two_tower")):
+        s2 = I.workload_inputs(wl)
         n2 = s2.x.shape[0]
         fs = Session(n2, s2.groups, B.BF16, B.MODE_FORWARD, dev)
         params = fs.upload_params(s2.weights, s2.biases)
@@ -280,7 +280,7 @@ def main():
     # 256 sources of 3x256x256; each call runs the forward pass on the 2560
     # views (four corners and the centre, each also mirrored) and averages
     # the ten softmax outputs per source.
-    s5 = I.config_inputs(5)
+    s5 = I.workload_inputs("tenview_256_sources")
     n5 = s5.x.shape[0]
     ts = Session(n5, 1, B.BF16, B.MODE_TENVIEW, dev)
     params5 = ts.upload_params(s5.weights, s5.biases)
@@ -299,7 +299,7 @@ def main():
     # ---------------------------------------------------------------- batch-1 fp32 forward (latency)
     # One image, fp32 weights and activations: each call is waited for on
     # its own, so the figure is the latency of one call, launches included.
-    s1 = I.config_inputs(1)
+    s1 = I.workload_inputs("fp32_batch1")
     ls = Session(1, 1, B.F32, B.MODE_FORWARD, dev)
     params1 = ls.upload_params(s1.weights, s1.biases)
     x1 = to_device(s1.x, B.F32, dev)
@@ -398,7 +398,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         k = args.cpu_sample
-        s3 = I.config_inputs(4, batch=k)
+        s3 = I.workload_inputs("train_batch128", batch=k)
         zw = [np.zeros(w.shape) for w in s3.master_w]
         zb = [np.zeros(b.shape) for b in s3.biases]
         t0 = time.perf_counter()

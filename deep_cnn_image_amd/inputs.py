@@ -117,20 +117,22 @@ def synthetic(seed: int, batch: int, groups: int = 1, bf16: bool = True,
     return Synthetic(seed, groups, bf16, x, ws, bs, masters, labels, names)
 
 
-# The five workloads: (seed, batch, groups, bf16, mode)
-CONFIGS = {
-    1: dict(seed=0, batch=1, groups=1, bf16=False, mode="forward"),
-    2: dict(seed=1, batch=128, groups=1, bf16=True, mode="forward"),
-    3: dict(seed=2, batch=128, groups=2, bf16=True, mode="forward"),
-    4: dict(seed=3, batch=128, groups=1, bf16=True, mode="train"),
-    5: dict(seed=4, batch=256, groups=1, bf16=True, mode="tenview"),
+# The five workloads, by name: (seed, batch, groups, bf16, mode)
+WORKLOADS = {
+    "fp32_batch1": dict(seed=0, batch=1, groups=1, bf16=False, mode="forward"),
+    "bf16_batch128": dict(seed=1, batch=128, groups=1, bf16=True, mode="forward"),
+    "two_tower_batch128": dict(seed=2, batch=128, groups=2, bf16=True, mode="forward"),
+    "train_batch128": dict(seed=3, batch=128, groups=1, bf16=True, mode="train"),
+    "tenview_256_sources": dict(seed=4, batch=256, groups=1, bf16=True, mode="tenview"),
 }
 
 TRAIN_HYPER = dict(lr=0.01, momentum=0.9, weight_decay=5e-4, dropout_seed=3, step=0)
 
 
-def config_inputs(cfg: int, batch: Optional[int] = None) -> Synthetic:
-    c = CONFIGS[cfg]
+def workload_inputs(name: str, batch: Optional[int] = None) -> Synthetic:
+    """Seeded inputs and weights of a named workload (optionally fewer or more
+    images, same seed and distributions)."""
+    c = WORKLOADS[name]
     n = c["batch"] if batch is None else batch
     image = SOURCE if c["mode"] == "tenview" else IMAGE
     return synthetic(c["seed"], n, c["groups"], c["bf16"], image=image)

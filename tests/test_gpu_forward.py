@@ -106,7 +106,7 @@ def end_to_end(orc, syn, h, groups, tol, rows=None, store=None):
 
 # ---------------------------------------------------------------- fp32, batch 1
 def test_fp32_batch1_matches_oracle(orc):
-    syn = I.config_inputs(1)
+    syn = I.workload_inputs("fp32_batch1")
     g = run_forward(syn, B.F32)
     h = hostify(g)
     layerwise(orc, syn, h, 1, TOL_F32)
@@ -130,9 +130,10 @@ def test_fp32_two_tower_batch2_matches_oracle(orc):
 
 
 # ---------------------------------------------------------------- bf16, small batches
-@pytest.mark.parametrize("cfg,batch", [(2, 3), (3, 2), (2, 1), (2, 4), (2, 5)])
-def test_bf16_small_batch_layerwise_and_end_to_end(orc, cfg, batch):
-    syn = I.config_inputs(cfg, batch=batch)
+@pytest.mark.parametrize("wl,batch", [("bf16_batch128", 3), ("two_tower_batch128", 2), ("bf16_batch128", 1),
+                                      ("bf16_batch128", 4), ("bf16_batch128", 5)])
+def test_bf16_small_batch_layerwise_and_end_to_end(orc, wl, batch):
+    syn = I.workload_inputs(wl, batch=batch)
     g = run_forward(syn, B.BF16)
     h = hostify(g)
     layerwise(orc, syn, h, syn.groups, TOL_LAYER_BF16)
@@ -145,7 +146,7 @@ def test_bf16_small_batch_layerwise_and_end_to_end(orc, cfg, batch):
 
 
 def test_tenview_small(orc):
-    syn = I.config_inputs(5, batch=2)
+    syn = I.workload_inputs("tenview_256_sources", batch=2)
     g = run_forward(syn, B.BF16, B.MODE_TENVIEW, batch=2)
     views = orc.tenview_crop(syn.x)
     # layer 1 reads the crops and mirrors straight from the sources
@@ -162,7 +163,7 @@ def test_tenview_small(orc):
 def test_fused_lrn_pool_equals_stored_path():
     """The default forward (LRN and max-pool fused, LRN output never stored)
     gives bit-identical pooled values, argmax and probabilities."""
-    syn = I.config_inputs(2, batch=3)
+    syn = I.workload_inputs("bf16_batch128", batch=3)
     a = run_forward(syn, B.BF16, lrn_taps=True)
     b = run_forward(syn, B.BF16, lrn_taps=False)
     for k in b:
@@ -171,7 +172,7 @@ def test_fused_lrn_pool_equals_stored_path():
 
 
 def test_forward_is_deterministic():
-    syn = I.config_inputs(2, batch=4)
+    syn = I.workload_inputs("bf16_batch128", batch=4)
     a = run_forward(syn, B.BF16)
     b = run_forward(syn, B.BF16)
     for k in FWD_TAPS + ("probs",):
@@ -180,9 +181,9 @@ def test_forward_is_deterministic():
 
 
 # ---------------------------------------------------------------- full-size, sampled images
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_full_batch128_sampled_images(orc, cfg):
-    syn = I.config_inputs(cfg)
+@pytest.mark.parametrize("wl", ["bf16_batch128", "two_tower_batch128"])
+def test_full_batch128_sampled_images(orc, wl):
+    syn = I.workload_inputs(wl)
     g = run_forward(syn, B.BF16)
     rows = np.array([0, 77, 127])
     h = hostify(g, rows)
@@ -193,7 +194,7 @@ def test_full_batch128_sampled_images(orc, cfg):
 
 
 def test_full_tenview_256_sources_sampled(orc):
-    syn = I.config_inputs(5)
+    syn = I.workload_inputs("tenview_256_sources")
     g = run_forward(syn, B.BF16, B.MODE_TENVIEW, batch=256)
     for src in (0, 255):
         t = orc.alexnet.forward_tenview(syn.weights, syn.biases, syn.x[src:src + 1], store="bf16")

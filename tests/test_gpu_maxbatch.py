@@ -71,7 +71,7 @@ def train_repeated(syn, reps):
 
 
 def test_max_batch_is_32_copies_of_the_base_batch(orc):
-    syn = I.config_inputs(4)                      # the 128-image training workload
+    syn = I.workload_inputs("train_batch128")                      # the 128-image training workload
     base = train_repeated(syn, 1)
     big = train_repeated(syn, REPS)
     n = syn.x.shape[0]

@@ -158,7 +158,7 @@ def check_sgd(r, syn):
 # ----------------------------------------------------------------------- batch 3
 @pytest.fixture(scope="module")
 def small(orc):
-    syn = I.config_inputs(4, batch=3)
+    syn = I.workload_inputs("train_batch128", batch=3)
     r = run_train(syn)
     z = [np.zeros_like(w, dtype=np.float64) for w in syn.master_w]
     zb = [np.zeros_like(b, dtype=np.float64) for b in syn.biases]
@@ -315,7 +315,7 @@ def test_fp32_train_step_small(orc):
 def test_train_step_fused_lrn_pool_equals_stored_path():
     """Training with LRN and max-pool fused (the default) updates every tensor
     bit-identically to the path that also stores the LRN outputs."""
-    syn = I.config_inputs(4, batch=2)
+    syn = I.workload_inputs("train_batch128", batch=2)
     a = run_train(syn, lrn_taps=True)
     b = run_train(syn, lrn_taps=False)
     assert a["loss"] == b["loss"]
@@ -325,7 +325,7 @@ def test_train_step_fused_lrn_pool_equals_stored_path():
 
 
 def test_train_step_is_deterministic():
-    syn = I.config_inputs(4, batch=2)
+    syn = I.workload_inputs("train_batch128", batch=2)
     a = run_train(syn)
     b = run_train(syn)
     for i in range(8):
@@ -335,7 +335,7 @@ def test_train_step_is_deterministic():
 
 # ----------------------------------------------------------------------- full batch 128
 def test_full_batch128_train_step(orc):
-    syn = I.config_inputs(4)
+    syn = I.workload_inputs("train_batch128")
     r = run_train(syn)
     n = 128
     gm = gpu_masks(n)
@@ -470,7 +470,7 @@ def test_dropout_probability_other_than_one_half(orc, p):
     """cfg.dropout_p other than the pages' 0.5: the training step drops
     exactly the units the Philox rule with threshold floor(p 2^32) drops (the
     oracle's mask for p), and inference scales the FC6/FC7 outputs by 1 - p."""
-    syn = I.config_inputs(4, batch=2)
+    syn = I.workload_inputs("train_batch128", batch=2)
     sess = Session(2, 1, B.BF16, B.MODE_TRAIN, DEV)
     sess.cfg.dropout_p = p
     master = params_f32(syn.master_w, syn.biases)
