@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/alexnet.h"
 #include "launch.hpp"
@@ -161,6 +162,49 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
 //    the start of the step;
 //  - biases with their gradients, in the last two launches.
 // Every gradient except the FC weights' also lands in the workspace (taps).
+// Helper stream of the current device (default priority, non-blocking),
+// created on first use and kept for the life of the process.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
+// Fork/join of the side stream: fork() makes it wait for the work enqueued on
+// the main stream so far; the destructor makes the main stream wait for
+// everything enqueued on the side stream (also on an early error return).
+struct SideFork {
+  hipStream_t main = nullptr, side = nullptr;
+  hipEvent_t ev[8] = {};
+  int n = 0;
+  SideFork(hipStream_t m, hipStream_t s) : main(m), side(s) {}
+  hipStream_t fork() {
+    if (!side || n == 7) return main;
+    if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) != hipSuccess) return main;
+    hipEventRecord(ev[n], main);
+    hipStreamWaitEvent(side, ev[n], 0);
+    ++n;
+    return side;
+  }
+  ~SideFork() {
+    if (n > 0) {
+      if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) == hipSuccess) {
+        hipEventRecord(ev[n], side);
+        hipStreamWaitEvent(main, ev[n], 0);
+        ++n;
+      } else {
+        hipStreamSynchronize(side);   // no event for the join: wait on the host instead
+      }
+    }
+    for (int i = 0; i < n; ++i) hipEventDestroy(ev[i]);   // released once the device has passed them
+  }
+};
+
 int enqueue_backward(const Plan& p, void* const* work, float* const* master, float* const* momentum,
                      const SgdHyper& hy, float* loss, void* ws, hipStream_t st, const Timers& T) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
@@ -199,10 +243,26 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       ALEXNET_KT_CONV4_WGRAD, ALEXNET_KT_CONV5_WGRAD};
   const int ktd[5] = {0, ALEXNET_KT_CONV2_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV4_DGRAD,
                       ALEXNET_KT_CONV5_DGRAD};
+  // The conv weight gradients (with their SGD update) need nothing from the
+  // data-gradient chain after their own output gradient, and nothing in the
+  // chain reads what they write: each is forked onto the side stream once its
+  // output gradient is complete, so it runs beside the rest of the backward
+  // pass.  Not when a data gradient of the step splits over k (small
+  // batches): both would use the split-K region of the workspace.  Nor when
+  // a caller times one of the kernels of that stretch (the conv gradient
+  // GEMMs, the pool/LRN backward kernels, the bias kernels): a kernel timed
+  // on its own runs with the GPU to itself, so its time is its own.
+  bool concurrent = true;
+  for (int i = 1; i < 5; ++i)
+    if (conv_dgrad_part_bytes(dt, net.conv[i]) != 0) concurrent = false;
+  for (int k = ALEXNET_KT_CONV5_WGRAD; k <= ALEXNET_KT_BIAS; ++k)
+    if (T.on[k]) concurrent = false;
+  SideFork side(st, concurrent ? side_stream() : nullptr);
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];
     const SgdTarget u{master[2 * i], momentum[2 * i], work[2 * i], hy};
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), &u, st, T(ktw[i])));
+    hipStream_t sw = side.fork();
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), &u, sw, T(ktw[i])));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
                       tp(ws, p, din[i]), part, p.part_bytes, st, T(ktd[i])));
   }
@@ -213,7 +273,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   {
     const ConvShape& s = net.conv[1];
     const SgdTarget u{master[2], momentum[2], work[2], hy};
-    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), &u, st,
+    hipStream_t sw = side.fork();
+    HIPCHK(conv_wgrad(dt, s, tp(ws, p, T_DCONV2), tp(ws, p, T_POOL1), part, p.part_bytes, gw(1), &u, sw,
                       T(ALEXNET_KT_CONV2_WGRAD)));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, T_DCONV2), at(ws, p.wt[1]), nullptr, tp(ws, p, T_DIN2), part,
                       p.part_bytes, st, T(ALEXNET_KT_CONV2_DGRAD)));
@@ -224,7 +285,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
   {
     const SgdTarget u{master[0], momentum[0], work[0], hy};
-    HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), &u, st,
+    hipStream_t sw = side.fork();
+    HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), &u, sw,
                        T(ALEXNET_KT_CONV1_WGRAD)));
   }
   // bias gradients of all eight layers, and their SGD update

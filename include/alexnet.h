@@ -30,13 +30,18 @@
  *    are fp32; labels are int32 in [0, 1000).
  *  - All pointers are device pointers unless stated otherwise and must be
  *    16-byte aligned; the workspace must be 256-byte aligned.  The caller owns
- *    every buffer, including the workspace.  The library allocates nothing
- *    and keeps no mutable global state; calls are reentrant given distinct
+ *    every buffer, including the workspace.  The library allocates no
+ *    memory; its only state is one helper stream per device (default
+ *    priority, created on first use).  Calls are reentrant given distinct
  *    workspaces.
  *  - Calls validate their arguments on the host before any launch and return
  *    an alexnet_status; on error nothing is enqueued.  Work is enqueued on
  *    `stream` (a hipStream_t, 0 = the default stream) and runs
  *    asynchronously; device faults surface at the caller's synchronisation.
+ *    A training step also runs its conv weight gradients on the helper
+ *    stream, forked from `stream` with events and joined back to it before
+ *    the call returns, so all of its work is ordered before anything the
+ *    caller enqueues on `stream` afterwards (stream capture included).
  *  - Activations, gradients and working weights are stored in cfg->dtype;
  *    every sum accumulates in fp32.
  */
@@ -216,7 +221,10 @@ int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t ro
  * (hipEvent_t handles passed as void*) on `stream` immediately before and
  * after the launch of the named kernel; for GEMM layers that is the product
  * kernel alone (the MFMA GEMM, or for an FC layer of at most 4 rows the row
- * kernel), not its split-K reduction.  The exception is a convolution split
+ * kernel), not its split-K reduction.  Timing any kernel from the conv
+ * gradients through the bias kernels runs the step's backward pass without
+ * the helper stream, so that kernel has the GPU to itself.  The exception to
+ * the first rule is a convolution split
  * over k because the batch is too small to fill the chip (never at batch
  * 128): its events also cover the reduction, which applies its epilogue.  A
  * kernel the call does not launch records nothing.  timers may be NULL when
