@@ -41,7 +41,7 @@
  *    A training step also runs its conv weight gradients on the helper
  *    stream, forked from `stream` with events and joined back to it before
  *    the call returns, so all of its work is ordered before anything the
- *    caller enqueues on `stream` afterwards (stream capture included).
+ *    caller enqueues on `stream` afterwards.
  *  - Activations, gradients and working weights are stored in cfg->dtype;
  *    every sum accumulates in fp32.
  */
