@@ -401,9 +401,10 @@ void orc_sgd(double* w, double* v, const double* g, int64_t n, double eps, doubl
  *   c <- (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
  * with the key bumped by (0x9E3779B9, 0xBB67AE85) between rounds.
  * The pages only ask for dropout with probability 0.5; the counter-based
- * generator is how the masks are made reproducible.  Absolute bit-stream
- * correctness is parity unpinned (no known-answer vectors here); the mask
- * statistics are pinned.
+ * generator is how the masks are made reproducible.  Pinned word for word
+ * against PyTorch's independent source-level engine (ATen PhiloxRNGEngine.h)
+ * by tests/test_oracle_philox.py, and the mask statistics by
+ * tests/test_oracle_layers.py.
  * ------------------------------------------------------------------------ */
 static inline void orc_mulhilo(uint32_t a, uint32_t b, uint32_t* hi, uint32_t* lo) {
   const uint64_t p = (uint64_t)a * (uint64_t)b;

@@ -344,8 +344,8 @@ def test_sgd_two_steps_by_hand(orc):
 
 # --------------------------------------------------------------------------- philox / dropout
 def test_dropout_mask_statistics(orc):
-    """Parity of the absolute Philox bit stream is unpinned; these pin the mask
-    semantics: keep probability 1/2, independence across layers, steps, seeds
+    """The bit stream itself is pinned in test_oracle_philox.py; these pin the
+    mask semantics: keep probability 1/2, independence across layers, steps, seeds
     and neighbouring elements, determinism."""
     rows, cols = 128, 4096
     n = rows * cols
