@@ -207,3 +207,32 @@ def test_bf16_storage_forward_and_backward(orc):
     for k in ("dlogits", "dfc7", "dfc6", "dflat", "dconv5", "dconv4", "dconv3", "din3", "dlrn2",
               "dconv2", "din2", "dlrn1", "dconv1"):
         np.testing.assert_array_equal(A.round_bf16(g[k]), g[k])
+
+
+def test_bf16_storage_alone_moves_weight_gradients_beyond_bf16_tolerance(orc):
+    """Why the bf16 gradient parity is taken on shared forward state.
+
+    The same oracle, run once with every inter-layer tensor rounded to bf16
+    (the bf16 workloads' storage) and once in float64 throughout, on the
+    training workload's first three images: the two runs' weight gradients
+    differ by more than the 2e-2 relative L2 tolerance on layers 1-7, with no
+    GPU involved.  Rounding moves pre-activations across zero and pool maxima
+    between near-equal window values, and each such flip routes a whole
+    gradient element differently.  So no bf16 implementation can meet 2e-2
+    against an independent run; the GPU tests feed the oracle's backward pass
+    the HIP path's stored forward state, so both sides take the ReLU-mask and
+    argmax decisions on the same stored values (those decisions are integer
+    results decided in the storage precision).  The forward outputs
+    themselves stay close: the probabilities agree far inside 2e-2."""
+    syn = I.workload_inputs("train_batch128", batch=3)
+    z = [np.zeros(w.shape) for w in syn.master_w]
+    zb = [np.zeros(b.shape) for b in syn.biases]
+    kw = dict(lr=0.01, momentum=0.9, weight_decay=5e-4, seed=3, step=0)
+    ob = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
+                                syn.labels, 1, store="bf16", **kw)
+    o64 = orc.alexnet.train_step(syn.weights, syn.biases, syn.master_w, syn.biases, z, zb, syn.x,
+                                 syn.labels, 1, store=None, **kw)
+    e = [rel(ob["grad_w"][i], o64["grad_w"][i]) for i in range(8)]
+    print("bf16-storage vs float64 grad_w rel-L2:", [f"{v:.2e}" for v in e])
+    assert min(e[:7]) > 2e-2, e
+    assert rel(ob["taps"]["probs"], o64["taps"]["probs"]) < 2e-2
