@@ -13,9 +13,9 @@ import torch
 
 from deep_cnn_image_amd import binding as B
 from deep_cnn_image_amd import inputs as I
-from deep_cnn_image_amd.session import Session, stream_handle, to_device
+from deep_cnn_image_amd.session import Session, SideStream, stream_handle, to_device
 
-from gpu_helpers import (DEV, TOL_BF16, TOL_F32_OUT, TOL_LAYER_BF16, flat, host, nchw, params_f32,
+from gpu_helpers import (DEV, TOL_BF16, TOL_F32, TOL_F32_OUT, TOL_LAYER_BF16, flat, host, nchw, params_f32,
                          rel_l2, say)
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,7 @@ TAPS = ("conv1", "lrn1", "pool1", "arg1", "conv2", "lrn2", "pool2", "arg2", "con
 HYPER = dict(lr=0.01, momentum_coef=0.9, weight_decay=5e-4)
 
 
-def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None, lrn_taps=True):
+def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None, lrn_taps=True, side=None):
     n = syn.x.shape[0]
     say(f"[gpu] train batch={n} groups={syn.groups} dtype={dtype} seed={syn.seed} step={step} lrn_taps={lrn_taps}")
     sess = Session(n, syn.groups, dtype, B.MODE_TRAIN, DEV, lrn_taps=lrn_taps)
@@ -47,7 +47,7 @@ def run_train(syn, dtype=B.BF16, seed=3, step=0, v0=None, lrn_taps=True):
     torch.cuda.synchronize()
     r = dict(master0=[host(m) for m in master], mom0=[host(v) for v in mom],
              work0=[w.clone() for w in work])
-    sess.train_step(master, mom, work, x, labels, loss, probs, seed=seed, step=step, **{
+    sess.train_step(master, mom, work, x, labels, loss, probs, seed=seed, step=step, side=side, **{
         "lr": HYPER["lr"], "momentum_coef": HYPER["momentum_coef"], "weight_decay": HYPER["weight_decay"]})
     torch.cuda.synchronize()
     r.update(sess=sess, loss=float(loss.item()), probs=host(probs), master=[host(m) for m in master],
@@ -190,7 +190,27 @@ def test_dropout_masks_bit_exact(orc, small):
     for i, name in enumerate(("mask6", "mask7")):
         assert np.array_equal(gm[i], o["taps"][name]), name
     h = hostify(r["taps"])
-    assert np.all(h["drop6"][gm[0] == 0] == 0) and np.all(h["drop7"][gm[1] == 0] == 0)
+    check_applied_dropout(orc, syn, h, gm)
+
+
+def check_applied_dropout(orc, syn, h, masks, rows=None):
+    """The mask the FC epilogue applies, in both directions, layer-isolated
+    on the stored FC input: a dropped unit is exactly 0; a kept unit whose
+    pre-activation is clearly positive passes through (non-zero); and the
+    whole output equals mask * ReLU(W x + b) to one bf16 rounding."""
+    W, b = syn.weights, syn.biases
+    for layer, (tap, x_in) in enumerate((("drop6", "pool5"), ("drop7", "drop6"))):
+        m = masks[layer] if rows is None else masks[layer][rows]
+        pre = orc.fc(h[x_in], W[5 + layer], b[5 + layer])
+        d = h[tap]
+        assert np.all(d[m == 0] == 0), f"{tap}: a dropped unit is non-zero"
+        pos = (m == 1) & (pre > 1e-2 * np.sqrt(np.mean(pre ** 2)))
+        assert pos.sum() > 0.2 * m.size, f"{tap}: too few kept positive units to check"
+        assert np.all(d[pos] != 0), f"{tap}: a kept unit with positive pre-activation was zeroed"
+        e = rel_l2(d, m * orc.relu(pre))
+        say(f"[gpu] {tap}: {int((m == 0).sum())} dropped are 0, {int(pos.sum())} kept positive pass; "
+            f"rel-L2 vs mask*ReLU(Wx+b) {e:.2e}")
+        assert e <= TOL_LAYER_BF16, (tap, e)
 
 
 def test_loss_probs_and_gradients_end_to_end(small):
@@ -307,7 +327,7 @@ def test_fp32_train_step_small(orc):
     oloss, gw, _ = fp32_backward_on_state(orc, syn, h, syn.master_w, syn.biases, masks, "fp32 step")
     ew = [rel_l2(r["gw"][i], gw[i]) for i in range(8)]
     say("[gpu] fp32 grad_w rel-L2:", [f"{x:.2e}" for x in ew])
-    assert max(ew) <= 1e-4
+    assert max(ew) <= TOL_F32
     assert abs(r["loss"] - oloss) / abs(oloss) <= 1e-5
     check_sgd(r, syn)
 
@@ -333,6 +353,31 @@ def test_train_step_is_deterministic():
     assert a["loss"] == b["loss"]
 
 
+def test_side_stream_step_is_bit_identical_to_serial():
+    """At batch 128 the weight gradients run on a caller's side stream beside
+    the data-gradient chain.  Two such steps and one serial step from the same
+    state give bit-identical updated weights, momenta, working copies, conv
+    weight gradients, bias gradients, activation gradients and loss."""
+    syn = I.workload_inputs("train_batch128")
+    side = SideStream(DEV)
+    runs = [run_train(syn, lrn_taps=False, side=side), run_train(syn, lrn_taps=False, side=side),
+            run_train(syn, lrn_taps=False, side=None)]
+    a = runs[0]
+    for b in runs[1:]:
+        assert a["loss"] == b["loss"]
+        for j in range(16):
+            assert np.array_equal(a["master"][j], b["master"][j]), ("master", j)
+            assert np.array_equal(a["mom"][j], b["mom"][j]), ("momentum", j)
+            assert torch.equal(a["work"][j].view(torch.uint8), b["work"][j].view(torch.uint8)), ("work", j)
+        for i in range(5):
+            assert np.array_equal(a["gw"][i], b["gw"][i]), ("gw", i)
+        for i in range(8):
+            assert np.array_equal(a["gb"][i], b["gb"][i]), ("gb", i)
+        for k in ("dfc7", "dfc6", "dflat", "dconv5", "dconv4", "dconv3", "din3", "dconv2", "din2", "dconv1"):
+            assert torch.equal(a["taps"][k].view(torch.uint8), b["taps"][k].view(torch.uint8)), k
+    say(f"[gpu] side-stream and serial steps bit-identical; loss {a['loss']:.6f}")
+
+
 # ----------------------------------------------------------------------- full batch 128
 def test_full_batch128_train_step(orc):
     syn = I.workload_inputs("train_batch128")
@@ -343,6 +388,7 @@ def test_full_batch128_train_step(orc):
     assert np.array_equal(gm[0], om[0]) and np.array_equal(gm[1], om[1])
     rows = np.array([0, 64, 127])
     hs = hostify(r["taps"], rows)
+    check_applied_dropout(orc, syn, hostify({k: r["taps"][k] for k in ("pool5", "drop6", "drop7")}), om)
     t = orc.alexnet.forward(syn.weights, syn.biases, syn.x[rows], 1, train=True,
                             masks=(om[0][rows], om[1][rows]), store="bf16")
     rl = -np.log(t["probs"][np.arange(3), syn.labels[rows]])
@@ -455,7 +501,7 @@ def test_fp32_three_steps_momentum_carry_and_lr_schedule(orc):
         g = [(float(mu32) * v0[j] - wdlr32 * s0[j] - host(mom[j])) / float(lr32) for j in range(16)]
         eg = [rel_l2(g[2 * i], gw[i]) for i in range(8)] + [rel_l2(g[2 * i + 1], gb[i]) for i in range(8)]
         say(f"[gpu] step {step} gradient rel-L2 (weights, biases)", [f"{e:.1e}" for e in eg])
-        assert max(eg[:8]) <= 1e-4
+        assert max(eg[:8]) <= TOL_F32
         # the bias gradients recovered this way carry the fp32 rounding of mu v0 and wd lr b (b ~ 1)
         assert max(eg[8:]) <= 1e-3
         # the update itself, element by element: w1 = fl(w0 + v1), working copy = w1
