@@ -109,6 +109,17 @@ def measured_traffic(kernel):
     return int(t["read_bytes"] + t["write_bytes"])
 
 
+def cpu_model():
+    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,7 +144,7 @@ def main():
 
     from deep_cnn_image_amd import binding as B
     from deep_cnn_image_amd import inputs as I
-    from deep_cnn_image_amd.session import Session, stream_handle, to_device
+    from deep_cnn_image_amd.session import Session, SideStream, stream_handle, to_device
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -163,11 +174,14 @@ def main():
     labels = torch.from_numpy(syn.labels).to(dev)
     loss = torch.zeros(1, dtype=torch.float32, device=dev)
     stream = stream_handle()
+    # the caller's second stream: the weight gradients run on it beside the
+    # data-gradient chain (alexnet_train_step_ex)
+    side = SideStream(dev)
 
     def train(i, timers=()):
-        B.alexnet_train_step_timed(sess.cfg, master, mom, work, x, labels, h["lr"], h["momentum"],
-                                   h["weight_decay"], h["dropout_seed"], i, loss, None, sess.ws,
-                                   sess.ws_bytes, stream, list(timers))
+        B.alexnet_train_step_ex(sess.cfg, master, mom, work, x, None, 0, 0, labels, h["lr"], h["momentum"],
+                                h["weight_decay"], h["dropout_seed"], i, loss, None, sess.ws, sess.ws_bytes,
+                                stream, side.handle, side.event_handles, list(timers))
 
     step = 0
     for _ in range(args.warmup):
@@ -230,9 +244,9 @@ def main():
     aug = B.augment(crop, alpha, eigval, eigvec)
 
     def train_aug(i, timers=()):
-        B.alexnet_train_step_augmented_timed(sess.cfg, master, mom, work, src, hs, ws_, aug, labels, h["lr"],
-                                             h["momentum"], h["weight_decay"], h["dropout_seed"], i, loss, None,
-                                             sess.ws, sess.ws_bytes, stream, list(timers))
+        B.alexnet_train_step_ex(sess.cfg, master, mom, work, src, aug, hs, ws_, labels, h["lr"], h["momentum"],
+                                h["weight_decay"], h["dropout_seed"], i, loss, None, sess.ws, sess.ws_bytes,
+                                stream, side.handle, side.event_handles, list(timers))
 
     for _ in range(args.warmup):
         train_aug(step); step += 1
@@ -406,7 +420,7 @@ def main():
                                   seed=3, step=0, store="bf16")
         cpu_s = time.perf_counter() - t0
         rec["cpu_baseline"] = {"value": round(k / cpu_s, 3), "unit": "images/s", "cores": oracle.num_threads(),
-                               "kind": "oracle",
+                               "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"one training step (forward, loss, backward, SGD) on {k} images of the "
                                          f"batch-128 workload, float64 direct loops, {cpu_s:.1f} s"}
     print(json.dumps(rec), flush=True)

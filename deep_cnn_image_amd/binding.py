@@ -25,7 +25,7 @@ EXPORTED = (
     "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string", "alexnet_forward_timed",
     "alexnet_train_step_timed", "alexnet_augment_images", "alexnet_train_step_augmented",
     "alexnet_train_step_augmented_timed", "alexnet_rgb_pca_workspace_bytes", "alexnet_rgb_pca",
-    "alexnet_rgb_pca_timed",
+    "alexnet_rgb_pca_timed", "alexnet_train_step_ex",
 )
 
 # alexnet_kernel ids (kernel-timing hooks)
@@ -47,6 +47,16 @@ class Cfg(C.Structure):
 
 class Timer(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("start", C.c_void_p), ("stop", C.c_void_p)]
+
+
+SIDE_EVENTS = 10   # ALEXNET_SIDE_EVENTS
+
+
+class Exec(C.Structure):
+    """alexnet_exec: side stream and its fork/join events (hipStream_t and
+    hipEvent_t handles), kernel timers."""
+    _fields_ = [("side_stream", C.c_void_p), ("events", C.c_void_p * SIDE_EVENTS),
+                ("timers", C.POINTER(Timer)), ("n_timers", C.c_int32)]
 
 
 class Augment(C.Structure):
@@ -105,6 +115,10 @@ def lib():
     L.alexnet_train_step_augmented.restype = C.c_int
     L.alexnet_train_step_augmented_timed.argtypes = L.alexnet_train_step_augmented.argtypes + [tp, C.c_int32]
     L.alexnet_train_step_augmented_timed.restype = C.c_int
+    L.alexnet_train_step_ex.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, augp, C.c_int32, C.c_int32, vp,
+                                        C.c_float, C.c_float, C.c_float, C.c_uint64, C.c_uint64, vp, vp, vp,
+                                        C.c_size_t, vp, C.POINTER(Exec)]
+    L.alexnet_train_step_ex.restype = C.c_int
     L.alexnet_rgb_pca_workspace_bytes.argtypes = []
     L.alexnet_rgb_pca_workspace_bytes.restype = C.c_size_t
     L.alexnet_rgb_pca.argtypes = [cfgp, vp, C.c_int32, C.c_int32, C.c_int32, vp, vp, vp, C.c_size_t, vp]
@@ -209,6 +223,23 @@ def alexnet_train_step_timed(cfg, master, momentum, work, x, labels, lr, momentu
                                        weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None,
                                        _ptr(ws) or None, ws_bytes, _ptr(stream) or None, arr, n)
     return _check(s, "alexnet_train_step_timed") if check else s
+
+
+def alexnet_train_step_ex(cfg, master, momentum, work, x, aug, src_h, src_w, labels, lr, momentum_coef,
+                          weight_decay, seed, step, loss, probs, ws, ws_bytes, stream=0, side_stream=0,
+                          events=(), timers=(), check=True) -> int:
+    """aug: an Augment or None; side_stream: a hipStream_t handle or 0;
+    events: SIDE_EVENTS hipEvent_t handles when side_stream is given."""
+    arr, n = _timers(timers)
+    ev = list(events) + [0] * (SIDE_EVENTS - len(events))
+    ex = Exec(_ptr(side_stream) or None, (C.c_void_p * SIDE_EVENTS)(*[e or None for e in ev[:SIDE_EVENTS]]),
+              arr, n)
+    s = lib().alexnet_train_step_ex(
+        C.byref(cfg), _ptr16(master), _ptr16(momentum), _ptr16(work), _ptr(x) or None,
+        C.byref(aug) if aug is not None else None, src_h, src_w, _ptr(labels) or None, lr, momentum_coef,
+        weight_decay, seed, step, _ptr(loss) or None, _ptr(probs) or None, _ptr(ws) or None, ws_bytes,
+        _ptr(stream) or None, C.byref(ex))
+    return _check(s, "alexnet_train_step_ex") if check else s
 
 
 def alexnet_augment_images(cfg, src, src_h, src_w, aug: Augment, x, stream=0, check=True) -> int:

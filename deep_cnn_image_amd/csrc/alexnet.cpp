@@ -6,7 +6,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
 
 #include "../../include/alexnet.h"
 #include "launch.hpp"
@@ -154,6 +153,43 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
   return ALEXNET_OK;
 }
 
+// Fork/join of the caller's side stream, with the caller's events.  fork()
+// makes the side stream wait for everything enqueued on the main stream so
+// far and returns it; join() (also run by the destructor, so an early error
+// return still joins) makes the main stream wait for everything enqueued on
+// the side stream.  Each fork uses its own event, the join the last one.  If
+// a fork cannot be enqueued, the host waits for the side stream and the rest
+// of the call runs on the main stream alone.
+struct SideFork {
+  hipStream_t main = nullptr, side = nullptr;
+  void* const* ev = nullptr;
+  int n = 0;
+  bool used = false;
+  SideFork(hipStream_t m, hipStream_t s, void* const* events) : main(m), side(s), ev(events) {}
+  hipStream_t fork() {
+    if (!side) return main;
+    if (n >= ALEXNET_SIDE_EVENTS - 1) return serial();
+    hipEvent_t e = (hipEvent_t)ev[n++];
+    if (hipEventRecord(e, main) != hipSuccess || hipStreamWaitEvent(side, e, 0) != hipSuccess) return serial();
+    used = true;
+    return side;
+  }
+  hipStream_t serial() {
+    if (used) hipStreamSynchronize(side);
+    side = nullptr;
+    used = false;
+    return main;
+  }
+  void join() {
+    if (!side || !used) return;
+    hipEvent_t e = (hipEvent_t)ev[ALEXNET_SIDE_EVENTS - 1];
+    if (hipEventRecord(e, side) != hipSuccess || hipStreamWaitEvent(main, e, 0) != hipSuccess)
+      hipStreamSynchronize(side);
+    used = false;
+  }
+  ~SideFork() { join(); }
+};
+
 // Backward pass, with the SGD update of every tensor folded in:
 //  - FC weights inside their weight-gradient GEMM, after the layer's data
 //    gradient has read the old working weights;
@@ -162,51 +198,10 @@ int enqueue_forward(const Plan& p, const void* const* prm, const void* x, void* 
 //    the start of the step;
 //  - biases with their gradients, in the last two launches.
 // Every gradient except the FC weights' also lands in the workspace (taps).
-// Helper stream of the current device (default priority, non-blocking),
-// created on first use and kept for the life of the process.
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
-    streams[dev] = nullptr;
-  return streams[dev];
-}
-
-// Fork/join of the side stream: fork() makes it wait for the work enqueued on
-// the main stream so far; the destructor makes the main stream wait for
-// everything enqueued on the side stream (also on an early error return).
-struct SideFork {
-  hipStream_t main = nullptr, side = nullptr;
-  hipEvent_t ev[8] = {};
-  int n = 0;
-  SideFork(hipStream_t m, hipStream_t s) : main(m), side(s) {}
-  hipStream_t fork() {
-    if (!side || n == 7) return main;
-    if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) != hipSuccess) return main;
-    hipEventRecord(ev[n], main);
-    hipStreamWaitEvent(side, ev[n], 0);
-    ++n;
-    return side;
-  }
-  ~SideFork() {
-    if (n > 0) {
-      if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) == hipSuccess) {
-        hipEventRecord(ev[n], side);
-        hipStreamWaitEvent(main, ev[n], 0);
-        ++n;
-      } else {
-        hipStreamSynchronize(side);   // no event for the join: wait on the host instead
-      }
-    }
-    for (int i = 0; i < n; ++i) hipEventDestroy(ev[i]);   // released once the device has passed them
-  }
-};
-
+// With a side stream, the weight gradients run on it (see below).
 int enqueue_backward(const Plan& p, void* const* work, float* const* master, float* const* momentum,
-                     const SgdHyper& hy, float* loss, void* ws, hipStream_t st, const Timers& T) {
+                     const SgdHyper& hy, float* loss, void* ws, hipStream_t st, const Timers& T,
+                     hipStream_t side_st, void* const* side_ev) {
   const DType dt = p.cfg.dtype == ALEXNET_BF16 ? BF16 : F32;
   const Net& net = p.net;
   const int N = p.N;
@@ -245,19 +240,19 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       ALEXNET_KT_CONV5_DGRAD};
   // The conv weight gradients (with their SGD update) need nothing from the
   // data-gradient chain after their own output gradient, and nothing in the
-  // chain reads what they write: each is forked onto the side stream once its
-  // output gradient is complete, so it runs beside the rest of the backward
-  // pass.  Not when a data gradient of the step splits over k (small
+  // chain reads what they write: given a side stream, each is forked onto it
+  // once its output gradient is complete, so it runs beside the rest of the
+  // backward pass.  Not when a data gradient of the step splits over k (small
   // batches): both would use the split-K region of the workspace.  Nor when
   // a caller times one of the kernels of that stretch (the conv gradient
   // GEMMs, the pool/LRN backward kernels, the bias kernels): a kernel timed
   // on its own runs with the GPU to itself, so its time is its own.
-  bool concurrent = true;
+  bool concurrent = side_st != nullptr;
   for (int i = 1; i < 5; ++i)
     if (conv_dgrad_part_bytes(dt, net.conv[i]) != 0) concurrent = false;
   for (int k = ALEXNET_KT_CONV5_WGRAD; k <= ALEXNET_KT_BIAS; ++k)
     if (T.on[k]) concurrent = false;
-  SideFork side(st, concurrent ? side_stream() : nullptr);
+  SideFork side(st, concurrent ? side_st : nullptr, side_ev);
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];
     const SgdTarget u{master[2 * i], momentum[2 * i], work[2 * i], hy};
@@ -396,7 +391,15 @@ int train_step_impl(const alexnet_cfg* cfg, float* const master[16], float* cons
                     void* const work[16], const void* x, const AugSrc* aug, int aug_h, int aug_w,
                     const int32_t* labels, float lr, float momentum_coef, float weight_decay, uint64_t seed,
                     uint64_t step, float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
-                    const alexnet_timer* timers, int32_t n_timers) {
+                    const alexnet_exec* ex) {
+  const alexnet_timer* timers = ex ? ex->timers : nullptr;
+  const int32_t n_timers = ex ? ex->n_timers : 0;
+  hipStream_t side_st = ex ? (hipStream_t)ex->side_stream : nullptr;
+  if (side_st) {
+    if (side_st == (hipStream_t)stream) return ALEXNET_E_ARG;
+    for (int i = 0; i < ALEXNET_SIDE_EVENTS; ++i)
+      if (!ex->events[i]) return ALEXNET_E_NULL;
+  }
   Plan p;
   int r = prepare(cfg, ALEXNET_MODE_TRAIN, ws, ws_bytes, &p);
   if (r != ALEXNET_OK) return r;
@@ -416,7 +419,9 @@ int train_step_impl(const alexnet_cfg* cfg, float* const master[16], float* cons
                            aug_w)) != ALEXNET_OK)
     return r;
   const SgdHyper hy{lr, momentum_coef, weight_decay * lr};
-  if ((r = enqueue_backward(p, work, master, momentum, hy, loss, ws, st, T)) != ALEXNET_OK) return r;
+  if ((r = enqueue_backward(p, work, master, momentum, hy, loss, ws, st, T, side_st,
+                            side_st ? ex->events : nullptr)) != ALEXNET_OK)
+    return r;
   return ALEXNET_OK;
 }
 
@@ -424,13 +429,31 @@ int train_step_impl(const alexnet_cfg* cfg, float* const master[16], float* cons
 
 extern "C" {
 
+int alexnet_train_step_ex(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                          void* const work[16], const void* x, const alexnet_augment* aug, int32_t src_h,
+                          int32_t src_w, const int32_t* labels, float lr, float momentum_coef,
+                          float weight_decay, uint64_t seed, uint64_t step, float* loss, float* probs, void* ws,
+                          size_t ws_bytes, void* stream, const alexnet_exec* ex) {
+  if (!aug)
+    return train_step_impl(cfg, master, momentum, work, x, nullptr, 0, 0, labels, lr, momentum_coef,
+                           weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, ex);
+  AugSrc a;
+  const int r = check_augment(aug, src_h, src_w, &a);
+  if (r != ALEXNET_OK) return r;
+  return train_step_impl(cfg, master, momentum, work, x, &a, src_h, src_w, labels, lr, momentum_coef,
+                         weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, ex);
+}
+
 int alexnet_train_step_timed(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
                              void* const work[16], const void* x, const int32_t* labels, float lr,
                              float momentum_coef, float weight_decay, uint64_t seed, uint64_t step,
                              float* loss, float* probs, void* ws, size_t ws_bytes, void* stream,
                              const alexnet_timer* timers, int32_t n_timers) {
-  return train_step_impl(cfg, master, momentum, work, x, nullptr, 0, 0, labels, lr, momentum_coef, weight_decay,
-                         seed, step, loss, probs, ws, ws_bytes, stream, timers, n_timers);
+  alexnet_exec ex{};
+  ex.timers = timers;
+  ex.n_timers = n_timers;
+  return alexnet_train_step_ex(cfg, master, momentum, work, x, nullptr, 0, 0, labels, lr, momentum_coef,
+                               weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, &ex);
 }
 
 int alexnet_train_step_augmented_timed(const alexnet_cfg* cfg, float* const master[16],
@@ -440,11 +463,12 @@ int alexnet_train_step_augmented_timed(const alexnet_cfg* cfg, float* const mast
                                        uint64_t seed, uint64_t step, float* loss, float* probs, void* ws,
                                        size_t ws_bytes, void* stream, const alexnet_timer* timers,
                                        int32_t n_timers) {
-  AugSrc a;
-  const int r = check_augment(aug, src_h, src_w, &a);
-  if (r != ALEXNET_OK) return r;
-  return train_step_impl(cfg, master, momentum, work, src, &a, src_h, src_w, labels, lr, momentum_coef,
-                         weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, timers, n_timers);
+  if (!aug) return ALEXNET_E_NULL;
+  alexnet_exec ex{};
+  ex.timers = timers;
+  ex.n_timers = n_timers;
+  return alexnet_train_step_ex(cfg, master, momentum, work, src, aug, src_h, src_w, labels, lr, momentum_coef,
+                               weight_decay, seed, step, loss, probs, ws, ws_bytes, stream, &ex);
 }
 
 int alexnet_train_step_augmented(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],

@@ -27,6 +27,28 @@ def stream_handle() -> int:
     return int(torch.cuda.current_stream().cuda_stream)
 
 
+class SideStream:
+    """A caller-owned second stream and the fork/join events the training
+    step uses with it (alexnet_train_step_ex).  The stream has the default
+    priority; the events are created by torch (timing disabled) and made to
+    exist by one record each."""
+
+    def __init__(self, device: str = "cuda:0"):
+        self.stream = torch.cuda.Stream(device=device)
+        self.events = [torch.cuda.Event(enable_timing=False) for _ in range(B.SIDE_EVENTS)]
+        for e in self.events:
+            e.record()
+        torch.cuda.synchronize(device)
+
+    @property
+    def handle(self) -> int:
+        return int(self.stream.cuda_stream)
+
+    @property
+    def event_handles(self) -> List[int]:
+        return [int(e.cuda_event) for e in self.events]
+
+
 class Session:
     """One configuration (batch, groups, dtype, mode) with its workspace."""
 
@@ -69,7 +91,17 @@ class Session:
         return probs
 
     def train_step(self, master, momentum, work, x, labels, loss, probs=None, lr=0.01,
-                   momentum_coef=0.9, weight_decay=5e-4, seed=3, step=0):
-        B.alexnet_train_step(self.cfg, master, momentum, work, x, labels, lr, momentum_coef,
-                             weight_decay, seed, step, loss, probs, self.ws, self.ws_bytes,
-                             stream_handle())
+                   momentum_coef=0.9, weight_decay=5e-4, seed=3, step=0,
+                   side: Optional[SideStream] = None, timers=()):
+        """alexnet_train_step, or with a side stream (or timers)
+        alexnet_train_step_ex."""
+        if side is None and not timers:
+            B.alexnet_train_step(self.cfg, master, momentum, work, x, labels, lr, momentum_coef,
+                                 weight_decay, seed, step, loss, probs, self.ws, self.ws_bytes,
+                                 stream_handle())
+            return
+        B.alexnet_train_step_ex(self.cfg, master, momentum, work, x, None, 0, 0, labels, lr,
+                                momentum_coef, weight_decay, seed, step, loss, probs, self.ws,
+                                self.ws_bytes, stream_handle(),
+                                side.handle if side is not None else 0,
+                                side.event_handles if side is not None else (), timers)

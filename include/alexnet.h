@@ -30,18 +30,19 @@
  *    are fp32; labels are int32 in [0, 1000).
  *  - All pointers are device pointers unless stated otherwise and must be
  *    16-byte aligned; the workspace must be 256-byte aligned.  The caller owns
- *    every buffer, including the workspace.  The library allocates no
- *    memory; its only state is one helper stream per device (default
- *    priority, created on first use).  Calls are reentrant given distinct
- *    workspaces.
+ *    every buffer, including the workspace, and every stream and event.  The
+ *    library allocates no memory and creates no streams or events; the only
+ *    state it keeps between calls is a per-device cache of whether the
+ *    device is a gfx950 (a fixed fact once read).  Calls are reentrant given
+ *    distinct workspaces (and, for alexnet_train_step_ex, distinct side
+ *    streams and events).
  *  - Calls validate their arguments on the host before any launch and return
  *    an alexnet_status; on error nothing is enqueued.  Work is enqueued on
  *    `stream` (a hipStream_t, 0 = the default stream) and runs
  *    asynchronously; device faults surface at the caller's synchronisation.
- *    A training step also runs its conv weight gradients on the helper
- *    stream, forked from `stream` with events and joined back to it before
- *    the call returns, so all of its work is ordered before anything the
- *    caller enqueues on `stream` afterwards.
+ *    Only alexnet_train_step_ex uses a second stream, the caller's, and joins
+ *    it back to `stream` before returning, so all of a call's work is ordered
+ *    before anything the caller enqueues on `stream` afterwards.
  *  - Activations, gradients and working weights are stored in cfg->dtype;
  *    every sum accumulates in fp32.
  */
@@ -98,7 +99,8 @@ void alexnet_default_cfg(alexnet_cfg* cfg, int32_t batch, int32_t groups, int32_
 size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode);
 
 /* Inference forward pass (fermi.ai ALEXNET_FORWARD; paper-graph-ui layer list,
- * test-time dropout rule "use all neurons, multiply outputs by 0.5").
+ * test-time dropout rule of paper-graph-ui "Dropout": inference keeps every
+ * unit and scales the FC6/FC7 outputs by 0.5).
  *   x     [batch][3][227][227] cfg->dtype
  *   probs [batch][1000] fp32 softmax output (written) */
 int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x,
@@ -221,9 +223,8 @@ int alexnet_dropout_mask(uint64_t seed, uint64_t step, int32_t layer, int32_t ro
  * (hipEvent_t handles passed as void*) on `stream` immediately before and
  * after the launch of the named kernel; for GEMM layers that is the product
  * kernel alone (the MFMA GEMM, or for an FC layer of at most 4 rows the row
- * kernel), not its split-K reduction.  Timing any kernel from the conv
- * gradients through the bias kernels runs the step's backward pass without
- * the helper stream, so that kernel has the GPU to itself.  The exception to
+ * kernel), not its split-K reduction.  (The timed training calls run with no
+ * side stream; see alexnet_train_step_ex for timers beside one.)  The exception to
  * the first rule is a convolution split
  * over k because the batch is too small to fill the chip (never at batch
  * 128): its events also cover the reduction, which applies its epilogue.  A
@@ -277,6 +278,49 @@ int alexnet_train_step_augmented_timed(const alexnet_cfg* cfg, float* const mast
 int alexnet_rgb_pca_timed(const alexnet_cfg* cfg, const void* images, int32_t n, int32_t h,
                           int32_t w, float* eigval, float* eigvec, void* ws, size_t ws_bytes,
                           void* stream, const alexnet_timer* timers, int32_t n_timers);
+
+/* The training step with every option (all other training entry points are
+ * this call with some options fixed):
+ *   aug          NULL: x is images [batch][3][227][227] and src_h, src_w are
+ *                ignored; else x is sources [batch][3][src_h][src_w] and the
+ *                call is alexnet_train_step_augmented.
+ *   ex           may be NULL (no side stream, no timers).
+ *   ex->side_stream  a caller-owned hipStream_t other than `stream`, or NULL.
+ *                Given one, the layers' weight gradients with their SGD
+ *                updates run on it, each forked from `stream` (event record +
+ *                stream wait) once the gradient w.r.t. that layer's output is
+ *                complete, while `stream` carries on with the data gradients;
+ *                the side stream is joined back to `stream` before the call
+ *                returns.  Results are bit-identical to the serial order: no
+ *                kernel of either chain reads what the other writes, and every
+ *                reduction runs in a fixed order.  The step stays serial when
+ *                a conv data gradient splits over k (small batches share the
+ *                split-K scratch with the weight gradients) or when a timer
+ *                names a kernel from the conv gradients through the bias
+ *                kernels.  NULL: everything runs on `stream` in order.
+ *   ex->events   ALEXNET_SIDE_EVENTS caller-created hipEvent_t handles (timing
+ *                may be disabled), all non-null when side_stream is set;
+ *                recorded and waited on by every call, never created or
+ *                destroyed by the library.  Reusing them across calls is safe:
+ *                a stream wait binds to the record enqueued before it.  Two
+ *                calls in flight at once need distinct sets.
+ *   ex->timers, ex->n_timers  as for alexnet_train_step_timed; a timed kernel
+ *                that runs on the side stream has its events recorded there.
+ * Returns ALEXNET_E_ARG if side_stream == stream, ALEXNET_E_NULL if an event
+ * is missing. */
+#define ALEXNET_SIDE_EVENTS 10
+typedef struct {
+  void* side_stream;
+  void* events[ALEXNET_SIDE_EVENTS];
+  const alexnet_timer* timers;
+  int32_t n_timers;
+} alexnet_exec;
+
+int alexnet_train_step_ex(const alexnet_cfg* cfg, float* const master[16], float* const momentum[16],
+                          void* const work[16], const void* x, const alexnet_augment* aug, int32_t src_h,
+                          int32_t src_w, const int32_t* labels, float lr, float momentum_coef,
+                          float weight_decay, uint64_t seed, uint64_t step, float* loss, float* probs, void* ws,
+                          size_t ws_bytes, void* stream, const alexnet_exec* ex);
 
 /* Test and diagnostic access to the tensors a call leaves in its workspace.
  * Host only.  For tap `tap_id` of a call in `mode` with `cfg`, returns its

@@ -222,3 +222,33 @@ def test_rgb_pca_validation_errors_before_launch():
     assert f(wsb=nb - 1) == B.E_WORKSPACE
     assert f(ws=FAKE + 64) == B.E_ALIGN and f(lam=FAKE + 2) == B.E_ALIGN
     assert f(cfg=B.alexnet_default_cfg(1, 1, 7)) == B.E_DTYPE
+
+
+def test_train_step_ex_side_stream_validation():
+    """alexnet_train_step_ex: the side stream must differ from the main one
+    and come with all ALEXNET_SIDE_EVENTS events; checked before any launch."""
+    c = B.alexnet_default_cfg(2, 1, B.BF16)
+    ws = B.alexnet_workspace_bytes(c, B.MODE_TRAIN)
+    p = fake_params()
+    evs = [FAKE + 512 * i for i in range(B.SIDE_EVENTS)]
+    f = lambda **kw: B.alexnet_train_step_ex(c, p, p, p, FAKE, None, 0, 0, FAKE, 0.01, 0.9, 5e-4, 3, 0, FAKE,
+                                             None, FAKE, kw.get("wsb", ws), kw.get("stream", FAKE + 64),
+                                             kw.get("side", FAKE + 128), kw.get("events", evs), check=False)
+    assert f(side=FAKE + 64) == B.E_ARG                    # same stream as the main one
+    assert f(events=evs[:-1]) == B.E_NULL                   # one event missing
+    assert f(events=evs[:3] + [0] + evs[4:]) == B.E_NULL
+    assert f(wsb=ws - 256) == B.E_WORKSPACE                 # the usual checks still run
+    assert f(side=0, events=(), wsb=ws - 256) == B.E_WORKSPACE
+    txt = open(HEADER).read()
+    assert int(re.search(r"#define ALEXNET_SIDE_EVENTS (\d+)", txt).group(1)) == B.SIDE_EVENTS
+
+
+def test_library_creates_no_streams_events_or_memory():
+    """The caller owns every buffer, stream and event: the library's sources
+    call no HIP allocation or stream/event creation routine."""
+    csrc = os.path.join(ROOT, "deep_cnn_image_amd", "csrc")
+    banned = re.compile(r"\bhip(Malloc\w*|Free\w*|HostMalloc|ExtMalloc\w*|StreamCreate\w*|"
+                        r"EventCreate\w*|StreamDestroy|EventDestroy)\s*\(")
+    for name in sorted(os.listdir(csrc)):
+        txt = open(os.path.join(csrc, name)).read()
+        assert not banned.search(txt), (name, banned.search(txt).group(0))
