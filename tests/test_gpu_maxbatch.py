@@ -116,3 +116,70 @@ def test_max_batch_is_32_copies_of_the_base_batch(orc):
 def syn_master(syn, j):
     i = j // 2
     return np.asarray(syn.master_w[i] if j % 2 == 0 else syn.biases[i], np.float64)
+
+
+# ---------------------------------------------------------------- forward at the largest sizes
+def forward_taps(syn_weights, syn_biases, x_host, n, mode, groups=1):
+    sess = Session(n, groups, B.BF16, mode, DEV)
+    params = sess.upload_params(syn_weights, syn_biases)
+    x = to_device(x_host, B.BF16, DEV) if isinstance(x_host, np.ndarray) else x_host
+    probs = sess.forward(params, x)
+    torch.cuda.synchronize()
+    return sess, probs
+
+
+def test_forward_batch4096_is_32_copies_of_batch128():
+    """Forward pass at the largest batch (4096 = 32 copies of the 128-image
+    workload): the first and last copies are bit-identical to each other and
+    to the 128-image run through pool5 (each conv output is the same dot
+    product in the same order whatever the batch); the probabilities of every
+    copy agree with the 128-image run up to the FC layers' summation order."""
+    syn = I.workload_inputs("bf16_batch128")
+    n = syn.x.shape[0]
+    say(f"[gpu] forward batch {n}")
+    s1, p1 = forward_taps(syn.weights, syn.biases, syn.x, n, B.MODE_FORWARD)
+    pool5_base, probs_base = s1.tap("pool5").clone(), p1.cpu().numpy()
+    del s1
+    say(f"[gpu] forward batch {n * REPS} ({REPS} copies)")
+    xb = to_device(syn.x, B.BF16, DEV).repeat(REPS, 1, 1, 1).contiguous()
+    s2, p2 = forward_taps(syn.weights, syn.biases, xb, n * REPS, B.MODE_FORWARD)
+    pool5 = s2.tap("pool5")
+    assert torch.equal(pool5[:n], pool5_base) and torch.equal(pool5[-n:], pool5_base)
+    assert torch.equal(s2.tap("drop7")[:n], s2.tap("drop7")[-n:])
+    p = p2.cpu().numpy().reshape(REPS, n, 1000)
+    e = max(rel_l2(p[k], probs_base) for k in range(REPS))
+    say(f"[gpu] batch-4096 probabilities vs batch 128: max rel-L2 {e:.1e}")
+    assert e <= TOL_SUM_ORDER
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-5)
+    del s2, xb
+    torch.cuda.empty_cache()
+
+
+def test_tenview_512_sources(orc):
+    """Ten-view inference at the largest count the library accepts, 512
+    sources (5120 views, the conv1 output alone about 3 GB, byte offsets near
+    the top of the 32-bit buffer range): the first 256 sources are the
+    256-source workload and give bit-identical conv stacks to its own run;
+    sources from the second half, the last one included, match the oracle."""
+    syn = I.workload_inputs("tenview_256_sources")
+    extra = I.synthetic(14, 256, image=256, with_labels=False).x
+    say("[gpu] ten-view 256 sources")
+    s1, _ = forward_taps(syn.weights, syn.biases, syn.x, 256, B.MODE_TENVIEW)
+    pool5_base = s1.tap("pool5").clone()
+    del s1
+    torch.cuda.empty_cache()
+    say("[gpu] ten-view 512 sources (5120 views)")
+    x512 = np.concatenate([syn.x, extra])
+    s2, p2 = forward_taps(syn.weights, syn.biases, x512, 512, B.MODE_TENVIEW)
+    assert torch.equal(s2.tap("pool5")[:2560], pool5_base)
+    probs = host(p2)
+    vp = host(s2.tap("view_probs"))
+    np.testing.assert_allclose(probs.sum(1), 1.0, atol=1e-5)
+    for src in (300, 511):
+        t = orc.alexnet.forward_tenview(syn.weights, syn.biases, x512[src:src + 1], store="bf16")
+        e_mean = rel_l2(probs[src:src + 1], t["mean_probs"])
+        e_views = rel_l2(vp[src * 10:src * 10 + 10], t["probs"])
+        say(f"[gpu] ten-view 512 sources, source {src}: mean {e_mean:.2e} views {e_views:.2e}")
+        assert e_mean <= 2e-2 and e_views <= 2e-2
+    del s2
+    torch.cuda.empty_cache()
