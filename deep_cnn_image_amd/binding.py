@@ -15,7 +15,8 @@ from typing import Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libalexnet.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_WORKSPACE, E_ALIGN, E_DEVICE, E_HIP, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WORKSPACE, E_ALIGN, E_DEVICE, E_HIP, E_ARG, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ALEXNET_NOALLOC_SCRATCH_BYTES
 F32, BF16, U8 = 0, 1, 2
 MODE_FORWARD, MODE_TRAIN, MODE_TENVIEW = 0, 1, 2
 
@@ -25,7 +26,7 @@ EXPORTED = (
     "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string", "alexnet_forward_timed",
     "alexnet_train_step_timed", "alexnet_augment_images", "alexnet_train_step_augmented",
     "alexnet_train_step_augmented_timed", "alexnet_rgb_pca_workspace_bytes", "alexnet_rgb_pca",
-    "alexnet_rgb_pca_timed", "alexnet_train_step_ex",
+    "alexnet_rgb_pca_timed", "alexnet_train_step_ex", "alexnet_forward_noalloc",
 )
 
 # alexnet_kernel ids (kernel-timing hooks)
@@ -94,6 +95,8 @@ def lib():
     L.alexnet_workspace_bytes.restype = C.c_size_t
     L.alexnet_forward.argtypes = [cfgp, _PTR16, vp, vp, vp, C.c_size_t, vp]
     L.alexnet_forward.restype = C.c_int
+    L.alexnet_forward_noalloc.argtypes = [cfgp, _PTR16, vp, vp, vp]
+    L.alexnet_forward_noalloc.restype = C.c_int
     L.alexnet_forward_tenview.argtypes = [cfgp, _PTR16, vp, vp, vp, C.c_size_t, vp]
     L.alexnet_forward_tenview.restype = C.c_int
     L.alexnet_train_step.argtypes = [cfgp, _PTR16, _PTR16, _PTR16, vp, vp, C.c_float, C.c_float,
@@ -182,6 +185,12 @@ def alexnet_forward(cfg, params, x, probs, ws, ws_bytes, stream=0, check=True) -
     s = lib().alexnet_forward(C.byref(cfg), _ptr16(params), _ptr(x) or None, _ptr(probs) or None,
                               _ptr(ws) or None, ws_bytes, _ptr(stream) or None)
     return _check(s, "alexnet_forward") if check else s
+
+
+def alexnet_forward_noalloc(cfg, params, x, probs, stream=0, check=True) -> int:
+    s = lib().alexnet_forward_noalloc(C.byref(cfg), _ptr16(params), _ptr(x) or None, _ptr(probs) or None,
+                                      _ptr(stream) or None)
+    return _check(s, "alexnet_forward_noalloc") if check else s
 
 
 def alexnet_forward_tenview(cfg, params, src, probs, ws, ws_bytes, stream=0, check=True) -> int:

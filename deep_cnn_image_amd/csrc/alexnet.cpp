@@ -1,11 +1,12 @@
 // C ABI of the AlexNet library: argument validation (host only), the
 // workspace plan, and the launch sequences of the forward pass, the ten-view
 // forward pass and the training step.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/alexnet.h"
 #include "launch.hpp"
@@ -32,6 +33,32 @@ int check_device() {
     g_arch_ok[dev].store(s, std::memory_order_relaxed);
   }
   return s == 1 ? ALEXNET_OK : ALEXNET_E_DEVICE;
+}
+
+// Device scratch of alexnet_forward_noalloc: the whole forward workspace
+// (layer-1 staging, re-laid-out weights, activations, split-K partials) of
+// any configuration that fits.  One copy per GPU, loaded with the code
+// object and held until the process ends; every call on a GPU shares it.
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not the device copy): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[ALEXNET_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ALEXNET_E_HIP;
+  if (dev < 0 || dev >= 64) return ALEXNET_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ALEXNET_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ALEXNET_OK;
 }
 
 int check_params(const void* const* params, int n) {
@@ -354,6 +381,22 @@ int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const 
   return alexnet_forward_timed(cfg, params, x, probs, ws, ws_bytes, stream, nullptr, 0);
 }
 
+int alexnet_forward_noalloc(const alexnet_cfg* cfg, const void* const params[16], const void* x, float* probs,
+                            void* stream) {
+  Plan p;
+  int r = make_plan(cfg, ALEXNET_MODE_FORWARD, &p);
+  if (r != ALEXNET_OK) return r;
+  if (p.total > ALEXNET_NOALLOC_SCRATCH_BYTES) return ALEXNET_E_SCRATCH;
+  if ((r = check_params(params, 16)) != ALEXNET_OK) return r;
+  if (!x || !probs) return ALEXNET_E_NULL;
+  if (!aligned(x, 16) || !aligned(probs, 16)) return ALEXNET_E_ALIGN;
+  if ((r = check_device()) != ALEXNET_OK) return r;
+  void* ws = nullptr;
+  if ((r = scratch_address(&ws)) != ALEXNET_OK) return r;
+  return enqueue_forward(p, params, x, ws, false, 0, 0, (hipStream_t)stream, Timers(),
+                         Head{nullptr, probs, nullptr, nullptr});
+}
+
 int alexnet_forward_tenview(const alexnet_cfg* cfg, const void* const params[16], const void* src,
                             float* probs, void* ws, size_t ws_bytes, void* stream) {
   Plan p;
@@ -596,6 +639,7 @@ const char* alexnet_status_string(int s) {
     case ALEXNET_E_DEVICE: return "device is not gfx950";
     case ALEXNET_E_HIP: return "HIP error while enqueueing";
     case ALEXNET_E_ARG: return "invalid argument";
+    case ALEXNET_E_SCRATCH: return "configuration needs more than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }

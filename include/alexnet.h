@@ -35,7 +35,9 @@
  *    state it keeps between calls is a per-device cache of whether the
  *    device is a gfx950 (a fixed fact once read).  Calls are reentrant given
  *    distinct workspaces (and, for alexnet_train_step_ex, distinct side
- *    streams and events).
+ *    streams and events).  alexnet_forward_noalloc is the exception: its
+ *    workspace is a static device array, one per GPU, and it caches that
+ *    array's address per device.
  *  - Calls validate their arguments on the host before any launch and return
  *    an alexnet_status; on error nothing is enqueued.  Work is enqueued on
  *    `stream` (a hipStream_t, 0 = the default stream) and runs
@@ -65,7 +67,9 @@ typedef enum {
   ALEXNET_E_ALIGN = -5,     /* pointer misaligned                              */
   ALEXNET_E_DEVICE = -6,    /* current device is not gfx950                    */
   ALEXNET_E_HIP = -7,       /* a HIP call failed while enqueueing              */
-  ALEXNET_E_ARG = -8        /* other invalid argument (mode, tap id, LRN size) */
+  ALEXNET_E_ARG = -8,       /* other invalid argument (mode, tap id, LRN size) */
+  ALEXNET_E_SCRATCH = -9    /* alexnet_forward_noalloc: the configuration's
+                               workspace exceeds ALEXNET_NOALLOC_SCRATCH_BYTES */
 } alexnet_status;
 
 typedef enum { ALEXNET_F32 = 0, ALEXNET_BF16 = 1, ALEXNET_U8 = 2 } alexnet_dtype;
@@ -105,6 +109,23 @@ size_t alexnet_workspace_bytes(const alexnet_cfg* cfg, int mode);
  *   probs [batch][1000] fp32 softmax output (written) */
 int alexnet_forward(const alexnet_cfg* cfg, const void* const params[16], const void* x,
                     float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* alexnet_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results, bit for bit, with no workspace argument.
+ * The workspace lives in a static device array of ALEXNET_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that each GPU the library runs on holds until the process ends.
+ * A configuration whose forward workspace (alexnet_workspace_bytes with
+ * ALEXNET_MODE_FORWARD) exceeds it is rejected with ALEXNET_E_SCRATCH before
+ * anything is enqueued: fp32 and bf16 up to batch 8 fit.  The call allocates
+ * nothing; on the first call on a device it looks up that device's copy of the
+ * array (hipGetSymbolAddress).  Every call on one GPU shares the array, so
+ * calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race; calls ordered on one stream do not.  The
+ * array keeps the last call's contents; each call writes every part it reads. */
+#define ALEXNET_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int alexnet_forward_noalloc(const alexnet_cfg* cfg, const void* const params[16], const void* x,
+                            float* probs, void* stream);
 
 /* Ten-patch test-time averaging (paper-graph-ui "Data Augmentation": the four
  * corner 227x227 patches and the centre patch, each also mirrored, softmax

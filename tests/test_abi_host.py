@@ -252,3 +252,23 @@ def test_library_creates_no_streams_events_or_memory():
     for name in sorted(os.listdir(csrc)):
         txt = open(os.path.join(csrc, name)).read()
         assert not banned.search(txt), (name, banned.search(txt).group(0))
+
+
+def test_noalloc_forward_refuses_oversized_configurations_before_launch():
+    """alexnet_forward_noalloc keeps its workspace in a static device array of
+    ALEXNET_NOALLOC_SCRATCH_BYTES; larger configurations are refused on the
+    host with ALEXNET_E_SCRATCH, smaller ones reach the usual checks."""
+    txt = open(HEADER).read()
+    m = re.search(r"#define ALEXNET_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", txt)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    p = fake_params()
+    for dtype, n in ((B.F32, 16), (B.BF16, 64), (B.BF16, 4096)):
+        c = B.alexnet_default_cfg(n, 1, dtype)
+        assert B.alexnet_workspace_bytes(c, B.MODE_FORWARD) > B.NOALLOC_SCRATCH_BYTES
+        assert B.alexnet_forward_noalloc(c, p, FAKE, FAKE, 0, check=False) == B.E_SCRATCH
+    for dtype in (B.F32, B.BF16):
+        c = B.alexnet_default_cfg(8, 2, dtype)
+        assert B.alexnet_workspace_bytes(c, B.MODE_FORWARD) <= B.NOALLOC_SCRATCH_BYTES
+        assert B.alexnet_forward_noalloc(c, p, 0, FAKE, 0, check=False) == B.E_NULL
+        assert B.alexnet_forward_noalloc(c, p, FAKE + 2, FAKE, 0, check=False) == B.E_ALIGN
+    assert B.status_string(B.E_SCRATCH).startswith("configuration needs more")
