@@ -127,6 +127,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="images in the CPU-oracle sample")
+    ap.add_argument("--train-only", action="store_true",
+                    help="time the training step only (for short profiled runs) and print its kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -150,6 +152,15 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     h = I.TRAIN_HYPER
+
+    def copy_calibration():
+        # a plain 512 MiB device copy, the reference for the HBM byte counters
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        return {"read": src.numel() * 2, "write": dst.numel() * 2}
 
     def new_events(k):
         evs = []
@@ -215,6 +226,16 @@ def main():
     train_s = (time.perf_counter() - t0) / args.steps
     dom_ms = sum(a.elapsed_time(b) for a, b in tev) / args.steps
     final_loss = float(loss.item())
+    if args.train_only:
+        # the training step alone (short runs under a profiler): its per-kernel
+        # fractions and the dominant kernel's figure, nothing else
+        out = {"ms_per_step": round(train_s * 1e3, 4), "value": round(n / train_s, 1), "unit": "images/s",
+               "loss": round(final_loss, 5), "dominant": dominant, "dominant_us": round(dom_ms * 1e3, 2),
+               "kernels_train_us": {nm: round(ms * 1e3, 2) for nm, ms in per_kernel.items()}}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration()
+        print(json.dumps(out), flush=True)
+        return
 
     # ---------------------------------------------------------------- augmented training step
     # Same step fed by the section-4.1 augmentation: 227x227 patches of 256x256
@@ -400,13 +421,7 @@ def main():
     }
 
     if args.copy_calibration:
-        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
-        del src, dst
+        rec["copy_calibration_bytes"] = copy_calibration()
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:

@@ -175,6 +175,7 @@ struct GemmGrid {
   int splits;           // split-K factor
   int groups;           // independent GEMMs (convolution groups)
   int kt_per_split;     // k-tiles per split
+  int strip_n;          // tile order: 0 = n fastest over whole rows; w > 0 = strips of w n-tiles (see k_gemm)
 };
 
 // ------------------------------------------------------------------ loaders
@@ -888,7 +889,7 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   const int wm = wave / WGN, wn = wave % WGN;
 
   // Work order.  The 1-D grid enumerates (group, split, tile) with tiles
-  // fastest.  Hardware deals workgroups round-robin over the eight XCDs, each
+  // fastest (within a GEMM, n fastest, over whole rows or strips: strip_n).  Hardware deals workgroups round-robin over the eight XCDs, each
   // with its own L2; the remap gives XCD x one contiguous run of that order
   // (the first nb % 8 XCDs one workgroup more), so workgroups that share
   // operand rows (neighbouring tiles, tiles of one split) share an L2.
@@ -898,7 +899,20 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   const int tiles = gg.tiles_m * gg.tiles_n;
   const int gs = b / tiles, t = b - gs * tiles;
   const int g = gs / gg.splits, s = gs - g * gg.splits;
-  const int bm = t / gg.tiles_n, bn = t - bm * gg.tiles_n;
+  int bm, bn;
+  if (gg.strip_n > 0 && gg.strip_n < gg.tiles_n) {
+    // column strips of strip_n n-tiles, n fastest within a strip, strips one
+    // after the other: the workgroups an XCD runs at once share one strip's
+    // B blocks over several rows of tiles, so those stay in L2 while the
+    // rows go by
+    const int per = gg.strip_n * gg.tiles_m, sidx = t / per, n0s = sidx * gg.strip_n;
+    const int wdt = min(gg.tiles_n - n0s, gg.strip_n), r = t - sidx * per;
+    bm = r / wdt;
+    bn = n0s + (r - bm * wdt);
+  } else {
+    bm = t / gg.tiles_n;
+    bn = t - bm * gg.tiles_n;
+  }
   const int m0 = bm * BM, n0 = bn * BN;
   const int total_kt = (gg.K + BK - 1) / BK;
   const int kt0 = s * gg.kt_per_split;

@@ -39,7 +39,7 @@ static inline void rec_stop(const KTimer* kt, hipStream_t st) { if (kt) hipEvent
 // ST = 0: the tile's default LDS stage count.
 template <typename T, int BM, int BN, int WGM, int WGN, int ST0 = 0, class AL, class BL, class EP>
 static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
-                           int splits, hipStream_t st, const KTimer* kt = nullptr) {
+                           int splits, hipStream_t st, const KTimer* kt = nullptr, int strip_n = 0) {
   constexpr int ST = ST0 ? ST0 : gemm_default_stages<T, BM, BN>();
   GemmGrid gg;
   gg.M = M; gg.N = N; gg.K = K;
@@ -49,6 +49,7 @@ static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int 
   gg.splits = eff_splits(K, splits);
   gg.kt_per_split = cdiv(ktiles, gg.splits);
   gg.groups = groups;
+  gg.strip_n = strip_n;
   dim3 grid(gg.tiles_m * gg.tiles_n * groups * gg.splits);
   rec_start(kt, st);
   hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP, ST>), grid, dim3(NTHREADS), 0, st, al, bl,
@@ -832,6 +833,7 @@ struct EpSgd {
   }
 };
 
+constexpr int FC_WGRAD_STRIP = 18;
 template <typename T>
 static hipError_t fc_wgrad_sgd_t(int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,
                                  float* w, float* v, void* wb, hipStream_t st, const KTimer* kt) {
@@ -843,7 +845,7 @@ static hipError_t fc_wgrad_sgd_t(int M, int K, int O, const void* dy, const void
   bl.p = (const T*)x; bl.ld = K; bl.rows = K; bl.K = M; bl.gstride = 0;
   EpSgd<T> e;
   e.w = w; e.v = v; e.wb = (T*)wb; e.ldo = K; e.M = O; e.N = K; e.h = h;
-  return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st, kt);
+  return run_gemm<T, BM, BN, 2, 2>(a, bl, e, O, K, M, 1, 1, st, kt, FC_WGRAD_STRIP);
 }
 
 hipError_t fc_wgrad_sgd(DType dt, int M, int K, int O, const void* dy, const void* x, const SgdHyper& h,
@@ -1438,8 +1440,8 @@ __device__ __forceinline__ void lrn_bwd_unit(const T* apx, const T* gpx, int c0,
 // has one pooled row and three input rows), one contiguous run of NHWC:
 //   1. the run is copied into LDS with direct-to-LDS loads (one wait);
 //   2. each thread normalises its (row, column, 8-channel) units from LDS into
-//      registers and, after a barrier, writes them back in place -- rows 0..2
-//      and then rows 3..4, to bound the registers held;
+//      registers, packed as stored, and, after a barrier, writes them back in
+//      place;
 //   3. the pooled rows and their argmax are taken from LDS.
 // For bf16 the window maximum is taken on integer keys (value bits << 16 |
 // 15 - d): the inputs are ReLU outputs, so every LRN output is >= +0 and its
@@ -1450,31 +1452,55 @@ __device__ __forceinline__ void lrn_bwd_unit(const T* apx, const T* gpx, int c0,
 // that the pairs of one image, which share an input row, run on one XCD.
 constexpr int LRNPOOL_TPB = 512;
 
-template <typename T, int H, bool B075, int Win, int C, int R0, int R1>
+// Eight values of T packed as a stored tensor holds them (bf16: one 16-byte
+// word, fp32: two), rounded as Pack8<T>::store rounds.
+template <typename T> struct Packed8 { uint4 q[sizeof(T) / 2]; };
+template <typename T>
+__device__ __forceinline__ Packed8<T> pack8(const float* v) {
+  Packed8<T> o;
+  if constexpr (std::is_same<T, bf16>::value) {
+    o.q[0] = make_uint4(f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7]));
+  } else {
+    o.q[0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    o.q[1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
+  }
+  return o;
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const Packed8<T>& o) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) reinterpret_cast<uint4*>(p)[i] = o.q[i];
+}
+
+// LRN of rows 0 .. nrows-1 of the LDS tile, in place: every thread computes
+// its (row, column, 8-channel) units from LDS into packed registers (a unit
+// past the end recomputes the last one, so no thread branches around the
+// arithmetic), then, after a barrier, writes them back.
+template <typename T, int H, bool B075, int Win, int C>
 __device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, T* __restrict__ dbg, size_t dbg_row0, int own_last,
                                               float k, float alpha, float beta) {
   constexpr int cpp = C / 8, rowu = Win * cpp;
-  constexpr int UPT = ((R1 - R0) * rowu + LRNPOOL_TPB - 1) / LRNPOOL_TPB;
+  constexpr int UPT = (5 * rowu + LRNPOOL_TPB - 1) / LRNPOOL_TPB;
   const int tid = threadIdx.x;
-  const int units = (min(R1, nrows) - R0) * rowu;
-  float o[UPT][8];
+  const int units = nrows * rowu;
+  Packed8<T> o[UPT];
 #pragma unroll
   for (int t = 0; t < UPT; ++t) {
-    const int u = tid + t * LRNPOOL_TPB;
-    if (u < units) {
-      const int pix = R0 * Win + u / cpp, c0 = (u % cpp) * 8;
-      lrn_unit<T, H, B075, C>(rows + pix * C, c0, k, alpha, beta, o[t]);
-    }
+    const int u = min(tid + t * LRNPOOL_TPB, units - 1);
+    const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
+    float r[8];
+    lrn_unit<T, H, B075, C>(rows + pix * C, c0, k, alpha, beta, r);
+    o[t] = pack8<T>(r);
   }
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < UPT; ++t) {
     const int u = tid + t * LRNPOOL_TPB;
     if (u < units) {
-      const int pix = R0 * Win + u / cpp, c0 = (u % cpp) * 8;
-      Pack8<T>::store(rows + pix * C + c0, o[t]);
+      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
+      store8<T>(rows + pix * C + c0, o[t]);
       const int rr = pix / Win;
-      if (dbg && (rr < 4 || own_last)) Pack8<T>::store(dbg + dbg_row0 + (size_t)pix * C + c0, o[t]);
+      if (dbg && (rr < 4 || own_last)) store8<T>(dbg + dbg_row0 + (size_t)pix * C + c0, o[t]);
     }
   }
 }
@@ -1510,8 +1536,7 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
   // 2. LRN in place, rows 0..2 then 3..4
   const size_t dbg_row0 = ((size_t)n * Hin + 2 * i0) * Win * C;
   const int own_last = 2 * i0 + nrows == Hin;
-  lrn_pool_rows<T, H, B075, Win, C, 0, 3>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
-  if (nrows > 3) lrn_pool_rows<T, H, B075, Win, C, 3, 5>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
+  lrn_pool_rows<T, H, B075, Win, C>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
   __syncthreads();
   // 3. pool: pooled row i0 + ii from LDS rows 2 ii .. 2 ii + 2, columns 2j .. 2j+2
   for (int u = tid; u < npool * Wo * cpp; u += LRNPOOL_TPB) {
@@ -1607,13 +1632,14 @@ __device__ __forceinline__ void pool_bwd8_lds(const T* dyL, const uint8_t* argL,
 //      LDS, applies the ReLU mask and writes da.
 // da therefore equals that of the separate steps.  `dbg`, if not null,
 // receives g.
-constexpr int POOLLRN_UPT = 4;   // units per thread: Win * C / 8 / 256 <= 4
+constexpr int PLB_TPB = 512;   // eight waves per row: more loads in flight per LDS byte than four
 template <typename T, int H, bool B075, int Win, int C>
-__global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
+__global__ void __launch_bounds__(PLB_TPB) k_pool_lrn_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
                                                       const T* __restrict__ a, T* __restrict__ da,
                                                       T* __restrict__ dbg, float k, float alpha, float beta) {
   constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, cpp = C / 8, units = Win * cpp;
-  static_assert(units <= POOLLRN_UPT * TPB && C % 8 == 0, "pool/LRN backward geometry");
+  constexpr int UPT = (units + PLB_TPB - 1) / PLB_TPB;   // units per thread
+  static_assert(C % 8 == 0, "pool/LRN backward geometry");
   constexpr int KB = 1024;
   constexpr int ROW_BYTES = (Win * C * (int)sizeof(T) + KB - 1) / KB * KB;
   constexpr int DY_BYTES = (2 * Wo * C * (int)sizeof(T) + KB - 1) / KB * KB;
@@ -1638,20 +1664,20 @@ __global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, 
     const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a + row0, (uint32_t)(Win * C * sizeof(T)));
     const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dy + prow, pel * (uint32_t)sizeof(T));
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(arg + prow, pel);
-    for (int j = wave; j < ROW_BYTES / KB; j += TPB / 64)
+    for (int j = wave; j < ROW_BYTES / KB; j += PLB_TPB / 64)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(lds + j * KB), 16, j * KB + lane * 16, 0, 0, 0);
-    for (int j = wave; j < DY_BYTES / KB; j += TPB / 64)
+    for (int j = wave; j < DY_BYTES / KB; j += PLB_TPB / 64)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(lds + 2 * ROW_BYTES + j * KB), 16,
                                                j * KB + lane * 16, 0, 0, 0);
-    for (int j = wave; j < ARG_BYTES / KB; j += TPB / 64)
+    for (int j = wave; j < ARG_BYTES / KB; j += PLB_TPB / 64)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void_t*)(lds + 2 * ROW_BYTES + DY_BYTES + j * KB), 16,
                                                j * KB + lane * 16, 0, 0, 0);
     wait_vmcnt<0>();
     __syncthreads();
   }
 #pragma unroll
-  for (int t = 0; t < POOLLRN_UPT; ++t) {
-    const int u = tid + t * TPB;
+  for (int t = 0; t < UPT; ++t) {
+    const int u = tid + t * PLB_TPB;
     if (u < units) {
       const int w = u / cpp, c0 = (u - w * cpp) * 8;
       float g[8];
@@ -1662,8 +1688,8 @@ __global__ void __launch_bounds__(TPB) k_pool_lrn_bwd(const T* __restrict__ dy, 
   }
   __syncthreads();
 #pragma unroll
-  for (int t = 0; t < POOLLRN_UPT; ++t) {
-    const int u = tid + t * TPB;
+  for (int t = 0; t < UPT; ++t) {
+    const int u = tid + t * PLB_TPB;
     if (u < units) {
       const int w = u / cpp, c0 = (u - w * cpp) * 8;
       float o[8];
@@ -1704,7 +1730,7 @@ struct PoolLrnBwdFn {
   hipStream_t st;
   template <int H, bool B075>
   hipError_t operator()() const {
-    hipLaunchKernelGGL((k_pool_lrn_bwd<T, H, B075, Win, C>), dim3(N * Win), dim3(TPB), 0, st, (const T*)dy, arg,
+    hipLaunchKernelGGL((k_pool_lrn_bwd<T, H, B075, Win, C>), dim3(N * Win), dim3(PLB_TPB), 0, st, (const T*)dy, arg,
                        (const T*)a, (T*)da, (T*)dbg, k, alpha, beta);
     return hipGetLastError();
   }
