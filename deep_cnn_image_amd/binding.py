@@ -13,7 +13,8 @@ import os
 from typing import Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libalexnet.so")
+# ALEXNET_LIB selects another build of the same sources (the sanitizer test uses it)
+LIB_PATH = os.environ.get("ALEXNET_LIB") or os.path.join(_HERE, "lib", "libalexnet.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_WORKSPACE, E_ALIGN, E_DEVICE, E_HIP, E_ARG, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 NOALLOC_SCRATCH_BYTES = 64 << 20   # ALEXNET_NOALLOC_SCRATCH_BYTES
