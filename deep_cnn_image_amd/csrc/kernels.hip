@@ -1587,37 +1587,51 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
 }
 
 // Max-pool backward (3x3 / stride 2, argmax codes dy*3+dx) for channels
-// c0 .. c0+7 of input pixel (h, w): the sum, over the windows (i, j) that
-// contain the pixel and whose argmax is it, of dy[i][j] -- windows in
-// row-major order -- rounded to T as a stored gradient would be.  dyL / argL
-// hold pooled rows ilo .. ihi of the image (at most two), [row][j][c].
-template <typename T, int C>
-__device__ __forceinline__ void pool_bwd8_lds(const T* dyL, const uint8_t* argL, int h, int w, int c0, int ilo,
-                                              int ihi, int Wo, float* out) {
-  const int j0 = w >= 2 ? (w - 1) / 2 : 0, j1 = min(w / 2, Wo - 1);
-  float acc[8];
+// c0 .. c0+7 of the input pixels (h, 2m) and (h, 2m + 1): each one's sum,
+// over the windows (i, j) that contain it and whose argmax it is, of
+// dy[i][j] -- windows in row-major order -- rounded to T as a stored
+// gradient would be.  Window column m - 1 reaches pixel 2m (dx = 2) only;
+// window column m reaches pixel 2m (dx = 0) and 2m + 1 (dx = 1); window rows
+// are ilo .. ihi (at most two, the same for the whole input row h).  Taking
+// the pixels in pairs loads each window once and skips the windows that
+// cannot contain a pixel.  dyL / argL hold pooled rows ilo .. ihi of the
+// image, [row][j][c].
+template <typename T, int C, int Wo>
+__device__ __forceinline__ void pool_bwd_pair_lds(const T* dyL, const uint8_t* argL, int h, int m, int c0, int ilo,
+                                                  int ihi, Packed8<T>& g0, Packed8<T>& g1) {
+  float acc0[8], acc1[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int q = 0; q < 8; ++q) acc0[q] = acc1[q] = 0.f;
 #pragma unroll
-  for (int di = 0; di < 2; ++di)
+  for (int di = 0; di < 2; ++di) {
+    const int i = ilo + di;
+    if (i > ihi) break;   // uniform over the workgroup
+    const uint32_t row_code = (uint32_t)(h - 2 * i) * 3u;
+    float g[8];
+    if (m >= 1) {   // window (i, m - 1)
+      const int off = (di * Wo + m - 1) * C + c0;
+      const uint2 am = *reinterpret_cast<const uint2*>(argL + off);
+      Pack8<T>::load(dyL + off, g);
 #pragma unroll
-    for (int dj = 0; dj < 2; ++dj) {
-      const int i = ilo + di, j = j0 + dj;
-      if (i <= ihi && j <= j1) {
-        const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
-        const int off = (di * Wo + j) * C + c0;
-        const uint2 am = *reinterpret_cast<const uint2*>(argL + off);
-        float g[8];
-        Pack8<T>::load(dyL + off, g);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t bq = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
-          if (bq == code) acc[q] += g[q];
-        }
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t bq = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+        if (bq == row_code + 2u) acc0[q] += g[q];
       }
     }
+    if (m < Wo) {   // window (i, m)
+      const int off = (di * Wo + m) * C + c0;
+      const uint2 am = *reinterpret_cast<const uint2*>(argL + off);
+      Pack8<T>::load(dyL + off, g);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) out[q] = Num<T>::load(Num<T>::store(acc[q]));
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t bq = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
+        if (bq == row_code) acc0[q] += g[q];
+        if (bq == row_code + 1u) acc1[q] += g[q];
+      }
+    }
+  }
+  g0 = pack8<T>(acc0);
+  g1 = pack8<T>(acc1);
 }
 
 // Max-pool backward, LRN backward and the ReLU mask in one pass.  One
@@ -1626,8 +1640,8 @@ __device__ __forceinline__ void pool_bwd8_lds(const T* dyL, const uint8_t* argL,
 //      argmax whose windows cover row h, are copied into LDS with
 //      direct-to-LDS loads, all issued before one wait;
 //   2. each thread forms the pooled gradient g (w.r.t. the LRN output) of its
-//      (column, 8-channel) units from LDS, rounded as a stored gradient would
-//      be, into a third LDS row;
+//      (pair of columns, 8-channel) units from LDS, rounded as a stored
+//      gradient would be, into a third LDS row;
 //   3. each unit's LRN backward reads its channel neighbours of a and g from
 //      LDS, applies the ReLU mask and writes da.
 // da therefore equals that of the separate steps.  `dbg`, if not null,
@@ -1675,15 +1689,21 @@ __global__ void __launch_bounds__(PLB_TPB) k_pool_lrn_bwd(const T* __restrict__ 
     wait_vmcnt<0>();
     __syncthreads();
   }
+  // 2. pooled gradient, a pair of columns per (unit, 8 channels)
+  constexpr int pair_units = (Win + 1) / 2 * cpp;
 #pragma unroll
-  for (int t = 0; t < UPT; ++t) {
+  for (int t = 0; t < (pair_units + PLB_TPB - 1) / PLB_TPB; ++t) {
     const int u = tid + t * PLB_TPB;
-    if (u < units) {
-      const int w = u / cpp, c0 = (u - w * cpp) * 8;
-      float g[8];
-      pool_bwd8_lds<T, C>(dyL, argL, h, w, c0, ilo, ihi, Wo, g);
-      Pack8<T>::store(grow + w * C + c0, g);
-      if (dbg) Pack8<T>::store(dbg + row0 + w * C + c0, g);
+    if (u < pair_units) {
+      const int m = u / cpp, c0 = (u - m * cpp) * 8;
+      Packed8<T> g0, g1;
+      pool_bwd_pair_lds<T, C, Wo>(dyL, argL, h, m, c0, ilo, ihi, g0, g1);
+      store8<T>(grow + 2 * m * C + c0, g0);
+      if (dbg) store8<T>(dbg + row0 + 2 * m * C + c0, g0);
+      if (2 * m + 1 < Win) {
+        store8<T>(grow + (2 * m + 1) * C + c0, g1);
+        if (dbg) store8<T>(dbg + row0 + (2 * m + 1) * C + c0, g1);
+      }
     }
   }
   __syncthreads();
