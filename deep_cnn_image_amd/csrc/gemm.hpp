@@ -400,8 +400,9 @@ struct DmaIm2col {
   static constexpr int NI = Slots::NI;
   const bf16* p; ConvGeom cg; int M; int K; bool blocked = false;
   __amdgpu_buffer_rsrc_t rs;
-  int hb[NI], wb[NI], pix[NI];   // pix: element offset of input pixel (hb, wb) of the row's image
-  int kc, kh, kw, ci;            // blocked: kh, kw uniform, ci = block base + this lane's granule
+  int pix[NI];         // element offset of input pixel (ho s - pad, wo s - pad) of the row's image
+  uint32_t skip[NI];   // bit t set: tap t (= kh KW + kw) of the row falls outside the input, or t >= KH KW
+  int kh, kw, ci, tap; // blocked: kh, kw, tap uniform, ci = block base + this lane's granule
   __device__ void setup(int r0, int g, int kb) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hw = cg.Ho * cg.Wo;
@@ -410,56 +411,63 @@ struct DmaIm2col {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int m = r0 + Slots::slot(wave, i) * 8 + (lane >> 3);
-      hb[i] = -(1 << 28); wb[i] = 0; pix[i] = 0;
+      uint32_t valid = 0;
+      pix[i] = 0;
       if (m < M) {
         const int n = m / hw, rem = m - n * hw;
         const int ho = rem / cg.Wo, wo = rem - ho * cg.Wo;
-        hb[i] = ho * cg.stride - cg.pad;
-        wb[i] = wo * cg.stride - cg.pad;
-        pix[i] = ((n * cg.H + hb[i]) * cg.W + wb[i]) * cg.Ctot + g * cg.Cg;
+        const int hb = ho * cg.stride - cg.pad, wb = wo * cg.stride - cg.pad;
+        pix[i] = ((n * cg.H + hb) * cg.W + wb) * cg.Ctot + g * cg.Cg;
+        // taps inside the input: kh in [-hb, H - hb), kw in [-wb, W - wb)
+        const int c0 = max(0, -wb), c1 = min(cg.KW, cg.W - wb);
+        const int q0 = max(0, -hb), q1 = min(cg.KH, cg.H - hb);
+        const uint32_t cols = c1 > c0 ? (1u << c1) - (1u << c0) : 0u;
+        for (int q = q0; q < q1; ++q) valid |= cols << (q * cg.KW);
       }
+      skip[i] = ~valid;
     }
     const int gcol = Slots::granule(lane, wave & 1) * 8;
-    kc = kb + gcol;
     if (blocked) {
       const int kt = kb / BK, taps = cg.KH * cg.KW;
-      const int blk = kt / taps, tap = kt - blk * taps;
+      const int blk = kt / taps;
+      tap = kt - blk * taps;
       kh = tap / cg.KW; kw = tap - kh * cg.KW; ci = blk * BK + gcol;
     } else {
-      const int tap = kc / cg.Cg;
+      const int kc = kb + gcol;
+      tap = kc / cg.Cg;
       ci = kc - tap * cg.Cg; kh = tap / cg.KW; kw = tap - kh * cg.KW;
     }
   }
+  // A row's load goes out of range (reads zero) when its tap's skip bit is
+  // set: bit 31 of the byte offset, above every buffer size used.  The k
+  // tail (k >= K, tap >= KH KW) is covered by the same bits.
   __device__ __forceinline__ void issue(bf16* s) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (blocked) {   // K = Cg * KH * KW is a multiple of BK: no k tail
-      const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int hi = hb[i] + kh, wi = wb[i] + kw;
-        const bool ok = ((unsigned)hi < (unsigned)cg.H) & ((unsigned)wi < (unsigned)cg.W);
-        dma16(rs, ok ? (uint32_t)(pix[i] + tapoff) * 2u : BUF_OOB, s + Slots::slot(wave, i) * 8 * BK);
-      }
-      if (++kw == cg.KW) { kw = 0; if (++kh == cg.KH) { kh = 0; ci += BK; } }
-      return;
-    }
-    const bool kok = kc < K;
     const int tapoff = (kh * cg.W + kw) * cg.Ctot + ci;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int hi = hb[i] + kh, wi = wb[i] + kw;
-      const bool ok = kok & ((unsigned)hi < (unsigned)cg.H) & ((unsigned)wi < (unsigned)cg.W);
-      const uint32_t o = ok ? (uint32_t)(pix[i] + tapoff) * 2u : BUF_OOB;
+      const uint32_t o = ((uint32_t)(pix[i] + tapoff) << 1) | (((skip[i] >> tap) & 1u) << 31);
       dma16(rs, o, s + Slots::slot(wave, i) * 8 * BK);
     }
-    kc += BK;
+    if (blocked) {   // K = Cg * KH * KW is a multiple of BK: no k tail
+      ++tap;
+      if (++kw == cg.KW) { kw = 0; if (++kh == cg.KH) { kh = 0; tap = 0; ci += BK; } }
+      return;
+    }
     ci += BK;
     while (ci >= cg.Cg) {
       ci -= cg.Cg;
+      ++tap;
       if (++kw == cg.KW) { kw = 0; ++kh; }
     }
   }
 };
+// The skip bits above cover taps 0 .. 31: KH KW taps, plus the k tail of
+// the tap-major order, whose last slice reaches at most (BK - 1) / Cg taps
+// beyond them.
+__host__ __device__ constexpr bool im2col_taps_fit(int KH, int KW, int Cg, bool blocked) {
+  return KH * KW + (blocked ? 0 : (BK - 1) / Cg) <= 31;
+}
 
 // Output pixel p = (n, ho, wo) over [Nimg][Ho][Wo], stepped by BK at a time.
 struct PixelIter {

@@ -26,6 +26,11 @@ using WgradBLd = std::conditional_t<std::is_same<T, bf16>::value, DmaWgradB<R>, 
 // channel-blocked k order (direct-to-LDS im2col only; see DmaIm2col)
 template <int R> static void set_blocked(DmaIm2col<R>& a, bool b) { a.blocked = b; }
 template <typename T, int R> static void set_blocked(LdIm2col<T, R>&, bool) {}
+// the direct-to-LDS im2col's per-row tap bits (see DmaIm2col) hold the geometry
+template <int R> static bool im2col_fits(const DmaIm2col<R>& a) {
+  return im2col_taps_fit(a.cg.KH, a.cg.KW, a.cg.Cg, a.blocked);
+}
+template <typename T, int R> static bool im2col_fits(const LdIm2col<T, R>&) { return true; }
 bool im2col_blocked(DType dt, int Cg);
 
 static inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + TPB - 1) / TPB)); }
@@ -281,6 +286,7 @@ struct Conv1FwdFn {
   hipError_t operator()() const {
     Im2colLd<T, BM> a;
     a.p = (const T*)xs; a.cg = conv1_geom(); a.M = Nimg * 3025; a.K = S2D_K;
+    if (!im2col_fits(a)) return hipErrorInvalidValue;
     RowsLd<T, BN> b;
     b.p = (const T*)ws2d; b.ld = S2D_K; b.rows = 96; b.K = S2D_K; b.gstride = 0;
     const int S = conv_split_count(cdiv(a.M, BM) * cdiv(96, BN), S2D_K, std::is_same<T, float>::value);
@@ -317,6 +323,7 @@ struct ConvFwdFn {
     a.cg = ConvGeom{s.H, s.W, s.Cin, Cig, s.K, s.K, s.stride, s.pad, s.Ho, s.Wo};
     a.M = s.Nimg * s.Ho * s.Wo;
     a.K = s.K * s.K * Cig;
+    if (!im2col_fits(a)) return hipErrorInvalidValue;
     RowsLd<T, BN> bl;
     bl.p = (const T*)wr; bl.ld = a.K; bl.rows = Cog; bl.K = a.K; bl.gstride = (int64_t)Cog * a.K;
     const int S = conv_split_count((int64_t)cdiv(a.M, BM) * cdiv(Cog, BN) * s.groups, a.K,
@@ -366,6 +373,7 @@ struct ConvDgradFn {
     a.cg = ConvGeom{s.Ho, s.Wo, s.Cout, Cog, s.K, s.K, 1, s.K - 1 - s.pad, s.H, s.W};
     a.M = s.Nimg * s.H * s.W;
     a.K = s.K * s.K * Cog;
+    if (!im2col_fits(a)) return hipErrorInvalidValue;
     RowsLd<T, BN> bl;
     bl.p = (const T*)wt; bl.ld = a.K; bl.rows = Cig; bl.K = a.K; bl.gstride = (int64_t)Cig * a.K;
     const int S = conv_split_count((int64_t)cdiv(a.M, BM) * cdiv(Cig, BN) * s.groups, a.K,
