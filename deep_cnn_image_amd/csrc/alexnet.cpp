@@ -290,8 +290,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   }
   // pool2 -> LRN2 -> ReLU2
   HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN3), (const uint8_t*)tp(ws, p, T_ARG2), tp(ws, p, T_CONV2),
-                      tp(ws, p, T_DCONV2), c.lrn_taps ? tp(ws, p, T_DLRN2) : nullptr, N, 27, 27, 256, c.lrn_k,
-                      c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN2_BWD)));
+                      tp(ws, p, T_DCONV2), c.lrn_taps ? tp(ws, p, T_DLRN2) : nullptr, (float*)at(ws, p.bias_rows[1]),
+                      N, 27, 27, 256, c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN2_BWD)));
   {
     const ConvShape& s = net.conv[1];
     const SgdTarget u{master[2], momentum[2], work[2], hy};
@@ -303,8 +303,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   }
   // pool1 -> LRN1 -> ReLU1, then layer-1 weight gradient (no input gradient)
   HIPCHK(pool_lrn_bwd(dt, tp(ws, p, T_DIN2), (const uint8_t*)tp(ws, p, T_ARG1), tp(ws, p, T_CONV1),
-                      tp(ws, p, T_DCONV1), c.lrn_taps ? tp(ws, p, T_DLRN1) : nullptr, N, 55, 55, 96, c.lrn_k,
-                      c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
+                      tp(ws, p, T_DCONV1), c.lrn_taps ? tp(ws, p, T_DLRN1) : nullptr, (float*)at(ws, p.bias_rows[0]),
+                      N, 55, 55, 96, c.lrn_k, c.lrn_alpha, c.lrn_beta, c.lrn_n, st, T(ALEXNET_KT_POOLLRN1_BWD)));
   {
     const SgdTarget u{master[0], momentum[0], work[0], hy};
     hipStream_t sw = side.fork();
@@ -313,12 +313,17 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   }
   // bias gradients of all eight layers, and their SGD update
   {
+    // layers 1 and 2: the per-row sums left by their pool/LRN backward
     const int dys[8] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5, T_DFC6, T_DFC7, T_DLOGITS};
     BiasJob jobs[8];
     for (int i = 0; i < 8; ++i) {
-      const int64_t rows = i < 5 ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo : N;
-      jobs[i] = BiasJob{tp(ws, p, dys[i]), rows, (int)net.bcount[i], gb(i), master[2 * i + 1],
-                        momentum[2 * i + 1], work[2 * i + 1]};
+      const bool rows_f32 = i < 2;
+      const int64_t rows = rows_f32 ? (int64_t)N * net.conv[i].Ho
+                           : i < 5  ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo
+                                    : N;
+      const void* src = rows_f32 ? (const void*)at(ws, p.bias_rows[i]) : tp(ws, p, dys[i]);
+      jobs[i] = BiasJob{src, rows, (int)net.bcount[i], gb(i), master[2 * i + 1], momentum[2 * i + 1],
+                        work[2 * i + 1], rows_f32};
     }
     HIPCHK(bias_grads_sgd(dt, jobs, 8, hy, cs, (const float*)tp(ws, p, T_ROWLOSS), N, loss, st,
                           T(ALEXNET_KT_BIAS)));

@@ -1653,12 +1653,16 @@ __device__ __forceinline__ void pool_bwd_pair_lds(const T* dyL, const uint8_t* a
 //   3. each unit's LRN backward reads its channel neighbours of a and g from
 //      LDS, applies the ReLU mask and writes da.
 // da therefore equals that of the separate steps.  `dbg`, if not null,
-// receives g.
+// receives g.  `brow`, if not null, receives the row's column sums of da as
+// stored (the bias gradient's share of the row): the stored units go back
+// into LDS, eight threads' runs of pixels per channel group are summed, then
+// the eight runs in order.
 constexpr int PLB_TPB = 512;   // eight waves per row: more loads in flight per LDS byte than four
 template <typename T, int H, bool B075, int Win, int C>
 __global__ void __launch_bounds__(PLB_TPB) k_pool_lrn_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
                                                       const T* __restrict__ a, T* __restrict__ da,
-                                                      T* __restrict__ dbg, float k, float alpha, float beta) {
+                                                      T* __restrict__ dbg, float* __restrict__ brow, float k,
+                                                      float alpha, float beta) {
   constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, cpp = C / 8, units = Win * cpp;
   constexpr int UPT = (units + PLB_TPB - 1) / PLB_TPB;   // units per thread
   static_assert(C % 8 == 0, "pool/LRN backward geometry");
@@ -1715,6 +1719,7 @@ __global__ void __launch_bounds__(PLB_TPB) k_pool_lrn_bwd(const T* __restrict__ 
     }
   }
   __syncthreads();
+  Packed8<T> od[UPT];
 #pragma unroll
   for (int t = 0; t < UPT; ++t) {
     const int u = tid + t * PLB_TPB;
@@ -1722,7 +1727,41 @@ __global__ void __launch_bounds__(PLB_TPB) k_pool_lrn_bwd(const T* __restrict__ 
       const int w = u / cpp, c0 = (u - w * cpp) * 8;
       float o[8];
       lrn_bwd_unit<T, H, B075, C>(arow + w * C, grow + w * C, c0, k, alpha, beta, o);
-      Pack8<T>::store(da + row0 + w * C + c0, o);
+      od[t] = pack8<T>(o);
+      store8<T>(da + row0 + w * C + c0, od[t]);
+    }
+  }
+  if (brow) {   // uniform
+    constexpr int S = 8, L = (Win + S - 1) / S;   // runs of pixels per channel group
+    static_assert(S * C * 4 <= DY_BYTES + ARG_BYTES, "run sums fit the pooled-row staging");
+    float* runs = reinterpret_cast<float*>(lds + 2 * ROW_BYTES);   // [S][C], over the staging no longer read
+    __syncthreads();   // every unit's channel neighbours have been read from arow and grow
+#pragma unroll
+    for (int t = 0; t < UPT; ++t) {
+      const int u = tid + t * PLB_TPB;
+      if (u < units) store8<T>(arow + u * 8, od[t]);   // unit u = (w, c0) sits at w * C + c0
+    }
+    __syncthreads();
+    if (tid < S * cpp) {
+      const int s = tid / cpp, c0 = (tid - s * cpp) * 8;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int w = s * L; w < min(Win, s * L + L); ++w) {
+        float v[8];
+        Pack8<T>::load(arow + w * C + c0, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) runs[s * C + c0 + e] = acc[e];
+    }
+    __syncthreads();
+    for (int c = tid; c < C; c += PLB_TPB) {
+      float sum = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) sum += runs[s * C + c];
+      brow[((size_t)n * Hin + h) * C + c] = sum;
     }
   }
 }
@@ -1754,12 +1793,12 @@ struct LrnPoolFn {
 };
 template <typename T, int Win, int C>
 struct PoolLrnBwdFn {
-  const void* dy; const uint8_t* arg; const void* a; void* da; void* dbg; int N; float k, alpha, beta;
+  const void* dy; const uint8_t* arg; const void* a; void* da; void* dbg; float* brow; int N; float k, alpha, beta;
   hipStream_t st;
   template <int H, bool B075>
   hipError_t operator()() const {
     hipLaunchKernelGGL((k_pool_lrn_bwd<T, H, B075, Win, C>), dim3(N * Win), dim3(PLB_TPB), 0, st, (const T*)dy, arg,
-                       (const T*)a, (T*)da, (T*)dbg, k, alpha, beta);
+                       (const T*)a, (T*)da, (T*)dbg, brow, k, alpha, beta);
     return hipGetLastError();
   }
 };
@@ -1782,20 +1821,25 @@ hipError_t lrn_pool_fwd(DType dt, const void* a, void* y, uint8_t* arg, void* db
 }
 
 
-hipError_t pool_lrn_bwd(DType dt, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg, int N,
-                        int H, int W, int C, float k, float alpha, float beta, int n, hipStream_t st,
-                        const KTimer* kt) {
+hipError_t pool_lrn_bwd(DType dt, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg,
+                        float* bias_rows, int N, int H, int W, int C, float k, float alpha, float beta, int n,
+                        hipStream_t st, const KTimer* kt) {
   // the two layers of the network: 55 x 55 x 96 and 27 x 27 x 256
   const int layer = (H == 55 && W == 55 && C == 96) ? 1 : (H == 27 && W == 27 && C == 256) ? 2 : 0;
   if (!layer) return hipErrorInvalidValue;
   rec_start(kt, st);
   hipError_t e;
   if (layer == 1)
-    e = dt == BF16 ? lrn_dispatch(n / 2, beta, PoolLrnBwdFn<bf16, 55, 96>{dy, arg, a, da, dbg, N, k, alpha, beta, st})
-                   : lrn_dispatch(n / 2, beta, PoolLrnBwdFn<float, 55, 96>{dy, arg, a, da, dbg, N, k, alpha, beta, st});
+    e = dt == BF16
+            ? lrn_dispatch(n / 2, beta, PoolLrnBwdFn<bf16, 55, 96>{dy, arg, a, da, dbg, bias_rows, N, k, alpha, beta, st})
+            : lrn_dispatch(n / 2, beta,
+                           PoolLrnBwdFn<float, 55, 96>{dy, arg, a, da, dbg, bias_rows, N, k, alpha, beta, st});
   else
-    e = dt == BF16 ? lrn_dispatch(n / 2, beta, PoolLrnBwdFn<bf16, 27, 256>{dy, arg, a, da, dbg, N, k, alpha, beta, st})
-                   : lrn_dispatch(n / 2, beta, PoolLrnBwdFn<float, 27, 256>{dy, arg, a, da, dbg, N, k, alpha, beta, st});
+    e = dt == BF16
+            ? lrn_dispatch(n / 2, beta,
+                           PoolLrnBwdFn<bf16, 27, 256>{dy, arg, a, da, dbg, bias_rows, N, k, alpha, beta, st})
+            : lrn_dispatch(n / 2, beta,
+                           PoolLrnBwdFn<float, 27, 256>{dy, arg, a, da, dbg, bias_rows, N, k, alpha, beta, st});
   rec_stop(kt, st);
   return e;
 }
@@ -2166,7 +2210,7 @@ struct BiasArgs1 {
   const void* x[BIAS_MAX];
   float* part[BIAS_MAX];
   int64_t rows[BIAS_MAX], rb[BIAS_MAX];
-  int C[BIAS_MAX], nb[BIAS_MAX];
+  int C[BIAS_MAX], nb[BIAS_MAX], f32[BIAS_MAX];
   int bstart[BIAS_MAX + 1];
   int n;
 };
@@ -2193,7 +2237,10 @@ __global__ void __launch_bounds__(TPB) k_bias_colsum(BiasArgs1 a) {
   for (int q = 1; q < BIAS_MAX; ++q) j += (q < a.n && bid >= a.bstart[q]) ? 1 : 0;
   const int local = bid - a.bstart[j];
   const int ctile = local / a.nb[j], rowblock = local - ctile * a.nb[j];
-  colsum_block<T>(static_cast<const T*>(a.x[j]), a.rows[j], a.C[j], a.rb[j], rowblock, ctile, a.part[j]);
+  if (a.f32[j])
+    colsum_block<float>(static_cast<const float*>(a.x[j]), a.rows[j], a.C[j], a.rb[j], rowblock, ctile, a.part[j]);
+  else
+    colsum_block<T>(static_cast<const T*>(a.x[j]), a.rows[j], a.C[j], a.rb[j], rowblock, ctile, a.part[j]);
 }
 
 template <typename T>
@@ -2257,6 +2304,7 @@ hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& 
     a1.rb[j] = (b.rows + nb - 1) / nb;
     a1.C[j] = b.C;
     a1.nb[j] = nb;
+    a1.f32[j] = b.f32 ? 1 : 0;
     a1.bstart[j] = blocks;
     blocks += nb * cdiv(b.C, COLSUM_CW);
     a2.part[j] = part;

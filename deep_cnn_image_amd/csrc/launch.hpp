@@ -148,10 +148,12 @@ hipError_t lrn_pool_fwd(DType, const void* a, void* y, uint8_t* arg, void* dbg, 
                         float k, float alpha, float beta, int n, hipStream_t, const KTimer* kt = nullptr);
 // Max-pool backward, LRN backward and the preceding ReLU's mask in one pass:
 // dy (pooled gradient) and arg -> da w.r.t. the LRN input a.  `dbg` (may be
-// null) also receives the gradient w.r.t. the LRN output.
-hipError_t pool_lrn_bwd(DType, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg, int N,
-                        int H, int W, int C, float k, float alpha, float beta, int n, hipStream_t,
-                        const KTimer* kt = nullptr);
+// null) also receives the gradient w.r.t. the LRN output.  `bias_rows` (may
+// be null) receives, per row (n, h) of da, the column sums of its stored
+// values, fp32 [N * H][C]: the layer's bias gradient summed over w.
+hipError_t pool_lrn_bwd(DType, const void* dy, const uint8_t* arg, const void* a, void* da, void* dbg,
+                        float* bias_rows, int N, int H, int W, int C, float k, float alpha, float beta, int n,
+                        hipStream_t, const KTimer* kt = nullptr);
 // 3x3/s2 max-pool; flat_out: y written [N][C*Ho*Wo] in (c,h,w) order
 // Pool 5 (3x3 / stride 2) with its output flattened in (c, h, w) order for
 // FC6, and its backward times the ReLU mask of the pool input.  C % 128 == 0.
@@ -170,8 +172,9 @@ hipError_t fc_head(DType, int M, int K, int O, const void* x, const void* w, con
 hipError_t view_mean(const float* p, float* out, int N, int O, hipStream_t);
 // Bias gradients of up to BIAS_MAX layers, grad[c] = sum over the rows of
 // dy[rows][C] (fp32), each followed by the SGD update of the bias (w, v fp32
-// in place; wb the working copy in the compute type).  Partial sums go to
-// `scratch` (bias_grad_scratch_bytes).
+// in place; wb the working copy in the compute type).  dy is in the compute
+// type, or fp32 with `f32` (row partial sums left by the kernel that made the
+// gradient).  Partial sums go to `scratch` (bias_grad_scratch_bytes).
 constexpr int BIAS_MAX = 8;
 struct BiasJob {
   const void* dy;
@@ -181,6 +184,7 @@ struct BiasJob {
   float* w;
   float* v;
   void* wb;
+  bool f32;
 };
 size_t bias_grad_scratch_bytes(const BiasJob* jobs, int n);
 // Also, if rowloss is not null, *loss = mean of rowloss[0..nrow) (fixed order).

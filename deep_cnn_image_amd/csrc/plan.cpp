@@ -168,11 +168,14 @@ int make_plan(const alexnet_cfg* cfg, int mode, Plan* p) {
       part = mx(part, conv_wgrad_part_bytes(net.conv[i]));
       part = mx(part, conv_dgrad_part_bytes(ddt, net.conv[i]));
     }
-    // bias-gradient partials of all eight layers at once
+    // bias-gradient partials of all eight layers at once; layers 1 and 2
+    // start from the per-row sums their pool/LRN backward leaves
+    for (int i = 0; i < 2; ++i) p->bias_rows[i] = a.take((size_t)N * net.conv[i].Ho * net.conv[i].Cout * 4);
     BiasJob bj[8] = {};
     for (int i = 0; i < 8; ++i) {
-      bj[i].rows = i < 5 ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo : N;
+      bj[i].rows = i < 2 ? (int64_t)N * net.conv[i].Ho : i < 5 ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo : N;
       bj[i].C = (int)net.bcount[i];
+      bj[i].f32 = i < 2;
     }
     cs = bias_grad_scratch_bytes(bj, 8);
   }

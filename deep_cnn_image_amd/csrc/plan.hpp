@@ -49,6 +49,7 @@ struct Plan {
   Buf xs2d, w1s, wr[5], wt[5];   // layer-1 blocks, re-laid-out weights
   TapDesc tap[T_COUNT];
   Buf part, colsum;
+  Buf bias_rows[2];   // training: layers 1 and 2's bias gradients per row of dconv (fp32 [N * H][C])
   size_t part_bytes = 0, colsum_bytes = 0;
   size_t total = 0;
 };
