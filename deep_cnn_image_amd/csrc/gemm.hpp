@@ -135,6 +135,18 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   }
 }
 
+// Waits until at most n (0 <= n <= MAX) vector-memory operations of this
+// wave are in flight.
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  if constexpr (MAX > 0) {
+    if (n >= MAX) wait_vmcnt<MAX>();
+    else wait_vmcnt_at_most<MAX - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Calls f(integral_constant<int, I>) for I in the sequence, in order.
 template <int... I, class F>
 __device__ __forceinline__ void unroll_steps(std::integer_sequence<int, I...>, F&& f) {
@@ -863,6 +875,17 @@ template <typename T, int BM, int BN>
 constexpr int gemm_waves_per_simd() { return sizeof(T) == 2 ? 2 : 1; }
 template <typename T, int BM, int BN>
 constexpr int gemm_default_stages() { return 2; }
+// LDS stages of each operand for the read-ahead schedule of bf16 tiles: the
+// A operand (the one gathered from activations: implicit im2col) three, the
+// B operand two, for 96-row tiles (3 A + 2 B slices stay within the 80 KB
+// that leaves room for a second workgroup on the CU); otherwise two each.
+// A slice of A is then requested two slices before it is multiplied instead
+// of one.  Measured: 96 x 128 tiles 10% faster; 128 x 128 tiles, whose 3 + 2
+// slices take the whole 80 KB, 3-6% slower.
+template <typename T, int BM, int BN>
+constexpr int gemm_a_stages() {
+  return sizeof(T) == 2 && BM <= 96 && (3 * BM + 2 * BN) * GEMM_BK * 2 <= 80 * 1024 ? 3 : 2;
+}
 // Read-ahead schedule (see k_gemm) for k-contiguous LDS tiles with wave tiles
 // of up to 18 fragments, where it measured faster; the slice-at-a-time
 // schedule elsewhere (it measured faster with transposing fragment reads and
@@ -872,7 +895,7 @@ constexpr bool gemm_read_ahead() {
   return std::is_same<LA, LayoutKC<bf16>>::value && std::is_same<LB, LayoutKC<bf16>>::value && FM * FN <= 18;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP, int ST = 2>
+template <typename T, int BM, int BN, int WGM, int WGN, class AL, class BL, class EP, int ST = 2, int STB = ST>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd<T, BM, BN>(), gemm_waves_per_simd<T, BM, BN>())))
 k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
@@ -884,13 +907,14 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int A_EL = LA::template tile_elems<BM>(), B_EL = LB::template tile_elems<BN>();
   static_assert(ST >= 2 && (ST == 2 || AL::DMA), "LDS stages: 2, or more with direct-to-LDS operands");
-  constexpr int MAIN_BYTES = ST * (A_EL + B_EL) * (int)sizeof(T);
+  static_assert(STB == ST || (STB == 2 && ST == 3), "B stages: as many as A, or two beside three");
+  constexpr int MAIN_BYTES = (ST * A_EL + STB * B_EL) * (int)sizeof(T);
   constexpr int CST = BN + 4;
   constexpr int EPI_BYTES = WTM * CST * 4;   // one wave row of the tile at a time
   constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   T* As = reinterpret_cast<T*>(smem);
-  T* Bs = As + ST * A_EL;
+  T* Bs = As + ST * A_EL;   // ST A slices, then STB B slices
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave offsets scalar
@@ -941,7 +965,56 @@ k_gemm(AL al, BL bl, EP ep, GemmGrid gg) {
     using MM = Mma<T, FM, FN, LA, LB>;
     constexpr int OPS = AL::NI + BL::NI;   // loads per wave per slice
     constexpr bool RA = gemm_read_ahead<LA, LB, FM, FN>();
-    if constexpr (RA) {
+    static_assert(STB == ST || RA, "fewer B stages only with the read-ahead schedule");
+    if constexpr (RA && STB != ST) {
+      // Read-ahead with three A stages and two B stages.  At the middle of
+      // slice kt, once every wave is done with that slice, B(kt + 2) and then
+      // A(kt + 3) are issued into its buffers.  Loads complete in order, so
+      // waiting for B(kt + 1) (issued one slice earlier, followed only by
+      // A(kt + 2)) also waits for A(kt + 1) and leaves A(kt + 2) in flight.
+      // The prologue issues the same sequence: A(0); B(0), A(1); B(1), A(2).
+      if (kt0 < kt1) {
+        constexpr int NA = AL::NI, NB = BL::NI;
+        static_assert(2 * NA + NB < 64, "vmcnt range");
+        const int ra = wm * WTM, rb = wn * WTN;
+        al.issue(As);
+        int after_b0 = 0;   // loads issued after B(kt0)
+        bl.issue(Bs);
+        if (kt0 + 1 < kt1) { al.issue(As + A_EL); after_b0 += NA; }
+        if (kt0 + 1 < kt1) { bl.issue(Bs + B_EL); after_b0 += NB; }
+        if (kt0 + 2 < kt1) { al.issue(As + 2 * A_EL); after_b0 += NA; }
+        wait_vmcnt_at_most<2 * NA + NB>(after_b0);
+        lds_barrier();
+        typename MM::Half h0, h1;
+        MM::read_half(As, ra, Bs, rb, 0, h0, lane);
+        auto step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
+          constexpr int CA = decltype(cur_c)::value % 3, CB = decltype(cur_c)::value % 2;
+          constexpr int NXA = (CA + 1) % 3, NXB = (CB + 1) % 2;
+          MM::read_half(As + CA * A_EL, ra, Bs + CB * B_EL, rb, 32, h1, lane);
+          MM::mul_half(h0, acc);
+          __builtin_amdgcn_sched_barrier(0);
+          const bool more = kt + 1 < kt1;
+          if (more) {
+            if (kt + 2 < kt1) wait_vmcnt<NA>();   // A(kt + 2) may stay in flight
+            else wait_vmcnt<0>();
+          }
+          lds_barrier();
+          if (kt + 2 < kt1) bl.issue(Bs + CB * B_EL);
+          if (kt + 3 < kt1) al.issue(As + CA * A_EL);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) MM::read_half(As + NXA * A_EL, ra, Bs + NXB * B_EL, rb, 0, h0, lane);
+          MM::mul_half(h1, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = kt0;
+        for (; kt + 5 < kt1; kt += 6)
+          unroll_steps(std::make_integer_sequence<int, 6>{},
+                       [&](auto i) __attribute__((always_inline)) { step(i, kt + decltype(i)::value); });
+        unroll_steps(std::make_integer_sequence<int, 5>{}, [&](auto i) __attribute__((always_inline)) {
+          if (kt + decltype(i)::value < kt1) step(i, kt + decltype(i)::value);
+        });
+      }
+    } else if constexpr (RA) {
       // Read-ahead: slice kt sits in buffer (kt - kt0) % ST and up to ST
       // slices are in flight.  Each k-step's fragments are read while the
       // matrix cores multiply the previous k-step's, so no product waits on

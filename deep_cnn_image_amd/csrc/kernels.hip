@@ -41,11 +41,17 @@ static inline void rec_stop(const KTimer* kt, hipStream_t st) { if (kt) hipEvent
 // =========================================================================
 // GEMM launches
 // =========================================================================
-// ST = 0: the tile's default LDS stage count.
+// ST = 0: the tile's default LDS stages (for direct-to-LDS k-contiguous
+// operands under the read-ahead schedule: three of A and two of B where they
+// fit beside a second workgroup).
 template <typename T, int BM, int BN, int WGM, int WGN, int ST0 = 0, class AL, class BL, class EP>
 static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int N, int K, int groups,
                            int splits, hipStream_t st, const KTimer* kt = nullptr, int strip_n = 0) {
-  constexpr int ST = ST0 ? ST0 : gemm_default_stages<T, BM, BN>();
+  constexpr bool ASYM = ST0 == 0 && AL::DMA &&
+                        gemm_read_ahead<typename AL::Layout, typename BL::Layout, BM / WGM / 16, BN / WGN / 16>() &&
+                        gemm_a_stages<T, BM, BN>() == 3;
+  constexpr int ST = ASYM ? 3 : ST0 ? ST0 : gemm_default_stages<T, BM, BN>();
+  constexpr int STB = ASYM ? 2 : ST;
   GemmGrid gg;
   gg.M = M; gg.N = N; gg.K = K;
   gg.tiles_m = cdiv(M, BM);
@@ -57,7 +63,7 @@ static hipError_t run_gemm(const AL& al, const BL& bl, const EP& ep, int M, int 
   gg.strip_n = strip_n;
   dim3 grid(gg.tiles_m * gg.tiles_n * groups * gg.splits);
   rec_start(kt, st);
-  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP, ST>), grid, dim3(NTHREADS), 0, st, al, bl,
+  hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AL, BL, EP, ST, STB>), grid, dim3(NTHREADS), 0, st, al, bl,
                      ep, gg);
   rec_stop(kt, st);
   return hipGetLastError();
