@@ -5,9 +5,11 @@ inputs resident in HBM.
 Prints one JSON line.  `value` is training images/s over the timed steps.
 Beside it: the forward pass alone at batch 128 (single tower and two-tower),
 per-kernel MFMA / HBM fractions from HIP events recorded around each kernel
-(one untimed diagnostic pass), the roofline figure of the dominant kernel
-measured with HIP events inside the timed region, and the CPU oracle timed on
-a bounded sample of the same workload.
+(one untimed diagnostic pass without the side stream, so that each kernel has
+the GPU to itself), the roofline figure of the dominant kernel measured with
+HIP events inside the timed region (on the stream the kernel runs on; a
+weight-gradient kernel there shares the GPU with the data-gradient chain), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -99,14 +101,15 @@ def kernel_source_sha256():
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from profiles/traffic.json (two rocprofv3
     --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None if
-    the counters were taken on other kernel sources or another kernel."""
+    the counters were taken on other kernel sources or do not cover `kernel`."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
-    if t.get("kernel") != kernel or t.get("source_sha256") != kernel_source_sha256():
+    k = t.get("kernels", {}).get(kernel)
+    if k is None or t.get("source_sha256") != kernel_source_sha256():
         return None
-    return int(t["read_bytes"] + t["write_bytes"])
+    return int(k["read_bytes"] + k["write_bytes"])
 
 
 def cpu_model():
@@ -189,23 +192,25 @@ def main():
     # data-gradient chain (alexnet_train_step_ex)
     side = SideStream(dev)
 
-    def train(i, timers=()):
+    def train(i, timers=(), serial=False):
+        # serial: no side stream, so that every timed kernel has the GPU to itself
         B.alexnet_train_step_ex(sess.cfg, master, mom, work, x, None, 0, 0, labels, h["lr"], h["momentum"],
                                 h["weight_decay"], h["dropout_seed"], i, loss, None, sess.ws, sess.ws_bytes,
-                                stream, side.handle, side.event_handles, list(timers))
+                                stream, 0 if serial else side.handle, () if serial else side.event_handles,
+                                list(timers))
 
     step = 0
     for _ in range(args.warmup):
         train(step); step += 1
     torch.cuda.synchronize()
 
-    # diagnostic pass (untimed): every kernel bracketed by its own events
+    # diagnostic pass (untimed, serial): every kernel bracketed by its own events
     diag_steps = 3
     names = [k for k in B.KERNELS if k != "RGB_PCA"]   # every kernel of the training step
     evs = [new_events(len(names)) for _ in range(diag_steps)]
     for d in range(diag_steps):
         train(step, [(B.KT[nm], evs[d][j][0].cuda_event, evs[d][j][1].cuda_event)
-                     for j, nm in enumerate(names)])
+                     for j, nm in enumerate(names)], serial=True)
         step += 1
     torch.cuda.synchronize()
     per_kernel = {}
@@ -215,7 +220,8 @@ def main():
             per_kernel[nm] = sum(ms) / len(ms)
     dominant = max(per_kernel, key=per_kernel.get)
 
-    # timed region: events only around the dominant kernel
+    # timed region: events only around the dominant kernel, on the stream it
+    # runs on (the order of the step is the same as without them)
     tev = new_events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -270,15 +270,13 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
   // chain reads what they write: given a side stream, each is forked onto it
   // once its output gradient is complete, so it runs beside the rest of the
   // backward pass.  Not when a data gradient of the step splits over k (small
-  // batches): both would use the split-K region of the workspace.  Nor when
-  // a caller times one of the kernels of that stretch (the conv gradient
-  // GEMMs, the pool/LRN backward kernels, the bias kernels): a kernel timed
-  // on its own runs with the GPU to itself, so its time is its own.
+  // batches): both would use the split-K region of the workspace.  Timers
+  // change nothing in this order: a timed kernel's events go on the stream it
+  // runs on, and its time then includes the GPU it shares with the other
+  // stream's kernels.
   bool concurrent = side_st != nullptr;
   for (int i = 1; i < 5; ++i)
     if (conv_dgrad_part_bytes(dt, net.conv[i]) != 0) concurrent = false;
-  for (int k = ALEXNET_KT_CONV5_WGRAD; k <= ALEXNET_KT_BIAS; ++k)
-    if (T.on[k]) concurrent = false;
   SideFork side(st, concurrent ? side_st : nullptr, side_ev);
   for (int i = 4; i >= 2; --i) {
     const ConvShape& s = net.conv[i];

@@ -316,17 +316,19 @@ int alexnet_rgb_pca_timed(const alexnet_cfg* cfg, const void* images, int32_t n,
  *                kernel of either chain reads what the other writes, and every
  *                reduction runs in a fixed order.  The step stays serial when
  *                a conv data gradient splits over k (small batches share the
- *                split-K scratch with the weight gradients) or when a timer
- *                names a kernel from the conv gradients through the bias
- *                kernels.  NULL: everything runs on `stream` in order.
+ *                split-K scratch with the weight gradients).  NULL:
+ *                everything runs on `stream` in order.
  *   ex->events   ALEXNET_SIDE_EVENTS caller-created hipEvent_t handles (timing
  *                may be disabled), all non-null when side_stream is set;
  *                recorded and waited on by every call, never created or
  *                destroyed by the library.  Reusing them across calls is safe:
  *                a stream wait binds to the record enqueued before it.  Two
  *                calls in flight at once need distinct sets.
- *   ex->timers, ex->n_timers  as for alexnet_train_step_timed; a timed kernel
- *                that runs on the side stream has its events recorded there.
+ *   ex->timers, ex->n_timers  as for alexnet_train_step_timed; timers do not
+ *                change the order above.  A timed kernel that runs on the
+ *                side stream has its events recorded there, and the time of
+ *                any kernel then includes the GPU it shares with the kernels
+ *                of the other stream (for isolated times: no side stream).
  * Returns ALEXNET_E_ARG if side_stream == stream, ALEXNET_E_NULL if an event
  * is missing. */
 #define ALEXNET_SIDE_EVENTS 10
