@@ -73,14 +73,16 @@ def kernel_work(kt, n, groups, train=True):
         # LRN + max-pool fused: LRN input read once, pooled values and argmax written
         "LRNPOOL1_FWD": e * act["55x96"] + (e + 1) * act["27x96"],
         "LRNPOOL2_FWD": e * act["27x256"] + (e + 1) * act["13x256"],
-        # pool, LRN and ReLU backward fused: pooled gradient, argmax and LRN input read, da written
-        "POOLLRN1_BWD": (e + 1) * act["27x96"] + 2 * e * act["55x96"],
-        "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"],
+        # pool, LRN and ReLU backward fused: pooled gradient, argmax and LRN input
+        # read, da written, and (training) da's fp32 column sums per row
+        "POOLLRN1_BWD": (e + 1) * act["27x96"] + 2 * e * act["55x96"] + (4 * n * 55 * 96 if train else 0),
+        "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"] + (4 * n * 27 * 256 if train else 0),
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
-        # bias gradients: every layer's output gradient read once (the partial
-        # sums and the 22 B per bias of the update are below 0.1%)
-        "BIAS": e * (act["55x96"] + act["27x256"] + 2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
+        # bias gradients: layers 1 and 2 from their per-row fp32 sums, the other
+        # layers' output gradients read once (the block partials and the 22 B
+        # per bias of the update are below 0.2%)
+        "BIAS": 4 * n * (55 * 96 + 27 * 256) + e * (2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
     }
     return "hbm", float(table[kt])
 
