@@ -304,9 +304,218 @@ struct Conv1FwdFn {
   }
 };
 
+// ---- layer 1 forward, bf16: direct convolution over block rows kept in LDS
+// In the space-to-depth form layer 1 has K = 432 (9 taps x 48 values) per
+// output and 96 outputs per pixel.  An implicit-GEMM workgroup would run only
+// 7 k-slices, so filling and draining its pipeline takes much of its life, and
+// it would gather each input block once per tap.  Here one workgroup per CU
+// stays resident.  It copies W' into LDS once, and its four waves take their
+// half of it (48 output channels x 432, as MFMA fragments) into registers for
+// the whole launch.  They then walk tiles of 4 output rows x 55 columns (220
+// pixels) of one image.  A tile's 6 input block rows go into LDS with
+// direct-to-LDS loads, each block's 48 values in a 112-byte slot whose last
+// 16-byte granule is loaded out of range (as zeros), into one of two buffers
+// while the previous tile is multiplied from the other.  Each product takes
+// the weights as the first MFMA operand (16 channels x 32 k) and the block
+// rows as the second (32 k x 16 pixels), so a lane ends with 4 consecutive
+// channels of one pixel.  The first product of a tile starts from the bias
+// instead of zero; ReLU and rounding are applied in registers.  The next
+// tile's loads and this tile's 8-byte output runs are issued between the
+// products, a few per k-step, instead of in bursts that every CU would issue
+// at the same moment.  k runs in the same order as in the implicit GEMM, 32 at
+// a time; the 14th step's upper half (k >= 432) has zero weights and reads the
+// zero granules.
+constexpr int C1_ROWS = 4;                               // output rows per tile
+constexpr int C1_TPI = (55 + C1_ROWS - 1) / C1_ROWS;     // tiles per image
+constexpr int C1_PROWS = C1_ROWS + 2;                    // input block rows per tile
+constexpr int C1_SLOT = 7;                               // 16-byte granules per block slot (6 + zeros)
+constexpr int C1_GRAN = C1_PROWS * S2D_B * C1_SLOT;      // granules per tile
+constexpr int C1_NI = (C1_GRAN + 63) / 64;               // direct-to-LDS loads per tile (1 KB each)
+constexpr int C1_NIW = (C1_NI + 3) / 4;                  // per wave, at most
+constexpr int C1_BUF = C1_NI * 64 * 8;                   // bf16 elements per block-row buffer
+constexpr int C1_KS = (S2D_K + 31) / 32;                 // k-steps of 32
+constexpr int C1_FM = 7, C1_FN = 3;                      // per wave: 7 x 16 pixels, 3 x 16 channels
+constexpr int C1_WL = (int)(S2D_W_ELEMS * 2 / 1024);     // direct-to-LDS loads of W' (1 KB each)
+constexpr int C1_WX = (int)S2D_W_ELEMS - C1_BUF;         // LDS past the second buffer that W' takes
+constexpr int C1_GRID = 256;                             // one workgroup per CU
+static_assert(2 * C1_FM * 16 >= C1_ROWS * 55 && 2 * C1_FN * 16 == 96, "four waves cover a tile");
+static_assert(S2D_C % 8 == 0, "an 8-value k run stays within one tap");
+static_assert(C1_NIW <= C1_KS && C1_FM <= C1_KS, "one load and one row of stores per k-step at most");
+static_assert(S2D_W_ELEMS * 2 % 1024 == 0 && C1_WX > 0, "W' goes through the second buffer and past it");
+static_assert(((C1_PROWS - 1) * S2D_B + S2D_B - 1) * S2D_C * 2 + S2D_C * 2 < 65536, "block offsets fit 16 bits");
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16* __restrict__ bias,
+            bf16* __restrict__ y, int Nimg) {
+  // two block-row buffers; W' passes through the second one and the space after it at the start
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C1_BUF + C1_WX];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  // Workgroups are dealt round-robin over the eight XCDs; XCD x takes a
+  // contiguous run of the tile order, so that neighbouring tiles, which share
+  // two block rows, share an L2.
+  const int tiles = Nimg * C1_TPI;
+  const int x = blockIdx.x & 7, per_x = gridDim.x >> 3;
+  const int tq = tiles >> 3, tr = tiles & 7;
+  const int t_end = x * tq + min(x, tr) + tq + (x < tr ? 1 : 0);
+  int t = x * tq + min(x, tr) + (blockIdx.x >> 3);
+  if (t >= t_end) return;
+
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xs, (uint32_t)((int64_t)Nimg * S2D_ELEMS * 2));
+  // Load i of this wave (j = wave + 4 i) fills granules 64 j .. 64 j + 63 of a
+  // buffer.  This lane's granule holds block row `row` of the tile at byte
+  // offset rel from the tile's first block, packed as (row << 16) | rel, or is
+  // zero (row 0xFFFF): a pad granule, or past the tile.
+  uint32_t drel[C1_NIW];
+#pragma unroll
+  for (int i = 0; i < C1_NIW; ++i) {
+    const int gidx = (wave + 4 * i) * 64 + lane;
+    const int slot = gidx / C1_SLOT, g = gidx - slot * C1_SLOT;
+    const int row = slot / S2D_B, bw = slot - row * S2D_B;
+    const bool ok = gidx < C1_GRAN && g < S2D_C / 8;
+    drel[i] = ok ? ((uint32_t)row << 16) | (uint32_t)(((row * S2D_B + bw) * S2D_C + g * 8) * 2) : 0xFFFF0000u;
+  }
+  auto dma = [&](int i, uint32_t base, int r0, bf16* buf) {
+    const int j = wave + 4 * i;
+    if (j < C1_NI) {
+      const uint32_t d = drel[i];
+      const uint32_t off = (int)(d >> 16) + r0 < S2D_B ? base + (d & 0xFFFFu) : BUF_OOB;
+      dma16(rs, off, buf + j * 64 * 8);
+    }
+  };
+  auto tile_base = [](int tile, int& r0) {
+    const int n = tile / C1_TPI;
+    r0 = (tile - n * C1_TPI) * C1_ROWS;
+    return (uint32_t)(((int64_t)n * S2D_B + r0) * S2D_B * S2D_C * 2);
+  };
+  {
+    int r0;
+    const uint32_t base = tile_base(t, r0);
+#pragma unroll
+    for (int i = 0; i < C1_NIW; ++i) dma(i, base, r0, lds);
+    // W' [96][432] as it is in memory
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(w, (uint32_t)(S2D_W_ELEMS * 2));
+    for (int j = wave; j < C1_WL; j += 4) dma16(rw, (uint32_t)(j * 1024 + lane * 16), lds + C1_BUF + j * 512);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+  // weight fragments (j, s): channel wn*48 + 16 j + (lane & 15), k = 32 s + 8 (lane >> 4) .. + 7
+  bf16x8_t wf[C1_FN][C1_KS];
+#pragma unroll
+  for (int j = 0; j < C1_FN; ++j)
+#pragma unroll
+    for (int s = 0; s < C1_KS; ++s) {
+      const int co = wn * 48 + j * 16 + (lane & 15), k = s * 32 + (lane >> 4) * 8;
+      wf[j][s] = k < S2D_K ? *reinterpret_cast<const bf16x8_t*>(lds + C1_BUF + co * S2D_K + k)
+                           : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+    }
+  // this lane's 4 output channels per n-fragment, and their biases as the
+  // accumulator a tile's first product starts from
+  const int c0 = wn * 48 + (lane >> 4) * 4;
+  f32x4_t bc[C1_FN];
+#pragma unroll
+  for (int j = 0; j < C1_FN; ++j)
+    bc[j] = f32x4_t{bf2f(bias[c0 + j * 16]), bf2f(bias[c0 + j * 16 + 1]), bf2f(bias[c0 + j * 16 + 2]),
+                    bf2f(bias[c0 + j * 16 + 3])};
+  // LDS element offsets: of the pixel's top-left block per m-fragment, of the tap and channel run per k-step
+  int poff[C1_FM];
+#pragma unroll
+  for (int i = 0; i < C1_FM; ++i) {
+    const int px = min(wm * C1_FM * 16 + i * 16 + (lane & 15), C1_ROWS * 55 - 1);
+    const int lr = px / 55;
+    poff[i] = (lr * S2D_B + px - lr * 55) * C1_SLOT * 8;
+  }
+  int toff[C1_KS];
+#pragma unroll
+  for (int s = 0; s < C1_KS; ++s) {
+    const int k = s * 32 + (lane >> 4) * 8;
+    const int tap = k / S2D_C, ci = k - tap * S2D_C, kh = tap / 3, kw = tap - kh * 3;
+    toff[s] = k < S2D_K ? (kh * S2D_B + kw) * C1_SLOT * 8 + ci : S2D_C;   // S2D_C: the slot's zero granule
+  }
+  lds_barrier();   // every wave has its fragments of W' before the second buffer is loaded again
+
+  // the previous tile's outputs, rounded, stored during this tile's k-steps
+  uint2 outv[C1_FM][C1_FN];
+  bf16* yprev = nullptr;
+  int npx_prev = 0;
+  auto store_row = [&](int i, int j) {
+    const int px = wm * C1_FM * 16 + i * 16 + (lane & 15);
+    if (px < npx_prev) *reinterpret_cast<uint2*>(yprev + (int64_t)px * 96 + j * 16) = outv[i][j];
+  };
+
+  for (int it = 0;; ++it) {
+    const bf16* cur = lds + (it & 1) * C1_BUF;
+    bf16* nxt = lds + ((it + 1) & 1) * C1_BUF;
+    wait_vmcnt<0>();
+    lds_barrier();   // tile t's block rows are in; every wave is done with the other buffer
+    const int tn = t + per_x;
+    const bool more = tn < t_end;
+    int nr0 = 0;
+    const uint32_t nbase = more ? tile_base(tn, nr0) : 0u;
+    const bool stores = yprev != nullptr;
+
+    f32x4_t acc[C1_FM][C1_FN];
+    bf16x8_t a[2][C1_FM];
+#pragma unroll
+    for (int i = 0; i < C1_FM; ++i) a[0][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + toff[0]);
+    // the next k-step's fragments are read before this one's products, which
+    // then cover the LDS latency (one wave per SIMD: no other wave would)
+#pragma unroll
+    for (int s = 0; s < C1_KS; ++s) {
+      if (s + 1 < C1_KS) {
+#pragma unroll
+        for (int i = 0; i < C1_FM; ++i)
+          a[(s + 1) & 1][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + toff[s + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < C1_FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C1_FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j][s], a[s & 1][i], s == 0 ? bc[j] : acc[i][j],
+                                                              0, 0, 0);
+        if (i == 0 && s < C1_NIW && more) dma(s, nbase, nr0, nxt);
+        if (i >= 1 && i <= C1_FN && s < C1_FM && stores) store_row(s, i - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    const int n = t / C1_TPI, r0 = (t - n * C1_TPI) * C1_ROWS;
+    npx_prev = min(C1_ROWS, 55 - r0) * 55;
+    yprev = y + ((int64_t)n * 3025 + r0 * 55) * 96 + c0;
+#pragma unroll
+    for (int i = 0; i < C1_FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C1_FN; ++j) {
+        const f32x4_t u = acc[i][j];
+        outv[i][j] = make_uint2(f2bf2(u[0] > 0.f ? u[0] : 0.f, u[1] > 0.f ? u[1] : 0.f),
+                                f2bf2(u[2] > 0.f ? u[2] : 0.f, u[3] > 0.f ? u[3] : 0.f));
+      }
+    t = tn;
+    if (!more) break;
+  }
+#pragma unroll
+  for (int i = 0; i < C1_FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C1_FN; ++j) store_row(i, j);
+}
+
+static hipError_t conv1_fwd_direct(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y,
+                                   hipStream_t st, const KTimer* kt) {
+  // byte offsets into the staged input are 32-bit, below the out-of-range marker
+  if (Nimg < 1 || (int64_t)Nimg * S2D_ELEMS * 2 >= (int64_t)BUF_OOB) return hipErrorInvalidValue;
+  rec_start(kt, st);
+  hipLaunchKernelGGL(k_conv1_fwd, dim3(C1_GRID), dim3(256), 0, st, (const bf16*)xs, (const bf16*)ws2d,
+                     (const bf16*)b1, (bf16*)y, Nimg);
+  rec_stop(kt, st);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t conv1_fwd_t(const void* xs, int Nimg, const void* ws2d, const void* b1, void* y, float* part,
                               size_t part_bytes, hipStream_t st, const KTimer* kt) {
+  if constexpr (std::is_same<T, bf16>::value) return conv1_fwd_direct(xs, Nimg, ws2d, b1, y, st, kt);
   return by_tile<T>(Nimg * 3025, 96, 1, Conv1FwdFn<T>{xs, Nimg, ws2d, b1, y, part, part_bytes, st, kt});
 }
 
@@ -361,6 +570,7 @@ size_t conv_fwd_part_bytes(DType dt, const ConvShape& s) {
   return S > 1 ? (size_t)S * s.groups * M * Cog * sizeof(float) : 0;
 }
 size_t conv1_fwd_part_bytes(DType dt, int Nimg) {
+  if (dt == BF16) return 0;   // k_conv1_fwd: no split
   const int S = conv_gemm_splits(dt, Nimg * 3025, 96, S2D_K, 1);
   return S > 1 ? (size_t)S * Nimg * 3025 * 96 * sizeof(float) : 0;
 }

@@ -83,8 +83,10 @@ hipError_t rgb_pca(DType, const void* src, int n, int H, int W, float* eigval, f
 constexpr size_t S2D_ELEMS = 57 * 57 * 48;   // per image
 constexpr size_t S2D_W_ELEMS = 96 * 432;
 
-// y NHWC [N][55][55][96] = relu(conv1 + b).  part: split-K partials, at
-// least conv1_fwd_part_bytes (0 unless the batch is too small to fill the chip).
+// y NHWC [N][55][55][96] = relu(conv1 + b).  bf16: a direct convolution with
+// the block rows in LDS (no partials); fp32: an implicit GEMM whose split-K
+// partials go to part, at least conv1_fwd_part_bytes (0 unless the batch is
+// too small to fill the chip).
 hipError_t conv1_fwd(DType, const void* xs, int Nimg, const void* ws, const void* b1, void* y, float* part,
                      size_t part_bytes, hipStream_t, const KTimer* kt = nullptr);
 // NHWC conv + bias + ReLU (layers 2-5); part as for conv1_fwd, at least
