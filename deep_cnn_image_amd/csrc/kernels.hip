@@ -637,7 +637,9 @@ size_t conv_wgrad_part_bytes(const ConvShape& s) {
   const int tiles = cdiv(Cog, 128) * cdiv(N, 128) * s.groups;
   return (size_t)s.groups * wgrad_splits(tiles, P) * Cog * N * sizeof(float);
 }
-size_t conv1_wgrad_part_bytes(int Nimg) {
+static int64_t conv1_wgrad_direct_splits(int Nimg);
+size_t conv1_wgrad_part_bytes(DType dt, int Nimg) {
+  if (dt == BF16) return (size_t)conv1_wgrad_direct_splits(Nimg) * 96 * S2D_K * sizeof(float);
   const int tiles = cdiv(96, 128) * cdiv(S2D_K, 128);
   return (size_t)wgrad_splits(tiles, Nimg * 3025) * 96 * S2D_K * sizeof(float);
 }
@@ -715,6 +717,8 @@ __global__ void __launch_bounds__(TPB) k_wgrad_reduce(const float* __restrict__ 
   if (live) {
     const float* p = part + ((int64_t)g * S * Mg + col) * Np + r0;
     const int64_t ss = (int64_t)Mg * Np;
+    // eight loads in flight; the adds stay in split order
+#pragma unroll 8
     for (int s = j; s < S; s += WR_G) {
       const float4 q = *reinterpret_cast<const float4*>(p + s * ss);
       acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
@@ -822,10 +826,241 @@ static hipError_t conv1_wgrad_t(int Nimg, const void* dy, const void* xs, float*
   return hipGetLastError();
 }
 
+// ---- layer 1 weight gradient, bf16: direct, with dY and the block rows in LDS
+// dW'[co][k] = sum over pixels p of dY[p][co] * X'(p)[k], k = tap*48 + ci the
+// space-to-depth order.  As an implicit GEMM (M = 96, N = 432, K = all
+// pixels) every split reloads its pixels' dY once per 128 columns of N and
+// gathers X' once per tap.  Here one workgroup per CU stays resident with all
+// of dW' in its accumulators (eight waves, two per SIMD, each 3 or 4 of the 27
+// fragments of 16 k x 96 channels) and walks the same tiles as the forward kernel: 4 output rows x 55
+// columns of one image.  A tile's dY rows (220 pixels, then 4 zero rows) and
+// its 6 input block rows are copied contiguously into LDS with direct-to-LDS
+// loads, into one of two buffers while the previous tile is multiplied from
+// the other; the first tile is copied with direct-to-LDS loads, later ones
+// through registers between the products (see below).  The pixels are the
+// contraction, 32 at a time: both operands are read as MFMA fragments with the
+// transposing LDS read (lane t reads 4 values of one row; the 16 lanes of a
+// group cover 4 pixel rows), the block rows as the first operand so that a
+// lane ends with 4 consecutive k of one channel.  Each workgroup then writes
+// its partial dW' (fp32) and k_wgrad_reduce sums the partials in workgroup
+// order.  Batches whose dY exceeds 31-bit offsets run as image slices, each
+// with its own partials.
+constexpr int W1_PXT = 224;                                       // dY rows per tile in LDS (220, then zeros)
+constexpr int W1_DYE = W1_PXT * 96;                               // bf16 elements of the dY tile
+constexpr int W1_DYL = W1_DYE * 2 / 1024;                         // its direct-to-LDS loads
+constexpr int W1_PTL = (C1_PROWS * S2D_B * S2D_C * 2 + 1023) / 1024;   // block-row loads
+constexpr int W1_NL = W1_DYL + W1_PTL;                            // loads per tile
+constexpr int W1_WAVES = 8;                                       // two waves per SIMD
+constexpr int W1_NLW = (W1_NL + W1_WAVES - 1) / W1_WAVES;         // per wave, at most
+constexpr int W1_BUF = W1_NL * 512;                               // bf16 elements per buffer
+constexpr int W1_KF = S2D_K / 16;                                 // 27 fragments of 16 k
+constexpr int W1_KFW = (W1_KF + W1_WAVES - 1) / W1_WAVES;         // per wave, at most
+constexpr int W1_CF = 96 / 16;                                    // 6 fragments of 16 channels
+constexpr int W1_CH = W1_PXT / 32;                                // pixel chunks of 32 per tile
+constexpr int W1_MAXIMG = (int)(((int64_t)1 << 31) / (3025 * 96 * 2));   // images per slice
+static_assert(W1_DYE * 2 % 1024 == 0 && S2D_K % 16 == 0 && S2D_C % 16 == 0, "fragment shapes");
+static_assert(W1_PXT >= C1_ROWS * 55 && W1_PXT % 32 == 0, "tile shapes");
+static_assert(2 * W1_BUF * 2 <= 160 * 1024, "two buffers fit in LDS");
+
+static int w1_grid(int Nimg) { return std::min(256, (Nimg * C1_TPI + 7) / 8 * 8); }
+
+__global__ void __launch_bounds__(64 * W1_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_conv1_wgrad(const bf16* __restrict__ dy, const bf16* __restrict__ xs, float* __restrict__ part, int Nimg) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * W1_BUF];   // per buffer: [dY tile][block rows]
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // XCD x takes a contiguous run of the tile order (as in the forward kernel)
+  const int tiles = Nimg * C1_TPI;
+  const int x = blockIdx.x & 7, per_x = gridDim.x >> 3;
+  const int tq = tiles >> 3, tr = tiles & 7;
+  const int t_end = x * tq + min(x, tr) + tq + (x < tr ? 1 : 0);
+  int t = x * tq + min(x, tr) + (blockIdx.x >> 3);
+
+  const __amdgpu_buffer_rsrc_t rsy = buf_rsrc(dy, (uint32_t)((int64_t)Nimg * 3025 * 96 * 2));
+  const __amdgpu_buffer_rsrc_t rsx = buf_rsrc(xs, (uint32_t)((int64_t)Nimg * S2D_ELEMS * 2));
+  // a tile's dY bytes (its valid pixels only; the rest of the 224 rows load
+  // as zeros) and its block rows (6 rows from its first; past the input they
+  // load as zeros, past the image they hold the next image's rows, which meet
+  // only zero dY rows)
+  auto geo = [](int tile, uint32_t& dbase, uint32_t& dlim, uint32_t& pbase) {
+    const int n = tile / C1_TPI, r0 = (tile - n * C1_TPI) * C1_ROWS;
+    dbase = (uint32_t)(((int64_t)n * 3025 + r0 * 55) * 96 * 2);
+    dlim = (uint32_t)(min(C1_ROWS, 55 - r0) * 55 * 96 * 2);
+    pbase = (uint32_t)(((int64_t)n * S2D_B + r0) * S2D_B * S2D_C * 2);
+  };
+  // load i of this wave, j = wave + W1_WAVES i: 1 KB at granule 64 j of the buffer
+  auto load = [&](int i, uint32_t dbase, uint32_t dlim, uint32_t pbase, bf16* buf) {
+    const int j = wave + W1_WAVES * i;
+    if (j < W1_DYL) {
+      const uint32_t o = (uint32_t)(j * 1024 + lane * 16);
+      dma16(rsy, o < dlim ? dbase + o : BUF_OOB, buf + j * 512);
+    } else if (j < W1_NL) {
+      dma16(rsx, pbase + (uint32_t)((j - W1_DYL) * 1024 + lane * 16), buf + j * 512);
+    }
+  };
+  if (t < t_end) {
+    uint32_t dbase, dlim, pbase;
+    geo(t, dbase, dlim, pbase);
+#pragma unroll
+    for (int i = 0; i < W1_NLW; ++i) load(i, dbase, dlim, pbase, lds);
+  }
+  // Later tiles come in through registers: load i of this wave fetches 16
+  // bytes per lane and writes them to the same place in LDS as the
+  // direct-to-LDS copy would, two chunks later.  (The compiler would make every
+  // transposing LDS read wait for all direct-to-LDS loads issued before it, as
+  // it cannot tell the buffers apart, and a chunk's reads follow the loads.)
+  // No branches around these loads, so that the compiler can count them and
+  // wait for each one alone: a wave short of a load repeats the previous
+  // wave's last one (the same bytes to the same place), and after the last
+  // tile the loads still run (zeros and rows of the first image, into the
+  // buffer nothing reads again).
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  auto slot_of = [&](int i) { return min(wave + W1_WAVES * i, W1_NL - 1); };
+  auto fetch = [&](int i, uint32_t dbase, uint32_t dlim, uint32_t pbase) {
+    const int j = slot_of(i);
+    const bool in_dy = j < W1_DYL;
+    const uint32_t od = (uint32_t)(j * 1024 + lane * 16), op = (uint32_t)((j - W1_DYL) * 1024 + lane * 16);
+    const uint32_t off = in_dy ? (od < dlim ? dbase + od : BUF_OOB) : pbase + op;
+    return __builtin_amdgcn_raw_buffer_load_b128(in_dy ? rsy : rsx, off, 0, 0);
+  };
+
+  // transposing-read addresses (elements within a buffer).  Lane (g, q) of
+  // chunk c, half h reads pixel row 32 c + 8 g + 4 h + q / 4 at 4 (q % 4) past
+  // the fragment's first column.
+  const int g = lane >> 4, q = lane & 15;
+  int dyo[W1_CH][2], pso[W1_CH][2];
+#pragma unroll
+  for (int c = 0; c < W1_CH; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int px = 32 * c + 8 * g + 4 * h + (q >> 2);
+      const int lr = px / 55, col = px - lr * 55;
+      dyo[c][h] = px * 96 + 4 * (q & 3);
+      pso[c][h] = W1_DYE + (lr * S2D_B + col) * S2D_C + 4 * (q & 3);
+    }
+  // k-fragment i of this wave: kf = wave + W1_WAVES i, tap kf / 3, channels (kf % 3) * 16 ..
+  int ko[W1_KFW];
+#pragma unroll
+  for (int i = 0; i < W1_KFW; ++i) {
+    const int kf = min(wave + W1_WAVES * i, W1_KF - 1), tap = kf / 3, kh = tap / 3, kw = tap - kh * 3;
+    ko[i] = (kh * S2D_B + kw) * S2D_C + (kf - tap * 3) * 16;
+  }
+  auto trd = [](const bf16* p, int o0, int o1) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + o0));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + o1));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const bool full = wave + W1_WAVES * (W1_KFW - 1) < W1_KF;   // this wave's last k-fragment exists
+
+  f32x4_t acc[W1_KFW][W1_CF];
+#pragma unroll
+  for (int i = 0; i < W1_KFW; ++i)
+#pragma unroll
+    for (int j = 0; j < W1_CF; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; t < t_end; ++it) {
+    const bf16* cur = lds + (it & 1) * W1_BUF;
+    bf16* nxt = lds + ((it + 1) & 1) * W1_BUF;
+    wait_vmcnt<0>();
+    lds_barrier();   // tile t is in; every wave is done with the other buffer
+    const int tn = t + per_x;
+    const bool more = tn < t_end;
+    uint32_t dbase = 0, dlim = 0, pbase = 0;
+    if (more) geo(tn, dbase, dlim, pbase);
+
+    bf16x8_t fa[2][W1_KFW], fb[2][W1_CF];
+    // fragment f of a chunk: f < W1_CF the dY fragments (every product of the
+    // chunk needs them), then the k-fragments in the order of use
+    auto read_frag = [&](int c, int b, int f) {
+      if (f < W1_CF) {
+        fb[b][f] = trd(cur, dyo[c][0] + f * 16, dyo[c][1] + f * 16);
+      } else {
+        const int i = f - W1_CF;
+        if (i < W1_KFW - 1 || full) fa[b][i] = trd(cur, pso[c][0] + ko[i], pso[c][1] + ko[i]);
+      }
+    };
+#pragma unroll
+    for (int f = 0; f < W1_CF + W1_KFW; ++f) read_frag(0, 0, f);
+    // The next chunk's fragments are read between this chunk's products, a
+    // few per group of products: at most 15 LDS reads may be in flight, so a
+    // chunk's 20 reads issued at once would stall the products behind them.
+    // The next tile's data: LPC loads per chunk from chunk 0, each written to
+    // LDS two chunks after it was issued.
+    constexpr int FPG = (W1_CF + W1_KFW + W1_KFW - 1) / W1_KFW;   // fragments read per group
+    constexpr int LPC = (W1_NLW + W1_CH - 3) / (W1_CH - 2);
+    static_assert(LPC <= W1_KFW, "loads per group");
+    v4u stage[3][LPC];
+#pragma unroll
+    for (int c = 0; c < W1_CH; ++c) {
+#pragma unroll
+      for (int i = 0; i < W1_KFW; ++i) {
+        if (i < W1_KFW - 1 || full) {
+#pragma unroll
+          for (int j = 0; j < W1_CF; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[c & 1][i], fb[c & 1][j], acc[i][j], 0, 0, 0);
+        }
+        if (c + 1 < W1_CH) {
+#pragma unroll
+          for (int f = FPG * i; f < FPG * i + FPG; ++f)
+            if (f < W1_CF + W1_KFW) read_frag(c + 1, (c + 1) & 1, f);
+        }
+        if (i < LPC) {
+          const int lw = (c - 2) * LPC + i;   // written in this group: load issued two chunks ago
+          if (c >= 2 && lw < W1_NLW) *reinterpret_cast<v4u*>(nxt + slot_of(lw) * 512 + lane * 8) = stage[(c - 2) % 3][i];
+          const int li = c * LPC + i;         // issued in this group
+          if (li < W1_NLW) stage[c % 3][i] = fetch(li, dbase, dlim, pbase);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    t = tn;
+  }
+
+  // partial dW' of this workgroup: lane (g, q) holds k = 16 kf + 4 g .. + 3 of channel 16 j + q
+  float* pw = part + (int64_t)blockIdx.x * 96 * S2D_K;
+#pragma unroll
+  for (int i = 0; i < W1_KFW; ++i) {
+    if (i < W1_KFW - 1 || full) {
+      const int kf = wave + W1_WAVES * i;
+#pragma unroll
+      for (int j = 0; j < W1_CF; ++j)
+        *reinterpret_cast<f32x4_t*>(pw + (j * 16 + q) * S2D_K + kf * 16 + g * 4) = acc[i][j];
+    }
+  }
+}
+
+static int64_t conv1_wgrad_direct_splits(int Nimg) {
+  int64_t s = 0;
+  for (int n0 = 0; n0 < Nimg; n0 += W1_MAXIMG) s += w1_grid(std::min(W1_MAXIMG, Nimg - n0));
+  return s;
+}
+
+static hipError_t conv1_wgrad_direct(int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
+                                     float* gw, const SgdTarget& u, hipStream_t st, const KTimer* kt) {
+  const int64_t S = conv1_wgrad_direct_splits(Nimg);
+  if (Nimg < 1 || (size_t)S * 96 * S2D_K * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  rec_start(kt, st);
+  float* pp = part;
+  for (int n0 = 0; n0 < Nimg; n0 += W1_MAXIMG) {
+    const int n = std::min(W1_MAXIMG, Nimg - n0);
+    const int G = w1_grid(n);
+    hipLaunchKernelGGL(k_conv1_wgrad, dim3(G), dim3(64 * W1_WAVES), 0, st, (const bf16*)dy + (int64_t)n0 * 3025 * 96,
+                       (const bf16*)xs + (int64_t)n0 * S2D_ELEMS, pp, n);
+    pp += (int64_t)G * 96 * S2D_K;
+  }
+  hipLaunchKernelGGL((k_wgrad_reduce<bf16>), wgrad_reduce_grid(96 * S2D_K / 4), dim3(TPB), 0, st, part, 1, (int)S,
+                     96, S2D_K, 3, 11, 11, 2, gw, u.w, u.v, (bf16*)u.wb, u.hy.lr, u.hy.mom, u.hy.wdlr);
+  rec_stop(kt, st);
+  return hipGetLastError();
+}
+
 hipError_t conv1_wgrad(DType dt, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
                        float* gw, const SgdTarget* u, hipStream_t st, const KTimer* kt) {
   const SgdTarget& t = u ? *u : kNoSgd;
-  return dt == BF16 ? conv1_wgrad_t<bf16>(Nimg, dy, xs, part, part_bytes, gw, t, st, kt)
+  return dt == BF16 ? conv1_wgrad_direct(Nimg, dy, xs, part, part_bytes, gw, t, st, kt)
                     : conv1_wgrad_t<float>(Nimg, dy, xs, part, part_bytes, gw, t, st, kt);
 }
 

@@ -110,12 +110,14 @@ struct SgdTarget { float* w; float* v; void* wb; SgdHyper hy; };
 hipError_t conv_wgrad(DType, const ConvShape&, const void* dy, const void* x, float* part,
                       size_t part_bytes, float* gw, const SgdTarget* sgd, hipStream_t,
                       const KTimer* kt = nullptr);
-// fp32 weight gradient (OIHW) of layer 1 from the space-to-depth input xs
+// fp32 weight gradient (OIHW) of layer 1 from the space-to-depth input xs;
+// part at least conv1_wgrad_part_bytes (bf16: one partial per workgroup of
+// the direct kernel; fp32: split-K partials)
 hipError_t conv1_wgrad(DType, int Nimg, const void* dy, const void* xs, float* part, size_t part_bytes,
                        float* gw, const SgdTarget* sgd, hipStream_t,
                       const KTimer* kt = nullptr);
 size_t conv_wgrad_part_bytes(const ConvShape&);
-size_t conv1_wgrad_part_bytes(int Nimg);
+size_t conv1_wgrad_part_bytes(DType, int Nimg);
 
 // ---- fully-connected layers
 struct FcEpi {
