@@ -309,49 +309,55 @@ struct Conv1FwdFn {
 // output and 96 outputs per pixel.  An implicit-GEMM workgroup would run only
 // 7 k-slices, so filling and draining its pipeline takes much of its life, and
 // it would gather each input block once per tap.  Here one workgroup per CU
-// stays resident.  It copies W' into LDS once, and its four waves take their
-// half of it (48 output channels x 432, as MFMA fragments) into registers for
-// the whole launch.  They then walk tiles of 4 output rows x 55 columns (220
-// pixels) of one image.  A tile's 6 input block rows go into LDS with
-// direct-to-LDS loads, each block's 48 values in a 112-byte slot whose last
-// 16-byte granule is loaded out of range (as zeros), into one of two buffers
-// while the previous tile is multiplied from the other.  Each product takes
-// the weights as the first MFMA operand (16 channels x 32 k) and the block
-// rows as the second (32 k x 16 pixels), so a lane ends with 4 consecutive
-// channels of one pixel.  The first product of a tile starts from the bias
-// instead of zero; ReLU and rounding are applied in registers.  The next
-// tile's loads and this tile's 8-byte output runs are issued between the
-// products, a few per k-step, instead of in bursts that every CU would issue
-// at the same moment.  k runs in the same order as in the implicit GEMM, 32 at
-// a time; the 14th step's upper half (k >= 432) has zero weights and reads the
-// zero granules.
+// stays resident, with W' in LDS for the whole launch (rows padded to 55
+// granules of 16 bytes, the last one zero).  It walks tiles of 4 output rows
+// x 55 columns (220 pixels) of one image.  A tile's 6 input block rows go into
+// LDS with direct-to-LDS loads, each block's 48 values in a 112-byte slot
+// whose last 16-byte granule is loaded out of range (as zeros), into one of
+// two buffers while the previous tile is multiplied from the other.  Eight
+// waves (two per SIMD) each take 48 channels and a quarter of the tile's
+// pixels.  Each product takes the weights as the first MFMA operand (16
+// channels x 32 k) and the block rows as the second (32 k x 16 pixels), so a
+// lane ends with 4 consecutive channels of one pixel.  The first product of a
+// tile starts from the bias instead of zero; ReLU and rounding are applied in
+// registers.  The next tile's loads and this tile's 8-byte output runs are
+// issued between the products, a few per k-step, instead of in bursts that
+// every CU would issue at the same moment.  k runs in the same order as in the
+// implicit GEMM, 32 at a time; the 14th step's upper half (k >= 432) reads the
+// zero granules of both operands.
 constexpr int C1_ROWS = 4;                               // output rows per tile
 constexpr int C1_TPI = (55 + C1_ROWS - 1) / C1_ROWS;     // tiles per image
 constexpr int C1_PROWS = C1_ROWS + 2;                    // input block rows per tile
 constexpr int C1_SLOT = 7;                               // 16-byte granules per block slot (6 + zeros)
 constexpr int C1_GRAN = C1_PROWS * S2D_B * C1_SLOT;      // granules per tile
 constexpr int C1_NI = (C1_GRAN + 63) / 64;               // direct-to-LDS loads per tile (1 KB each)
-constexpr int C1_NIW = (C1_NI + 3) / 4;                  // per wave, at most
+constexpr int C1_WAVES = 8;                              // two per SIMD
+constexpr int C1_NIW = (C1_NI + C1_WAVES - 1) / C1_WAVES;   // per wave, at most
 constexpr int C1_BUF = C1_NI * 64 * 8;                   // bf16 elements per block-row buffer
 constexpr int C1_KS = (S2D_K + 31) / 32;                 // k-steps of 32
-constexpr int C1_FM = 7, C1_FN = 3;                      // per wave: 7 x 16 pixels, 3 x 16 channels
-constexpr int C1_WL = (int)(S2D_W_ELEMS * 2 / 1024);     // direct-to-LDS loads of W' (1 KB each)
-constexpr int C1_WX = (int)S2D_W_ELEMS - C1_BUF;         // LDS past the second buffer that W' takes
+constexpr int C1_FM = 4, C1_FN = 3;                      // per wave: up to 4 x 16 pixels, 3 x 16 channels
+constexpr int C1_WG = S2D_K / 8 + 1;                     // granules per W' row in LDS (54 + a zero one)
+constexpr int C1_WGR = 96 * C1_WG;                       // W' granules
+constexpr int C1_WL = (C1_WGR + 63) / 64;                // direct-to-LDS loads of W'
 constexpr int C1_GRID = 256;                             // one workgroup per CU
-static_assert(2 * C1_FM * 16 >= C1_ROWS * 55 && 2 * C1_FN * 16 == 96, "four waves cover a tile");
-static_assert(S2D_C % 8 == 0, "an 8-value k run stays within one tap");
+static_assert(C1_ROWS * 55 <= 224 && 2 * C1_FN * 16 == 96, "eight waves cover a tile: m-fragments 4, 4, 3, 3");
+static_assert(S2D_C % 8 == 0 && S2D_K % 8 == 0, "an 8-value k run stays within one tap");
 static_assert(C1_NIW <= C1_KS && C1_FM <= C1_KS, "one load and one row of stores per k-step at most");
-static_assert(S2D_W_ELEMS * 2 % 1024 == 0 && C1_WX > 0, "W' goes through the second buffer and past it");
+static_assert((2 * C1_BUF + C1_WL * 512) * 2 <= 160 * 1024, "block rows and W' fit in LDS");
 static_assert(((C1_PROWS - 1) * S2D_B + S2D_B - 1) * S2D_C * 2 + S2D_C * 2 < 65536, "block offsets fit 16 bits");
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * C1_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16* __restrict__ bias,
             bf16* __restrict__ y, int Nimg) {
-  // two block-row buffers; W' passes through the second one and the space after it at the start
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C1_BUF + C1_WX];
+  // [block rows 0][block rows 1][W' rows of C1_WG granules]
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C1_BUF + C1_WL * 512];
+  const bf16* const wl = lds + 2 * C1_BUF;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
+  // this wave's m-fragments: 4 from fragment 4 wm (wm < 2), else 3 from 8 + 3 (wm - 2)
+  const int mf0 = wm < 2 ? 4 * wm : 8 + 3 * (wm - 2);
+  const bool full = wm < 2;
   // Workgroups are dealt round-robin over the eight XCDs; XCD x takes a
   // contiguous run of the tile order, so that neighbouring tiles, which share
   // two block rows, share an L2.
@@ -363,21 +369,21 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
   if (t >= t_end) return;
 
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xs, (uint32_t)((int64_t)Nimg * S2D_ELEMS * 2));
-  // Load i of this wave (j = wave + 4 i) fills granules 64 j .. 64 j + 63 of a
-  // buffer.  This lane's granule holds block row `row` of the tile at byte
-  // offset rel from the tile's first block, packed as (row << 16) | rel, or is
-  // zero (row 0xFFFF): a pad granule, or past the tile.
+  // Load i of this wave (j = wave + C1_WAVES i) fills granules 64 j .. 64 j + 63
+  // of a buffer.  This lane's granule holds block row `row` of the tile at
+  // byte offset rel from the tile's first block, packed as (row << 16) | rel,
+  // or is zero (row 0xFFFF): a pad granule, or past the tile.
   uint32_t drel[C1_NIW];
 #pragma unroll
   for (int i = 0; i < C1_NIW; ++i) {
-    const int gidx = (wave + 4 * i) * 64 + lane;
+    const int gidx = (wave + C1_WAVES * i) * 64 + lane;
     const int slot = gidx / C1_SLOT, g = gidx - slot * C1_SLOT;
     const int row = slot / S2D_B, bw = slot - row * S2D_B;
     const bool ok = gidx < C1_GRAN && g < S2D_C / 8;
     drel[i] = ok ? ((uint32_t)row << 16) | (uint32_t)(((row * S2D_B + bw) * S2D_C + g * 8) * 2) : 0xFFFF0000u;
   }
   auto dma = [&](int i, uint32_t base, int r0, bf16* buf) {
-    const int j = wave + 4 * i;
+    const int j = wave + C1_WAVES * i;
     if (j < C1_NI) {
       const uint32_t d = drel[i];
       const uint32_t off = (int)(d >> 16) + r0 < S2D_B ? base + (d & 0xFFFFu) : BUF_OOB;
@@ -394,22 +400,15 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
     const uint32_t base = tile_base(t, r0);
 #pragma unroll
     for (int i = 0; i < C1_NIW; ++i) dma(i, base, r0, lds);
-    // W' [96][432] as it is in memory
+    // W' [96][432]: row co's 54 granules, then a zero one
     const __amdgpu_buffer_rsrc_t rw = buf_rsrc(w, (uint32_t)(S2D_W_ELEMS * 2));
-    for (int j = wave; j < C1_WL; j += 4) dma16(rw, (uint32_t)(j * 1024 + lane * 16), lds + C1_BUF + j * 512);
-  }
-  wait_vmcnt<0>();
-  lds_barrier();
-  // weight fragments (j, s): channel wn*48 + 16 j + (lane & 15), k = 32 s + 8 (lane >> 4) .. + 7
-  bf16x8_t wf[C1_FN][C1_KS];
-#pragma unroll
-  for (int j = 0; j < C1_FN; ++j)
-#pragma unroll
-    for (int s = 0; s < C1_KS; ++s) {
-      const int co = wn * 48 + j * 16 + (lane & 15), k = s * 32 + (lane >> 4) * 8;
-      wf[j][s] = k < S2D_K ? *reinterpret_cast<const bf16x8_t*>(lds + C1_BUF + co * S2D_K + k)
-                           : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+    for (int j = wave; j < C1_WL; j += C1_WAVES) {
+      const int gidx = j * 64 + lane, co = gidx / C1_WG, g = gidx - co * C1_WG;
+      const uint32_t off = gidx < C1_WGR && g < C1_WG - 1 ? (uint32_t)((co * S2D_K + g * 8) * 2) : BUF_OOB;
+      dma16(rw, off, lds + 2 * C1_BUF + j * 512);
     }
+  }
+
   // this lane's 4 output channels per n-fragment, and their biases as the
   // accumulator a tile's first product starts from
   const int c0 = wn * 48 + (lane >> 4) * 4;
@@ -418,37 +417,42 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
   for (int j = 0; j < C1_FN; ++j)
     bc[j] = f32x4_t{bf2f(bias[c0 + j * 16]), bf2f(bias[c0 + j * 16 + 1]), bf2f(bias[c0 + j * 16 + 2]),
                     bf2f(bias[c0 + j * 16 + 3])};
-  // LDS element offsets: of the pixel's top-left block per m-fragment, of the tap and channel run per k-step
+  // LDS element offsets: of the pixel's top-left block per m-fragment, of the
+  // tap and channel run per k-step; of the weight row per n-fragment
   int poff[C1_FM];
 #pragma unroll
   for (int i = 0; i < C1_FM; ++i) {
-    const int px = min(wm * C1_FM * 16 + i * 16 + (lane & 15), C1_ROWS * 55 - 1);
+    const int px = min((mf0 + i) * 16 + (lane & 15), C1_ROWS * 55 - 1);
     const int lr = px / 55;
     poff[i] = (lr * S2D_B + px - lr * 55) * C1_SLOT * 8;
   }
-  int toff[C1_KS];
+  int woff[C1_FN];
 #pragma unroll
-  for (int s = 0; s < C1_KS; ++s) {
+  for (int j = 0; j < C1_FN; ++j) woff[j] = (wn * 48 + j * 16 + (lane & 15)) * C1_WG * 8;
+  auto toff = [&](int s) {
     const int k = s * 32 + (lane >> 4) * 8;
     const int tap = k / S2D_C, ci = k - tap * S2D_C, kh = tap / 3, kw = tap - kh * 3;
-    toff[s] = k < S2D_K ? (kh * S2D_B + kw) * C1_SLOT * 8 + ci : S2D_C;   // S2D_C: the slot's zero granule
-  }
-  lds_barrier();   // every wave has its fragments of W' before the second buffer is loaded again
+    return k < S2D_K ? (kh * S2D_B + kw) * C1_SLOT * 8 + ci : S2D_C;   // S2D_C: the slot's zero granule
+  };
+  auto wk = [&](int s) {
+    const int k = s * 32 + (lane >> 4) * 8;
+    return k < S2D_K ? k : S2D_K;                                        // S2D_K: the row's zero granule
+  };
 
   // the previous tile's outputs, rounded, stored during this tile's k-steps
   uint2 outv[C1_FM][C1_FN];
   bf16* yprev = nullptr;
   int npx_prev = 0;
   auto store_row = [&](int i, int j) {
-    const int px = wm * C1_FM * 16 + i * 16 + (lane & 15);
-    if (px < npx_prev) *reinterpret_cast<uint2*>(yprev + (int64_t)px * 96 + j * 16) = outv[i][j];
+    const int px = (mf0 + i) * 16 + (lane & 15);
+    if ((i < C1_FM - 1 || full) && px < npx_prev) *reinterpret_cast<uint2*>(yprev + (int64_t)px * 96 + j * 16) = outv[i][j];
   };
 
   for (int it = 0;; ++it) {
     const bf16* cur = lds + (it & 1) * C1_BUF;
     bf16* nxt = lds + ((it + 1) & 1) * C1_BUF;
     wait_vmcnt<0>();
-    lds_barrier();   // tile t's block rows are in; every wave is done with the other buffer
+    lds_barrier();   // tile t's block rows (and at first W') are in; every wave is done with the other buffer
     const int tn = t + per_x;
     const bool more = tn < t_end;
     int nr0 = 0;
@@ -456,25 +460,29 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
     const bool stores = yprev != nullptr;
 
     f32x4_t acc[C1_FM][C1_FN];
-    bf16x8_t a[2][C1_FM];
+    bf16x8_t a[2][C1_FM], b[2][C1_FN];
+    auto read = [&](int s, int buf) {
+      const int to = toff(s), kk = wk(s);
 #pragma unroll
-    for (int i = 0; i < C1_FM; ++i) a[0][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + toff[0]);
-    // the next k-step's fragments are read before this one's products, which
-    // then cover the LDS latency (one wave per SIMD: no other wave would)
+      for (int i = 0; i < C1_FM; ++i)
+        if (i < C1_FM - 1 || full) a[buf][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + to);
+#pragma unroll
+      for (int j = 0; j < C1_FN; ++j) b[buf][j] = *reinterpret_cast<const bf16x8_t*>(wl + woff[j] + kk);
+    };
+    read(0, 0);
+    // the next k-step's fragments are read before this one's products
 #pragma unroll
     for (int s = 0; s < C1_KS; ++s) {
-      if (s + 1 < C1_KS) {
-#pragma unroll
-        for (int i = 0; i < C1_FM; ++i)
-          a[(s + 1) & 1][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + toff[s + 1]);
-      }
+      if (s + 1 < C1_KS) read(s + 1, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < C1_FM; ++i) {
+        if (i < C1_FM - 1 || full) {
 #pragma unroll
-        for (int j = 0; j < C1_FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j][s], a[s & 1][i], s == 0 ? bc[j] : acc[i][j],
-                                                              0, 0, 0);
+          for (int j = 0; j < C1_FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[s & 1][j], a[s & 1][i], s == 0 ? bc[j] : acc[i][j],
+                                                                0, 0, 0);
+        }
         if (i == 0 && s < C1_NIW && more) dma(s, nbase, nr0, nxt);
         if (i >= 1 && i <= C1_FN && s < C1_FM && stores) store_row(s, i - 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -506,7 +514,7 @@ static hipError_t conv1_fwd_direct(const void* xs, int Nimg, const void* ws2d, c
   // byte offsets into the staged input are 32-bit, below the out-of-range marker
   if (Nimg < 1 || (int64_t)Nimg * S2D_ELEMS * 2 >= (int64_t)BUF_OOB) return hipErrorInvalidValue;
   rec_start(kt, st);
-  hipLaunchKernelGGL(k_conv1_fwd, dim3(C1_GRID), dim3(256), 0, st, (const bf16*)xs, (const bf16*)ws2d,
+  hipLaunchKernelGGL(k_conv1_fwd, dim3(C1_GRID), dim3(64 * C1_WAVES), 0, st, (const bf16*)xs, (const bf16*)ws2d,
                      (const bf16*)b1, (bf16*)y, Nimg);
   rec_stop(kt, st);
   return hipGetLastError();
