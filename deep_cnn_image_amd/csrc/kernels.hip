@@ -309,12 +309,14 @@ struct Conv1FwdFn {
 // output and 96 outputs per pixel.  An implicit-GEMM workgroup would run only
 // 7 k-slices, so filling and draining its pipeline takes much of its life, and
 // it would gather each input block once per tap.  Here one workgroup per CU
-// stays resident, with W' in LDS for the whole launch (rows padded to 55
-// granules of 16 bytes, the last one zero).  It walks tiles of 4 output rows
-// x 55 columns (220 pixels) of one image.  A tile's 6 input block rows go into
-// LDS with direct-to-LDS loads, each block's 48 values in a 112-byte slot
-// whose last 16-byte granule is loaded out of range (as zeros), into one of
-// two buffers while the previous tile is multiplied from the other.  Eight
+// stays resident, with W' in LDS for the whole launch.  It walks tiles of 4
+// output rows x 55 columns (220 pixels) of one image.  A tile's 6 input block
+// rows (96 bytes per block) are copied into LDS with direct-to-LDS loads, into
+// one of two buffers while the previous tile is multiplied from the other.
+// Rows of 96 bytes (W' rows of 864) keep the fragment reads free of bank
+// conflicts: a 16-byte LDS read serves 32 lanes at a time over 128 banks, and
+// 16 rows at that stride, with the next 16 lanes 16 bytes further on, touch
+// every bank once (rows of 112 or 144 bytes conflict two-way).  Eight
 // waves (two per SIMD) each take 48 channels and a quarter of the tile's
 // pixels.  Each product takes the weights as the first MFMA operand (16
 // channels x 32 k) and the block rows as the second (32 k x 16 pixels), so a
@@ -323,12 +325,12 @@ struct Conv1FwdFn {
 // registers.  The next tile's loads and this tile's 8-byte output runs are
 // issued between the products, a few per k-step, instead of in bursts that
 // every CU would issue at the same moment.  k runs in the same order as in the
-// implicit GEMM, 32 at a time; the 14th step's upper half (k >= 432) reads the
-// zero granules of both operands.
+// implicit GEMM, 32 at a time; in the 14th step's upper half (k >= 432) the
+// weight fragment is zero (and the block-row fragment any finite data).
 constexpr int C1_ROWS = 4;                               // output rows per tile
 constexpr int C1_TPI = (55 + C1_ROWS - 1) / C1_ROWS;     // tiles per image
 constexpr int C1_PROWS = C1_ROWS + 2;                    // input block rows per tile
-constexpr int C1_SLOT = 7;                               // 16-byte granules per block slot (6 + zeros)
+constexpr int C1_SLOT = S2D_C / 8;                       // 16-byte granules per block
 constexpr int C1_GRAN = C1_PROWS * S2D_B * C1_SLOT;      // granules per tile
 constexpr int C1_NI = (C1_GRAN + 63) / 64;               // direct-to-LDS loads per tile (1 KB each)
 constexpr int C1_WAVES = 8;                              // two per SIMD
@@ -336,20 +338,18 @@ constexpr int C1_NIW = (C1_NI + C1_WAVES - 1) / C1_WAVES;   // per wave, at most
 constexpr int C1_BUF = C1_NI * 64 * 8;                   // bf16 elements per block-row buffer
 constexpr int C1_KS = (S2D_K + 31) / 32;                 // k-steps of 32
 constexpr int C1_FM = 4, C1_FN = 3;                      // per wave: up to 4 x 16 pixels, 3 x 16 channels
-constexpr int C1_WG = S2D_K / 8 + 1;                     // granules per W' row in LDS (54 + a zero one)
-constexpr int C1_WGR = 96 * C1_WG;                       // W' granules
-constexpr int C1_WL = (C1_WGR + 63) / 64;                // direct-to-LDS loads of W'
+constexpr int C1_WL = (int)(S2D_W_ELEMS * 2 / 1024);     // direct-to-LDS loads of W' (1 KB each)
 constexpr int C1_GRID = 256;                             // one workgroup per CU
 static_assert(C1_ROWS * 55 <= 224 && 2 * C1_FN * 16 == 96, "eight waves cover a tile: m-fragments 4, 4, 3, 3");
 static_assert(S2D_C % 8 == 0 && S2D_K % 8 == 0, "an 8-value k run stays within one tap");
 static_assert(C1_NIW <= C1_KS && C1_FM <= C1_KS, "one load and one row of stores per k-step at most");
-static_assert((2 * C1_BUF + C1_WL * 512) * 2 <= 160 * 1024, "block rows and W' fit in LDS");
+static_assert(S2D_W_ELEMS * 2 % 1024 == 0 && (2 * C1_BUF + C1_WL * 512) * 2 <= 160 * 1024, "block rows and W' fit in LDS");
 static_assert(((C1_PROWS - 1) * S2D_B + S2D_B - 1) * S2D_C * 2 + S2D_C * 2 < 65536, "block offsets fit 16 bits");
 
 __global__ void __launch_bounds__(64 * C1_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16* __restrict__ bias,
             bf16* __restrict__ y, int Nimg) {
-  // [block rows 0][block rows 1][W' rows of C1_WG granules]
+  // [block rows 0][block rows 1][W' [96][432]]
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * C1_BUF + C1_WL * 512];
   const bf16* const wl = lds + 2 * C1_BUF;
   const int lane = threadIdx.x & 63;
@@ -369,18 +369,16 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
   if (t >= t_end) return;
 
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(xs, (uint32_t)((int64_t)Nimg * S2D_ELEMS * 2));
-  // Load i of this wave (j = wave + C1_WAVES i) fills granules 64 j .. 64 j + 63
-  // of a buffer.  This lane's granule holds block row `row` of the tile at
-  // byte offset rel from the tile's first block, packed as (row << 16) | rel,
-  // or is zero (row 0xFFFF): a pad granule, or past the tile.
+  // Load i of this wave (j = wave + C1_WAVES i) copies granules 64 j .. 64 j
+  // + 63 of the tile's block rows, which are contiguous in memory.  This
+  // lane's granule lies in block row `row` of the tile, packed as (row << 16)
+  // | byte offset, or past the tile (row 0xFFFF): loaded as zero.
   uint32_t drel[C1_NIW];
 #pragma unroll
   for (int i = 0; i < C1_NIW; ++i) {
     const int gidx = (wave + C1_WAVES * i) * 64 + lane;
-    const int slot = gidx / C1_SLOT, g = gidx - slot * C1_SLOT;
-    const int row = slot / S2D_B, bw = slot - row * S2D_B;
-    const bool ok = gidx < C1_GRAN && g < S2D_C / 8;
-    drel[i] = ok ? ((uint32_t)row << 16) | (uint32_t)(((row * S2D_B + bw) * S2D_C + g * 8) * 2) : 0xFFFF0000u;
+    const int row = gidx / (S2D_B * C1_SLOT);
+    drel[i] = gidx < C1_GRAN ? ((uint32_t)row << 16) | (uint32_t)(gidx * 16) : 0xFFFF0000u;
   }
   auto dma = [&](int i, uint32_t base, int r0, bf16* buf) {
     const int j = wave + C1_WAVES * i;
@@ -400,13 +398,9 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
     const uint32_t base = tile_base(t, r0);
 #pragma unroll
     for (int i = 0; i < C1_NIW; ++i) dma(i, base, r0, lds);
-    // W' [96][432]: row co's 54 granules, then a zero one
+    // W' [96][432] as it is in memory
     const __amdgpu_buffer_rsrc_t rw = buf_rsrc(w, (uint32_t)(S2D_W_ELEMS * 2));
-    for (int j = wave; j < C1_WL; j += C1_WAVES) {
-      const int gidx = j * 64 + lane, co = gidx / C1_WG, g = gidx - co * C1_WG;
-      const uint32_t off = gidx < C1_WGR && g < C1_WG - 1 ? (uint32_t)((co * S2D_K + g * 8) * 2) : BUF_OOB;
-      dma16(rw, off, lds + 2 * C1_BUF + j * 512);
-    }
+    for (int j = wave; j < C1_WL; j += C1_WAVES) dma16(rw, (uint32_t)(j * 1024 + lane * 16), lds + 2 * C1_BUF + j * 512);
   }
 
   // this lane's 4 output channels per n-fragment, and their biases as the
@@ -428,15 +422,11 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
   }
   int woff[C1_FN];
 #pragma unroll
-  for (int j = 0; j < C1_FN; ++j) woff[j] = (wn * 48 + j * 16 + (lane & 15)) * C1_WG * 8;
+  for (int j = 0; j < C1_FN; ++j) woff[j] = (wn * 48 + j * 16 + (lane & 15)) * S2D_K;
   auto toff = [&](int s) {
-    const int k = s * 32 + (lane >> 4) * 8;
+    const int k = min(s * 32 + (lane >> 4) * 8, S2D_K - 8);   // past K: any data (its weights are zero)
     const int tap = k / S2D_C, ci = k - tap * S2D_C, kh = tap / 3, kw = tap - kh * 3;
-    return k < S2D_K ? (kh * S2D_B + kw) * C1_SLOT * 8 + ci : S2D_C;   // S2D_C: the slot's zero granule
-  };
-  auto wk = [&](int s) {
-    const int k = s * 32 + (lane >> 4) * 8;
-    return k < S2D_K ? k : S2D_K;                                        // S2D_K: the row's zero granule
+    return (kh * S2D_B + kw) * C1_SLOT * 8 + ci;
   };
 
   // the previous tile's outputs, rounded, stored during this tile's k-steps
@@ -462,12 +452,15 @@ k_conv1_fwd(const bf16* __restrict__ xs, const bf16* __restrict__ w, const bf16*
     f32x4_t acc[C1_FM][C1_FN];
     bf16x8_t a[2][C1_FM], b[2][C1_FN];
     auto read = [&](int s, int buf) {
-      const int to = toff(s), kk = wk(s);
+      const int to = toff(s), kr = s * 32 + (lane >> 4) * 8;
 #pragma unroll
       for (int i = 0; i < C1_FM; ++i)
         if (i < C1_FM - 1 || full) a[buf][i] = *reinterpret_cast<const bf16x8_t*>(cur + poff[i] + to);
 #pragma unroll
-      for (int j = 0; j < C1_FN; ++j) b[buf][j] = *reinterpret_cast<const bf16x8_t*>(wl + woff[j] + kk);
+      for (int j = 0; j < C1_FN; ++j) {
+        const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(wl + woff[j] + min(kr, S2D_K - 8));
+        b[buf][j] = (s + 1) * 32 <= S2D_K || kr < S2D_K ? v : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+      }
     };
     read(0, 0);
     // the next k-step's fragments are read before this one's products
@@ -899,11 +892,19 @@ k_conv1_wgrad(const bf16* __restrict__ dy, const bf16* __restrict__ xs, float* _
     dlim = (uint32_t)(min(C1_ROWS, 55 - r0) * 55 * 96 * 2);
     pbase = (uint32_t)(((int64_t)n * S2D_B + r0) * S2D_B * S2D_C * 2);
   };
+  // The dY tile sits in LDS as two halves of 48 channels, [224 pixels][48]
+  // (96-byte rows); LDS granule G of it holds granule dy_src(G) of the tile's
+  // rows in memory (12 per pixel), at a byte offset that stays below dlim
+  // exactly for the tile's valid pixels.
+  auto dy_src = [](int G) {
+    const int hh = G / (W1_PXT * 6), r = G - hh * (W1_PXT * 6), px = r / 6;
+    return (uint32_t)((px * 12 + hh * 6 + (r - px * 6)) * 16);
+  };
   // load i of this wave, j = wave + W1_WAVES i: 1 KB at granule 64 j of the buffer
   auto load = [&](int i, uint32_t dbase, uint32_t dlim, uint32_t pbase, bf16* buf) {
     const int j = wave + W1_WAVES * i;
     if (j < W1_DYL) {
-      const uint32_t o = (uint32_t)(j * 1024 + lane * 16);
+      const uint32_t o = dy_src(j * 64 + lane);
       dma16(rsy, o < dlim ? dbase + o : BUF_OOB, buf + j * 512);
     } else if (j < W1_NL) {
       dma16(rsx, pbase + (uint32_t)((j - W1_DYL) * 1024 + lane * 16), buf + j * 512);
@@ -930,23 +931,27 @@ k_conv1_wgrad(const bf16* __restrict__ dy, const bf16* __restrict__ xs, float* _
   auto fetch = [&](int i, uint32_t dbase, uint32_t dlim, uint32_t pbase) {
     const int j = slot_of(i);
     const bool in_dy = j < W1_DYL;
-    const uint32_t od = (uint32_t)(j * 1024 + lane * 16), op = (uint32_t)((j - W1_DYL) * 1024 + lane * 16);
+    const uint32_t od = dy_src(min(j, W1_DYL - 1) * 64 + lane), op = (uint32_t)((j - W1_DYL) * 1024 + lane * 16);
     const uint32_t off = in_dy ? (od < dlim ? dbase + od : BUF_OOB) : pbase + op;
     return __builtin_amdgcn_raw_buffer_load_b128(in_dy ? rsy : rsx, off, 0, 0);
   };
 
-  // transposing-read addresses (elements within a buffer).  Lane (g, q) of
-  // chunk c, half h reads pixel row 32 c + 8 g + 4 h + q / 4 at 4 (q % 4) past
-  // the fragment's first column.
+  // Transposing-read addresses (elements within a buffer).  The MFMA's k
+  // index kappa of a chunk (lane group g holds kappa = 8 g .. 8 g + 7) stands
+  // for pixel 32 c + 16 h + 4 g + j, kappa = 8 g + 4 h + j: the same
+  // order for both operands, so that each read of the 64 lanes covers 16
+  // consecutive pixel rows, which at 96 bytes per row touch every bank once.
+  // Lane (g, q) of chunk c, half h reads pixel row 32 c + 16 h + 4 g + q / 4
+  // at 4 (q % 4) past the fragment's first column.
   const int g = lane >> 4, q = lane & 15;
   int dyo[W1_CH][2], pso[W1_CH][2];
 #pragma unroll
   for (int c = 0; c < W1_CH; ++c)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int px = 32 * c + 8 * g + 4 * h + (q >> 2);
+      const int px = 32 * c + 16 * h + 4 * g + (q >> 2);
       const int lr = px / 55, col = px - lr * 55;
-      dyo[c][h] = px * 96 + 4 * (q & 3);
+      dyo[c][h] = px * 48 + 4 * (q & 3);
       pso[c][h] = W1_DYE + (lr * S2D_B + col) * S2D_C + 4 * (q & 3);
     }
   // k-fragment i of this wave: kf = wave + W1_WAVES i, tap kf / 3, channels (kf % 3) * 16 ..
@@ -984,7 +989,8 @@ k_conv1_wgrad(const bf16* __restrict__ dy, const bf16* __restrict__ xs, float* _
     // chunk needs them), then the k-fragments in the order of use
     auto read_frag = [&](int c, int b, int f) {
       if (f < W1_CF) {
-        fb[b][f] = trd(cur, dyo[c][0] + f * 16, dyo[c][1] + f * 16);
+        const int ho = (f / 3) * (W1_PXT * 48) + (f % 3) * 16;   // channel half, column in it
+        fb[b][f] = trd(cur, dyo[c][0] + ho, dyo[c][1] + ho);
       } else {
         const int i = f - W1_CF;
         if (i < W1_KFW - 1 || full) fa[b][i] = trd(cur, pso[c][0] + ko[i], pso[c][1] + ko[i]);
