@@ -1190,8 +1190,20 @@ __global__ void k_fc_reduce(const float* __restrict__ part, int S, int M, int N,
   const int64_t e0 = t * 4;
   const int m = (int)(e0 / N), n = (int)(e0 - (int64_t)m * N);
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float4 q = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * N + n);
+  // splits summed in order; eight partials in flight at a time instead of one
+  // load's latency per split
+  const float* pp = part + (int64_t)m * N + n;
+  const int64_t sstride = (int64_t)M * N;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = *reinterpret_cast<const float4*>(pp + (s + u) * sstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { v[0] += q[u].x; v[1] += q[u].y; v[2] += q[u].z; v[3] += q[u].w; }
+  }
+  for (; s < S; ++s) {
+    const float4 q = *reinterpret_cast<const float4*>(pp + s * sstride);
     v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
   }
   if (bias) {
@@ -2399,34 +2411,68 @@ __global__ void __launch_bounds__(TPB) k_pool5_fwd(const T* __restrict__ x, T* _
 // The block's run of the flat gradient (POOL5_CB * P values) is read once in
 // 4-element pieces and transposed into LDS as [h*Wo+w][c]; each thread then
 // sums, for its (row, column, 8-channel) units, the windows whose argmax is
-// the pixel (windows in row-major order).
+// the pixel (windows in row-major order).  Every global read of a thread (its
+// gradient pieces, its units' argmax codes and mask rows) is issued before the
+// first is used, so the thread waits one memory latency, not one per unit.
+constexpr int POOL5_UIT = 4;   // units per thread: H W (POOL5_CB / 8) <= POOL5_UIT TPB (host-checked)
+constexpr int POOL5_GIT = (POOL5_CB * POOL5_P / 4 + TPB - 1) / TPB;   // gradient pieces per thread
+
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_pool5_bwd(const T* __restrict__ dy, const uint8_t* __restrict__ arg,
                                                    const T* __restrict__ mask, T* __restrict__ dx, int H, int W,
                                                    int C, int Ho, int Wo) {
   constexpr int LS = POOL5_CB + 8;   // padded row: the transposing writes spread over banks
+  constexpr int CPP = POOL5_CB / 8;
   __shared__ __attribute__((aligned(16))) T lg[POOL5_P * LS];
   const int nblk = C / POOL5_CB, n = blockIdx.x / nblk, cb = blockIdx.x - n * nblk;
-  const int P = Ho * Wo;
+  const int P = Ho * Wo, pieces = POOL5_CB * P / 4, units = H * W * CPP;
   const T* src = dy + (size_t)n * C * P + (size_t)cb * POOL5_CB * P;
-  for (int e4 = threadIdx.x; e4 < POOL5_CB * P / 4; e4 += TPB) {
-    T v[4];
+  // reads: indices past the end are clamped to the last valid one (a valid
+  // address; those values are never used)
+  T g4[POOL5_GIT][4];
+#pragma unroll
+  for (int it = 0; it < POOL5_GIT; ++it) {
+    const int e4 = min((int)threadIdx.x + it * TPB, pieces - 1);
     if constexpr (sizeof(T) == 2) {
       const uint2 q = *reinterpret_cast<const uint2*>(src + e4 * 4);
-      v[0] = (T)(q.x & 0xFFFFu); v[1] = (T)(q.x >> 16); v[2] = (T)(q.y & 0xFFFFu); v[3] = (T)(q.y >> 16);
+      g4[it][0] = (T)(q.x & 0xFFFFu); g4[it][1] = (T)(q.x >> 16);
+      g4[it][2] = (T)(q.y & 0xFFFFu); g4[it][3] = (T)(q.y >> 16);
     } else {
       const float4 q = *reinterpret_cast<const float4*>(src + e4 * 4);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      g4[it][0] = q.x; g4[it][1] = q.y; g4[it][2] = q.z; g4[it][3] = q.w;
     }
+  }
+  uint2 am[POOL5_UIT][4];
+  float mk[POOL5_UIT][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = e4 * 4 + k, c = e / P, pos = e - c * P;
-      lg[pos * LS + c] = v[k];
+  for (int it = 0; it < POOL5_UIT; ++it) {
+    const int u = min((int)threadIdx.x + it * TPB, units - 1);
+    const int hw = u / CPP, ch8 = u - hw * CPP, h = hw / W, w = hw - h * W;
+    const int c0 = cb * POOL5_CB + ch8 * 8;
+    const int i0 = h >= 2 ? (h - 1) / 2 : 0, j0 = w >= 2 ? (w - 1) / 2 : 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int i = min(i0 + (d >> 1), Ho - 1), j = min(j0 + (d & 1), Wo - 1);
+      am[it][d] = *reinterpret_cast<const uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0);
+    }
+    Pack8<T>::load(mask + (((size_t)n * H + h) * W + w) * C + c0, mk[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < POOL5_GIT; ++it) {
+    const int e4 = threadIdx.x + it * TPB;
+    if (e4 < pieces) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = e4 * 4 + k, c = e / P, pos = e - c * P;
+        lg[pos * LS + c] = g4[it][k];
+      }
     }
   }
   __syncthreads();
-  constexpr int CPP = POOL5_CB / 8;
-  for (int u = threadIdx.x; u < H * W * CPP; u += TPB) {
+#pragma unroll
+  for (int it = 0; it < POOL5_UIT; ++it) {
+    const int u = threadIdx.x + it * TPB;
+    if (u >= units) break;
     const int hw = u / CPP, ch8 = u - hw * CPP, h = hw / W, w = hw - h * W;
     const int c0 = cb * POOL5_CB + ch8 * 8;
     const int i0 = h >= 2 ? (h - 1) / 2 : 0, i1 = min(h / 2, Ho - 1);
@@ -2435,35 +2481,29 @@ __global__ void __launch_bounds__(TPB) k_pool5_bwd(const T* __restrict__ dy, con
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
 #pragma unroll
-    for (int di = 0; di < 2; ++di)
+    for (int d = 0; d < 4; ++d) {
+      const int i = i0 + (d >> 1), j = j0 + (d & 1);
+      if (i <= i1 && j <= j1) {
+        const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
+        float g[8];
+        Pack8<T>::load(lg + (i * Wo + j) * LS + ch8 * 8, g);
 #pragma unroll
-      for (int dj = 0; dj < 2; ++dj) {
-        const int i = i0 + di, j = j0 + dj;
-        if (i <= i1 && j <= j1) {
-          const uint32_t code = (uint32_t)((h - 2 * i) * 3 + (w - 2 * j));
-          const uint2 am = *reinterpret_cast<const uint2*>(arg + (((size_t)n * Ho + i) * Wo + j) * C + c0);
-          float g[8];
-          Pack8<T>::load(lg + (i * Wo + j) * LS + ch8 * 8, g);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t b = ((q < 4 ? am.x : am.y) >> ((q & 3) * 8)) & 0xFFu;
-            if (b == code) acc[q] += g[q];
-          }
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t b = ((q < 4 ? am[it][d].x : am[it][d].y) >> ((q & 3) * 8)) & 0xFFu;
+          if (b == code) acc[q] += g[q];
         }
       }
-    const size_t o = (((size_t)n * H + h) * W + w) * C + c0;
-    float mk[8];
-    Pack8<T>::load(mask + o, mk);
+    }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = mk[q] > 0.f ? acc[q] : 0.f;
-    Pack8<T>::store(dx + o, acc);
+    for (int q = 0; q < 8; ++q) acc[q] = mk[it][q] > 0.f ? acc[q] : 0.f;
+    Pack8<T>::store(dx + (((size_t)n * H + h) * W + w) * C + c0, acc);
   }
 }
 
 static bool pool5_shape_ok(int H, int W, int C, int& Ho, int& Wo) {
   Ho = (H - 3) / 2 + 1; Wo = (W - 3) / 2 + 1;
   return C % POOL5_CB == 0 && Ho * Wo <= POOL5_P && Ho * Wo * (POOL5_CB / 8) <= TPB &&
-         (POOL5_CB * Ho * Wo) % 8 == 0;
+         (POOL5_CB * Ho * Wo) % 8 == 0 && H * W * (POOL5_CB / 8) <= POOL5_UIT * TPB;
 }
 
 hipError_t pool5_fwd(DType dt, const void* x, void* y, uint8_t* arg, int N, int H, int W, int C, hipStream_t st,
