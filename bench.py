@@ -151,7 +151,7 @@ def main():
 
     from deep_cnn_image_amd import binding as B
     from deep_cnn_image_amd import inputs as I
-    from deep_cnn_image_amd.session import Session, SideStream, stream_handle, to_device
+    from deep_cnn_image_amd.session import Session, SideStream, Timer, stream_handle, to_device
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -168,13 +168,9 @@ def main():
         return {"read": src.numel() * 2, "write": dst.numel() * 2}
 
     def new_events(k):
-        evs = []
-        for _ in range(k):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(); b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        return evs
+        # start/stop pairs without the system-scope fence of a default event,
+        # which would add a cache write-back to every timed span
+        return [Timer() for _ in range(k)]
 
     # ---------------------------------------------------------------- training step
     syn = I.workload_inputs("train_batch128")
@@ -211,13 +207,13 @@ def main():
     names = [k for k in B.KERNELS if k != "RGB_PCA"]   # every kernel of the training step
     evs = [new_events(len(names)) for _ in range(diag_steps)]
     for d in range(diag_steps):
-        train(step, [(B.KT[nm], evs[d][j][0].cuda_event, evs[d][j][1].cuda_event)
+        train(step, [(B.KT[nm], evs[d][j].start, evs[d][j].stop)
                      for j, nm in enumerate(names)], serial=True)
         step += 1
     torch.cuda.synchronize()
     per_kernel = {}
     for j, nm in enumerate(names):
-        ms = [evs[d][j][0].elapsed_time(evs[d][j][1]) for d in range(diag_steps)]
+        ms = [evs[d][j].elapsed_ms() for d in range(diag_steps)]
         if min(ms) > 0:
             per_kernel[nm] = sum(ms) / len(ms)
     # the dominant kernel: the longest of those on the step's main stream.  The
@@ -233,11 +229,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        train(step, [(B.KT[dominant], tev[i][0].cuda_event, tev[i][1].cuda_event)])
+        train(step, [(B.KT[dominant], tev[i].start, tev[i].stop)])
         step += 1
     torch.cuda.synchronize()
     train_s = (time.perf_counter() - t0) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in tev) / args.steps
+    dom_ms = sum(t.elapsed_ms() for t in tev) / args.steps
     final_loss = float(loss.item())
     if args.train_only:
         # the training step alone (short runs under a profiler): its per-kernel
@@ -272,9 +268,9 @@ def main():
         pca()
     pev = new_events(args.steps)
     for i in range(args.steps):
-        pca([(B.KT["RGB_PCA"], pev[i][0].cuda_event, pev[i][1].cuda_event)])
+        pca([(B.KT["RGB_PCA"], pev[i].start, pev[i].stop)])
     torch.cuda.synchronize()
-    pca_ms = sum(a.elapsed_time(b) for a, b in pev) / args.steps
+    pca_ms = sum(t.elapsed_ms() for t in pev) / args.steps
     aug = B.augment(crop, alpha, eigval, eigvec)
 
     def train_aug(i, timers=()):
@@ -288,11 +284,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        train_aug(step, [(B.KT["S2D"], sev[i][0].cuda_event, sev[i][1].cuda_event)])
+        train_aug(step, [(B.KT["S2D"], sev[i].start, sev[i].stop)])
         step += 1
     torch.cuda.synchronize()
     aug_s = (time.perf_counter() - t0) / args.steps
-    aug_stage_ms = sum(a.elapsed_time(b) for a, b in sev) / args.steps
+    aug_stage_ms = sum(t.elapsed_ms() for t in sev) / args.steps
     del sess, src, pca_ws
 
     # ---------------------------------------------------------------- forward passes
@@ -313,9 +309,9 @@ def main():
             fwd_call()
         fnames = [nm for nm in names if nm.endswith("_FWD") or nm == "S2D"]
         fev = new_events(len(fnames))
-        fwd_call([(B.KT[nm], fev[j][0].cuda_event, fev[j][1].cuda_event) for j, nm in enumerate(fnames)])
+        fwd_call([(B.KT[nm], fev[j].start, fev[j].stop) for j, nm in enumerate(fnames)])
         torch.cuda.synchronize()
-        fwd_kernels[key] = {nm: fev[j][0].elapsed_time(fev[j][1]) for j, nm in enumerate(fnames)}
+        fwd_kernels[key] = {nm: fev[j].elapsed_ms() for j, nm in enumerate(fnames)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):

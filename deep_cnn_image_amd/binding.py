@@ -27,7 +27,8 @@ EXPORTED = (
     "alexnet_tap_count", "alexnet_tap_name", "alexnet_status_string", "alexnet_forward_timed",
     "alexnet_train_step_timed", "alexnet_augment_images", "alexnet_train_step_augmented",
     "alexnet_train_step_augmented_timed", "alexnet_rgb_pca_workspace_bytes", "alexnet_rgb_pca",
-    "alexnet_rgb_pca_timed", "alexnet_train_step_ex", "alexnet_forward_noalloc",
+    "alexnet_rgb_pca_timed", "alexnet_train_step_ex", "alexnet_forward_noalloc", "alexnet_event_create",
+    "alexnet_event_destroy", "alexnet_event_elapsed_ms",
 )
 
 # alexnet_kernel ids (kernel-timing hooks)
@@ -143,6 +144,12 @@ def lib():
     L.alexnet_tap_name.restype = C.c_char_p
     L.alexnet_status_string.argtypes = [C.c_int]
     L.alexnet_status_string.restype = C.c_char_p
+    L.alexnet_event_create.argtypes = [C.c_int32, C.POINTER(vp)]
+    L.alexnet_event_create.restype = C.c_int
+    L.alexnet_event_destroy.argtypes = [vp]
+    L.alexnet_event_destroy.restype = C.c_int
+    L.alexnet_event_elapsed_ms.argtypes = [vp, vp, C.POINTER(C.c_float)]
+    L.alexnet_event_elapsed_ms.restype = C.c_int
     _lib = L
     return L
 
@@ -319,6 +326,22 @@ def alexnet_tap(cfg, mode: int, tap_id: int):
     _check(lib().alexnet_tap(C.byref(cfg), mode, tap_id, C.byref(off), shape, C.byref(dt),
                              C.byref(lay)), "alexnet_tap")
     return off.value, tuple(shape), dt.value, lay.value
+
+
+def alexnet_event_create(timing: bool) -> int:
+    e = C.c_void_p()
+    _check(lib().alexnet_event_create(1 if timing else 0, C.byref(e)), "alexnet_event_create")
+    return int(e.value)
+
+
+def alexnet_event_destroy(event: int) -> None:
+    _check(lib().alexnet_event_destroy(event), "alexnet_event_destroy")
+
+
+def alexnet_event_elapsed_ms(start: int, stop: int) -> float:
+    ms = C.c_float()
+    _check(lib().alexnet_event_elapsed_ms(start, stop, C.byref(ms)), "alexnet_event_elapsed_ms")
+    return float(ms.value)
 
 
 def alexnet_tap_count() -> int:

@@ -628,6 +628,26 @@ int alexnet_tap(const alexnet_cfg* cfg, int mode, int tap_id, size_t* offset, in
   return ALEXNET_OK;
 }
 
+int alexnet_event_create(int32_t timing, void** event) {
+  if (!event) return ALEXNET_E_NULL;
+  *event = nullptr;
+  hipEvent_t e;
+  const unsigned flags = hipEventDisableSystemFence | (timing ? 0u : (unsigned)hipEventDisableTiming);
+  if (hipEventCreateWithFlags(&e, flags) != hipSuccess) return ALEXNET_E_HIP;
+  *event = e;
+  return ALEXNET_OK;
+}
+
+int alexnet_event_destroy(void* event) {
+  if (!event) return ALEXNET_E_NULL;
+  return hipEventDestroy((hipEvent_t)event) == hipSuccess ? ALEXNET_OK : ALEXNET_E_HIP;
+}
+
+int alexnet_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return ALEXNET_E_NULL;
+  return hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop) == hipSuccess ? ALEXNET_OK : ALEXNET_E_HIP;
+}
+
 int alexnet_tap_count(void) { return T_COUNT; }
 const char* alexnet_tap_name(int tap_id) { return tap_name(tap_id); }
 

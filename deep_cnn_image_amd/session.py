@@ -27,18 +27,29 @@ def stream_handle() -> int:
     return int(torch.cuda.current_stream().cuda_stream)
 
 
+def _destroy_event(e) -> None:
+    # also runs at interpreter exit, when the runtime may already be gone
+    if e:
+        try:
+            B.lib().alexnet_event_destroy(e)
+        except Exception:
+            pass
+
+
 class SideStream:
     """A caller-owned second stream and the fork/join events the training
     step uses with it (alexnet_train_step_ex).  The stream has the default
-    priority; the events are created by torch (timing disabled) and made to
-    exist by one record each."""
+    priority; the events come from alexnet_event_create (timing disabled, no
+    system-scope fence: they only order the two streams)."""
 
     def __init__(self, device: str = "cuda:0"):
         self.stream = torch.cuda.Stream(device=device)
-        self.events = [torch.cuda.Event(enable_timing=False) for _ in range(B.SIDE_EVENTS)]
-        for e in self.events:
-            e.record()
-        torch.cuda.synchronize(device)
+        with torch.cuda.device(device):
+            self.events = [B.alexnet_event_create(False) for _ in range(B.SIDE_EVENTS)]
+
+    def __del__(self):
+        for e in getattr(self, "events", ()):
+            _destroy_event(e)
 
     @property
     def handle(self) -> int:
@@ -46,7 +57,24 @@ class SideStream:
 
     @property
     def event_handles(self) -> List[int]:
-        return [int(e.cuda_event) for e in self.events]
+        return list(self.events)
+
+
+class Timer:
+    """A start/stop pair of timing events from alexnet_event_create, for the
+    *_timed calls' timers (no system-scope fence, so the timed span holds the
+    kernel alone)."""
+
+    def __init__(self):
+        self.start = B.alexnet_event_create(True)
+        self.stop = B.alexnet_event_create(True)
+
+    def elapsed_ms(self) -> float:
+        return B.alexnet_event_elapsed_ms(self.start, self.stop)
+
+    def __del__(self):
+        for e in (getattr(self, "start", None), getattr(self, "stop", None)):
+            _destroy_event(e)
 
 
 class Session:

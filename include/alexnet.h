@@ -31,8 +31,9 @@
  *  - All pointers are device pointers unless stated otherwise and must be
  *    16-byte aligned; the workspace must be 256-byte aligned.  The caller owns
  *    every buffer, including the workspace, and every stream and event.  The
- *    library allocates no memory and creates no streams or events; the only
- *    state it keeps between calls is a per-device cache of whether the
+ *    library allocates no memory and creates no streams or events of its
+ *    own (alexnet_event_create makes an event for the caller, who owns it);
+ *    the only state it keeps between calls is a per-device cache of whether the
  *    device is a gfx950 (a fixed fact once read).  Calls are reentrant given
  *    distinct workspaces (and, for alexnet_train_step_ex, distinct side
  *    streams and events).  alexnet_forward_noalloc is the exception: its
@@ -344,6 +345,24 @@ int alexnet_train_step_ex(const alexnet_cfg* cfg, float* const master[16], float
                           int32_t src_w, const int32_t* labels, float lr, float momentum_coef,
                           float weight_decay, uint64_t seed, uint64_t step, float* loss, float* probs, void* ws,
                           size_t ws_bytes, void* stream, const alexnet_exec* ex);
+
+/* Events for ex->events and for kernel timers, created without the
+ * system-scope memory fence that a default HIP event carries: a default event
+ * writes the GPU caches back for the host's sake when it completes, which
+ * idles the GPU for some microseconds at every record and, for a timer,
+ * counts that write-back in the timed kernel.  Kernels of one device see each
+ * other's results across streams without that fence; the host does not, so
+ * these events order device work (stream waits, timing) and do not make
+ * results visible to the host (synchronize the stream for that).
+ *   timing != 0: the event can be timed (alexnet_event_elapsed_ms); else
+ *   timing is disabled.  The caller owns the event and destroys it with
+ *   alexnet_event_destroy.  Host only; creates a HIP event on the current
+ *   device.  Returns ALEXNET_E_NULL for a null pointer, ALEXNET_E_HIP if
+ *   the HIP call fails. */
+int alexnet_event_create(int32_t timing, void** event);
+int alexnet_event_destroy(void* event);
+/* Milliseconds from `start` to `stop`, two completed timing events. */
+int alexnet_event_elapsed_ms(void* start, void* stop, float* ms);
 
 /* Test and diagnostic access to the tensors a call leaves in its workspace.
  * Host only.  For tap `tap_id` of a call in `mode` with `cfg`, returns its

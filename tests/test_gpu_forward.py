@@ -11,7 +11,7 @@ import torch
 
 from deep_cnn_image_amd import binding as B
 from deep_cnn_image_amd import inputs as I
-from deep_cnn_image_amd.session import Session, to_device
+from deep_cnn_image_amd.session import Session, Timer, stream_handle, to_device
 
 from gpu_helpers import (DEV, TOL_BF16, TOL_F32, TOL_F32_OUT, TOL_LAYER_BF16, flat, host, nchw,
                          rel_l2, say)
@@ -178,6 +178,27 @@ def test_forward_is_deterministic():
     for k in FWD_TAPS + ("probs",):
         assert torch.equal(a[k].view(torch.uint8) if a[k].dtype != torch.uint8 else a[k],
                            b[k].view(torch.uint8) if b[k].dtype != torch.uint8 else b[k]), k
+
+
+def test_timers_time_their_kernels_and_change_no_result():
+    """Timers from alexnet_event_create around three kernels of a forward
+    pass: each span is positive and below a second, and the probabilities are
+    bit-identical to those of the untimed call."""
+    syn = I.workload_inputs("bf16_batch128", batch=8)
+    sess = Session(8, 1, B.BF16, B.MODE_FORWARD, DEV)
+    params = sess.upload_params(syn.weights, syn.biases)
+    x = to_device(syn.x, B.BF16, DEV)
+    plain = sess.forward(params, x).clone()
+    names = ("S2D", "CONV2_FWD", "FC6_FWD")
+    timers = [Timer() for _ in names]
+    probs = torch.empty_like(plain)
+    B.alexnet_forward_timed(sess.cfg, params, x, probs, sess.ws, sess.ws_bytes, stream_handle(),
+                            [(B.KT[nm], t.start, t.stop) for nm, t in zip(names, timers)])
+    torch.cuda.synchronize()
+    ms = [t.elapsed_ms() for t in timers]
+    say(f"[gpu] timed spans (ms) {dict(zip(names, ms))}")
+    assert all(0.0 < m < 1000.0 for m in ms), ms
+    assert torch.equal(probs, plain)
 
 
 # ---------------------------------------------------------------- full-size, sampled images
