@@ -79,10 +79,11 @@ def kernel_work(kt, n, groups, train=True):
         "POOLLRN2_BWD": (e + 1) * act["13x256"] + 2 * e * act["27x256"] + (4 * n * 27 * 256 if train else 0),
         "POOL5_FWD": e * act["13x256"] + (e + 1) * act["6x256"],
         "POOL5_BWD": (e + 1) * act["6x256"] + 2 * e * act["13x256"],
-        # bias gradients: layers 1 and 2 from their per-row fp32 sums, the other
-        # layers' output gradients read once (the block partials and the 22 B
-        # per bias of the update are below 0.2%)
-        "BIAS": 4 * n * (55 * 96 + 27 * 256) + e * (2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
+        # bias gradients of layers 3-8: their output gradients read once (the
+        # block partials and the 22 B per bias of the update are below 0.2%)
+        "BIAS": e * (2 * n * 13 * 13 * 384 + act["13x256"] + n * (2 * 4096 + 1000)),
+        # layers 1 and 2 from their per-row fp32 sums
+        "BIAS12": 4 * n * (55 * 96 + 27 * 256),
     }
     return "hbm", float(table[kt])
 

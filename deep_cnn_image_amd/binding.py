@@ -37,7 +37,7 @@ KERNELS = (
     "LRNPOOL2_FWD", "POOL5_FWD", "FC6_FWD", "FC7_FWD", "FC8_FWD", "FC8_DGRAD", "FC7_DGRAD",
     "FC6_DGRAD", "FC8_WGRAD", "FC7_WGRAD", "FC6_WGRAD", "POOL5_BWD", "CONV5_WGRAD", "CONV4_WGRAD",
     "CONV3_WGRAD", "CONV2_WGRAD", "CONV1_WGRAD", "CONV5_DGRAD", "CONV4_DGRAD", "CONV3_DGRAD",
-    "CONV2_DGRAD", "POOLLRN2_BWD", "POOLLRN1_BWD", "BIAS", "RGB_PCA",
+    "CONV2_DGRAD", "POOLLRN2_BWD", "POOLLRN1_BWD", "BIAS", "RGB_PCA", "BIAS12",
 )
 KT = {name: i + 1 for i, name in enumerate(KERNELS)}
 

@@ -265,6 +265,32 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
                       ALEXNET_KT_CONV4_WGRAD, ALEXNET_KT_CONV5_WGRAD};
   const int ktd[5] = {0, ALEXNET_KT_CONV2_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV4_DGRAD,
                       ALEXNET_KT_CONV5_DGRAD};
+  // Bias gradients with their SGD, in two passes over disjoint parts of the
+  // column-sum scratch.  Layers 3-8 read their stored output gradients; all
+  // of them are complete once layer 3's is, so that pass follows layer 3's
+  // weight gradient (on the side stream, beside the rest of the backward
+  // pass, when there is one).  Layers 1 and 2 start from the per-row sums
+  // their pool/LRN backward leaves; that pass, with the batch-mean loss, ends
+  // the step.
+  BiasJob bias_jobs[8];
+  {
+    const int dys[8] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5, T_DFC6, T_DFC7, T_DLOGITS};
+    for (int i = 0; i < 8; ++i) {
+      const bool rows_f32 = i < 2;
+      const int64_t rows = rows_f32 ? (int64_t)N * net.conv[i].Ho
+                           : i < 5  ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo
+                                    : N;
+      const void* src = rows_f32 ? (const void*)at(ws, p.bias_rows[i]) : tp(ws, p, dys[i]);
+      bias_jobs[i] = BiasJob{src, rows, (int)net.bcount[i], gb(i), master[2 * i + 1], momentum[2 * i + 1],
+                             work[2 * i + 1], rows_f32};
+    }
+  }
+  float* const bias_cs12 = cs + bias_grad_scratch_bytes(bias_jobs + 2, 6) / sizeof(float);
+  auto bias_pass = [&](const BiasJob* jobs, int first, int n, float* scratch, const float* rowloss,
+                       hipStream_t s, const KTimer* kt) {
+    return bias_grads_sgd(dt, jobs + first, n, hy, scratch, rowloss, N, loss, s, kt);
+  };
+
   // The conv weight gradients (with their SGD update) need nothing from the
   // data-gradient chain after their own output gradient, and nothing in the
   // chain reads what they write: given a side stream, each is forked onto it
@@ -283,6 +309,7 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
     const SgdTarget u{master[2 * i], momentum[2 * i], work[2 * i], hy};
     hipStream_t sw = side.fork();
     HIPCHK(conv_wgrad(dt, s, tp(ws, p, dz[i]), tp(ws, p, xin[i]), part, p.part_bytes, gw(i), &u, sw, T(ktw[i])));
+    if (i == 2) HIPCHK(bias_pass(bias_jobs, 2, 6, cs, nullptr, sw, T(ALEXNET_KT_BIAS)));
     HIPCHK(conv_dgrad(dt, s, tp(ws, p, dz[i]), at(ws, p.wt[i]), mask[i] >= 0 ? tp(ws, p, mask[i]) : nullptr,
                       tp(ws, p, din[i]), part, p.part_bytes, st, T(ktd[i])));
   }
@@ -309,23 +336,8 @@ int enqueue_backward(const Plan& p, void* const* work, float* const* master, flo
     HIPCHK(conv1_wgrad(dt, N, tp(ws, p, T_DCONV1), at(ws, p.xs2d), part, p.part_bytes, gw(0), &u, sw,
                        T(ALEXNET_KT_CONV1_WGRAD)));
   }
-  // bias gradients of all eight layers, and their SGD update
-  {
-    // layers 1 and 2: the per-row sums left by their pool/LRN backward
-    const int dys[8] = {T_DCONV1, T_DCONV2, T_DCONV3, T_DCONV4, T_DCONV5, T_DFC6, T_DFC7, T_DLOGITS};
-    BiasJob jobs[8];
-    for (int i = 0; i < 8; ++i) {
-      const bool rows_f32 = i < 2;
-      const int64_t rows = rows_f32 ? (int64_t)N * net.conv[i].Ho
-                           : i < 5  ? (int64_t)N * net.conv[i].Ho * net.conv[i].Wo
-                                    : N;
-      const void* src = rows_f32 ? (const void*)at(ws, p.bias_rows[i]) : tp(ws, p, dys[i]);
-      jobs[i] = BiasJob{src, rows, (int)net.bcount[i], gb(i), master[2 * i + 1], momentum[2 * i + 1],
-                        work[2 * i + 1], rows_f32};
-    }
-    HIPCHK(bias_grads_sgd(dt, jobs, 8, hy, cs, (const float*)tp(ws, p, T_ROWLOSS), N, loss, st,
-                          T(ALEXNET_KT_BIAS)));
-  }
+  // bias gradients of all eight layers, and their SGD update, in two passes
+  HIPCHK(bias_pass(bias_jobs, 0, 2, bias_cs12, (const float*)tp(ws, p, T_ROWLOSS), st, T(ALEXNET_KT_BIAS12)));
   return ALEXNET_OK;
 }
 

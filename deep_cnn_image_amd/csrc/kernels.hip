@@ -2713,9 +2713,11 @@ __device__ __forceinline__ void colsum_block(const T* __restrict__ x, int64_t ro
 // gradient dy[rows][C] over its N*H*W rows, followed by the SGD update of the
 // bias, in two launches:
 //   1. every (layer, row block, column tile) block writes one partial row;
-//   2. one wave per bias element sums that element's partials in block order,
-//      stores the gradient and updates the bias (fp32 master, momentum, and
-//      working copy).
+//   2. one workgroup per 32 consecutive bias elements of a layer sums their
+//      partials (eight row groups, each over every eighth partial row in
+//      order, then the eight group sums in order), stores the gradients and
+//      updates the biases (fp32 master, momentum, and working copy).  A row
+//      group reads 128 contiguous bytes of each partial row.
 struct BiasArgs1 {
   const void* x[BIAS_MAX];
   float* part[BIAS_MAX];
@@ -2730,14 +2732,15 @@ struct BiasArgs2 {
   float* w[BIAS_MAX];
   float* v[BIAS_MAX];
   void* wb[BIAS_MAX];
-  int nb[BIAS_MAX];
-  int cstart[BIAS_MAX + 1];   // first bias element of each layer
+  int nb[BIAS_MAX], C[BIAS_MAX];
+  int gstart[BIAS_MAX + 1];   // first workgroup of each layer (32 bias elements per workgroup)
   int n;
   float lr, mom, wdlr;
-  const float* rowloss;       // optional: loss = mean of rowloss[0..nrow), by one more wave
+  const float* rowloss;       // optional: loss = mean of rowloss[0..nrow), by one more workgroup
   int nrow;
   float* loss;
 };
+constexpr int BIAS_COLS = 32, BIAS_RG = TPB / BIAS_COLS;
 
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_bias_colsum(BiasArgs1 a) {
@@ -2755,31 +2758,45 @@ __global__ void __launch_bounds__(TPB) k_bias_colsum(BiasArgs1 a) {
 
 template <typename T>
 __global__ void __launch_bounds__(TPB) k_bias_sgd(BiasArgs2 a) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
-  if (e == a.cstart[a.n] && a.rowloss) {
+  const int bid = blockIdx.x, t = threadIdx.x;
+  if (bid == a.gstart[a.n]) {
+    // the batch-mean loss, by the first wave of the last workgroup
+    if (!a.rowloss || t >= 64) return;
     float s = 0.f;
-    for (int r = lane; r < a.nrow; r += 64) s += a.rowloss[r];
+    for (int r = t; r < a.nrow; r += 64) s += a.rowloss[r];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0) *a.loss = s / (float)a.nrow;
+    if (t == 0) *a.loss = s / (float)a.nrow;
     return;
   }
-  if (e >= a.cstart[a.n]) return;
   int j = 0;
 #pragma unroll
-  for (int q = 1; q < BIAS_MAX; ++q) j += (q < a.n && e >= a.cstart[q]) ? 1 : 0;
-  const int col = e - a.cstart[j], C = a.cstart[j + 1] - a.cstart[j];
-  const float* part = a.part[j];
+  for (int q = 1; q < BIAS_MAX; ++q) j += (q < a.n && bid >= a.gstart[q]) ? 1 : 0;
+  const int C = a.C[j], nb = a.nb[j];
+  const int cl = t % BIAS_COLS, rg = t / BIAS_COLS;
+  const int col = (bid - a.gstart[j]) * BIAS_COLS + cl;
+  const bool on = col < C;
+  const float* part = a.part[j] + (on ? col : 0);
   float s = 0.f;
-#pragma unroll 4
-  for (int b = lane; b < a.nb[j]; b += 64) s += part[(int64_t)b * C + col];
+  int b = rg;
+  for (; b + 7 * BIAS_RG < nb; b += 8 * BIAS_RG) {
+    float q[8];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (lane == 0) {
-    a.grad[j][col] = s;
+    for (int u = 0; u < 8; ++u) q[u] = part[(int64_t)(b + u * BIAS_RG) * C];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += q[u];
+  }
+  for (; b < nb; b += BIAS_RG) s += part[(int64_t)b * C];
+  __shared__ float sh[BIAS_RG][BIAS_COLS];
+  sh[rg][cl] = s;
+  __syncthreads();
+  if (rg == 0 && on) {
+    float g = 0.f;
+#pragma unroll
+    for (int r = 0; r < BIAS_RG; ++r) g += sh[r][cl];
+    a.grad[j][col] = g;
     float w = a.w[j][col], v = a.v[j][col];
-    sgd_elem(w, v, s, a.mom, a.wdlr, a.lr);
+    sgd_elem(w, v, g, a.mom, a.wdlr, a.lr);
     a.w[j][col] = w;
     a.v[j][col] = v;
     if (sizeof(T) == 2) static_cast<bf16*>(a.wb[j])[col] = f2bf(w);
@@ -2802,7 +2819,7 @@ hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& 
   a2.nrow = nrow;
   a2.loss = loss;
   a1.n = a2.n = n;
-  int blocks = 0, cols = 0;
+  int blocks = 0, groups = 0;
   float* part = scratch;
   for (int j = 0; j < n; ++j) {
     const BiasJob& b = jobs[j];
@@ -2823,22 +2840,23 @@ hipError_t bias_grads_sgd(DType dt, const BiasJob* jobs, int n, const SgdHyper& 
     a2.v[j] = b.v;
     a2.wb[j] = b.wb;
     a2.nb[j] = nb;
-    a2.cstart[j] = cols;
-    cols += b.C;
+    a2.C[j] = b.C;
+    a2.gstart[j] = groups;
+    groups += cdiv(b.C, BIAS_COLS);
     part += (size_t)nb * b.C;
   }
   a1.bstart[n] = blocks;
-  a2.cstart[n] = cols;
+  a2.gstart[n] = groups;
   a2.lr = hy.lr;
   a2.mom = hy.mom;
   a2.wdlr = hy.wdlr;
   rec_start(kt, st);
   if (dt == BF16) {
     hipLaunchKernelGGL((k_bias_colsum<bf16>), dim3(blocks), dim3(TPB), 0, st, a1);
-    hipLaunchKernelGGL((k_bias_sgd<bf16>), dim3(cdiv(cols + 1, TPB / 64)), dim3(TPB), 0, st, a2);
+    hipLaunchKernelGGL((k_bias_sgd<bf16>), dim3(groups + 1), dim3(TPB), 0, st, a2);
   } else {
     hipLaunchKernelGGL((k_bias_colsum<float>), dim3(blocks), dim3(TPB), 0, st, a1);
-    hipLaunchKernelGGL((k_bias_sgd<float>), dim3(cdiv(cols + 1, TPB / 64)), dim3(TPB), 0, st, a2);
+    hipLaunchKernelGGL((k_bias_sgd<float>), dim3(groups + 1), dim3(TPB), 0, st, a2);
   }
   rec_stop(kt, st);
   return hipGetLastError();

@@ -269,8 +269,12 @@ typedef enum {
   ALEXNET_KT_CONV5_DGRAD, ALEXNET_KT_CONV4_DGRAD, ALEXNET_KT_CONV3_DGRAD, ALEXNET_KT_CONV2_DGRAD,
   ALEXNET_KT_POOLLRN2_BWD,     /* pool2, LRN2 and ReLU2 backward (one kernel)    */
   ALEXNET_KT_POOLLRN1_BWD,     /* pool1, LRN1 and ReLU1 backward                 */
-  ALEXNET_KT_BIAS,             /* all bias gradients + their SGD (two launches)  */
+  ALEXNET_KT_BIAS,             /* bias gradients of layers 3-8 + their SGD (two
+                                  launches)                                      */
   ALEXNET_KT_RGB_PCA,          /* alexnet_rgb_pca: moments + eigen-decomposition */
+  ALEXNET_KT_BIAS12,           /* bias gradients of layers 1 and 2 from their row
+                                  sums + their SGD, and the batch-mean loss (two
+                                  launches)                                      */
   ALEXNET_KT_COUNT
 } alexnet_kernel;
 
