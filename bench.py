@@ -137,7 +137,43 @@ def parse():
                     help="time the training step only (for short profiled runs) and print its kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--cache-probe", action="store_true",
+                    help="only time a streaming read of FC6's weight-matrix size after the last-level "
+                         "cache holds clean or dirty lines, and print that")
     return ap.parse_args()
+
+
+def cache_probe(dev):
+    """Streaming-read time of a 75.5 MB bf16 matrix (the size of FC6's
+    weights, 4096 x 9216) by a plain reduction, after a 400 MB read has filled
+    the last-level cache with clean lines and after a 400 MB write has filled it
+    with dirty ones, and with the matrix itself just read (cached).  Medians of
+    10 reps with torch events, whose span includes a cache write-back fence of a
+    few microseconds; the kernel trace of the same run has the kernel alone."""
+    import torch
+    m = torch.ones(4096, 9216, dtype=torch.bfloat16, device=dev)
+    big = torch.empty(100 << 20, dtype=torch.float32, device=dev)
+    res = {}
+    for state in ("after_400MB_read", "after_400MB_write", "after_reading_itself"):
+        ts = []
+        for _ in range(10):
+            if state == "after_400MB_read":
+                big.sum()
+            elif state == "after_400MB_write":
+                big.fill_(1.0)
+            else:
+                big.fill_(1.0)
+                m.sum(dtype=torch.float32)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            m.sum(dtype=torch.float32)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        med = sorted(ts)[len(ts) // 2]
+        res[state] = {"us": round(med, 2), "GB/s": round(m.numel() * 2 / med / 1e3, 1)}
+    return {"cache_probe": res, "bytes": m.numel() * 2}
 
 
 def main():
@@ -156,6 +192,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.cache_probe:
+        print(json.dumps(cache_probe(dev)))
+        return
     B.lib()
     h = I.TRAIN_HYPER
 
