@@ -161,20 +161,35 @@ __device__ __forceinline__ void s2d_block(int blk, const T* __restrict__ x, T* _
     *reinterpret_cast<uint4*>(rows + r * RS + ch * V) = q;
   }
   __syncthreads();
+  // An output chunk holds V consecutive values c*16 + dh*4 + dw of one block:
+  // one channel, V / 4 consecutive rows dh (two for bf16, one for fp32) and
+  // the four columns of each, so row base, shift, direction and bounds are
+  // worked out once per row rather than per value.
+  static_assert(V % 4 == 0 && S2D_C % V == 0, "an output chunk spans whole 4-column runs");
   T* out = xs + (int64_t)blk * S2D_B * S2D_C;
   for (int i = threadIdx.x; i < S2D_B * S2D_C / V; i += TPB) {
     const int bw = (i * V) / S2D_C, q0 = i * V - bw * S2D_C;
+    const int c = q0 >> 4, dh0 = (q0 >> 2) & 3;
+    const int ncol = min(4, 227 - 4 * bw);   // columns inside the image
+    float sh = 0.f;
+    if (kind == SRC_AUGMENT) sh = c == 0 ? rgb[0] : c == 1 ? rgb[1] : rgb[2];
     T e[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int q = q0 + j, c = q >> 4, dh = (q >> 2) & 3, dw = q & 3;
-      const int r = c * 4 + dh, yc = 4 * bh + dh, xc = 4 * bw + dw;
-      T v = T(0);
-      if (yc < 227 && xc < 227) {
-        v = rows[r * RS + shift[r] + (flip ? 226 - xc : xc)];
-        if (kind == SRC_AUGMENT) v = aug_value(v, rgb[c]);
+    for (int h = 0; h < V / 4; ++h) {
+      const int dh = dh0 + h, r = c * 4 + dh;
+      const bool rowok = 4 * bh + dh < 227;
+      // column xc of the view is at p[dw * stp]: xc = 4 bw + dw, mirrored 226 - xc
+      const T* p = rows + r * RS + shift[r] + (flip ? 226 - 4 * bw : 4 * bw);
+      const int stp = flip ? -1 : 1;
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        T v = T(0);
+        if (rowok && dw < ncol) {
+          v = p[dw * stp];
+          if (kind == SRC_AUGMENT) v = aug_value(v, sh);
+        }
+        e[h * 4 + dw] = v;
       }
-      e[j] = v;
     }
     *reinterpret_cast<uint4*>(out + i * V) = pack_u4(e);
   }
