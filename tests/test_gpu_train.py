@@ -440,6 +440,17 @@ def test_full_batch128_train_step(orc):
     hs2 = hostify({k: r["taps"][k] for k in ("dconv2", "pool1", "din2", "conv2", "dlrn2")}, rows)
     e["din2[rows]"] = rel_l2(hs2["din2"], orc.conv2d_bwd_data(hs2["dconv2"], W[1], hs2["pool1"].shape, 1, 2))
     e["dconv2[rows]"] = rel_l2(hs2["dconv2"], orc.lrn_bwd(hs2["conv2"], hs2["dlrn2"]) * (hs2["conv2"] > 0))
+    # every bias gradient in full (paper-graph-ui "Training Procedure Details":
+    # the update of every parameter; a bias's gradient is the sum over images
+    # and pixels of its layer's output gradient): column sums, in float64, of
+    # the stored output gradients.  Layers 3-8 are summed beside the data
+    # gradients on the side stream, layers 1 and 2 from the pool/LRN
+    # backward's row sums.
+    for i, k in enumerate(("dconv1", "dconv2", "dconv3", "dconv4", "dconv5", "dfc6", "dfc7", "dlogits")):
+        g = host(r["taps"][k]).astype(np.float64)
+        c = r["gb"][i].size   # channels are innermost: NHWC conv taps, [N][C][1][1] FC taps
+        e[f"gb{i + 1}(all)"] = rel_l2(r["gb"][i], g.reshape(-1, c).sum(0))
+        del g
     say("[gpu] bs128 isolated backward rel-L2:", {k: f"{v:.2e}" for k, v in e.items()})
     for k, v in e.items():
         limit = TOL_F32_OUT if k[:2] in ("gw", "gb") else TOL_LAYER_BF16
