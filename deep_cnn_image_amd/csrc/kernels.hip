@@ -1940,7 +1940,8 @@ __device__ __forceinline__ void lrn_bwd_unit(const T* apx, const T* gpx, int c0,
 // LRN followed by the overlapping 3x3 / stride-2 max-pool with argmax, fused:
 // the LRN output is kept only in LDS (rounded to T exactly as a stored tensor
 // would be), so pooled values and argmax equal those of the two separate
-// steps.  One workgroup per (image n, pair of pooled rows i0 = 2 p, i0 + 1)
+// steps.  One workgroup per (image n, pair of pooled rows i0 = 2 p, i0 + 1,
+// channel group: see lrnpool_cg)
 // over input rows 2 i0 .. 2 i0 + 4 (Hin = 2 Ho + 1; the last pair of an odd Ho
 // has one pooled row and three input rows), one contiguous run of NHWC:
 //   1. the run is copied into LDS with direct-to-LDS loads (one wait);
@@ -1977,14 +1978,28 @@ __device__ __forceinline__ void store8(T* p, const Packed8<T>& o) {
   for (int i = 0; i < (int)(sizeof(T) / 2); ++i) reinterpret_cast<uint4*>(p)[i] = o.q[i];
 }
 
+// Channels per workgroup of the fused LRN/pool (CG of the layer's C): a layer
+// whose five-row tile of all channels leaves room for fewer than three
+// workgroups per CU is split into channel groups of 128, each staged with an
+// 8-channel halo on both sides (the LRN window reaches H <= 4 channels), so
+// that four fit: layer 2 (27 x 256) 69 KB -> 39 KB.
+template <typename T, int Win, int C>
+constexpr int lrnpool_cg() {
+  return 160 * 1024 / (5 * Win * C * (int)sizeof(T)) < 3 && C % 128 == 0 && C > 128 ? 128 : C;
+}
+
 // LRN of rows 0 .. nrows-1 of the LDS tile, in place: every thread computes
 // its (row, column, 8-channel) units from LDS into packed registers (a unit
 // past the end recomputes the last one, so no thread branches around the
-// arithmetic), then, after a barrier, writes them back.
+// arithmetic), then, after a barrier, writes them back.  The tile holds the
+// workgroup's channels cg0 .. cg0 + CG - 1 of each pixel at a pixel stride of
+// PS values, channel c at offset c - cg0 + HALO (HALO = 8 with channel groups,
+// else 0); lrn_unit's bounds use the layer's C.
 template <typename T, int H, bool B075, int Win, int C>
-__device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, T* __restrict__ dbg, size_t dbg_row0, int own_last,
-                                              float k, float alpha, float beta) {
-  constexpr int cpp = C / 8, rowu = Win * cpp;
+__device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, int cg0, T* __restrict__ dbg, size_t dbg_row0,
+                                              int own_last, float k, float alpha, float beta) {
+  constexpr int CG = lrnpool_cg<T, Win, C>(), HALO = CG < C ? 8 : 0, PS = CG + 2 * HALO;
+  constexpr int cpp = CG / 8, rowu = Win * cpp;
   constexpr int UPT = (5 * rowu + LRNPOOL_TPB - 1) / LRNPOOL_TPB;
   const int tid = threadIdx.x;
   const int units = nrows * rowu;
@@ -1992,9 +2007,9 @@ __device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, T* __restrict_
 #pragma unroll
   for (int t = 0; t < UPT; ++t) {
     const int u = min(tid + t * LRNPOOL_TPB, units - 1);
-    const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
+    const int pix = u / cpp, c0 = cg0 + (u - pix * cpp) * 8;
     float r[8];
-    lrn_unit<T, H, B075, C>(rows + pix * C, c0, k, alpha, beta, r);
+    lrn_unit<T, H, B075, C>(rows + pix * PS + HALO - cg0, c0, k, alpha, beta, r);
     o[t] = pack8<T>(r);
   }
   __syncthreads();
@@ -2002,10 +2017,10 @@ __device__ __forceinline__ void lrn_pool_rows(T* rows, int nrows, T* __restrict_
   for (int t = 0; t < UPT; ++t) {
     const int u = tid + t * LRNPOOL_TPB;
     if (u < units) {
-      const int pix = u / cpp, c0 = (u - pix * cpp) * 8;
-      store8<T>(rows + pix * C + c0, o[t]);
+      const int pix = u / cpp, cl = (u - pix * cpp) * 8;
+      store8<T>(rows + pix * PS + HALO + cl, o[t]);
       const int rr = pix / Win;
-      if (dbg && (rr < 4 || own_last)) store8<T>(dbg + dbg_row0 + (size_t)pix * C + c0, o[t]);
+      if (dbg && (rr < 4 || own_last)) store8<T>(dbg + dbg_row0 + (size_t)pix * C + cg0 + cl, o[t]);
     }
   }
 }
@@ -2015,39 +2030,58 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
                                                           uint8_t* __restrict__ arg, T* __restrict__ dbg,
                                                           float k, float alpha, float beta) {
   constexpr int Hin = Win, Ho = (Win - 1) / 2, Wo = Ho, NP = (Ho + 1) / 2;
-  static_assert(C % 8 == 0 && Hin == 2 * Ho + 1, "fused LRN/pool geometry");
-  constexpr int LDS_BYTES = ((5 * Win * C * (int)sizeof(T) + 1023) / 1024) * 1024;
+  constexpr int CG = lrnpool_cg<T, Win, C>(), NG = C / CG, HALO = CG < C ? 8 : 0, PS = CG + 2 * HALO;
+  static_assert(C % 8 == 0 && Hin == 2 * Ho + 1 && C % CG == 0, "fused LRN/pool geometry");
+  constexpr int LDS_BYTES = ((5 * Win * PS * (int)sizeof(T) + 1023) / 1024) * 1024;
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   T* rows = reinterpret_cast<T*>(lds);
   const int nb = gridDim.x, xcd = blockIdx.x & 7, q = nb >> 3, rq = nb & 7;
   const int b = xcd * q + (xcd < rq ? xcd : rq) + (blockIdx.x >> 3);
-  const int n = b / NP, i0 = (b - n * NP) * 2;
+  const int bp = b / NG, cg0 = (b - bp * NG) * CG;
+  const int n = bp / NP, i0 = (bp - n * NP) * 2;
   const int npool = min(2, Ho - i0), nrows = 2 * npool + 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int cpp = C >> 3;
   const size_t img = (size_t)Hin * Win * C;
   // 1. input rows 2 i0 .. 2 i0 + nrows - 1 -> LDS (1 KB per wave instruction; past the image reads as zero)
   {
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a + n * img, (uint32_t)(img * sizeof(T)));
     const uint32_t base = (uint32_t)((size_t)2 * i0 * Win * C * sizeof(T));
-    const int nins = (nrows * Win * C * (int)sizeof(T) + 1023) / 1024;
-    for (int j = wave; j < nins; j += LRNPOOL_TPB / 64)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
-                                               (int)(base + j * 1024 + lane * 16), 0, 0, 0);
+    if constexpr (NG == 1) {
+      // the rows are one contiguous run of NHWC
+      const int nins = (nrows * Win * C * (int)sizeof(T) + 1023) / 1024;
+      for (int j = wave; j < nins; j += LRNPOOL_TPB / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
+                                                 (int)(base + j * 1024 + lane * 16), 0, 0, 0);
+    } else {
+      // each pixel's PS channels cg0 - 8 .. cg0 + CG + 7 as 16-byte granules,
+      // laid out one after the other; a granule before the image's first
+      // value (wrapped offset) or past its end reads as zero, and halo
+      // channels of a neighbouring pixel are read but never used
+      constexpr int GPP = PS * (int)sizeof(T) / 16;   // granules per pixel
+      const int ng = nrows * Win * GPP, nins = (ng + 63) / 64;
+      for (int j = wave; j < nins; j += LRNPOOL_TPB / 64) {
+        const int g = min(j * 64 + lane, ng - 1);      // lanes past the end fetch the last granule again, into the tile's padding
+        const int pix = g / GPP, gi = g - pix * GPP;
+        const int64_t off = (int64_t)base + ((int64_t)pix * C + cg0 - HALO) * (int)sizeof(T) + gi * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + j * 1024), 16,
+                                                 (int)(uint32_t)off, 0, 0, 0);
+      }
+    }
     wait_vmcnt<0>();
     __syncthreads();
   }
-  // 2. LRN in place, rows 0..2 then 3..4
+  // 2. LRN in place
   const size_t dbg_row0 = ((size_t)n * Hin + 2 * i0) * Win * C;
   const int own_last = 2 * i0 + nrows == Hin;
-  lrn_pool_rows<T, H, B075, Win, C>(rows, nrows, dbg, dbg_row0, own_last, k, alpha, beta);
+  lrn_pool_rows<T, H, B075, Win, C>(rows, nrows, cg0, dbg, dbg_row0, own_last, k, alpha, beta);
   __syncthreads();
   // 3. pool: pooled row i0 + ii from LDS rows 2 ii .. 2 ii + 2, columns 2j .. 2j+2
+  constexpr int cpp = CG >> 3;
   for (int u = tid; u < npool * Wo * cpp; u += LRNPOOL_TPB) {
     const int ii = u / (Wo * cpp), ju = u - ii * (Wo * cpp);
-    const int j = ju / cpp, c0 = (ju - j * cpp) * 8;
-    const T* px = rows + ((2 * ii) * Win + 2 * j) * C + c0;
+    const int j = ju / cpp, cl = (ju - j * cpp) * 8, c0 = cg0 + cl;
+    const T* px = rows + ((2 * ii) * Win + 2 * j) * PS + HALO + cl;
     const size_t og = (((size_t)n * Ho + i0 + ii) * Wo + j) * C + c0;
     uint32_t bi[8];
     if constexpr (std::is_same<T, bf16>::value) {
@@ -2055,7 +2089,7 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
 #pragma unroll
       for (int d = 0; d < 9; ++d) {
         const int dy = d / 3, dx = d % 3;
-        const uint4 qv = *reinterpret_cast<const uint4*>(px + (dy * Win + dx) * C);
+        const uint4 qv = *reinterpret_cast<const uint4*>(px + (dy * Win + dx) * PS);
         const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
         const uint32_t code = 15u - (uint32_t)d;
 #pragma unroll
@@ -2079,7 +2113,7 @@ __global__ void __launch_bounds__(LRNPOOL_TPB) k_lrn_pool(const T* __restrict__ 
 #pragma unroll
       for (int d = 1; d < 9; ++d) {
         const int dy = d / 3, dx = d % 3;
-        Pack8<T>::load(px + (dy * Win + dx) * C, v);
+        Pack8<T>::load(px + (dy * Win + dx) * PS, v);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (v[e] > best[e]) { best[e] = v[e]; bi[e] = d; }
@@ -2281,8 +2315,8 @@ struct LrnPoolFn {
   const void* a; void* y; uint8_t* arg; void* dbg; int N; float k, alpha, beta; hipStream_t st;
   template <int H, bool B075>
   hipError_t operator()() const {
-    constexpr int Ho = (Win - 1) / 2;
-    hipLaunchKernelGGL((k_lrn_pool<T, H, B075, Win, C>), dim3(N * ((Ho + 1) / 2)), dim3(LRNPOOL_TPB), 0, st,
+    constexpr int Ho = (Win - 1) / 2, NG = C / lrnpool_cg<T, Win, C>();
+    hipLaunchKernelGGL((k_lrn_pool<T, H, B075, Win, C>), dim3(N * ((Ho + 1) / 2) * NG), dim3(LRNPOOL_TPB), 0, st,
                        (const T*)a,
                        (T*)y, arg, (T*)dbg, k, alpha, beta);
     return hipGetLastError();
