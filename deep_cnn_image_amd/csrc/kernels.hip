@@ -1941,10 +1941,12 @@ __device__ __forceinline__ void lrn_bwd_unit(const T* apx, const T* gpx, int c0,
 // the LRN output is kept only in LDS (rounded to T exactly as a stored tensor
 // would be), so pooled values and argmax equal those of the two separate
 // steps.  One workgroup per (image n, pair of pooled rows i0 = 2 p, i0 + 1,
-// channel group: see lrnpool_cg)
-// over input rows 2 i0 .. 2 i0 + 4 (Hin = 2 Ho + 1; the last pair of an odd Ho
-// has one pooled row and three input rows), one contiguous run of NHWC:
-//   1. the run is copied into LDS with direct-to-LDS loads (one wait);
+// channel group: see lrnpool_cg) over input rows 2 i0 .. 2 i0 + 4 (Hin =
+// 2 Ho + 1; the last pair of an odd Ho has one pooled row and three input
+// rows):
+//   1. those rows (one contiguous run of NHWC; with channel groups, each
+//      pixel's group and halo) are copied into LDS with direct-to-LDS loads
+//      (one wait);
 //   2. each thread normalises its (row, column, 8-channel) units from LDS into
 //      registers, packed as stored, and, after a barrier, writes them back in
 //      place;
